@@ -1,0 +1,6 @@
+"""CPU oracle for Sketch Attention compression -- test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package.  It shares no code with the HIP library or its binding.
+"""
+from .sa_oracle import affinity, assignment, sketch_user, sketch_batch, fold_reference  # noqa: F401
