@@ -1,0 +1,215 @@
+"""Benchmark of Sketch Attention compression on one MI355X.
+
+A step is one sa_compress_batch call over one batch of synthetic histories:
+fold-free fused pass (affinity, prototype-axis softmax, aggregation) plus the
+split-n reduction, i.e. the whole cache-miss path of the SequenceO1 page
+(section 2.4) for that batch.  Inputs are resident in HBM before timing
+starts; the batch is rotated over several copies whose total size exceeds
+the 256 MB Infinity Cache, so X is read from HBM.
+
+Default workload: 4 users x n = 100000 behaviours, d = 128, k = 256
+prototypes, bfloat16 inputs with float32 accumulation.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+MALL_BYTES = 256 * 2 ** 20
+METRIC = "history behaviors/sec compressed (n=100K,k=256,d=128); % bf16 MFMA/HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(k: int, d: int, rows: int) -> float:
+    """Affinity plus aggregation, 2kd + 2kd per history row (softmax and fold excluded)."""
+    return 4.0 * k * d * rows
+
+
+def algorithmic_bytes(rows: int, users: int, k: int, d: int, elem: int) -> float:
+    """X read once plus the float32 sketches written once."""
+    return float(rows) * d * elem + 4.0 * users * k * d
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the fp64 CPU oracle on whole users of the workload until about budget_s seconds."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import sa_oracle
+
+    rows = 0
+    users = 0
+    t0 = time.perf_counter()
+    for u in range(wl.num_users):
+        sa_oracle.sketch_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau)
+        rows += int(wl.offsets[u + 1] - wl.offsets[u])
+        users += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {
+        "value": rows / dt if dt > 0 else None,
+        "unit": "behaviors/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{users} of {wl.num_users} users ({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s",
+    }
+
+
+def copy_calibration(steps: int) -> None:
+    """Plain device-to-device copies of known size, for scaling HBM byte counters."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_dispatch": nbytes, "copy_bytes_written_per_dispatch": nbytes,
+                      "dispatches": steps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long", choices=["tiny", "recent", "long", "many_proto", "ragged"])
+    ap.add_argument("--users", type=int, default=None, help="change the number of users (same per-user shape)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true", help="run plain copies only (counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return 0
+
+    from sketch_attention_amd import SketchAttention, binding
+    from sketch_attention_amd import workloads
+
+    t_gen = time.perf_counter()
+    wl = workloads.named_workload(args.workload, users=args.users)
+    log(f"[bench] workload {wl.name}: {wl.recipe}; users={wl.num_users} rows={wl.total_rows} "
+        f"(generated in {time.perf_counter() - t_gen:.1f} s)")
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    elem = 2 if wl.dtype == "bf16" else 4
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+    X0 = t(wl.X)
+    x_bytes = wl.total_rows * wl.d * elem
+    copies = max(1, math.ceil(2 * MALL_BYTES / max(x_bytes, 1)) + 1) if x_bytes < 2 * MALL_BYTES else 1
+    Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
+    sa = SketchAttention(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau)
+    outs = [torch.empty((wl.num_users, wl.k, wl.d), dtype=torch.float32, device=dev) for _ in range(2)]
+    offs = np.ascontiguousarray(wl.offsets, dtype=np.int64)
+    plan = sa.plan(wl.total_rows)
+    log(f"[bench] plan {plan}; input copies {copies} x {x_bytes / 1e6:.1f} MB")
+    stream = torch.cuda.current_stream(dev)
+
+    for i in range(args.warmup):
+        binding.sa_compress_batch(sa.handle, Xs[i % copies], offs, outs[i % 2], stream)
+    torch.cuda.synchronize(dev)
+    binding.sa_read_kernel_timing(sa.handle)  # discard anything recorded so far
+
+    binding.sa_set_kernel_timing(sa.handle, True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        binding.sa_compress_batch(sa.handle, Xs[i % copies], offs, outs[i % 2], stream)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    binding.sa_set_kernel_timing(sa.handle, False)
+    fused_ms, reduce_ms, launches = binding.sa_read_kernel_timing(sa.handle)
+    log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = wl.total_rows * args.steps / elapsed
+    flops = algorithmic_flops(wl.k, wl.d, wl.total_rows)
+    nbytes = algorithmic_bytes(wl.total_rows, wl.num_users, wl.k, wl.d, elem)
+    fused_avg_ms = fused_ms / max(launches, 1)
+    # launches == steps unless the batch spans several launches; per-launch work
+    per_launch_flops = flops * args.steps / max(launches, 1)
+    per_launch_bytes = nbytes * args.steps / max(launches, 1)
+    mfma_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    tflops = per_launch_flops / (fused_avg_ms * 1e-3) / 1e12 if fused_avg_ms > 0 else 0.0
+    gbs = per_launch_bytes / (fused_avg_ms * 1e-3) / 1e9 if fused_avg_ms > 0 else 0.0
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if flops / nbytes >= ridge else "hbm"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(tflops / mfma_peak, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "sa_fused_kernel"
+    roof["kernel_avg_us"] = round(fused_avg_ms * 1e3, 2)
+    log(f"[bench] fused kernel avg {fused_avg_ms * 1e3:.2f} us ({tflops:.1f} TFLOP/s, {gbs:.0f} GB/s), "
+        f"reduce avg {reduce_ms / max(launches, 1) * 1e3:.2f} us; whole step {ms_per_step * 1e3:.2f} us "
+        f"({flops / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_budget)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    sa.close()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "behaviors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.num_users} users x n={wl.total_rows // max(wl.num_users, 1)}, "
+                        f"d={wl.d}, k={wl.k}, {wl.dtype}",
+            "users": wl.num_users,
+            "rows": wl.total_rows,
+            "d": wl.d,
+            "k": wl.k,
+            "parallelism": "single-gpu",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,151 @@
+/*
+ * sa.h -- C ABI of the MI355X (gfx950) Sketch Attention compression library.
+ *
+ * The operation (SequenceO1 close-reading page, "SequenceO1: End-to-End
+ * Ultra-Long (100K) Sequence Modeling in Recommendation with Low-Rank
+ * Caching", section 2.1 "Sketch Attention"): for one user with history
+ * X (n x d) and the k shared prototypes P (k x d),
+ *
+ *     S  = tau * (P W_Q)(X W_K)^T               (k x n affinity)
+ *     A  = softmax of S over the prototype axis  (each column sums to one)
+ *     X~ = A X                                   (k x d sketch, no value projection)
+ *
+ * Section 2.4 asks for a fused kernel that never writes the k x n matrices
+ * to high-bandwidth memory and that accepts batches of unequal-length
+ * histories; that is sa_compress_batch below.  sa_create folds the weights
+ * once, M = tau * log2(e) * P W_Q W_K^T (k x d), so the history's key
+ * projection X W_K is never formed (section 1 cites the same reordering for
+ * single-query cross-attention); exp is then evaluated as exp2.
+ *
+ * Conventions
+ *   - Matrices are dense, row-major, with no padding between rows.
+ *   - Row-vector convention: x W, so W[a][b] maps input coordinate a to
+ *     output coordinate b.
+ *   - "device" pointers are HIP device allocations on the device that is
+ *     current when sa_create is called; "host" pointers are ordinary memory.
+ *   - Streams are hipStream_t values passed as void* (NULL = null stream).
+ *   - Every entry point validates its arguments on the host before any HIP
+ *     call or enqueue; on error nothing is enqueued and outputs are not
+ *     touched.  Nothing throws across this boundary.
+ *   - A handle must not be used from two host threads at once, nor by two
+ *     streams whose work can overlap (its workspace is shared).
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sa_handle_s* sa_handle;
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1,   /* null pointer, bad offsets, non-finite tau, misaligned buffer */
+  SA_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement (see sa_create) */
+  SA_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
+  SA_ERR_DEVICE = 4         /* a HIP call or kernel launch failed */
+} sa_status;
+
+typedef enum sa_dtype {
+  SA_F32 = 0,   /* float32 inputs, float32 matrix-core products */
+  SA_BF16 = 1   /* bfloat16 inputs, float32 accumulation */
+} sa_dtype;
+
+/*
+ * sa_create -- validate the configuration, copy and fold the weights.
+ *
+ *   out    host pointer receiving the new handle (set to NULL on error)
+ *   d      history / prototype width; supported: 64 or 128
+ *   k      number of prototypes; supported: 1..1024 with k*d <= 65536 for
+ *          SA_BF16, 1..256 for SA_F32
+ *   tau    affinity scale, finite (any sign, zero allowed)
+ *   dtype  element type of P, W_Q, W_K and of every X passed later
+ *   P      device, [k][d] prototypes (section 2.1: P^(0), shared by all users)
+ *   W_Q    device, [d][d] query projection
+ *   W_K    device, [d][d] key projection
+ *   stream stream on which the fold runs; sa_create waits for it before
+ *          returning, so the caller may free P, W_Q, W_K afterwards
+ *
+ * The handle owns the folded matrix (computed in float32, rounded once to
+ * dtype) and a workspace that grows on demand.  Returns SA_ERR_UNSUPPORTED
+ * for a d, k or dtype outside the supported set, SA_ERR_INVALID_ARG for null
+ * pointers, non-finite tau or pointers not aligned to 16 bytes.
+ */
+sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype,
+                    const void* P, const void* W_Q, const void* W_K, void* stream);
+
+/*
+ * sa_compress_batch -- sketches of a ragged batch of users (section 2.4).
+ *
+ *   h          handle from sa_create
+ *   X          device, [offsets[num_users]][d] packed history rows in the
+ *              handle's dtype, 16-byte aligned; user u owns rows
+ *              offsets[u] .. offsets[u+1]-1 (section 2.1: X in R^{n x d})
+ *   offsets    host, int64 [num_users + 1], offsets[0] == 0, non-decreasing
+ *   num_users  U >= 0; U == 0 is a no-op returning SA_OK
+ *   out        device, float32 [num_users][k][d], 16-byte aligned, fully
+ *              overwritten; a user with no rows gets a zero sketch (empty sum)
+ *   stream     the work is only enqueued on this stream (asynchronous):
+ *              X and out must stay valid until the stream has passed it
+ *
+ * X is read from memory once; the k x n affinity and assignment matrices
+ * exist only tile by tile in registers.  Results are deterministic: the same
+ * inputs give bitwise identical outputs.
+ */
+sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users,
+                            float* out, void* stream);
+
+/*
+ * sa_destroy -- free the handle and its device memory.  NULL is allowed.
+ * The caller must have synchronised every stream that used the handle.
+ */
+void sa_destroy(sa_handle h);
+
+/* sa_status_string -- static, NUL-terminated description of a status code. */
+const char* sa_status_string(sa_status s);
+
+/*
+ * Host-only checks with no HIP call, the same ones sa_create and
+ * sa_compress_batch run first.  sa_check_config returns what sa_create
+ * would return for these scalar arguments with valid pointers;
+ * sa_check_batch returns what sa_compress_batch would return for these
+ * offsets with valid buffers.
+ */
+sa_status sa_check_config(int32_t d, int32_t k, float tau, sa_dtype dtype);
+sa_status sa_check_batch(int32_t k, const int64_t* offsets, int32_t num_users);
+
+/*
+ * sa_get_folded -- write the folded matrix M = tau*log2(e)*P W_Q W_K^T as
+ * float32 [k][d] into the device buffer dst (enqueued on stream).  This is
+ * the matrix the compression kernels use, after rounding to the dtype.
+ */
+sa_status sa_get_folded(sa_handle h, float* dst, void* stream);
+
+/*
+ * Kernel timing for measurement.  While enabled, sa_compress_batch records
+ * HIP events on its stream around each launch of the fused compression
+ * kernel and of the partial-sum reduction.  sa_read_kernel_timing waits for
+ * the recorded events, returns the summed durations in milliseconds and the
+ * number of fused launches since the previous read, and starts a new count.
+ * Any output pointer may be NULL.
+ */
+sa_status sa_set_kernel_timing(sa_handle h, int32_t enable);
+sa_status sa_read_kernel_timing(sa_handle h, double* fused_ms, double* reduce_ms, int64_t* fused_launches);
+
+/*
+ * sa_describe_plan -- the launch configuration sa_compress_batch would use
+ * for a batch of total_rows rows: workgroups in the fused grid, waves per
+ * workgroup that split the prototypes and the rows, rows per tile and the
+ * padded prototype count.  Host only; any output pointer may be NULL.
+ */
+sa_status sa_describe_plan(sa_handle h, int64_t total_rows, int32_t* groups, int32_t* waves_k,
+                           int32_t* waves_rows, int32_t* tile_rows, int32_t* k_padded);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,21 @@
+"""MI355X-native Sketch Attention compression (SequenceO1 cache-miss path).
+
+The computation lives in libsa.so (hand-written HIP for gfx950, C ABI in
+include/sa.h); this package holds its thin binding and the seeded synthetic
+workloads.  The library itself is loaded on first use, so the workloads can
+be used without it; any call into the binding fails loudly when it is absent.
+"""
+from .binding import (  # noqa: F401
+    SAError,
+    SketchAttention,
+    sa_check_batch,
+    sa_check_config,
+    sa_compress_batch,
+    sa_create,
+    sa_describe_plan,
+    sa_destroy,
+    sa_get_folded,
+    sa_read_kernel_timing,
+    sa_set_kernel_timing,
+    sa_status_string,
+)

@@ -1,0 +1,244 @@
+"""Thin Python binding over libsa.so (include/sa.h), with the same names.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, and their device pointers and the caller's HIP stream are passed
+to the C ABI.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU fallback, and loading fails loudly when the library
+has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import numpy as np
+import torch
+
+from .build import LIB_PATH
+
+SA_OK = 0
+SA_ERR_INVALID_ARG = 1
+SA_ERR_UNSUPPORTED = 2
+SA_ERR_OUT_OF_MEMORY = 3
+SA_ERR_DEVICE = 4
+
+SA_F32 = 0
+SA_BF16 = 1
+
+_DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
+_DTYPE_NAMES = {"f32": SA_F32, "bf16": SA_BF16}
+
+EXPORTED = (
+    "sa_create", "sa_compress_batch", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
+    "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
+)
+
+
+class SAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {sa_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing; run __graft_entry__.build() first "
+                           "(this package has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    p_i64 = ctypes.POINTER(ctypes.c_int64)
+    p_i32 = ctypes.POINTER(ctypes.c_int32)
+    p_f64 = ctypes.POINTER(ctypes.c_double)
+    sig = {
+        "sa_create": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, vp]),
+        "sa_compress_batch": (i32, [vp, vp, p_i64, i32, vp, vp]),
+        "sa_destroy": (None, [vp]),
+        "sa_status_string": (ctypes.c_char_p, [i32]),
+        "sa_check_config": (i32, [i32, i32, f32, i32]),
+        "sa_check_batch": (i32, [i32, p_i64, i32]),
+        "sa_get_folded": (i32, [vp, vp, vp]),
+        "sa_set_kernel_timing": (i32, [vp, i32]),
+        "sa_read_kernel_timing": (i32, [vp, p_f64, p_f64, p_i64]),
+        "sa_describe_plan": (i32, [vp, i64, p_i32, p_i32, p_i32, p_i32, p_i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def sa_status_string(status: int) -> str:
+    return library().sa_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != SA_OK:
+        raise SAError(status, what)
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream], device: torch.device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _offsets_array(offsets) -> np.ndarray:
+    if isinstance(offsets, torch.Tensor):
+        if offsets.is_cuda:
+            raise ValueError("offsets are read on the host: pass a CPU tensor, numpy array or list")
+        offsets = offsets.numpy()
+    return np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+
+
+def _i64_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _device_tensor(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def sa_check_config(d: int, k: int, tau: float, dtype: Union[str, torch.dtype]) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else _DTYPE_NAMES.get(dtype, 99)
+    return int(library().sa_check_config(int(d), int(k), float(tau), code))
+
+
+def sa_check_batch(k: int, offsets) -> int:
+    offs = _offsets_array(offsets)
+    if offs.size == 0:
+        return SA_ERR_INVALID_ARG
+    return int(library().sa_check_batch(int(k), _i64_ptr(offs), int(offs.size - 1)))
+
+
+def sa_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
+              stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    """Fold the weights into a new handle (see include/sa.h)."""
+    for t, n in ((P, "P"), (W_Q, "W_Q"), (W_K, "W_K")):
+        _device_tensor(t, n)
+    if P.dtype not in _DTYPES or W_Q.dtype != P.dtype or W_K.dtype != P.dtype:
+        raise ValueError("P, W_Q, W_K must share dtype float32 or bfloat16")
+    if P.dim() != 2:
+        raise ValueError("P must be [k, d]")
+    k, d = P.shape
+    if tuple(W_Q.shape) != (d, d) or tuple(W_K.shape) != (d, d):
+        raise ValueError("W_Q and W_K must be [d, d]")
+    h = ctypes.c_void_p()
+    with torch.cuda.device(P.device):
+        st = library().sa_create(ctypes.byref(h), int(d), int(k), float(tau), _DTYPES[P.dtype],
+                                 ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
+                                 ctypes.c_void_p(W_K.data_ptr()), _stream_ptr(stream, P.device))
+    _check(st, "sa_create")
+    return h
+
+
+def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
+                      stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the compression of a packed batch into `out` ([U, k, d] float32)."""
+    offs = _offsets_array(offsets)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    _device_tensor(X, "X")
+    _device_tensor(out, "out")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    if X.dim() != 2 or X.shape[0] != int(offs[-1]):
+        raise ValueError("X must be [offsets[-1], d]")
+    with torch.cuda.device(X.device):
+        st = library().sa_compress_batch(handle, ctypes.c_void_p(X.data_ptr()), _i64_ptr(offs), int(offs.size - 1),
+                                         ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream, X.device))
+    _check(st, "sa_compress_batch")
+
+
+def sa_destroy(handle: Optional[ctypes.c_void_p]) -> None:
+    if handle is not None and handle.value:
+        library().sa_destroy(handle)
+
+
+def sa_get_folded(handle: ctypes.c_void_p, dst: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    _device_tensor(dst, "dst")
+    if dst.dtype != torch.float32:
+        raise ValueError("dst must be float32 [k, d]")
+    with torch.cuda.device(dst.device):
+        _check(library().sa_get_folded(handle, ctypes.c_void_p(dst.data_ptr()), _stream_ptr(stream, dst.device)),
+               "sa_get_folded")
+
+
+def sa_set_kernel_timing(handle: ctypes.c_void_p, enable: bool) -> None:
+    _check(library().sa_set_kernel_timing(handle, 1 if enable else 0), "sa_set_kernel_timing")
+
+
+def sa_read_kernel_timing(handle: ctypes.c_void_p):
+    """Returns (fused_ms_total, reduce_ms_total, fused_launches) since the last read."""
+    f, r, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(library().sa_read_kernel_timing(handle, ctypes.byref(f), ctypes.byref(r), ctypes.byref(n)),
+           "sa_read_kernel_timing")
+    return f.value, r.value, n.value
+
+
+def sa_describe_plan(handle: ctypes.c_void_p, total_rows: int) -> dict:
+    vals = [ctypes.c_int32() for _ in range(5)]
+    _check(library().sa_describe_plan(handle, int(total_rows), *[ctypes.byref(v) for v in vals]), "sa_describe_plan")
+    keys = ("groups", "waves_k", "waves_rows", "tile_rows", "k_padded")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+class SketchAttention:
+    """Owns one handle: the folded weights of one (P, W_Q, W_K, tau)."""
+
+    def __init__(self, P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.handle = sa_create(P, W_Q, W_K, tau, stream)
+        self.k, self.d = int(P.shape[0]), int(P.shape[1])
+        self.dtype = P.dtype
+        self.device = P.device
+        self.tau = float(tau)
+
+    def compress(self, X: torch.Tensor, offsets, out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        if X.dtype != self.dtype:
+            raise ValueError(f"X dtype {X.dtype} differs from the weights' {self.dtype}")
+        if X.dim() != 2 or X.shape[1] != self.d:
+            raise ValueError(f"X must be [N, {self.d}]")
+        offs = _offsets_array(offsets)
+        if out is None:
+            out = torch.empty((offs.size - 1, self.k, self.d), dtype=torch.float32, device=X.device)
+        sa_compress_batch(self.handle, X, offs, out, stream)
+        return out
+
+    def folded(self) -> torch.Tensor:
+        dst = torch.empty((self.k, self.d), dtype=torch.float32, device=self.device)
+        sa_get_folded(self.handle, dst)
+        return dst
+
+    def plan(self, total_rows: int) -> dict:
+        return sa_describe_plan(self.handle, total_rows)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None:
+            sa_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

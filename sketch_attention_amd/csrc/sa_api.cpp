@@ -1,0 +1,363 @@
+// Host side of the C ABI declared in include/sa.h: argument validation, plan
+// selection, the handle (folded weights + workspace), batching of users into
+// launches, and optional kernel timing.
+#include "sa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "sa_internal.h"
+
+#define SA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using sa::Plan;
+
+struct TimingSlot {
+  hipEvent_t ev[3];  // before fused, after fused, after reduce
+  bool fused;        // false when the launch had no rows (reduce only)
+};
+
+}  // namespace
+
+struct sa_handle_s {
+  int device = 0;
+  int cu_count = 0;
+  int groups_per_cu = 1;
+  float tau = 0.f;
+  Plan plan{};
+  void* M = nullptr;           // folded matrix [k_pad][d], dtype
+  float* workspace = nullptr;  // partial sketches
+  size_t workspace_bytes = 0;
+  bool timing = false;
+  std::vector<TimingSlot> slots;  // recorded since the last read
+  std::vector<TimingSlot> spare;  // event triples ready for reuse
+};
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634073599246810019;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Plan of the fused pass for a supported (dtype, d, k); see sa_fused.hpp.
+Plan make_plan(int dtype, int d, int k) {
+  Plan p{};
+  p.dtype = dtype;
+  p.d = d;
+  p.k = k;
+  const int k16 = (k + 15) / 16 * 16;
+  if (k16 <= 16) {
+    p.kw = 16; p.waves_k = 1;
+  } else if (k16 <= 32) {
+    p.kw = 32; p.waves_k = 1;
+  } else if (k16 <= 64) {
+    p.kw = 64; p.waves_k = 1;
+  } else if (k <= 128) {
+    p.kw = 64; p.waves_k = 2;
+  } else if (k <= 256) {
+    p.kw = 64; p.waves_k = 4;
+  } else if (k <= 512) {
+    p.kw = 128; p.waves_k = 4; p.m_in_lds = 1;
+  } else {
+    p.kw = 256; p.waves_k = 4; p.m_in_lds = 1;
+  }
+  p.waves_rows = sa::kWaves / p.waves_k;
+  p.k_pad = p.kw * p.waves_k;
+  p.tile_rows = sa::kRowsPerWave * p.waves_rows;
+  return p;
+}
+
+sa_status check_config(int32_t d, int32_t k, float tau, sa_dtype dtype) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_INVALID_ARG;
+  if (!std::isfinite(tau)) return SA_ERR_INVALID_ARG;
+  if (k < 1 || d < 1) return SA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_BF16 && (k > 1024 || (int64_t)k * d > 65536)) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_F32 && k > 256) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+sa_status check_batch(const int64_t* offsets, int32_t num_users) {
+  if (num_users < 0) return SA_ERR_INVALID_ARG;
+  if (num_users == 0) return SA_OK;
+  if (offsets == nullptr) return SA_ERR_INVALID_ARG;
+  if (offsets[0] != 0) return SA_ERR_INVALID_ARG;
+  for (int32_t u = 0; u < num_users; ++u)
+    if (offsets[u + 1] < offsets[u]) return SA_ERR_INVALID_ARG;
+  if (offsets[num_users] > (int64_t(1) << 40)) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
+// Work groups of the fused grid for a launch of `rows` rows: at most one full
+// wave of resident groups, and no more groups than tiles.
+int groups_for(const sa_handle_s* h, int64_t rows) {
+  const int64_t cap = (int64_t)h->cu_count * h->groups_per_cu;
+  const int64_t tiles = (rows + h->plan.tile_rows - 1) / h->plan.tile_rows;
+  int64_t g = tiles < cap ? tiles : cap;
+  return g < 1 ? 1 : (int)g;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && cur != dev) {
+      if (hipSetDevice(dev) == hipSuccess) prev = cur;
+    }
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+TimingSlot take_slot(sa_handle_s* h) {
+  if (!h->spare.empty()) {
+    TimingSlot s = h->spare.back();
+    h->spare.pop_back();
+    return s;
+  }
+  TimingSlot s{};
+  for (auto& e : s.ev) {
+    if (hipEventCreate(&e) != hipSuccess) e = nullptr;
+  }
+  return s;
+}
+
+}  // namespace
+
+SA_API const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "success";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case SA_ERR_DEVICE: return "HIP device error";
+  }
+  return "unknown status";
+}
+
+SA_API sa_status sa_check_config(int32_t d, int32_t k, float tau, sa_dtype dtype) {
+  return check_config(d, k, tau, dtype);
+}
+
+SA_API sa_status sa_check_batch(int32_t k, const int64_t* offsets, int32_t num_users) {
+  if (k < 1) return SA_ERR_INVALID_ARG;
+  return check_batch(offsets, num_users);
+}
+
+SA_API sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype, const void* P,
+                           const void* W_Q, const void* W_K, void* stream) {
+  if (out == nullptr) return SA_ERR_INVALID_ARG;
+  *out = nullptr;
+  sa_status st = check_config(d, k, tau, dtype);
+  if (st != SA_OK) return st;
+  if (P == nullptr || W_Q == nullptr || W_K == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned16(P) || !aligned16(W_Q) || !aligned16(W_K)) return SA_ERR_INVALID_ARG;
+
+  sa_handle_s* h = new (std::nothrow) sa_handle_s();
+  if (h == nullptr) return SA_ERR_OUT_OF_MEMORY;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  h->tau = tau;
+  h->plan = make_plan((int)dtype, d, k);
+  const size_t elem = dtype == SA_BF16 ? 2 : 4;
+  float* tmp = nullptr;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&h->device) != hipSuccess || hipGetDeviceProperties(&prop, h->device) != hipSuccess) {
+    delete h;
+    return SA_ERR_DEVICE;
+  }
+  h->cu_count = prop.multiProcessorCount;
+  int occ = 0;
+  if (sa::fused_occupancy(h->plan, &occ) != hipSuccess || occ < 1) {
+    delete h;
+    return SA_ERR_DEVICE;
+  }
+  h->groups_per_cu = occ;
+  if (hipMalloc(&h->M, (size_t)h->plan.k_pad * d * elem) != hipSuccess) {
+    delete h;
+    return SA_ERR_OUT_OF_MEMORY;
+  }
+  if (hipMalloc(&tmp, (size_t)k * d * sizeof(float)) != hipSuccess) {
+    (void)hipFree(h->M);
+    delete h;
+    return SA_ERR_OUT_OF_MEMORY;
+  }
+  const float scale = (float)((double)tau * kLog2e);
+  hipError_t e = sa::launch_fold((int)dtype, P, W_Q, W_K, scale, k, h->plan.k_pad, d, tmp, h->M, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(tmp);
+  if (e != hipSuccess) {
+    (void)hipFree(h->M);
+    delete h;
+    return SA_ERR_DEVICE;
+  }
+  *out = h;
+  return SA_OK;
+}
+
+SA_API void sa_destroy(sa_handle h) {
+  if (h == nullptr) return;
+  DeviceGuard guard(h->device);
+  for (auto* v : {&h->slots, &h->spare})
+    for (auto& s : *v)
+      for (auto& e : s.ev)
+        if (e) (void)hipEventDestroy(e);
+  if (h->workspace) (void)hipFree(h->workspace);
+  if (h->M) (void)hipFree(h->M);
+  delete h;
+}
+
+SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users, float* out,
+                                   void* stream) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  sa_status st = check_batch(offsets, num_users);
+  if (st != SA_OK) return st;
+  if (num_users == 0) return SA_OK;
+  const int64_t total = offsets[num_users];
+  if (out == nullptr || !aligned16(out)) return SA_ERR_INVALID_ARG;
+  if (total > 0 && (X == nullptr || !aligned16(X))) return SA_ERR_INVALID_ARG;
+
+  const Plan& plan = h->plan;
+  const size_t elem = plan.dtype == SA_BF16 ? 2 : 4;
+  const size_t slot_bytes = (size_t)plan.k_pad * plan.d * sizeof(float);
+
+  // Workspace for the largest launch of this call.
+  size_t need = 0;
+  for (int32_t u0 = 0; u0 < num_users; u0 += sa::kMaxUsersPerLaunch) {
+    const int32_t nu = num_users - u0 < sa::kMaxUsersPerLaunch ? num_users - u0 : sa::kMaxUsersPerLaunch;
+    const int64_t rows = offsets[u0 + nu] - offsets[u0];
+    if (rows > 0) {
+      const size_t b = (size_t)(groups_for(h, rows) + nu) * slot_bytes;
+      if (b > need) need = b;
+    }
+  }
+
+  DeviceGuard guard(h->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need > h->workspace_bytes) {
+    // Earlier launches on this stream may still read the old workspace.
+    if (h->workspace) {
+      if (hipStreamSynchronize(s) != hipSuccess) return SA_ERR_DEVICE;
+      (void)hipFree(h->workspace);
+      h->workspace = nullptr;
+      h->workspace_bytes = 0;
+    }
+    if (hipMalloc(&h->workspace, need) != hipSuccess) {
+      h->workspace = nullptr;
+      return SA_ERR_OUT_OF_MEMORY;
+    }
+    h->workspace_bytes = need;
+  }
+
+  for (int32_t u0 = 0; u0 < num_users; u0 += sa::kMaxUsersPerLaunch) {
+    const int32_t nu = num_users - u0 < sa::kMaxUsersPerLaunch ? num_users - u0 : sa::kMaxUsersPerLaunch;
+    const int64_t base = offsets[u0];
+    const int64_t rows = offsets[u0 + nu] - base;
+    const int groups = rows > 0 ? groups_for(h, rows) : 0;
+
+    sa::FusedArgs fa;
+    std::memset(&fa, 0, sizeof(fa));
+    fa.X = static_cast<const char*>(X) + (size_t)base * plan.d * elem;
+    fa.M = h->M;
+    fa.partial = h->workspace;
+    fa.rows = rows;
+    fa.users = nu;
+    fa.k = plan.k;
+    sa::ReduceArgs ra;
+    std::memset(&ra, 0, sizeof(ra));
+    ra.partial = h->workspace;
+    ra.out = out + (size_t)u0 * plan.k * plan.d;
+    ra.rows = rows;
+    ra.users = nu;
+    ra.groups = groups;
+    ra.k = plan.k;
+    ra.d = plan.d;
+    ra.kw = plan.kw;
+    ra.k_pad = plan.k_pad;
+    for (int32_t i = 0; i <= nu; ++i) {
+      fa.offsets[i] = offsets[u0 + i] - base;
+      ra.offsets[i] = fa.offsets[i];
+    }
+
+    TimingSlot ts{};
+    if (h->timing) {
+      ts = take_slot(h);
+      ts.fused = rows > 0;
+      if (ts.ev[0]) (void)hipEventRecord(ts.ev[0], s);
+    }
+    if (rows > 0) {
+      if (sa::launch_fused(plan, fa, groups, s) != hipSuccess) return SA_ERR_DEVICE;
+    }
+    if (h->timing && ts.ev[1]) (void)hipEventRecord(ts.ev[1], s);
+    if (sa::launch_reduce(ra, s) != hipSuccess) return SA_ERR_DEVICE;
+    if (h->timing) {
+      if (ts.ev[2]) (void)hipEventRecord(ts.ev[2], s);
+      h->slots.push_back(ts);
+    }
+  }
+  return SA_OK;
+}
+
+SA_API sa_status sa_get_folded(sa_handle h, float* dst, void* stream) {
+  if (h == nullptr || dst == nullptr) return SA_ERR_INVALID_ARG;
+  DeviceGuard guard(h->device);
+  if (sa::launch_unfold(h->plan.dtype, h->M, h->plan.k, h->plan.d, dst, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SA_ERR_DEVICE;
+  return SA_OK;
+}
+
+SA_API sa_status sa_set_kernel_timing(sa_handle h, int32_t enable) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  h->timing = enable != 0;
+  return SA_OK;
+}
+
+SA_API sa_status sa_read_kernel_timing(sa_handle h, double* fused_ms, double* reduce_ms, int64_t* fused_launches) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  DeviceGuard guard(h->device);
+  double f = 0.0, r = 0.0;
+  int64_t n = 0;
+  sa_status st = SA_OK;
+  for (auto& s : h->slots) {
+    if (!s.ev[0] || !s.ev[1] || !s.ev[2] || hipEventSynchronize(s.ev[2]) != hipSuccess) {
+      st = SA_ERR_DEVICE;
+      continue;
+    }
+    float a = 0.f, b = 0.f;
+    if (hipEventElapsedTime(&a, s.ev[0], s.ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&b, s.ev[1], s.ev[2]) != hipSuccess) {
+      st = SA_ERR_DEVICE;
+      continue;
+    }
+    if (s.fused) {
+      f += a;
+      ++n;
+    }
+    r += b;
+  }
+  for (auto& s : h->slots) h->spare.push_back(s);
+  h->slots.clear();
+  if (fused_ms) *fused_ms = f;
+  if (reduce_ms) *reduce_ms = r;
+  if (fused_launches) *fused_launches = n;
+  return st;
+}
+
+SA_API sa_status sa_describe_plan(sa_handle h, int64_t total_rows, int32_t* groups, int32_t* waves_k,
+                                  int32_t* waves_rows, int32_t* tile_rows, int32_t* k_padded) {
+  if (h == nullptr || total_rows < 0) return SA_ERR_INVALID_ARG;
+  if (groups) *groups = total_rows > 0 ? groups_for(h, total_rows) : 0;
+  if (waves_k) *waves_k = h->plan.waves_k;
+  if (waves_rows) *waves_rows = h->plan.waves_rows;
+  if (tile_rows) *tile_rows = h->plan.tile_rows;
+  if (k_padded) *k_padded = h->plan.k_pad;
+  return SA_OK;
+}

@@ -1,0 +1,79 @@
+// Internal interface between the host library (sa_api.cpp) and the HIP
+// kernels (sa_kernels.hip, sa_fused_*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sa {
+
+// Users whose offsets travel inline in one launch's kernel arguments.  A
+// batch with more users is processed in consecutive launches of at most this
+// many users each.
+constexpr int kMaxUsersPerLaunch = 256;
+
+// Threads per workgroup of the fused kernel: four wave64 wavefronts, one per
+// SIMD of a CDNA4 compute unit.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+// Rows of the history tile that one wave handles per step.
+constexpr int kRowsPerWave = 32;
+
+// Launch configuration of the fused pass for one (dtype, d, k).
+struct Plan {
+  int dtype;        // 0 = f32, 1 = bf16 (sa_dtype)
+  int d;            // 64 or 128
+  int k;            // prototypes
+  int k_pad;        // waves_k * kw
+  int kw;           // prototypes per wave (multiple of 16)
+  int waves_k;      // waves splitting the prototype axis
+  int waves_rows;   // waves splitting the rows of a tile (waves_k * waves_rows == kWaves)
+  int m_in_lds;     // folded matrix staged in LDS (1) or held in registers (0)
+  int tile_rows;    // kRowsPerWave * waves_rows
+};
+
+// Arguments of the fused kernel (passed by value in the dispatch packet).
+struct FusedArgs {
+  const void* X;        // rows of this launch, [rows][d]
+  const void* M;        // folded matrix [k_pad][d] in the dtype
+  float* partial;       // [slots][k_pad * d] float32, slot = group + user
+  int64_t rows;         // rows in this launch (offsets[users])
+  int32_t users;        // users in this launch (<= kMaxUsersPerLaunch)
+  int32_t k;            // real prototype count (rows k..k_pad-1 of M are padding)
+  int64_t offsets[kMaxUsersPerLaunch + 1];  // relative to this launch's first row
+};
+
+struct ReduceArgs {
+  const float* partial;  // as above
+  float* out;            // [users][k][d] float32
+  int64_t rows;
+  int32_t users;
+  int32_t groups;        // workgroups of the fused launch
+  int32_t k;
+  int32_t d;
+  int32_t kw;
+  int32_t k_pad;
+  int64_t offsets[kMaxUsersPerLaunch + 1];
+};
+
+// Launchers (defined in the .hip translation units).
+hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& args, hipStream_t stream);
+hipError_t launch_fold(int dtype, const void* P, const void* WQ, const void* WK, float scale, int k, int k_pad,
+                       int d, float* tmp, void* M, hipStream_t stream);
+hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hipStream_t stream);
+// Workgroups of the fused kernel that fit on one compute unit at once.
+hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
+
+// Per-instantiation entry points, one translation unit per (dtype, d).
+hipError_t launch_fused_bf16_d64(const Plan&, const FusedArgs&, int, hipStream_t);
+hipError_t launch_fused_bf16_d128(const Plan&, const FusedArgs&, int, hipStream_t);
+hipError_t launch_fused_f32_d64(const Plan&, const FusedArgs&, int, hipStream_t);
+hipError_t launch_fused_f32_d128(const Plan&, const FusedArgs&, int, hipStream_t);
+hipError_t occupancy_bf16_d64(const Plan&, int*);
+hipError_t occupancy_bf16_d128(const Plan&, int*);
+hipError_t occupancy_f32_d64(const Plan&, int*);
+hipError_t occupancy_f32_d128(const Plan&, int*);
+
+}  // namespace sa

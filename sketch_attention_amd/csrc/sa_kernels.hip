@@ -1,0 +1,144 @@
+// Support kernels: weight fold, split-n partial reduction, and the launch
+// dispatchers of the fused pass.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// ------------------------------------------------------------------ fold
+// Q = P W_Q (k x d, float32): the prototype queries of the affinity
+// (SequenceO1 page, section 2.1).
+template <typename T>
+__global__ __launch_bounds__(256) void fold_q_kernel(const T* P, const T* WQ, int k, int d, float* Q) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= k * d) return;
+  const int j = idx / d, b = idx % d;
+  float s = 0.f;
+  for (int a = 0; a < d; ++a) s = fmaf(to_f32(P[j * d + a]), to_f32(WQ[a * d + b]), s);
+  Q[idx] = s;
+}
+
+// M[j][c] = scale * sum_b Q[j][b] W_K[c][b]  (= scale * (P W_Q W_K^T)[j][c]),
+// rounded once to T; padded rows k..k_pad-1 are zero.
+template <typename T>
+__global__ __launch_bounds__(256) void fold_m_kernel(const float* Q, const T* WK, float scale, int k, int k_pad, int d,
+                                                     T* M) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= k_pad * d) return;
+  const int j = idx / d, c = idx % d;
+  float s = 0.f;
+  if (j < k) {
+    for (int b = 0; b < d; ++b) s = fmaf(Q[j * d + b], to_f32(WK[c * d + b]), s);
+    s *= scale;
+  }
+  M[idx] = (T)s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void unfold_kernel(const T* M, int k, int d, float* dst) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= k * d) return;
+  dst[idx] = to_f32(M[idx]);
+}
+
+hipError_t launch_fold(int dtype, const void* P, const void* WQ, const void* WK, float scale, int k, int k_pad, int d,
+                       float* tmp, void* M, hipStream_t stream) {
+  const int gq = (k * d + 255) / 256, gm = (k_pad * d + 255) / 256;
+  if (dtype == 1) {
+    hipLaunchKernelGGL(fold_q_kernel<bf16>, dim3(gq), dim3(256), 0, stream, (const bf16*)P, (const bf16*)WQ, k, d, tmp);
+    hipLaunchKernelGGL(fold_m_kernel<bf16>, dim3(gm), dim3(256), 0, stream, tmp, (const bf16*)WK, scale, k, k_pad, d,
+                       (bf16*)M);
+  } else {
+    hipLaunchKernelGGL(fold_q_kernel<float>, dim3(gq), dim3(256), 0, stream, (const float*)P, (const float*)WQ, k, d,
+                       tmp);
+    hipLaunchKernelGGL(fold_m_kernel<float>, dim3(gm), dim3(256), 0, stream, tmp, (const float*)WK, scale, k, k_pad,
+                       d, (float*)M);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hipStream_t stream) {
+  const int gr = (k * d + 255) / 256;
+  if (dtype == 1)
+    hipLaunchKernelGGL(unfold_kernel<bf16>, dim3(gr), dim3(256), 0, stream, (const bf16*)M, k, d, dst);
+  else
+    hipLaunchKernelGGL(unfold_kernel<float>, dim3(gr), dim3(256), 0, stream, (const float*)M, k, d, dst);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- reduce
+// out[u] = sum over the work groups b that touched user u of partial[b + u],
+// in increasing b (fixed order, so results are bitwise reproducible).  Work
+// group b of G covers rows [floor(b*R/G), floor((b+1)*R/G)), so the group
+// holding row r is floor(((r+1)*G - 1) / R).  A user with no rows gets zeros.
+//
+// Partial slots hold each lane's accumulator registers in order,
+// [wj][jb][cb][lane][4]; float4 number p of a slot holds prototypes
+// wj*kw + 16*jb + 4*(lane/16) + 0..3 at column 16*cb + lane%16.
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  const int u = blockIdx.y;
+  const int slot_f4 = a.k_pad * a.d / 4;
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= slot_f4) return;
+  const int64_t r0 = a.offsets[u], r1 = a.offsets[u + 1];
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (r1 > r0) {
+    const int64_t G = a.groups, R = a.rows;
+    const int64_t b0 = ((r0 + 1) * G - 1) / R;
+    const int64_t b1 = (r1 * G - 1) / R;
+    const f32x4* part = reinterpret_cast<const f32x4*>(a.partial);
+    for (int64_t b = b0; b <= b1; ++b) s += part[(b + u) * slot_f4 + p];
+  }
+  const int lane = p & 63;
+  int t = p >> 6;
+  const int cbs = a.d / 16, jbs = a.kw / 16;
+  const int cb = t % cbs;
+  t /= cbs;
+  const int jb = t % jbs;
+  const int wj = t / jbs;
+  const int j0 = wj * a.kw + 16 * jb + 4 * (lane >> 4);
+  const int c = 16 * cb + (lane & 15);
+  float* o = a.out + (int64_t)u * a.k * a.d;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (j0 + r < a.k) o[(int64_t)(j0 + r) * a.d + c] = s[r];
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
+  const int slot_f4 = a.k_pad * a.d / 4;
+  hipLaunchKernelGGL(reduce_kernel, dim3((slot_f4 + 255) / 256, a.users), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ dispatch
+hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream) {
+  if (plan.dtype == 1) {
+    if (plan.d == 64) return launch_fused_bf16_d64(plan, args, groups, stream);
+    if (plan.d == 128) return launch_fused_bf16_d128(plan, args, groups, stream);
+  } else {
+    if (plan.d == 64) return launch_fused_f32_d64(plan, args, groups, stream);
+    if (plan.d == 128) return launch_fused_f32_d128(plan, args, groups, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t fused_occupancy(const Plan& plan, int* n) {
+  if (plan.dtype == 1) {
+    if (plan.d == 64) return occupancy_bf16_d64(plan, n);
+    if (plan.d == 128) return occupancy_bf16_d128(plan, n);
+  } else {
+    if (plan.d == 64) return occupancy_f32_d64(plan, n);
+    if (plan.d == 128) return occupancy_f32_d128(plan, n);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa
