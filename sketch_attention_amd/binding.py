@@ -45,14 +45,15 @@ _lib = None
 
 
 def library() -> ctypes.CDLL:
-    """Load libsa.so (once).  Raises if it has not been built."""
+    """Load libsa.so (once; SA_LIB_PATH selects another build).  Raises if it is missing."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing; run __graft_entry__.build() first "
+    path = os.environ.get("SA_LIB_PATH") or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing; run __graft_entry__.build() first "
                            "(this package has no CPU fallback)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     p_i64 = ctypes.POINTER(ctypes.c_int64)
     p_i32 = ctypes.POINTER(ctypes.c_int32)

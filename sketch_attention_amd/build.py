@@ -26,9 +26,15 @@ SOURCES = [
     "sa_kernels.hip",
     "sa_fused_bf16_d64.hip",
     "sa_fused_bf16_d128.hip",
+    "sa_fused_bf16_d64_large.hip",
+    "sa_fused_bf16_d128_large.hip",
     "sa_fused_f32_d64.hip",
     "sa_fused_f32_d128.hip",
 ]
+# Plan groups whose accumulators fit in 128 architectural registers per lane
+# keep every matrix-core result in VGPRs, so the softmax reads the affinity
+# tile without AGPR moves; larger accumulators stay in AGPRs.
+VGPR_FORM = {"sa_fused_bf16_d64.hip", "sa_fused_bf16_d128.hip"}
 # Packed fp32 VALU instructions are disabled for all device code.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -65,7 +71,8 @@ def build_library(verbose: bool = False, jobs: int | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"] if src in VGPR_FORM else []
+        cmds.append([cc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for fut in [ex.submit(_run, c, verbose) for c in cmds]:

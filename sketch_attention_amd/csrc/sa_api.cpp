@@ -6,6 +6,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -47,6 +49,9 @@ constexpr double kLog2e = 1.4426950408889634073599246810019;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Plan of the fused pass for a supported (dtype, d, k); see sa_fused.hpp.
+// bf16 plans keep the folded matrix in LDS (shared by the waves); float32
+// plans keep it in registers.  SA_PLAN="kw,waves_k,m_in_lds" in the
+// environment overrides the choice when that plan exists for (dtype, d, k).
 Plan make_plan(int dtype, int d, int k) {
   Plan p{};
   p.dtype = dtype;
@@ -64,9 +69,17 @@ Plan make_plan(int dtype, int d, int k) {
   } else if (k <= 256) {
     p.kw = 64; p.waves_k = 4;
   } else if (k <= 512) {
-    p.kw = 128; p.waves_k = 4; p.m_in_lds = 1;
+    p.kw = 128; p.waves_k = 4;
   } else {
-    p.kw = 256; p.waves_k = 4; p.m_in_lds = 1;
+    p.kw = 256; p.waves_k = 4;
+  }
+  p.m_in_lds = dtype == SA_BF16 ? 1 : 0;
+  if (const char* env = std::getenv("SA_PLAN")) {
+    int kw = 0, wk = 0, ml = 0;
+    if (std::sscanf(env, "%d,%d,%d", &kw, &wk, &ml) == 3 && kw % 16 == 0 && kw > 0 &&
+        (wk == 1 || wk == 2 || wk == 4) && kw * wk >= k) {
+      p.kw = kw; p.waves_k = wk; p.m_in_lds = ml ? 1 : 0;
+    }
   }
   p.waves_rows = sa::kWaves / p.waves_k;
   p.k_pad = p.kw * p.waves_k;
@@ -177,7 +190,7 @@ SA_API sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_d
   int occ = 0;
   if (sa::fused_occupancy(h->plan, &occ) != hipSuccess || occ < 1) {
     delete h;
-    return SA_ERR_DEVICE;
+    return std::getenv("SA_PLAN") ? SA_ERR_UNSUPPORTED : SA_ERR_DEVICE;
   }
   h->groups_per_cu = occ;
   if (hipMalloc(&h->M, (size_t)h->plan.k_pad * d * elem) != hipSuccess) {

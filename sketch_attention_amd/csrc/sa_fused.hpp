@@ -98,12 +98,32 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Transposing butterfly over the 16 lanes of a DPP row: p[r] is this lane's
+// partial for row r (r = 0..3); on return every lane of a quad holds the
+// 16-lane total of row 2*bit3 + bit2 of its lane index.  11 VALU operations
+// instead of 16 for four independent all-reductions.
+__device__ __forceinline__ float rows4_sum_scatter(const float (&p)[4], int l16) {
+  const bool hi = (l16 & 8) != 0;
+  const float keep0 = hi ? p[2] : p[0], send0 = hi ? p[0] : p[2];
+  const float keep1 = hi ? p[3] : p[1], send1 = hi ? p[1] : p[3];
+  const float q0 = keep0 + dpp_f32<0x128>(send0);  // row_ror:8 = lane ^ 8
+  const float q1 = keep1 + dpp_f32<0x128>(send1);
+  const bool b2 = (l16 & 4) != 0;
+  const float keep = b2 ? q1 : q0, send = b2 ? q0 : q1;
+  float z = keep + dpp_f32<0x141>(send);           // row_half_mirror flips bit 2
+  z += dpp_f32<0xB1>(z);                           // quad xor 1
+  z += dpp_f32<0x4E>(z);                           // quad xor 2
+  return z;
+}
+
 // ------------------------------------------------------ static geometry
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
+// PIPE_REQ asks for the software-pipelined schedule (affinity of tile t+1
+// issued alongside the softmax of tile t, two Xt buffers); it is used when the
+// registers (two affinity tiles) and LDS allow it.
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE_REQ>
 struct FusedGeom {
   static_assert(WJ * WI == kWaves, "four waves per work group");
   static_assert(KW % 16 == 0 && D % 32 == 0, "tile shape");
-  static_assert(!(MLDS && WI > 1), "LDS-resident M is used only when all waves split the prototypes");
   static constexpr int NT = kRowsPerWave * WI;   // tile rows
   static constexpr int JB = KW / 16;             // 16-prototype blocks per wave
   static constexpr int CB = D / 16;              // 16-column blocks of the output
@@ -114,23 +134,34 @@ struct FusedGeom {
   static constexpr int MS = D + 8;                     // LDS M row stride (bf16 elements)
   static constexpr int XR_BYTES = NT * XRS * (int)sizeof(T);
   static constexpr int XT_BYTES = D * XTS * (int)sizeof(T);
-  static constexpr int RED_BYTES = WJ > 1 ? 2 * WJ * NT * 4 : 0;
+  static constexpr int XL_BYTES = NT * WJ * 4;         // per-wave row sums
+  static constexpr int FLAG_BYTES = 4 * kWaves;
   static constexpr int M_BYTES = MLDS ? KPAD * MS * 2 : 0;
-  static constexpr int MAIN_BYTES = XR_BYTES + XT_BYTES + RED_BYTES + M_BYTES;
-  static constexpr int ACC_BYTES = WI > 1 ? KPAD * D * 4 : 0;
-  static constexpr int LDS_BYTES = MAIN_BYTES > ACC_BYTES ? MAIN_BYTES : ACC_BYTES;
+  static constexpr int stage_bytes = WI > 1 ? WJ * CB * 64 * 16 : 0;  // one prototype block of every wave's accumulators
+  static constexpr int region(int nxt) { return XR_BYTES + nxt * XT_BYTES + 3 * XL_BYTES + FLAG_BYTES; }
+  static constexpr bool PIPE = PIPE_REQ && KW <= 128 && region(2) + M_BYTES <= 160 * 1024;
+  static constexpr int NXT = PIPE ? 2 : 1;
+  static constexpr int XREG = region(NXT) > stage_bytes ? region(NXT) : stage_bytes;
+  static constexpr int OFF_XT = XR_BYTES;
+  static constexpr int OFF_XL = XR_BYTES + NXT * XT_BYTES;
+  static constexpr int OFF_XSM = OFF_XL + XL_BYTES;     // slow path: per-wave row maxima
+  static constexpr int OFF_XSL = OFF_XSM + XL_BYTES;    // slow path: per-wave row sums
+  static constexpr int OFF_FLAG = OFF_XSL + XL_BYTES;
+  static constexpr int OFF_M = XREG;
+  static constexpr int LDS_BYTES = XREG + M_BYTES;
   static constexpr int QC = D / 4;                     // 4-column quads per row
   static constexpr int NBLK = (NT / 4) * QC;           // 4x4 blocks per tile
   static constexpr int BPT = (NBLK + kThreads - 1) / kThreads;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
-
 // ------------------------------------------------------- X tile staging
 // One thread moves a 4x4 block (rows 4rq..4rq+3, columns 4cq..4cq+3 of the
 // tile) from HBM into registers, then into both LDS layouts.  Consecutive
 // threads take consecutive column quads of the same rows, so each global load
-// instruction of a wave reads whole rows.
+// instruction of a wave reads whole rows.  Rows at or past row_end read the
+// last valid row (always in bounds) and are then zeroed, so no branch splits
+// the surrounding code.
 template <typename T>
 struct Quad;
 template <>
@@ -146,7 +177,10 @@ template <int D>
 __device__ __forceinline__ void quad_load(Quad<bf16>& q, const bf16* X, int64_t row, int64_t row_end, int col) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    q.v[r] = (row + r < row_end) ? *reinterpret_cast<const u32x2*>(X + (row + r) * D + col) : u32x2{0u, 0u};
+    const int64_t rr = row + r < row_end ? row + r : row_end - 1;
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(X + rr * D + col));
+    const bool ok = row + r < row_end;
+    q.v[r] = u32x2{ok ? v.x : 0u, ok ? v.y : 0u};
   }
 }
 
@@ -154,15 +188,24 @@ template <int D>
 __device__ __forceinline__ void quad_load(Quad<float>& q, const float* X, int64_t row, int64_t row_end, int col) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    q.v[r] = (row + r < row_end) ? *reinterpret_cast<const f32x4*>(X + (row + r) * D + col)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t rr = row + r < row_end ? row + r : row_end - 1;
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(X + rr * D + col));
+    const bool ok = row + r < row_end;
+    q.v[r] = f32x4{ok ? v[0] : 0.f, ok ? v[1] : 0.f, ok ? v[2] : 0.f, ok ? v[3] : 0.f};
   }
 }
 
-// xr -> Xr[4rq][4cq] (row stride xrs), xt -> Xt[4cq][4rq] (row stride xts)
-__device__ __forceinline__ void quad_store(const Quad<bf16>& q, bf16* xr, int xrs, bf16* xt, int xts) {
+// xr -> Xr[4rq][4cq] (row stride xrs)
+__device__ __forceinline__ void quad_store_r(const Quad<bf16>& q, bf16* xr, int xrs) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x2*>(xr + r * xrs) = q.v[r];
+}
+__device__ __forceinline__ void quad_store_r(const Quad<float>& q, float* xr, int xrs) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) *reinterpret_cast<f32x4*>(xr + r * xrs) = q.v[r];
+}
+// xt -> Xt[4cq][4rq] (row stride xts): column c of the four rows
+__device__ __forceinline__ void quad_store_t(const Quad<bf16>& q, bf16* xt, int xts) {
   const u32x2 c0 = {(q.v[0].x & 0xFFFFu) | (q.v[1].x << 16), (q.v[2].x & 0xFFFFu) | (q.v[3].x << 16)};
   const u32x2 c1 = {(q.v[0].x >> 16) | (q.v[1].x & 0xFFFF0000u), (q.v[2].x >> 16) | (q.v[3].x & 0xFFFF0000u)};
   const u32x2 c2 = {(q.v[0].y & 0xFFFFu) | (q.v[1].y << 16), (q.v[2].y & 0xFFFFu) | (q.v[3].y << 16)};
@@ -172,10 +215,7 @@ __device__ __forceinline__ void quad_store(const Quad<bf16>& q, bf16* xr, int xr
   *reinterpret_cast<u32x2*>(xt + 2 * xts) = c2;
   *reinterpret_cast<u32x2*>(xt + 3 * xts) = c3;
 }
-
-__device__ __forceinline__ void quad_store(const Quad<float>& q, float* xr, int xrs, float* xt, int xts) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) *reinterpret_cast<f32x4*>(xr + r * xrs) = q.v[r];
+__device__ __forceinline__ void quad_store_t(const Quad<float>& q, float* xt, int xts) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     *reinterpret_cast<f32x4*>(xt + c * xts) = f32x4{q.v[0][c], q.v[1][c], q.v[2][c], q.v[3][c]};
@@ -196,21 +236,127 @@ template <int D>
 __device__ __forceinline__ float frag_c(const float* base_row, int cs, int g) {
   return base_row[g * (D / 4) + cs];
 }
+// The same fragments gathered from the transposed copy Xt (column-major),
+// used only when a tile's affinity must be recomputed.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_c_t(const bf16* xt, int xts, int row, int cs, int g) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = xt[(32 * cs + 8 * g + e) * xts + row];
+  return f;
+}
+template <int D>
+__device__ __forceinline__ float frag_c_t(const float* xt, int xts, int row, int cs, int g) {
+  return xt[(g * (D / 4) + cs) * xts + row];
+}
 
-// -------------------------------------------------------------- kernel
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
-__global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
-  using G = FusedGeom<T, D, KW, WJ, WI, MLDS>;
+// ------------------------------------------------- exact (shifted) path
+// Recomputes one wave's affinity tile from the transposed copy Xt and the
+// folded matrix in global memory, shifts every row by the wave's own row
+// maximum, and combines the waves with the usual max/sum rescaling.  Used only
+// for a tile whose unshifted row sums leave [2^-100, 2^100]; kept out of line
+// so that it costs the common path no registers.  Every thread of the work
+// group calls it (it contains a barrier).
+template <typename T, int D, int KW, int WJ, int WI, bool PAD>
+__device__ __attribute__((noinline)) void exact_tile(const T* __restrict__ xt, const T* __restrict__ Mg,
+                                                    float* xsm, float* xsl, int k, int wave, int lane,
+                                                    f32x4* __restrict__ s_out, float* __restrict__ fac_out) {
+  using G = FusedGeom<T, D, KW, WJ, WI, false, false>;
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
+  constexpr int JB = G::JB, CS = G::CS, NT = G::NT;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int wj = wave % WJ, wi = wave / WJ;
+  const int rw = wi * kRowsPerWave, jbase = wj * KW;
+  f32x4 s[2][JB];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cs = 0; cs < CS; ++cs) {
+    Frag xa[2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) xa[ib] = frag_c_t<D>(xt, G::XTS, rw + 16 * ib + l16, cs, g);
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const Frag mf = frag_c<D>(Mg + (int64_t)(jbase + 16 * jb + l16) * D, cs, g);
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) s[ib][jb] = MF::run(xa[ib], mf, s[ib][jb]);
+    }
+  }
+  if constexpr (PAD) {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const bool ok = jbase + 16 * jb + l16 < k;
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
+    }
+  }
+  float mloc[2][4];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = s[ib][0][r];
+#pragma unroll
+      for (int jb = 1; jb < JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
+      m = row16_max(m);
+      const float mu = (m == -INFINITY) ? 0.f : m;  // a wave holding only padding
+      float l = 0.f;
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const float e = fast_exp2(s[ib][jb][r] - mu);
+        s[ib][jb][r] = e;
+        l += e;
+      }
+      l = row16_sum(l);
+      mloc[ib][r] = m;
+      if (l16 == 0) {
+        const int trow = rw + 16 * ib + 4 * g + r;
+        xsm[trow * WJ + wj] = m;
+        xsl[trow * WJ + wj] = l;
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int trow = rw + 16 * ib + 4 * g + r;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WJ; ++w) mx = fmaxf(mx, xsm[trow * WJ + w]);
+      float den = 0.f;
+#pragma unroll
+      for (int w = 0; w < WJ; ++w) den += xsl[trow * WJ + w] * fast_exp2(xsm[trow * WJ + w] - mx);
+      fac_out[ib * 4 + r] = fast_exp2(mloc[ib][r] - mx) / den;
+    }
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) s_out[ib * JB + jb] = s[ib][jb];
+}
+
+// -------------------------------------------------------------- kernel
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE_REQ, bool PAD>
+__global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
+  using G = FusedGeom<T, D, KW, WJ, WI, MLDS, PIPE_REQ>;
+  using MF = Mfma<T>;
+  using Frag = typename MF::Frag;
+  constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT;
   static_assert(!MLDS || sizeof(T) == 2, "LDS-resident M is bf16 only");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
-  T* Xr = reinterpret_cast<T*>(lds);
-  T* Xt = reinterpret_cast<T*>(lds + G::XR_BYTES);
-  float* red_m = reinterpret_cast<float*>(lds + G::XR_BYTES + G::XT_BYTES);
-  float* red_l = red_m + WJ * G::NT;
-  T* Ms = reinterpret_cast<T*>(lds + G::XR_BYTES + G::XT_BYTES + G::RED_BYTES);
+  T* const Xr = reinterpret_cast<T*>(lds);
+  T* const Xt0 = reinterpret_cast<T*>(lds + G::OFF_XT);
+  T* const Xt1 = reinterpret_cast<T*>(lds + G::OFF_XT + (G::NXT - 1) * G::XT_BYTES);
+  float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);    // [NT][WJ]
+  float* const xsm = reinterpret_cast<float*>(lds + G::OFF_XSM);  // [NT][WJ]
+  float* const xsl = reinterpret_cast<float*>(lds + G::OFF_XSL);  // [NT][WJ]
+  int* const flags = reinterpret_cast<int*>(lds + G::OFF_FLAG);   // [kWaves]
+  T* const Ms = reinterpret_cast<T*>(lds + G::OFF_M);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,8 +367,10 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   const int wi = wave / WJ;
   const int rw = wi * kRowsPerWave;  // first tile row of this wave
   const int jbase = wj * KW;         // first prototype of this wave
-  const T* X = static_cast<const T*>(args.X);
-  const T* Mg = static_cast<const T*>(args.M);
+  const T* const X = static_cast<const T*>(args.X);
+  const T* const Mg = static_cast<const T*>(args.M);
+  const int k = args.k;
+  const bool wave_has_protos = jbase < k;
 
   const int64_t rows = args.rows;
   const int64_t ngroups = gridDim.x;
@@ -232,22 +380,166 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   if (r_begin >= r_end) return;
 
   // Folded matrix: this wave's KW rows as B fragments of the affinity product.
-  Frag mreg[MLDS ? 1 : G::JB][MLDS ? 1 : G::CS];
+  Frag mreg[MLDS ? 1 : JB][MLDS ? 1 : CS];
   if constexpr (MLDS) {
     constexpr int CH = D / 8;  // 16-byte chunks per row
     for (int idx = tid; idx < G::KPAD * CH; idx += kThreads) {
       const int r = idx / CH, ch = idx % CH;
       *reinterpret_cast<u32x4*>(Ms + r * G::MS + ch * 8) = *reinterpret_cast<const u32x4*>(Mg + r * D + ch * 8);
     }
-    // ordered before the first read by the first tile's barriers
+    // ordered before the first read by the segment's first barrier
   } else {
 #pragma unroll
-    for (int jb = 0; jb < G::JB; ++jb) {
+    for (int jb = 0; jb < JB; ++jb) {
       const T* mrow = Mg + (int64_t)(jbase + 16 * jb + l16) * D;
 #pragma unroll
-      for (int cs = 0; cs < G::CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+      for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
     }
   }
+
+  // ---- affinity of one tile: s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][jbase + 16 jb + l16],
+  // padded prototypes set to -inf.
+  auto affinity = [&](f32x4 (&s)[2][JB], const T* xr) {
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      Frag xa[2];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+        xa[ib] = frag_c<D>(xr + (rw + 16 * ib + l16) * G::XRS, cs, g);
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        Frag mf;
+        if constexpr (MLDS) {
+          mf = frag_c<D>(Ms + (jbase + 16 * jb + l16) * G::MS, cs, g);
+        } else {
+          mf = mreg[jb][cs];
+        }
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) s[ib][jb] = MF::run(xa[ib], mf, s[ib][jb]);
+      }
+    }
+    if constexpr (PAD) {
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const bool ok = jbase + 16 * jb + l16 < k;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
+      }
+    }
+  };
+
+  // ---- softmax, fast half: e = 2^s' in place (no shift), this wave's row
+  // sums to xl, and a flag when a sum leaves [2^-100, 2^100] (then the exact
+  // shifted path recomputes the tile).
+  auto softmax_fast = [&](f32x4 (&s)[2][JB]) {
+    bool bad = false;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const float e = fast_exp2(s[ib][jb][r]);
+          s[ib][jb][r] = e;
+          acc += e;
+        }
+        p[r] = acc;
+      }
+      const float z = rows4_sum_scatter(p, l16);
+      bad |= !(z >= 0x1p-100f && z <= 0x1p100f);
+      if ((l16 & 3) == 0) {
+        const int trow = rw + 16 * ib + 4 * g + ((l16 >> 3) << 1) + ((l16 >> 2) & 1);
+        xl[trow * WJ + wj] = z;
+      }
+    }
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad && wave_has_protos) != 0;
+    if (lane == 0) flags[wave] = wave_bad ? 1 : 0;  // one flag per wave: waves that split rows share wj
+  };
+
+  // ---- after the exchange barrier: per-row factors 1 / sum_w l_w
+  auto combine_fast = [&](float (&fac)[2][4]) {
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float* p = xl + (rw + 16 * ib + 4 * g + r) * WJ;
+        float l = p[0];
+#pragma unroll
+        for (int w = 1; w < WJ; ++w) l += p[w];
+        fac[ib][r] = __builtin_amdgcn_rcpf(l);
+      }
+  };
+
+  auto any_flag = [&]() {
+    int f = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) f |= flags[w];
+    return __builtin_amdgcn_readfirstlane(f) != 0;
+  };
+
+  // ---- aggregation: acc[jb][cb][r] += sum_i a[jbase+16jb+4g+r][i] X[i][16cb+l16]
+  auto aggregate = [&](f32x4 (&acc)[JB][CB], const f32x4 (&s)[2][JB], const float (&fac)[2][4], const T* xt) {
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 a[JB];
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[jb][e] = (bf16)(s[e >> 2][jb][e & 3] * fac[e >> 2][e & 3]);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const T* p = xt + (16 * cb + l16) * G::XTS + rw + 4 * g;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const f32x4 xv = *reinterpret_cast<const f32x4*>(xt + (16 * cb + l16) * G::XTS + rw + 16 * ib + 4 * g);
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[jb][cb] = MF::run(s[ib][jb][r] * fac[ib][r], xv[r], acc[jb][cb]);
+        }
+    }
+  };
+
+  // ---- after the exchange barrier: factors for the tile's rows, then the
+  // aggregation.  The exact path (rare, out of line) has its own copy of the
+  // aggregation so that the common path merges no registers with it.
+  auto finish_tile = [&](f32x4 (&acc)[JB][CB], const f32x4 (&sc)[2][JB], const T* xt) {
+    if (any_flag()) {
+      f32x4 s_tmp[2 * JB];
+      float f_tmp[8];
+      exact_tile<T, D, KW, WJ, WI, PAD>(xt, Mg, xsm, xsl, k, wave, lane, s_tmp, f_tmp);
+      f32x4 se[2][JB];
+      float fe[2][4];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) se[ib][jb] = s_tmp[ib * JB + jb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fe[ib][r] = f_tmp[ib * 4 + r];
+      }
+      aggregate(acc, se, fe, xt);
+    } else {
+      float fac[2][4];
+      combine_fast(fac);
+      aggregate(acc, sc, fac, xt);
+    }
+  };
 
   // First user touched: the largest u with offsets[u] <= r_begin.  It is
   // non-empty because offsets[u+1] > r_begin.
@@ -261,19 +553,20 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     u = lo;
   }
 
-  const int k = args.k;
   int64_t row = r_begin;
   while (row < r_end) {
     const int64_t seg_end = min(r_end, args.offsets[u + 1]);
+    const int ntiles = (int)((seg_end - row + NT - 1) / NT);
 
-    f32x4 acc[G::JB][G::CB];
+    f32x4 acc[JB][CB];
 #pragma unroll
-    for (int jb = 0; jb < G::JB; ++jb)
+    for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int cb = 0; cb < G::CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Quad<T> pre[G::BPT];
-    auto prefetch = [&](int64_t t0) {
+    auto prefetch = [&](int it) {
+      const int64_t t0 = row + (int64_t)it * NT;
 #pragma unroll
       for (int s = 0; s < G::BPT; ++s) {
         const int blk = tid + s * kThreads;
@@ -283,182 +576,114 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
         }
       }
     };
-    prefetch(row);
-
-    for (int64_t t0 = row; t0 < seg_end; t0 += G::NT) {
-      __syncthreads();  // every wave is done with the previous tile
+    auto store_r = [&]() {
 #pragma unroll
       for (int s = 0; s < G::BPT; ++s) {
         const int blk = tid + s * kThreads;
         if (G::NBLK % kThreads == 0 || blk < G::NBLK) {
           const int rq = blk / G::QC, cq = blk % G::QC;
-          quad_store(pre[s], Xr + (4 * rq) * G::XRS + 4 * cq, G::XRS, Xt + (4 * cq) * G::XTS + 4 * rq, G::XTS);
+          quad_store_r(pre[s], Xr + (4 * rq) * G::XRS + 4 * cq, G::XRS);
         }
       }
+    };
+    auto store_t = [&](T* xt) {
+#pragma unroll
+      for (int s = 0; s < G::BPT; ++s) {
+        const int blk = tid + s * kThreads;
+        if (G::NBLK % kThreads == 0 || blk < G::NBLK) {
+          const int rq = blk / G::QC, cq = blk % G::QC;
+          quad_store_t(pre[s], xt + (4 * cq) * G::XTS + 4 * rq, G::XTS);
+        }
+      }
+    };
+
+    __syncthreads();  // LDS from the previous piece (and M staging) is settled
+    if constexpr (G::PIPE) {
+      // Schedule of iteration it (two barriers):
+      //   B1 | Xt(it+1) <- regs; regs <- X(it+2); S(it+1) = affinity(Xr)
+      //        alongside softmax_fast(S(it)) -> xl, flags
+      //   B2 | factors (or the exact path); aggregate S(it) with Xt(it);
+      //        Xr <- regs (= X(it+2))
+      f32x4 S0[2][JB], S1[2][JB];
+      prefetch(0);
+      store_r();
+      store_t(Xt0);
       __syncthreads();
-      if (t0 + G::NT < seg_end) prefetch(t0 + G::NT);
-
-      // ---- affinity: s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][jbase + 16 jb + l16]
-      f32x4 s[2][G::JB];
+      prefetch(1);
+      affinity(S0, Xr);
+      __syncthreads();
+      store_r();  // X(1) (zeros past the end of the piece)
+      auto body = [&](f32x4 (&Sc)[2][JB], f32x4 (&Sn)[2][JB], int it) {
+        T* const xt_cur = (it & 1) ? Xt1 : Xt0;
+        T* const xt_nxt = (it & 1) ? Xt0 : Xt1;
+        __syncthreads();  // B1
+        store_t(xt_nxt);
+        prefetch(it + 2);
+        affinity(Sn, Xr);
+        softmax_fast(Sc);
+        // interleave: one matrix op, then LDS reads and vector work of the softmax
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < G::JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cs = 0; cs < G::CS; ++cs) {
-        Frag xa[2];
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) xa[ib] = frag_c<D>(Xr + (rw + 16 * ib + l16) * G::XRS, cs, g);
-#pragma unroll
-        for (int jb = 0; jb < G::JB; ++jb) {
-          Frag mf;
-          if constexpr (MLDS) {
-            mf = frag_c<D>(Ms + (jbase + 16 * jb + l16) * G::MS, cs, g);
-          } else {
-            mf = mreg[jb][cs];
-          }
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib) s[ib][jb] = MF::run(xa[ib], mf, s[ib][jb]);
+        for (int i = 0; i < 2 * JB * CS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
         }
+        __syncthreads();  // B2
+        finish_tile(acc, Sc, xt_cur);
+        store_r();
+      };
+      for (int it = 0; it < ntiles; it += 2) {
+        body(S0, S1, it);
+        if (it + 1 < ntiles) body(S1, S0, it + 1);
       }
-
-      // padded prototypes take no mass
-#pragma unroll
-      for (int jb = 0; jb < G::JB; ++jb) {
-        if (jbase + 16 * jb + 16 > k) {
-          const bool ok = jbase + 16 * jb + l16 < k;
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
-        }
-      }
-
-      // ---- softmax over the prototype axis (base 2; M carries log2(e))
-      float fac[2][4];
-      float mloc[2][4];
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float m = s[ib][0][r];
-#pragma unroll
-          for (int jb = 1; jb < G::JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
-          m = row16_max(m);
-          const float mu = (m == -INFINITY) ? 0.f : m;  // a wave holding only padding
-          float l = 0.f;
-#pragma unroll
-          for (int jb = 0; jb < G::JB; ++jb) {
-            const float e = fast_exp2(s[ib][jb][r] - mu);
-            s[ib][jb][r] = e;
-            l += e;
-          }
-          l = row16_sum(l);
-          mloc[ib][r] = m;
-          fac[ib][r] = l;
-        }
-      }
-      if constexpr (WJ == 1) {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) fac[ib][r] = 1.f / fac[ib][r];
-      } else {
-        if (l16 == 0) {
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int trow = rw + 16 * ib + 4 * g + r;
-              red_m[wj * G::NT + trow] = mloc[ib][r];
-              red_l[wj * G::NT + trow] = fac[ib][r];
-            }
-        }
+    } else {
+      f32x4 S[2][JB];
+      prefetch(0);
+      for (int it = 0; it < ntiles; ++it) {
+        if (it > 0) __syncthreads();  // every wave is done with the previous tile
+        store_r();
+        store_t(Xt0);
         __syncthreads();
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int trow = rw + 16 * ib + 4 * g + r;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < WJ; ++w) mx = fmaxf(mx, red_m[w * G::NT + trow]);
-            float den = 0.f;
-#pragma unroll
-            for (int w = 0; w < WJ; ++w) den += red_l[w * G::NT + trow] * fast_exp2(red_m[w * G::NT + trow] - mx);
-            fac[ib][r] = fast_exp2(mloc[ib][r] - mx) / den;
-          }
-      }
-
-      // ---- aggregation: acc[jb][cb][r] += sum_i a[jbase+16jb+4g+r][i] X[i][16cb+l16]
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 xb[G::CB];
-#pragma unroll
-        for (int cb = 0; cb < G::CB; ++cb) {
-          const T* xt = Xt + (16 * cb + l16) * G::XTS + rw + 4 * g;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(xt);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(xt + 16);
-          xb[cb] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        }
-#pragma unroll
-        for (int jb = 0; jb < G::JB; ++jb) {
-          bf16x8 a;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a[e] = (bf16)(s[e >> 2][jb][e & 3] * fac[e >> 2][e & 3]);
-#pragma unroll
-          for (int cb = 0; cb < G::CB; ++cb) acc[jb][cb] = MF::run(a, xb[cb], acc[jb][cb]);
-        }
-      } else {
-        f32x4 xb[G::CB][2];
-#pragma unroll
-        for (int cb = 0; cb < G::CB; ++cb)
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib)
-            xb[cb][ib] = *reinterpret_cast<const f32x4*>(Xt + (16 * cb + l16) * G::XTS + rw + 16 * ib + 4 * g);
-#pragma unroll
-        for (int jb = 0; jb < G::JB; ++jb)
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float a = s[ib][jb][r] * fac[ib][r];
-#pragma unroll
-              for (int cb = 0; cb < G::CB; ++cb) acc[jb][cb] = MF::run(a, xb[cb][ib][r], acc[jb][cb]);
-            }
+        prefetch(it + 1);
+        affinity(S, Xr);
+        softmax_fast(S);
+        __syncthreads();
+        finish_tile(acc, S, Xt0);
       }
     }
 
     // ---- flush this (group, user) piece.  Partial layout per slot:
     // [wj][jb][cb][lane][4] float32, i.e. each lane's accumulator registers in
-    // order; the reduction kernel maps it back to (prototype, column).
+    // order; the reduction kernel maps it back to (prototype, column).  Waves
+    // that split the rows first add their accumulators through LDS, one
+    // prototype block at a time, in a fixed order.
     if constexpr (WI > 1) {
-      float* accbuf = reinterpret_cast<float*>(lds);
-      for (int st = WI - 1; st >= 1; --st) {
-        __syncthreads();
-        if (wi == st) {
+      float* stage = reinterpret_cast<float*>(lds);
 #pragma unroll
-          for (int jb = 0; jb < G::JB; ++jb)
+      for (int jb = 0; jb < JB; ++jb) {
+        for (int st = WI - 1; st >= 1; --st) {
+          __syncthreads();
+          if (wi == st) {
 #pragma unroll
-            for (int cb = 0; cb < G::CB; ++cb)
-              *reinterpret_cast<f32x4*>(accbuf + (((wj * G::JB + jb) * G::CB + cb) * 64 + lane) * 4) = acc[jb][cb];
-        }
-        __syncthreads();
-        if (wi == st - 1) {
+            for (int cb = 0; cb < CB; ++cb)
+              *reinterpret_cast<f32x4*>(stage + ((wj * CB + cb) * 64 + lane) * 4) = acc[jb][cb];
+          }
+          __syncthreads();
+          if (wi == st - 1) {
 #pragma unroll
-          for (int jb = 0; jb < G::JB; ++jb)
-#pragma unroll
-            for (int cb = 0; cb < G::CB; ++cb)
-              acc[jb][cb] += *reinterpret_cast<const f32x4*>(accbuf + (((wj * G::JB + jb) * G::CB + cb) * 64 + lane) * 4);
+            for (int cb = 0; cb < CB; ++cb)
+              acc[jb][cb] += *reinterpret_cast<const f32x4*>(stage + ((wj * CB + cb) * 64 + lane) * 4);
+          }
         }
       }
     }
     if (wi == 0) {
       float* dst = args.partial + (grp + u) * (int64_t)(G::KPAD * D);
 #pragma unroll
-      for (int jb = 0; jb < G::JB; ++jb)
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int cb = 0; cb < G::CB; ++cb)
-          *reinterpret_cast<f32x4*>(dst + (((wj * G::JB + jb) * G::CB + cb) * 64 + lane) * 4) = acc[jb][cb];
+        for (int cb = 0; cb < CB; ++cb)
+          *reinterpret_cast<f32x4*>(dst + (((wj * JB + jb) * CB + cb) * 64 + lane) * 4) = acc[jb][cb];
     }
 
     row = seg_end;
@@ -467,38 +692,31 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   }
 }
 
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE, bool PAD>
 hipError_t launch_fused_t(const FusedArgs& args, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS>), dim3(groups), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PIPE, PAD>), dim3(groups), dim3(kThreads), 0, stream,
+                     args);
   return hipGetLastError();
 }
 
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE, bool PAD>
 hipError_t occupancy_t(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, sa_fused_kernel<T, D, KW, WJ, WI, MLDS>, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PIPE, PAD>, kThreads,
+                                                      0);
 }
 
-// Plans compiled for one (dtype, d).  occ != nullptr turns the call into an
-// occupancy query for that plan.
-template <typename T, int D>
-hipError_t dispatch_fused(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
-#define SA_PLAN(KW_, WJ_, MLDS_)                                                          \
-  if (p.kw == KW_ && p.waves_k == WJ_ && p.m_in_lds == MLDS_)                             \
-    return occ ? occupancy_t<T, D, KW_, WJ_, kWaves / WJ_, MLDS_>(occ)                    \
-               : launch_fused_t<T, D, KW_, WJ_, kWaves / WJ_, MLDS_>(a, groups, st);
-  SA_PLAN(16, 1, 0)
-  SA_PLAN(32, 1, 0)
-  SA_PLAN(64, 1, 0)
-  SA_PLAN(64, 2, 0)
-  SA_PLAN(64, 4, 0)
-  if constexpr (sizeof(T) == 2) {
-    SA_PLAN(128, 4, 1)
-    if constexpr (D == 64) {
-      SA_PLAN(256, 4, 1)
-    }
-  }
-#undef SA_PLAN
-  return hipErrorInvalidValue;
+// One plan of the fused pass: launch it, or (occ != nullptr) report how
+// many of its work groups fit on a compute unit.
+template <typename T, int D, int KW, int WJ, bool MLDS>
+hipError_t run_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+  if (p.k == p.k_pad)
+    return occ ? occupancy_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, false>(occ)
+               : launch_fused_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, false>(a, groups, st);
+  return occ ? occupancy_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, true>(occ)
+             : launch_fused_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, true>(a, groups, st);
 }
+
+#define SA_PLAN(T_, D_, KW_, WJ_, MLDS_) \
+  if (p.kw == KW_ && p.waves_k == WJ_ && p.m_in_lds == MLDS_) return run_plan<T_, D_, KW_, WJ_, MLDS_>(p, a, groups, st, occ);
 
 }  // namespace sa

@@ -1,16 +1,24 @@
-// Fused compression kernels for bf16 inputs, d = 64.  One translation unit
-// per (dtype, d) so the instantiations compile in parallel.
+// Fused compression plans for bf16 inputs, d = 64: accumulators of at most 128 registers per lane.
+// Each plan group is its own translation unit so groups compile in parallel
+// and can take their own code-generation options.
 #include "sa_fused.hpp"
 
 namespace sa {
 
-hipError_t launch_fused_bf16_d64(const Plan& p, const FusedArgs& a, int groups, hipStream_t st) {
-  return dispatch_fused<bf16, 64>(p, a, groups, st, nullptr);
-}
-
-hipError_t occupancy_bf16_d64(const Plan& p, int* n) {
-  static const FusedArgs unused{};
-  return dispatch_fused<bf16, 64>(p, unused, 0, nullptr, n);
+hipError_t dispatch_bf16_d64(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+  SA_PLAN(bf16, 64, 16, 1, false)
+  SA_PLAN(bf16, 64, 32, 1, false)
+  SA_PLAN(bf16, 64, 64, 1, false)
+  SA_PLAN(bf16, 64, 64, 2, false)
+  SA_PLAN(bf16, 64, 64, 4, false)
+  SA_PLAN(bf16, 64, 16, 1, true)
+  SA_PLAN(bf16, 64, 32, 1, true)
+  SA_PLAN(bf16, 64, 64, 1, true)
+  SA_PLAN(bf16, 64, 64, 2, true)
+  SA_PLAN(bf16, 64, 64, 4, true)
+  SA_PLAN(bf16, 64, 128, 2, true)
+  SA_PLAN(bf16, 64, 128, 4, true)
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sa

@@ -1,16 +1,17 @@
-// Fused compression kernels for f32 inputs, d = 128.  One translation unit
-// per (dtype, d) so the instantiations compile in parallel.
+// Fused compression plans for float32 inputs, d = 128: float32 inputs.
+// Each plan group is its own translation unit so groups compile in parallel
+// and can take their own code-generation options.
 #include "sa_fused.hpp"
 
 namespace sa {
 
-hipError_t launch_fused_f32_d128(const Plan& p, const FusedArgs& a, int groups, hipStream_t st) {
-  return dispatch_fused<float, 128>(p, a, groups, st, nullptr);
-}
-
-hipError_t occupancy_f32_d128(const Plan& p, int* n) {
-  static const FusedArgs unused{};
-  return dispatch_fused<float, 128>(p, unused, 0, nullptr, n);
+hipError_t dispatch_f32_d128(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+  SA_PLAN(float, 128, 16, 1, false)
+  SA_PLAN(float, 128, 32, 1, false)
+  SA_PLAN(float, 128, 64, 1, false)
+  SA_PLAN(float, 128, 64, 2, false)
+  SA_PLAN(float, 128, 64, 4, false)
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sa

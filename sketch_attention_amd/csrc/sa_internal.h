@@ -66,14 +66,14 @@ hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hip
 // Workgroups of the fused kernel that fit on one compute unit at once.
 hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
 
-// Per-instantiation entry points, one translation unit per (dtype, d).
-hipError_t launch_fused_bf16_d64(const Plan&, const FusedArgs&, int, hipStream_t);
-hipError_t launch_fused_bf16_d128(const Plan&, const FusedArgs&, int, hipStream_t);
-hipError_t launch_fused_f32_d64(const Plan&, const FusedArgs&, int, hipStream_t);
-hipError_t launch_fused_f32_d128(const Plan&, const FusedArgs&, int, hipStream_t);
-hipError_t occupancy_bf16_d64(const Plan&, int*);
-hipError_t occupancy_bf16_d128(const Plan&, int*);
-hipError_t occupancy_f32_d64(const Plan&, int*);
-hipError_t occupancy_f32_d128(const Plan&, int*);
+// Plan groups, one translation unit each (see sa_fused_*.hip).  With
+// occ != nullptr they report occupancy instead of launching.
+using DispatchFn = hipError_t (*)(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_bf16_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_bf16_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_bf16_d64_large(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_bf16_d128_large(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_f32_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_f32_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 
 }  // namespace sa

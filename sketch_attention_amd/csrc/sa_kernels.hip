@@ -76,17 +76,24 @@ hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hip
 
 // --------------------------------------------------------------- reduce
 // out[u] = sum over the work groups b that touched user u of partial[b + u],
-// in increasing b (fixed order, so results are bitwise reproducible).  Work
+// in a fixed order (so results are bitwise reproducible).  Work
 // group b of G covers rows [floor(b*R/G), floor((b+1)*R/G)), so the group
 // holding row r is floor(((r+1)*G - 1) / R).  A user with no rows gets zeros.
 //
 // Partial slots hold each lane's accumulator registers in order,
 // [wj][jb][cb][lane][4]; float4 number p of a slot holds prototypes
 // wj*kw + 16*jb + 4*(lane/16) + 0..3 at column 16*cb + lane%16.
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+//
+// One thread per float4 of a slot, 64 threads per group (many groups, so the
+// partial reads of all users spread over the whole GPU); four running sums
+// over b = b0 + 4q + t, t = 0..3, keep four loads in flight and are added in
+// a fixed order at the end.
+constexpr int kReduceThreads = 64;
+
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   const int u = blockIdx.y;
   const int slot_f4 = a.k_pad * a.d / 4;
-  const int p = blockIdx.x * 256 + threadIdx.x;
+  const int p = blockIdx.x * kReduceThreads + threadIdx.x;
   if (p >= slot_f4) return;
   const int64_t r0 = a.offsets[u], r1 = a.offsets[u + 1];
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -94,8 +101,20 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
     const int64_t G = a.groups, R = a.rows;
     const int64_t b0 = ((r0 + 1) * G - 1) / R;
     const int64_t b1 = (r1 * G - 1) / R;
-    const f32x4* part = reinterpret_cast<const f32x4*>(a.partial);
-    for (int64_t b = b0; b <= b1; ++b) s += part[(b + u) * slot_f4 + p];
+    const f32x4* part = reinterpret_cast<const f32x4*>(a.partial) + (b0 + u) * slot_f4 + p;
+    const int64_t n = b1 - b0 + 1;
+    f32x4 t0 = s, t1 = s, t2 = s, t3 = s;
+    int64_t q = 0;
+    for (; q + 4 <= n; q += 4) {
+      t0 += __builtin_nontemporal_load(part + (q + 0) * slot_f4);
+      t1 += __builtin_nontemporal_load(part + (q + 1) * slot_f4);
+      t2 += __builtin_nontemporal_load(part + (q + 2) * slot_f4);
+      t3 += __builtin_nontemporal_load(part + (q + 3) * slot_f4);
+    }
+    if (q + 0 < n) t0 += __builtin_nontemporal_load(part + (q + 0) * slot_f4);
+    if (q + 1 < n) t1 += __builtin_nontemporal_load(part + (q + 1) * slot_f4);
+    if (q + 2 < n) t2 += __builtin_nontemporal_load(part + (q + 2) * slot_f4);
+    s = (t0 + t1) + (t2 + t3);
   }
   const int lane = p & 63;
   int t = p >> 6;
@@ -114,31 +133,35 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   const int slot_f4 = a.k_pad * a.d / 4;
-  hipLaunchKernelGGL(reduce_kernel, dim3((slot_f4 + 255) / 256, a.users), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(reduce_kernel, dim3((slot_f4 + kReduceThreads - 1) / kReduceThreads, a.users),
+                     dim3(kReduceThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ dispatch
-hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream) {
-  if (plan.dtype == 1) {
-    if (plan.d == 64) return launch_fused_bf16_d64(plan, args, groups, stream);
-    if (plan.d == 128) return launch_fused_bf16_d128(plan, args, groups, stream);
-  } else {
-    if (plan.d == 64) return launch_fused_f32_d64(plan, args, groups, stream);
-    if (plan.d == 128) return launch_fused_f32_d128(plan, args, groups, stream);
+// Accumulators of more than 128 registers per lane (kw * d > 8192) live in
+// AGPRs and are compiled separately from the smaller plans.
+static DispatchFn plan_group(const Plan& p) {
+  const bool large = p.kw * p.d > 8192;
+  if (p.dtype == 1) {
+    if (p.d == 64) return large ? dispatch_bf16_d64_large : dispatch_bf16_d64;
+    if (p.d == 128) return large ? dispatch_bf16_d128_large : dispatch_bf16_d128;
+  } else if (!large) {
+    if (p.d == 64) return dispatch_f32_d64;
+    if (p.d == 128) return dispatch_f32_d128;
   }
-  return hipErrorInvalidValue;
+  return nullptr;
+}
+
+hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream) {
+  DispatchFn f = plan_group(plan);
+  return f ? f(plan, args, groups, stream, nullptr) : hipErrorInvalidValue;
 }
 
 hipError_t fused_occupancy(const Plan& plan, int* n) {
-  if (plan.dtype == 1) {
-    if (plan.d == 64) return occupancy_bf16_d64(plan, n);
-    if (plan.d == 128) return occupancy_bf16_d128(plan, n);
-  } else {
-    if (plan.d == 64) return occupancy_f32_d64(plan, n);
-    if (plan.d == 128) return occupancy_f32_d128(plan, n);
-  }
-  return hipErrorInvalidValue;
+  DispatchFn f = plan_group(plan);
+  static const FusedArgs unused{};
+  return f ? f(plan, unused, 0, nullptr, n) : hipErrorInvalidValue;
 }
 
 }  // namespace sa

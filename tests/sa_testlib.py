@@ -22,11 +22,29 @@ def centred(a: np.ndarray) -> np.ndarray:
     return a - a.mean(axis=0, keepdims=True)
 
 
+# Unit roundoff of the weights as the aggregation product consumes them:
+# each weight a_ji is rounded once to bfloat16 (relative error <= 2^-9) or
+# used in float32.  Rounding every weight of row j perturbs the sketch row by
+# at most u * sum_i a_ji |x_i|, i.e. by u times the sketch of |X| under the
+# same weights; the row-centred comparison is allowed that much on top of its
+# relative tolerance, because when all sketch rows are nearly equal (say k = 2
+# with weights near 1/2) the centred sketch is tiny and the weight rounding
+# alone exceeds any relative bound on it.
+WEIGHT_ROUNDING = {"bf16": 2.0 ** -8, "f32": 2.0 ** -20}
+
+
 def worst_errors(got: np.ndarray, want: np.ndarray):
     """(max over users of the normwise error, same on the centred sketches)."""
     e = max(normwise_err(g, w) for g, w in zip(got, want))
     c = max(normwise_err(centred(g), centred(w)) for g, w in zip(got, want))
     return e, c
+
+
+def centred_within(got: np.ndarray, want: np.ndarray, abs_weighted: np.ndarray, tol: float, dtype: str) -> bool:
+    """Centred check with the weight-rounding allowance described above."""
+    gc, wc = centred(got), centred(want)
+    err = float(np.max(np.abs(gc - wc)))
+    return err <= tol * float(np.max(np.abs(wc))) + WEIGHT_ROUNDING[dtype] * float(np.max(abs_weighted))
 
 
 def torch_dtype(name: str):

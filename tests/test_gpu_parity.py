@@ -16,7 +16,7 @@ import torch
 from oracle import sa_oracle as O
 from sketch_attention_amd import SketchAttention, binding as B
 from sketch_attention_amd import workloads as W
-from sa_testlib import TOL, run_gpu, to_device, worst_errors, normwise_err
+from sa_testlib import TOL, centred_within, normwise_err, run_gpu, to_device, worst_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,16 @@ def _assert_parity(wl, got, users=None, tol=None):
     e, c = worst_errors(sel, want)
     tol = TOL[wl.dtype] if tol is None else tol
     print(f"[parity] {wl.name} users={'all' if users is None else list(users)} err={e:.3e} centred={c:.3e}", flush=True)
-    assert e <= tol and c <= tol, (e, c)
+    assert e <= tol, (e, c)
+    if c > tol:
+        # only ill-conditioned centred sketches reach this: apply the weight-rounding allowance
+        ulist = list(range(wl.num_users)) if users is None else list(users)
+        for g, w, u in zip(sel, want, ulist):
+            Xu = wl.user_rows(u).astype(np.float64)
+            if Xu.shape[0] == 0:
+                continue
+            A = O.assignment(O.affinity(Xu, wl.P, wl.W_Q, wl.W_K, wl.tau))
+            assert centred_within(g, w, A @ np.abs(Xu), tol, wl.dtype), (u, e, c)
     return e, c
 
 
@@ -197,6 +206,44 @@ def test_wk_zero_gives_uniform_rows():
 def test_large_tau_hard_assignment():
     """Scores far outside exp's range: the softmax must stay finite and exact."""
     wl = W.make_workload(lengths=[4000, 33], d=128, k=64, dtype="f32", seed=15, tau=40.0, name="hard-f32")
+    got = run_gpu(wl)
+    assert np.isfinite(got).all()
+    _assert_parity(wl, got)
+
+
+def _hard_bf16_workload(lengths, d, k, tau, seed, spike_rows=None):
+    """bf16-exact weights (P = 8 I, W_Q = W_K = I) and rows with one dominant
+    coordinate: scores reach several hundred (far past exp2's range), yet the
+    assignment is a clean argmax, so rounding cannot change the answer."""
+    rng = np.random.default_rng(seed)
+    n = int(sum(lengths))
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    rows = np.arange(n) if spike_rows is None else spike_rows
+    X[rows, rng.integers(0, min(d, k), rows.shape[0])] += 6.0
+    X = W.round_to_bf16(X)
+    P = np.zeros((k, d), np.float32)
+    P[np.arange(min(k, d)), np.arange(min(k, d))] = 8.0
+    eye = np.eye(d, dtype=np.float32)
+    offs = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return W.Workload(name="hard-bf16", X=X, offsets=offs, P=P, W_Q=eye, W_K=eye.copy(), tau=tau, dtype="bf16")
+
+
+@pytest.mark.parametrize("k,wave_split", [(64, "rows"), (128, "mixed"), (256, "prototypes")])
+def test_exact_path_bf16(k, wave_split):
+    """Every tile overflows the unshifted softmax and takes the exact path."""
+    wl = _hard_bf16_workload([3000, 77, 1], d=64, k=k, tau=4.0, seed=19 + k)
+    got = run_gpu(wl)
+    assert np.isfinite(got).all()
+    _assert_parity(wl, got)
+
+
+def test_exact_path_in_some_tiles_only():
+    """Only a few rows have huge scores: their tiles go exact, the rest stay fast."""
+    rng = np.random.default_rng(20)
+    spikes = np.sort(rng.choice(5000, size=7, replace=False))
+    wl = _hard_bf16_workload([5000], d=64, k=128, tau=4.0, seed=21, spike_rows=spikes)
+    wl.X = W.round_to_bf16(wl.X * np.float32(0.05))     # ordinary rows: small scores
+    wl.X[spikes] = W.round_to_bf16(wl.X[spikes] * np.float32(20.0))
     got = run_gpu(wl)
     assert np.isfinite(got).all()
     _assert_parity(wl, got)
