@@ -26,14 +26,12 @@ SOURCES = [
     "sa_kernels.hip",
     "sa_fused_bf16_d64.hip",
     "sa_fused_bf16_d128.hip",
-    "sa_fused_bf16_d64_large.hip",
-    "sa_fused_bf16_d128_large.hip",
     "sa_fused_f32_d64.hip",
     "sa_fused_f32_d128.hip",
 ]
-# Plan groups whose accumulators fit in 128 architectural registers per lane
-# keep every matrix-core result in VGPRs, so the softmax reads the affinity
-# tile without AGPR moves; larger accumulators stay in AGPRs.
+# The bf16 plans (accumulators of at most 128 registers per lane) keep every
+# matrix-core result in VGPRs, so the softmax reads the affinity tile without
+# AGPR moves.
 VGPR_FORM = {"sa_fused_bf16_d64.hip", "sa_fused_bf16_d128.hip"}
 # Packed fp32 VALU instructions are disabled for all device code.
 HIPCC_FLAGS = [

@@ -49,14 +49,16 @@ constexpr double kLog2e = 1.4426950408889634073599246810019;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Plan of the fused pass for a supported (dtype, d, k); see sa_fused.hpp.
-// bf16 plans keep the folded matrix in LDS (shared by the waves); float32
-// plans keep it in registers.  SA_PLAN="kw,waves_k,m_in_lds" in the
-// environment overrides the choice when that plan exists for (dtype, d, k).
+// bf16: eight waves per group (two per SIMD), the folded matrix in LDS, and
+// at most 128 accumulator registers per lane (kw * d <= 8192).  float32:
+// four waves, folded matrix in registers.  SA_PLAN="kw,waves_k,waves_rows,m_in_lds"
+// in the environment overrides the choice when that plan is compiled.
 Plan make_plan(int dtype, int d, int k) {
   Plan p{};
   p.dtype = dtype;
   p.d = d;
   p.k = k;
+  const int waves = dtype == SA_BF16 ? 8 : 4;
   const int k16 = (k + 15) / 16 * 16;
   if (k16 <= 16) {
     p.kw = 16; p.waves_k = 1;
@@ -69,19 +71,19 @@ Plan make_plan(int dtype, int d, int k) {
   } else if (k <= 256) {
     p.kw = 64; p.waves_k = 4;
   } else if (k <= 512) {
-    p.kw = 128; p.waves_k = 4;
+    p.kw = 64; p.waves_k = 8;
   } else {
-    p.kw = 256; p.waves_k = 4;
+    p.kw = 128; p.waves_k = 8;
   }
+  p.waves_rows = waves / p.waves_k;
   p.m_in_lds = dtype == SA_BF16 ? 1 : 0;
   if (const char* env = std::getenv("SA_PLAN")) {
-    int kw = 0, wk = 0, ml = 0;
-    if (std::sscanf(env, "%d,%d,%d", &kw, &wk, &ml) == 3 && kw % 16 == 0 && kw > 0 &&
-        (wk == 1 || wk == 2 || wk == 4) && kw * wk >= k) {
-      p.kw = kw; p.waves_k = wk; p.m_in_lds = ml ? 1 : 0;
+    int kw = 0, wk = 0, wr = 0, ml = 0;
+    if (std::sscanf(env, "%d,%d,%d,%d", &kw, &wk, &wr, &ml) == 4 && kw % 16 == 0 && kw > 0 && wk > 0 && wr > 0 &&
+        kw * wk >= k) {
+      p.kw = kw; p.waves_k = wk; p.waves_rows = wr; p.m_in_lds = ml ? 1 : 0;
     }
   }
-  p.waves_rows = sa::kWaves / p.waves_k;
   p.k_pad = p.kw * p.waves_k;
   p.tile_rows = sa::kRowsPerWave * p.waves_rows;
   return p;

@@ -117,41 +117,43 @@ __device__ __forceinline__ float rows4_sum_scatter(const float (&p)[4], int l16)
 }
 
 // ------------------------------------------------------ static geometry
-// PIPE_REQ asks for the software-pipelined schedule (affinity of tile t+1
-// issued alongside the softmax of tile t, two Xt buffers); it is used when the
-// registers (two affinity tiles) and LDS allow it.
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE_REQ>
+// NW waves per work group: WJ split the prototypes (KW each), WI = NW / WJ
+// split the rows of a tile (32 rows each).  The transposed tile copy Xt is
+// double-buffered (two barriers per tile) when LDS allows, else single (three).
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
 struct FusedGeom {
-  static_assert(WJ * WI == kWaves, "four waves per work group");
   static_assert(KW % 16 == 0 && D % 32 == 0, "tile shape");
+  static constexpr int NW = WJ * WI;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int NT = kRowsPerWave * WI;   // tile rows
   static constexpr int JB = KW / 16;             // 16-prototype blocks per wave
   static constexpr int CB = D / 16;              // 16-column blocks of the output
   static constexpr int CS = D / Mfma<T>::kStep;  // affinity reduction steps
   static constexpr int KPAD = KW * WJ;
   static constexpr int XRS = D + 16 / (int)sizeof(T);  // Xr row stride (elements), +16 bytes
-  static constexpr int XTS = NT + 4;                   // Xt row stride (elements)
+  static constexpr int XTS = NT + (sizeof(T) == 2 ? 8 : 4);  // Xt row stride (elements)
   static constexpr int MS = D + 8;                     // LDS M row stride (bf16 elements)
   static constexpr int XR_BYTES = NT * XRS * (int)sizeof(T);
   static constexpr int XT_BYTES = D * XTS * (int)sizeof(T);
   static constexpr int XL_BYTES = NT * WJ * 4;         // per-wave row sums
-  static constexpr int FLAG_BYTES = 4 * kWaves;
+  static constexpr int FLAG_BYTES = 4 * NW;
   static constexpr int M_BYTES = MLDS ? KPAD * MS * 2 : 0;
   static constexpr int stage_bytes = WI > 1 ? WJ * CB * 64 * 16 : 0;  // one prototype block of every wave's accumulators
-  static constexpr int region(int nxt) { return XR_BYTES + nxt * XT_BYTES + 3 * XL_BYTES + FLAG_BYTES; }
-  static constexpr bool PIPE = PIPE_REQ && KW <= 128 && region(2) + M_BYTES <= 160 * 1024;
-  static constexpr int NXT = PIPE ? 2 : 1;
+  static constexpr int XF_BYTES = NT * 4;              // per-row factors
+  static constexpr int region(int nxt) { return XR_BYTES + nxt * XT_BYTES + 3 * XL_BYTES + XF_BYTES + FLAG_BYTES; }
+  static constexpr int NXT = region(2) + M_BYTES <= 160 * 1024 ? 2 : 1;
   static constexpr int XREG = region(NXT) > stage_bytes ? region(NXT) : stage_bytes;
   static constexpr int OFF_XT = XR_BYTES;
   static constexpr int OFF_XL = XR_BYTES + NXT * XT_BYTES;
-  static constexpr int OFF_XSM = OFF_XL + XL_BYTES;     // slow path: per-wave row maxima
-  static constexpr int OFF_XSL = OFF_XSM + XL_BYTES;    // slow path: per-wave row sums
-  static constexpr int OFF_FLAG = OFF_XSL + XL_BYTES;
+  static constexpr int OFF_XSM = OFF_XL + XL_BYTES;     // exact path: per-wave row maxima
+  static constexpr int OFF_XSL = OFF_XSM + XL_BYTES;    // exact path: per-wave row sums
+  static constexpr int OFF_XF = OFF_XSL + XL_BYTES;
+  static constexpr int OFF_FLAG = OFF_XF + XF_BYTES;
   static constexpr int OFF_M = XREG;
   static constexpr int LDS_BYTES = XREG + M_BYTES;
   static constexpr int QC = D / 4;                     // 4-column quads per row
   static constexpr int NBLK = (NT / 4) * QC;           // 4x4 blocks per tile
-  static constexpr int BPT = (NBLK + kThreads - 1) / kThreads;
+  static constexpr int BPT = (NBLK + THREADS - 1) / THREADS;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
@@ -173,26 +175,34 @@ struct Quad<float> {
   f32x4 v[4];
 };
 
+// tile: first row of the tile (uniform); rows_left: valid rows from there,
+// 1..NT; r4 = 4*rq.  Offsets stay 32-bit.
 template <int D>
-__device__ __forceinline__ void quad_load(Quad<bf16>& q, const bf16* X, int64_t row, int64_t row_end, int col) {
+__device__ __forceinline__ void quad_load(Quad<bf16>& q, const bf16* tile, int rows_left, int r4, int col) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t rr = row + r < row_end ? row + r : row_end - 1;
-    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(X + rr * D + col));
-    const bool ok = row + r < row_end;
+    const int rr = r4 + r < rows_left ? r4 + r : rows_left - 1;
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + rr * D + col));
+    const bool ok = r4 + r < rows_left;
     q.v[r] = u32x2{ok ? v.x : 0u, ok ? v.y : 0u};
   }
 }
 
 template <int D>
-__device__ __forceinline__ void quad_load(Quad<float>& q, const float* X, int64_t row, int64_t row_end, int col) {
+__device__ __forceinline__ void quad_load(Quad<float>& q, const float* tile, int rows_left, int r4, int col) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t rr = row + r < row_end ? row + r : row_end - 1;
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(X + rr * D + col));
-    const bool ok = row + r < row_end;
+    const int rr = r4 + r < rows_left ? r4 + r : rows_left - 1;
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(tile + rr * D + col));
+    const bool ok = r4 + r < rows_left;
     q.v[r] = f32x4{ok ? v[0] : 0.f, ok ? v[1] : 0.f, ok ? v[2] : 0.f, ok ? v[3] : 0.f};
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void quad_zero(Quad<T>& q) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) q.v[r] = {};
 }
 
 // xr -> Xr[4rq][4cq] (row stride xrs)
@@ -250,102 +260,13 @@ __device__ __forceinline__ float frag_c_t(const float* xt, int xts, int row, int
   return xt[(g * (D / 4) + cs) * xts + row];
 }
 
-// ------------------------------------------------- exact (shifted) path
-// Recomputes one wave's affinity tile from the transposed copy Xt and the
-// folded matrix in global memory, shifts every row by the wave's own row
-// maximum, and combines the waves with the usual max/sum rescaling.  Used only
-// for a tile whose unshifted row sums leave [2^-100, 2^100]; kept out of line
-// so that it costs the common path no registers.  Every thread of the work
-// group calls it (it contains a barrier).
-template <typename T, int D, int KW, int WJ, int WI, bool PAD>
-__device__ __attribute__((noinline)) void exact_tile(const T* __restrict__ xt, const T* __restrict__ Mg,
-                                                    float* xsm, float* xsl, int k, int wave, int lane,
-                                                    f32x4* __restrict__ s_out, float* __restrict__ fac_out) {
-  using G = FusedGeom<T, D, KW, WJ, WI, false, false>;
-  using MF = Mfma<T>;
-  using Frag = typename MF::Frag;
-  constexpr int JB = G::JB, CS = G::CS, NT = G::NT;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int wj = wave % WJ, wi = wave / WJ;
-  const int rw = wi * kRowsPerWave, jbase = wj * KW;
-  f32x4 s[2][JB];
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int cs = 0; cs < CS; ++cs) {
-    Frag xa[2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) xa[ib] = frag_c_t<D>(xt, G::XTS, rw + 16 * ib + l16, cs, g);
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const Frag mf = frag_c<D>(Mg + (int64_t)(jbase + 16 * jb + l16) * D, cs, g);
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) s[ib][jb] = MF::run(xa[ib], mf, s[ib][jb]);
-    }
-  }
-  if constexpr (PAD) {
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const bool ok = jbase + 16 * jb + l16 < k;
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
-    }
-  }
-  float mloc[2][4];
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float m = s[ib][0][r];
-#pragma unroll
-      for (int jb = 1; jb < JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
-      m = row16_max(m);
-      const float mu = (m == -INFINITY) ? 0.f : m;  // a wave holding only padding
-      float l = 0.f;
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb) {
-        const float e = fast_exp2(s[ib][jb][r] - mu);
-        s[ib][jb][r] = e;
-        l += e;
-      }
-      l = row16_sum(l);
-      mloc[ib][r] = m;
-      if (l16 == 0) {
-        const int trow = rw + 16 * ib + 4 * g + r;
-        xsm[trow * WJ + wj] = m;
-        xsl[trow * WJ + wj] = l;
-      }
-    }
-  __syncthreads();
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int trow = rw + 16 * ib + 4 * g + r;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < WJ; ++w) mx = fmaxf(mx, xsm[trow * WJ + w]);
-      float den = 0.f;
-#pragma unroll
-      for (int w = 0; w < WJ; ++w) den += xsl[trow * WJ + w] * fast_exp2(xsm[trow * WJ + w] - mx);
-      fac_out[ib * 4 + r] = fast_exp2(mloc[ib][r] - mx) / den;
-    }
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) s_out[ib * JB + jb] = s[ib][jb];
-}
-
 // -------------------------------------------------------------- kernel
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE_REQ, bool PAD>
-__global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
-  using G = FusedGeom<T, D, KW, WJ, WI, MLDS, PIPE_REQ>;
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
+__global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) {
+  using G = FusedGeom<T, D, KW, WJ, WI, MLDS>;
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
-  constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT;
+  constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, NW = G::NW, THREADS = G::THREADS;
   static_assert(!MLDS || sizeof(T) == 2, "LDS-resident M is bf16 only");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
@@ -355,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);    // [NT][WJ]
   float* const xsm = reinterpret_cast<float*>(lds + G::OFF_XSM);  // [NT][WJ]
   float* const xsl = reinterpret_cast<float*>(lds + G::OFF_XSL);  // [NT][WJ]
-  int* const flags = reinterpret_cast<int*>(lds + G::OFF_FLAG);   // [kWaves]
+  float* const xf = reinterpret_cast<float*>(lds + G::OFF_XF);    // [NT]
+  int* const flags = reinterpret_cast<int*>(lds + G::OFF_FLAG);   // [NW]
   T* const Ms = reinterpret_cast<T*>(lds + G::OFF_M);
 
   const int tid = threadIdx.x;
@@ -383,11 +305,11 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   Frag mreg[MLDS ? 1 : JB][MLDS ? 1 : CS];
   if constexpr (MLDS) {
     constexpr int CH = D / 8;  // 16-byte chunks per row
-    for (int idx = tid; idx < G::KPAD * CH; idx += kThreads) {
+    for (int idx = tid; idx < G::KPAD * CH; idx += THREADS) {
       const int r = idx / CH, ch = idx % CH;
       *reinterpret_cast<u32x4*>(Ms + r * G::MS + ch * 8) = *reinterpret_cast<const u32x4*>(Mg + r * D + ch * 8);
     }
-    // ordered before the first read by the segment's first barrier
+    // ordered before the first read by the piece's first barrier
   } else {
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
@@ -398,8 +320,8 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   }
 
   // ---- affinity of one tile: s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][jbase + 16 jb + l16],
-  // padded prototypes set to -inf.
-  auto affinity = [&](f32x4 (&s)[2][JB], const T* xr) {
+  // padded prototypes set to -inf.  xfrag(ib, cs) supplies the X fragments.
+  auto affinity_from = [&](f32x4 (&s)[2][JB], auto&& xfrag) {
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -408,8 +330,7 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     for (int cs = 0; cs < CS; ++cs) {
       Frag xa[2];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-        xa[ib] = frag_c<D>(xr + (rw + 16 * ib + l16) * G::XRS, cs, g);
+      for (int ib = 0; ib < 2; ++ib) xa[ib] = xfrag(ib, cs);
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
         Frag mf;
@@ -434,9 +355,13 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     }
   };
 
+  auto affinity = [&](f32x4 (&s)[2][JB]) {
+    affinity_from(s, [&](int ib, int cs) { return frag_c<D>(Xr + (rw + 16 * ib + l16) * G::XRS, cs, g); });
+  };
+
   // ---- softmax, fast half: e = 2^s' in place (no shift), this wave's row
-  // sums to xl, and a flag when a sum leaves [2^-100, 2^100] (then the exact
-  // shifted path recomputes the tile).
+  // sums to xl, and a per-wave flag when a sum leaves [2^-100, 2^100] (then
+  // the exact shifted path recomputes the tile).
   auto softmax_fast = [&](f32x4 (&s)[2][JB]) {
     bool bad = false;
 #pragma unroll
@@ -464,43 +389,70 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     if (lane == 0) flags[wave] = wave_bad ? 1 : 0;  // one flag per wave: waves that split rows share wj
   };
 
-  // ---- after the exchange barrier: per-row factors 1 / sum_w l_w
+  // ---- after the exchange barrier: per-row factors 1 / sum_w l_w.  Lane
+  // L < 32 finishes row rw + L and leaves the factor in xf; each lane then
+  // reads the factors of its own eight rows (same wave, LDS in order).
   auto combine_fast = [&](float (&fac)[2][4]) {
+    if (lane < kRowsPerWave) {
+      const float* p = xl + (rw + lane) * WJ;
+      float l = p[0];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+      for (int w = 1; w < WJ; ++w) l += p[w];
+      xf[rw + lane] = __builtin_amdgcn_rcpf(l);
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float* p = xl + (rw + 16 * ib + 4 * g + r) * WJ;
-        float l = p[0];
+    for (int ib = 0; ib < 2; ++ib) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(xf + rw + 16 * ib + 4 * g);
 #pragma unroll
-        for (int w = 1; w < WJ; ++w) l += p[w];
-        fac[ib][r] = __builtin_amdgcn_rcpf(l);
-      }
+      for (int r = 0; r < 4; ++r) fac[ib][r] = f[r];
+    }
   };
 
   auto any_flag = [&]() {
     int f = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) f |= flags[w];
+    for (int w = 0; w < NW; ++w) f |= flags[w];
     return __builtin_amdgcn_readfirstlane(f) != 0;
   };
 
   // ---- aggregation: acc[jb][cb][r] += sum_i a[jbase+16jb+4g+r][i] X[i][16cb+l16]
   auto aggregate = [&](f32x4 (&acc)[JB][CB], const f32x4 (&s)[2][JB], const float (&fac)[2][4], const T* xt) {
     if constexpr (sizeof(T) == 2) {
-      bf16x8 a[JB];
+      auto weights = [&](int jb) {
+        bf16x8 a;
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[jb][e] = (bf16)(s[e >> 2][jb][e & 3] * fac[e >> 2][e & 3]);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
+        for (int e = 0; e < 8; ++e) a[e] = (bf16)(s[e >> 2][jb][e & 3] * fac[e >> 2][e & 3]);
+        return a;
+      };
+      auto xcol = [&](int cb) {
         const T* p = xt + (16 * cb + l16) * G::XTS + rw + 4 * g;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
-        const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      };
+      // keep the smaller operand set live: all weight fragments (cb outer) or
+      // all X fragments (jb outer)
+      if constexpr (JB <= CB) {
+        bf16x8 a[JB];
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
+        for (int jb = 0; jb < JB; ++jb) a[jb] = weights(jb);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const bf16x8 xb = xcol(cb);
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
+        }
+      } else {
+        bf16x8 xb[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) xb[cb] = xcol(cb);
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const bf16x8 a = weights(jb);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = MF::run(a, xb[cb], acc[jb][cb]);
+        }
       }
     } else {
 #pragma unroll
@@ -516,29 +468,68 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     }
   };
 
-  // ---- after the exchange barrier: factors for the tile's rows, then the
-  // aggregation.  The exact path (rare, out of line) has its own copy of the
-  // aggregation so that the common path merges no registers with it.
-  auto finish_tile = [&](f32x4 (&acc)[JB][CB], const f32x4 (&sc)[2][JB], const T* xt) {
-    if (any_flag()) {
-      f32x4 s_tmp[2 * JB];
-      float f_tmp[8];
-      exact_tile<T, D, KW, WJ, WI, PAD>(xt, Mg, xsm, xsl, k, wave, lane, s_tmp, f_tmp);
-      f32x4 se[2][JB];
-      float fe[2][4];
+  // ---- exact path for a tile whose unshifted row sums left the safe range:
+  // recompute the wave's affinity tile (the fast path overwrote it) with the
+  // tile's rows read again from global memory,
+  // shift each row by this wave's maximum, and combine the waves with the
+  // usual max/sum rescaling.  Every wave takes it together (it has a barrier).
+  auto softmax_exact = [&](f32x4 (&s)[2][JB], const T* tile, int rows_left, float (&fac)[2][4]) {
+    affinity_from(s, [&](int ib, int cs) {
+      const int rr = rw + 16 * ib + l16;
+      Frag f = frag_c<D>(tile + (int64_t)(rr < rows_left ? rr : rows_left - 1) * D, cs, g);
+      if (rr >= rows_left) f = Frag{};
+      return f;
+    });
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) se[ib][jb] = s_tmp[ib * JB + jb];
+      for (int r = 0; r < 4; ++r) {
+        float m = s[ib][0][r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) fe[ib][r] = f_tmp[ib * 4 + r];
+        for (int jb = 1; jb < JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
+        m = row16_max(m);
+        const float mu = (m == -INFINITY) ? 0.f : m;  // a wave holding only padding
+        float l = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const float e = fast_exp2(s[ib][jb][r] - mu);
+          s[ib][jb][r] = e;
+          l += e;
+        }
+        l = row16_sum(l);
+        fac[ib][r] = m;  // this wave's row maximum until the combine below
+        if (l16 == 0) {
+          const int trow = rw + 16 * ib + 4 * g + r;
+          xsm[trow * WJ + wj] = m;
+          xsl[trow * WJ + wj] = l;
+        }
       }
-      aggregate(acc, se, fe, xt);
+    __syncthreads();
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = rw + 16 * ib + 4 * g + r;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WJ; ++w) mx = fmaxf(mx, xsm[trow * WJ + w]);
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < WJ; ++w) den += xsl[trow * WJ + w] * fast_exp2(xsm[trow * WJ + w] - mx);
+        fac[ib][r] = fast_exp2(fac[ib][r] - mx) / den;
+      }
+  };
+
+  // ---- after the exchange barrier: factors for the tile's rows, then the
+  // aggregation (exact path in the rare tiles that need it).
+  auto finish_tile = [&](f32x4 (&acc)[JB][CB], f32x4 (&sc)[2][JB], const T* xt, int64_t t0, int rows_left) {
+    float fac[2][4];
+    if (any_flag()) {
+      softmax_exact(sc, X + t0 * D, rows_left, fac);
     } else {
-      float fac[2][4];
       combine_fast(fac);
-      aggregate(acc, sc, fac, xt);
     }
+    aggregate(acc, sc, fac, xt);
   };
 
   // First user touched: the largest u with offsets[u] <= r_begin.  It is
@@ -567,20 +558,24 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     Quad<T> pre[G::BPT];
     auto prefetch = [&](int it) {
       const int64_t t0 = row + (int64_t)it * NT;
+      const int64_t left = seg_end - t0;
+      const int rows_left = left < NT ? (int)left : NT;
+      const T* tile = X + t0 * D;
 #pragma unroll
       for (int s = 0; s < G::BPT; ++s) {
-        const int blk = tid + s * kThreads;
-        if (G::NBLK % kThreads == 0 || blk < G::NBLK) {
+        const int blk = tid + s * THREADS;
+        if (G::NBLK % THREADS == 0 || blk < G::NBLK) {
           const int rq = blk / G::QC, cq = blk % G::QC;
-          quad_load<D>(pre[s], X, t0 + 4 * rq, seg_end, 4 * cq);
+          if (rows_left > 0) quad_load<D>(pre[s], tile, rows_left, 4 * rq, 4 * cq);
+          else quad_zero(pre[s]);
         }
       }
     };
     auto store_r = [&]() {
 #pragma unroll
       for (int s = 0; s < G::BPT; ++s) {
-        const int blk = tid + s * kThreads;
-        if (G::NBLK % kThreads == 0 || blk < G::NBLK) {
+        const int blk = tid + s * THREADS;
+        if (G::NBLK % THREADS == 0 || blk < G::NBLK) {
           const int rq = blk / G::QC, cq = blk % G::QC;
           quad_store_r(pre[s], Xr + (4 * rq) * G::XRS + 4 * cq, G::XRS);
         }
@@ -589,67 +584,44 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
     auto store_t = [&](T* xt) {
 #pragma unroll
       for (int s = 0; s < G::BPT; ++s) {
-        const int blk = tid + s * kThreads;
-        if (G::NBLK % kThreads == 0 || blk < G::NBLK) {
+        const int blk = tid + s * THREADS;
+        if (G::NBLK % THREADS == 0 || blk < G::NBLK) {
           const int rq = blk / G::QC, cq = blk % G::QC;
           quad_store_t(pre[s], xt + (4 * cq) * G::XTS + 4 * rq, G::XTS);
         }
       }
     };
 
+    // Per tile it (rows row + it*NT ...):   affinity + fast softmax | B2 |
+    // stage tile it+1 into LDS, issue loads of tile it+2, factors +
+    // aggregation of tile it | B1.  With a single Xt buffer the staging of
+    // Xt waits for the aggregation behind one more barrier.
     __syncthreads();  // LDS from the previous piece (and M staging) is settled
-    if constexpr (G::PIPE) {
-      // Schedule of iteration it (two barriers):
-      //   B1 | Xt(it+1) <- regs; regs <- X(it+2); S(it+1) = affinity(Xr)
-      //        alongside softmax_fast(S(it)) -> xl, flags
-      //   B2 | factors (or the exact path); aggregate S(it) with Xt(it);
-      //        Xr <- regs (= X(it+2))
-      f32x4 S0[2][JB], S1[2][JB];
-      prefetch(0);
-      store_r();
-      store_t(Xt0);
-      __syncthreads();
-      prefetch(1);
-      affinity(S0, Xr);
-      __syncthreads();
-      store_r();  // X(1) (zeros past the end of the piece)
-      auto body = [&](f32x4 (&Sc)[2][JB], f32x4 (&Sn)[2][JB], int it) {
-        T* const xt_cur = (it & 1) ? Xt1 : Xt0;
-        T* const xt_nxt = (it & 1) ? Xt0 : Xt1;
-        __syncthreads();  // B1
-        store_t(xt_nxt);
+    prefetch(0);
+    store_r();
+    store_t(Xt0);
+    __syncthreads();
+    prefetch(1);
+    f32x4 S[2][JB];
+    for (int it = 0; it < ntiles; ++it) {
+      T* const xt_cur = (G::NXT == 2 && (it & 1)) ? Xt1 : Xt0;
+      const int64_t t0 = row + (int64_t)it * NT;
+      const int rows_left = seg_end - t0 < NT ? (int)(seg_end - t0) : NT;
+      affinity(S);
+      softmax_fast(S);
+      __syncthreads();  // B2: row sums visible; every wave is done reading Xr
+      store_r();        // X(it+1)
+      if constexpr (G::NXT == 2) {
+        store_t((it & 1) ? Xt0 : Xt1);
         prefetch(it + 2);
-        affinity(Sn, Xr);
-        softmax_fast(Sc);
-        // interleave: one matrix op, then LDS reads and vector work of the softmax
-#pragma unroll
-        for (int i = 0; i < 2 * JB * CS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-        }
-        __syncthreads();  // B2
-        finish_tile(acc, Sc, xt_cur);
-        store_r();
-      };
-      for (int it = 0; it < ntiles; it += 2) {
-        body(S0, S1, it);
-        if (it + 1 < ntiles) body(S1, S0, it + 1);
-      }
-    } else {
-      f32x4 S[2][JB];
-      prefetch(0);
-      for (int it = 0; it < ntiles; ++it) {
-        if (it > 0) __syncthreads();  // every wave is done with the previous tile
-        store_r();
+        finish_tile(acc, S, xt_cur, t0, rows_left);
+      } else {
+        finish_tile(acc, S, Xt0, t0, rows_left);
+        __syncthreads();  // every wave is done reading Xt
         store_t(Xt0);
-        __syncthreads();
-        prefetch(it + 1);
-        affinity(S, Xr);
-        softmax_fast(S);
-        __syncthreads();
-        finish_tile(acc, S, Xt0);
+        prefetch(it + 2);
       }
+      __syncthreads();  // B1: tile it+1 staged
     }
 
     // ---- flush this (group, user) piece.  Partial layout per slot:
@@ -692,31 +664,32 @@ __global__ __launch_bounds__(kThreads) void sa_fused_kernel(FusedArgs args) {
   }
 }
 
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE, bool PAD>
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
 hipError_t launch_fused_t(const FusedArgs& args, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PIPE, PAD>), dim3(groups), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>), dim3(groups), dim3(64 * WJ * WI), 0, stream,
                      args);
   return hipGetLastError();
 }
 
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PIPE, bool PAD>
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
 hipError_t occupancy_t(int* n) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PIPE, PAD>, kThreads,
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>, 64 * WJ * WI,
                                                       0);
 }
 
 // One plan of the fused pass: launch it, or (occ != nullptr) report how
 // many of its work groups fit on a compute unit.
-template <typename T, int D, int KW, int WJ, bool MLDS>
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
 hipError_t run_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
   if (p.k == p.k_pad)
-    return occ ? occupancy_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, false>(occ)
-               : launch_fused_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, false>(a, groups, st);
-  return occ ? occupancy_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, true>(occ)
-             : launch_fused_t<T, D, KW, WJ, kWaves / WJ, MLDS, true, true>(a, groups, st);
+    return occ ? occupancy_t<T, D, KW, WJ, WI, MLDS, false>(occ)
+               : launch_fused_t<T, D, KW, WJ, WI, MLDS, false>(a, groups, st);
+  return occ ? occupancy_t<T, D, KW, WJ, WI, MLDS, true>(occ)
+             : launch_fused_t<T, D, KW, WJ, WI, MLDS, true>(a, groups, st);
 }
 
-#define SA_PLAN(T_, D_, KW_, WJ_, MLDS_) \
-  if (p.kw == KW_ && p.waves_k == WJ_ && p.m_in_lds == MLDS_) return run_plan<T_, D_, KW_, WJ_, MLDS_>(p, a, groups, st, occ);
+#define SA_PLAN(T_, D_, KW_, WJ_, WI_, MLDS_)                                                       \
+  if (p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.m_in_lds == MLDS_)              \
+    return run_plan<T_, D_, KW_, WJ_, WI_, MLDS_>(p, a, groups, st, occ);
 
 }  // namespace sa

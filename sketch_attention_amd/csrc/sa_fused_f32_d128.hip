@@ -1,4 +1,4 @@
-// Fused compression plans for float32 inputs, d = 128: float32 inputs.
+// Fused compression plans, d = 128: float32 inputs; four waves per group, folded matrix in registers.
 // Each plan group is its own translation unit so groups compile in parallel
 // and can take their own code-generation options.
 #include "sa_fused.hpp"
@@ -6,11 +6,11 @@
 namespace sa {
 
 hipError_t dispatch_f32_d128(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
-  SA_PLAN(float, 128, 16, 1, false)
-  SA_PLAN(float, 128, 32, 1, false)
-  SA_PLAN(float, 128, 64, 1, false)
-  SA_PLAN(float, 128, 64, 2, false)
-  SA_PLAN(float, 128, 64, 4, false)
+  SA_PLAN(float, 128, 16, 1, 4, false)
+  SA_PLAN(float, 128, 32, 1, 4, false)
+  SA_PLAN(float, 128, 64, 1, 4, false)
+  SA_PLAN(float, 128, 64, 2, 2, false)
+  SA_PLAN(float, 128, 64, 4, 1, false)
   return hipErrorInvalidValue;
 }
 

@@ -12,11 +12,6 @@ namespace sa {
 // many users each.
 constexpr int kMaxUsersPerLaunch = 256;
 
-// Threads per workgroup of the fused kernel: four wave64 wavefronts, one per
-// SIMD of a CDNA4 compute unit.
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-
 // Rows of the history tile that one wave handles per step.
 constexpr int kRowsPerWave = 32;
 
@@ -28,7 +23,7 @@ struct Plan {
   int k_pad;        // waves_k * kw
   int kw;           // prototypes per wave (multiple of 16)
   int waves_k;      // waves splitting the prototype axis
-  int waves_rows;   // waves splitting the rows of a tile (waves_k * waves_rows == kWaves)
+  int waves_rows;   // waves splitting the rows of a tile (waves_k * waves_rows waves per group)
   int m_in_lds;     // folded matrix staged in LDS (1) or held in registers (0)
   int tile_rows;    // kRowsPerWave * waves_rows
 };
@@ -71,8 +66,6 @@ hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
 using DispatchFn = hipError_t (*)(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 hipError_t dispatch_bf16_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 hipError_t dispatch_bf16_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_bf16_d64_large(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_bf16_d128_large(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 hipError_t dispatch_f32_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 hipError_t dispatch_f32_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 

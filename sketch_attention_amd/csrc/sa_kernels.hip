@@ -139,14 +139,11 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
 }
 
 // ------------------------------------------------------------ dispatch
-// Accumulators of more than 128 registers per lane (kw * d > 8192) live in
-// AGPRs and are compiled separately from the smaller plans.
 static DispatchFn plan_group(const Plan& p) {
-  const bool large = p.kw * p.d > 8192;
   if (p.dtype == 1) {
-    if (p.d == 64) return large ? dispatch_bf16_d64_large : dispatch_bf16_d64;
-    if (p.d == 128) return large ? dispatch_bf16_d128_large : dispatch_bf16_d128;
-  } else if (!large) {
+    if (p.d == 64) return dispatch_bf16_d64;
+    if (p.d == 128) return dispatch_bf16_d128;
+  } else {
     if (p.d == 64) return dispatch_f32_d64;
     if (p.d == 128) return dispatch_f32_d128;
   }
