@@ -130,13 +130,15 @@ struct FusedGeom {
   static constexpr int CB = D / 16;              // 16-column blocks of the output
   static constexpr int CS = D / Mfma<T>::kStep;  // affinity reduction steps
   static constexpr int KPAD = KW * WJ;
-  static constexpr int XRS = D + 16 / (int)sizeof(T);  // Xr row stride (elements), +16 bytes
-  static constexpr int XTS = NT + (sizeof(T) == 2 ? 8 : 4);  // Xt row stride (elements)
-  static constexpr int MS = D + 8;                     // LDS M row stride (bf16 elements)
+  static constexpr int XRS = D + 32 / (int)sizeof(T);  // Xr row stride (elements): +32 bytes keeps fragment reads conflict-free
+  static constexpr int XTS = NT + 4;                   // Xt row stride (elements): odd multiple of 4 spreads the stores
+  static constexpr int MS_WIDE = D + 16, MS_NARROW = D + 8;  // LDS M row stride (bf16 elements)
   static constexpr int XR_BYTES = NT * XRS * (int)sizeof(T);
   static constexpr int XT_BYTES = D * XTS * (int)sizeof(T);
   static constexpr int XL_BYTES = NT * WJ * 4;         // per-wave row sums
   static constexpr int FLAG_BYTES = 4 * NW;
+  static constexpr int region0 = NT * XRS * (int)sizeof(T) + D * XTS * (int)sizeof(T) + 3 * NT * WJ * 4 + NT * 4 + 4 * NW;
+  static constexpr int MS = (!MLDS || region0 + KPAD * MS_WIDE * 2 <= 160 * 1024) ? MS_WIDE : MS_NARROW;
   static constexpr int M_BYTES = MLDS ? KPAD * MS * 2 : 0;
   static constexpr int stage_bytes = WI > 1 ? WJ * CB * 64 * 16 : 0;  // one prototype block of every wave's accumulators
   static constexpr int XF_BYTES = NT * 4;              // per-row factors
