@@ -18,17 +18,19 @@
 // split is exact because the softmax of one row does not depend on any other
 // row, so the sketch is additive over any partition of a user's rows.
 //
-// Inside a work group.  Four waves; WJ waves split the k_pad prototypes
-// (KW each) and WI = 4 / WJ waves split the rows of a tile (32 rows each).
-// Per tile of NT = 32 * WI rows:
-//   1. the tile is staged from HBM (read once, prefetched one tile ahead into
+// Inside a work group.  NW waves (eight for bf16, two per SIMD; four for
+// float32): WJ waves split the k_pad prototypes (KW each) and WI = NW / WJ
+// split the rows of a tile (32 rows each).  Per tile of NT = 32 * WI rows:
+//   1. the tile is staged from HBM (read once, prefetched two tiles ahead into
 //      registers) into LDS twice: row-major Xr for the affinity product and
 //      transposed Xt for the aggregation product;
-//   2. S^T (32 rows x KW prototypes per wave) = Xr . M^T on the matrix cores
-//      (16x16x32 bf16 or 16x16x4 f32), M fragments in registers or LDS;
+//   2. S'^T (32 rows x KW prototypes per wave) = Xr . M^T on the matrix cores
+//      (16x16x32 bf16 or 16x16x4 f32), M fragments from LDS or registers;
 //   3. in the output layout of that product each lane holds one prototype and
-//      four rows per 16x16 block, so the prototype-axis max and sum are a
-//      16-lane DPP reduction (plus an LDS exchange across the WJ waves);
+//      four rows per 16x16 block, so the prototype-axis sums are a 16-lane DPP
+//      butterfly plus an LDS exchange across the WJ waves; the exponent is
+//      taken without a max shift, and a tile whose row sums leave the safe
+//      range is recomputed on an exact, max-shifted path;
 //   4. the normalised weights are rounded to the operand type in registers
 //      and used directly as the A operand of X~ (KW x D) += A (KW x 32) .
 //      X (32 x D): the reduction index of that product is the row index, and
