@@ -15,9 +15,11 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -32,6 +34,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MALL_BYTES = 256 * 2 ** 20
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "sketch_attention_amd", "csrc")
 METRIC = "history behaviors/sec compressed (n=100K,k=256,d=128); % bf16 MFMA/HBM peak"
 
 
@@ -50,7 +54,8 @@ def algorithmic_bytes(rows: int, users: int, k: int, d: int, elem: int) -> float
 
 
 def cpu_baseline(wl, budget_s: float):
-    """Time the fp64 CPU oracle on whole users of the workload until about budget_s seconds."""
+    """Time the fp64 CPU oracle on whole users of the workload, cycling over
+    them until about budget_s seconds have passed."""
     from threadpoolctl import threadpool_info
 
     from oracle import sa_oracle
@@ -58,7 +63,8 @@ def cpu_baseline(wl, budget_s: float):
     rows = 0
     users = 0
     t0 = time.perf_counter()
-    for u in range(wl.num_users):
+    while True:
+        u = users % wl.num_users
         sa_oracle.sketch_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau)
         rows += int(wl.offsets[u + 1] - wl.offsets[u])
         users += 1
@@ -71,22 +77,56 @@ def cpu_baseline(wl, budget_s: float):
         "unit": "behaviors/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{users} of {wl.num_users} users ({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s",
+        "sample": f"{users} user sketches cycling over the {wl.num_users} users of the workload ({rows} rows), "
+                  f"fp64 numpy/OpenBLAS, {dt:.2f} s",
     }
 
 
+def kernel_source_hash(dtype: str = "bf16", d: int = 128) -> str:
+    """sha256 over the sources and build flags that decide the fused kernel a launch runs."""
+    files = [os.path.join(CSRC, f) for f in ("sa_fused.hpp", f"sa_fused_{dtype}_d{d}.hip", "sa_internal.h",
+                                             "sa_api.cpp")]
+    files.append(os.path.join(ROOT, "sketch_attention_amd", "build.py"))
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, dtype: str, d: int):
+    """HBM bytes per fused launch from the committed profiler summary of this
+    workload, or None when there is none or the kernel has changed since."""
+    path = os.path.join(PROFILES, f"sa_fused_{workload}_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^([a-z0-9_]+): (\S+)$", line.strip())
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256") != kernel_source_hash(dtype, d):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def copy_calibration(steps: int) -> None:
-    """Plain device-to-device copies of known size, for scaling HBM byte counters."""
+    """Plain elementwise copies of known size (1 GiB read, 1 GiB written per
+    dispatch), for scaling the HBM byte counters of a profiler run."""
     nbytes = 1 << 30
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    src.fill_(1)
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    src.fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(steps):
-        dst.copy_(src)
+        torch.neg(src, out=dst)   # one vectorised elementwise kernel: read once, write once
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read_per_dispatch": nbytes, "copy_bytes_written_per_dispatch": nbytes,
-                      "dispatches": steps}), flush=True)
+    print(json.dumps({"kernel": "elementwise neg (float32)", "bytes_read_per_dispatch": nbytes,
+                      "bytes_written_per_dispatch": nbytes, "dispatches": steps}), flush=True)
 
 
 def main() -> int:
@@ -96,7 +136,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="long", choices=["tiny", "recent", "long", "many_proto", "ragged"])
     ap.add_argument("--users", type=int, default=None, help="change the number of users (same per-user shape)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true", help="run plain copies only (counter scaling)")
     args = ap.parse_args()
@@ -169,7 +209,7 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name, wl.dtype, wl.d) if args.users is None else None
     roof["kernel"] = "sa_fused_kernel"
     roof["kernel_avg_us"] = round(fused_avg_ms * 1e3, 2)
     log(f"[bench] fused kernel avg {fused_avg_ms * 1e3:.2f} us ({tflops:.1f} TFLOP/s, {gbs:.0f} GB/s), "
