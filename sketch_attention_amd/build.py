@@ -28,11 +28,13 @@ SOURCES = [
     "sa_fused_bf16_d128.hip",
     "sa_fused_f32_d64.hip",
     "sa_fused_f32_d128.hip",
+    "sa_stream_d64.hip",
+    "sa_stream_d128.hip",
 ]
 # The bf16 plans (accumulators of at most 128 registers per lane) keep every
 # matrix-core result in VGPRs, so the softmax reads the affinity tile without
 # AGPR moves.
-VGPR_FORM = {"sa_fused_bf16_d64.hip", "sa_fused_bf16_d128.hip"}
+VGPR_FORM = {"sa_fused_bf16_d64.hip", "sa_fused_bf16_d128.hip", "sa_stream_d64.hip", "sa_stream_d128.hip"}
 # Packed fp32 VALU instructions are disabled for all device code.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

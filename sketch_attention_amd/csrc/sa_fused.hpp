@@ -693,7 +693,7 @@ hipError_t run_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t s
 }
 
 #define SA_PLAN(T_, D_, KW_, WJ_, WI_, MLDS_)                                                       \
-  if (p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.m_in_lds == MLDS_)              \
+  if (p.kind == 0 && p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.m_in_lds == MLDS_) \
     return run_plan<T_, D_, KW_, WJ_, WI_, MLDS_>(p, a, groups, st, occ);
 
 }  // namespace sa

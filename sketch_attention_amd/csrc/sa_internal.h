@@ -26,6 +26,8 @@ struct Plan {
   int waves_rows;   // waves splitting the rows of a tile (waves_k * waves_rows waves per group)
   int m_in_lds;     // folded matrix staged in LDS (1) or held in registers (0)
   int tile_rows;    // kRowsPerWave * waves_rows
+  int kind;         // 0 = lockstep pass (sa_fused.hpp), 1 = streamed pass (sa_stream.hpp, bf16)
+  int prefetch;     // streamed pass: tiles held in registers between HBM and LDS (1 or 2)
 };
 
 // Arguments of the fused kernel (passed by value in the dispatch packet).
@@ -68,5 +70,7 @@ hipError_t dispatch_bf16_d64(const Plan&, const FusedArgs&, int, hipStream_t, in
 hipError_t dispatch_bf16_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 hipError_t dispatch_f32_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 hipError_t dispatch_f32_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_stream_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+hipError_t dispatch_stream_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
 
 }  // namespace sa

@@ -140,6 +140,12 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
 
 // ------------------------------------------------------------ dispatch
 static DispatchFn plan_group(const Plan& p) {
+  if (p.kind == 1) {
+    if (p.dtype != 1) return nullptr;
+    if (p.d == 64) return dispatch_stream_d64;
+    if (p.d == 128) return dispatch_stream_d128;
+    return nullptr;
+  }
   if (p.dtype == 1) {
     if (p.d == 64) return dispatch_bf16_d64;
     if (p.d == 128) return dispatch_bf16_d128;

@@ -1,0 +1,15 @@
+// Streamed compression plans, bf16, d = 64 (sa_stream.hpp): 32 prototypes per
+// wave (64 above k = 256), folded matrix in registers, eight waves per group.
+#include "sa_stream.hpp"
+
+namespace sa {
+
+hipError_t dispatch_stream_d64(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+  SA_STREAM_PLAN(64, 64, 8, 1, 2)
+  SA_STREAM_PLAN(64, 32, 8, 1, 2)
+  SA_STREAM_PLAN(64, 32, 4, 2, 2)
+  SA_STREAM_PLAN(64, 32, 2, 4, 2)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa
