@@ -25,9 +25,10 @@ struct Plan {
   int waves_k;      // waves splitting the prototype axis
   int waves_rows;   // waves splitting the rows of a tile (waves_k * waves_rows waves per group)
   int m_in_lds;     // folded matrix staged in LDS (1) or held in registers (0)
-  int tile_rows;    // kRowsPerWave * waves_rows
+  int tile_rows;    // rows per tile: kRowsPerWave * waves_rows (lockstep), 16 * row_blocks * waves_rows (streamed)
   int kind;         // 0 = lockstep pass (sa_fused.hpp), 1 = streamed pass (sa_stream.hpp, bf16)
   int prefetch;     // streamed pass: tiles held in registers between HBM and LDS (1 or 2)
+  int row_blocks;   // streamed pass: 16-row blocks per wave and tile (2 or 4)
 };
 
 // Arguments of the fused kernel (passed by value in the dispatch packet).

@@ -7,23 +7,26 @@
 // sum_j' 2^s'_j'i, X~_j += a_ji x_i, float32 partial sketches per (group,
 // user) piece reduced by a second kernel.
 //
-// What changes is the schedule inside a group.  The group walks one list of
-// tiles (NT = 32 * WI rows, never crossing a user boundary) over all the
-// pieces it owns, and each wave keeps two affinity tiles in flight:
+// What changes is the schedule inside a group.  WJ waves split the
+// prototypes (KW each) and WI split the rows; a wave owns RW = 16 * RB rows
+// of every tile of NT = RW * WI rows.  The group walks one list of tiles
+// (never crossing a user boundary) over all the pieces it owns, and each
+// wave keeps two affinity tiles in flight:
 //
 //   iteration t  (one barrier at its end)
 //     stage tile t+2 from registers into the LDS ring, issue the HBM loads
 //       of tile t+2+PF
 //     S(t+1) = X(t+1) . M^T          matrix cores (M held in registers)
-//     factors of tile t               LDS exchange of row sums, 1/sum
+//     factors of tile t               row sums of all waves from LDS, 1/sum,
+//                                     spread to the lanes by DPP broadcasts
 //     A(t) = S(t) * factors -> bf16   VALU
 //     acc += A(t) . X(t)              matrix cores
-//     S(t+1) <- 2^S(t+1), row sums    VALU + DPP, partial sums to LDS
+//     S(t+1) <- 2^S(t+1), row sums    VALU + DPP, this wave's sums to LDS
 //     flush acc when tile t ends a piece
 //
 // so the affinity product of one tile overlaps the normalisation of the
 // previous one and the aggregation product overlaps the exponentials of the
-// next one, inside one basic block the compiler can interleave.
+// next one.
 //
 // X is staged once, row-major, in a ring of three LDS tiles (tile t is read
 // by the aggregation while t+1 is read by the affinity and t+2 is written).
@@ -35,9 +38,11 @@
 // 16-column block, and receives one column of four consecutive rows.
 //
 // Rows past the end of a piece are staged as zeros: their affinity is 0,
-// their weights are finite and they add nothing to the sketch.  A tile whose
-// unshifted row sums leave [2^-100, 2^100] in any wave is recomputed with
-// the max-shifted softmax (all waves take that branch together).
+// their weights are finite and they add nothing to the sketch.  The softmax
+// takes 2^s' without a shift; when the total of a row leaves [2^-100, 2^100]
+// the wave holding it recomputes its rows with the max-shifted softmax on
+// its own (an online max/sum pass over all prototypes, M read from global
+// memory), so no other wave waits for it.
 #pragma once
 
 #include "sa_fused.hpp"
@@ -53,12 +58,20 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int D, int KW, int WJ, int WI, int PF>
+// Value of lane n of this lane's 16-lane row (DPP row_newbcast).
+template <int n>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + n, 0xF, 0xF,
+                                                                false));
+}
+
+template <int D, int KW, int WJ, int WI, int RB, int PF>
 struct StreamGeom {
-  static_assert(KW % 16 == 0 && D % 32 == 0 && (PF == 1 || PF == 2), "tile shape");
+  static_assert(KW % 16 == 0 && D % 32 == 0 && (PF == 1 || PF == 2) && (RB == 2 || RB == 4), "tile shape");
   static constexpr int NW = WJ * WI;
   static constexpr int THREADS = 64 * NW;
-  static constexpr int NT = kRowsPerWave * WI;  // rows per tile
+  static constexpr int RW = 16 * RB;           // rows per wave and tile
+  static constexpr int NT = RW * WI;           // rows per tile
   static constexpr int JB = KW / 16;
   static constexpr int CB = D / 16;
   static constexpr int CS = D / 32;
@@ -70,34 +83,24 @@ struct StreamGeom {
   static constexpr int NCH = NT * CH;
   static constexpr int CPT = (NCH + THREADS - 1) / THREADS;  // chunks per thread
   static constexpr int XR_BYTES = NXR * XR_ELEMS * 2;
-  static constexpr int XL_BYTES = 2 * NT * WJ * 4;  // row sums, two parities
-  static constexpr int XS_BYTES = NT * WJ * 4;      // exact path: maxima / sums
-  static constexpr int XF_BYTES = NW * kRowsPerWave * 4;
-  static constexpr int FLAG_BYTES = 2 * NW * 4;
+  static constexpr int XL_BYTES = 2 * NT * WJ * 4;  // row sums of every wave, two parities
   static constexpr int STAGE_BYTES = WI > 1 ? WJ * CB * 64 * 16 : 0;
   static constexpr int OFF_XL = XR_BYTES;
-  static constexpr int OFF_XSM = OFF_XL + XL_BYTES;
-  static constexpr int OFF_XSL = OFF_XSM + XS_BYTES;
-  static constexpr int OFF_XF = OFF_XSL + XS_BYTES;
-  static constexpr int OFF_FLAG = OFF_XF + XF_BYTES;
-  static constexpr int OFF_STAGE = (OFF_FLAG + FLAG_BYTES + 15) / 16 * 16;
+  static constexpr int OFF_STAGE = OFF_XL + XL_BYTES;
   static constexpr int LDS_BYTES = OFF_STAGE + STAGE_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
-template <int D, int KW, int WJ, int WI, int PF, bool PAD>
+template <int D, int KW, int WJ, int WI, int RB, int PF, bool PAD>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args) {
-  using G = StreamGeom<D, KW, WJ, WI, PF>;
+  using G = StreamGeom<D, KW, WJ, WI, RB, PF>;
   using MF = Mfma<bf16>;
-  constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, NW = G::NW, THREADS = G::THREADS;
+  constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, RW = G::RW, THREADS = G::THREADS;
   constexpr int XRS = G::XRS;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
   bf16* const Xr = reinterpret_cast<bf16*>(lds);
-  float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);    // [2][NT][WJ]
-  float* const xsm = reinterpret_cast<float*>(lds + G::OFF_XSM);  // [NT][WJ]
-  float* const xsl = reinterpret_cast<float*>(lds + G::OFF_XSL);  // [NT][WJ]
-  int* const flags = reinterpret_cast<int*>(lds + G::OFF_FLAG);   // [2][NW]
+  float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);  // [2][NT][WJ]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,13 +109,11 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wj = wave % WJ;
   const int wi = wave / WJ;
-  const int rw = wi * kRowsPerWave;
-  const int jbase = wj * KW;
-  float* const xf = reinterpret_cast<float*>(lds + G::OFF_XF) + wave * kRowsPerWave;  // this wave's row factors
+  const int rw = wi * RW;     // first tile row of this wave
+  const int jbase = wj * KW;  // first prototype of this wave
   const bf16* const X = static_cast<const bf16*>(args.X);
   const bf16* const Mg = static_cast<const bf16*>(args.M);
   const int k = args.k;
-  const bool wave_has_protos = jbase < k;
 
   const int64_t rows = args.rows;
   const int64_t ngroups = gridDim.x;
@@ -171,22 +172,24 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
   }
 
-  // ---- staging: thread chunk s covers row (tid + s*THREADS) / CH, 16 bytes
+  // ---- staging: thread chunk s covers row (tid + s*THREADS) / CH, 16 bytes.
+  // Rows past the piece (or a tile past the list) load the piece's last row,
+  // always in bounds, and are replaced by zeros: no branch in the hot block.
   u32x4 pre[PF][G::CPT];
   auto load_tile = [&](u32x4 (&dst)[G::CPT], const Cursor& c, bool valid) {
     const int64_t left = c.end - c.row;
     const int rows_left = !valid ? 0 : (left < NT ? (int)left : NT);
+    const int last = (int)(c.end - 1 - c.row);  // -1 past the list: c.row + last = c.end - 1 >= 0
     const bf16* tile = X + c.row * D;
 #pragma unroll
     for (int s = 0; s < G::CPT; ++s) {
       const int ci = tid + s * THREADS;
       const int r = ci / G::CH, ch = ci % G::CH;
       if (G::NCH % THREADS == 0 || ci < G::NCH) {
-        if (r < rows_left) {
-          dst[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + r * D + 8 * ch));
-        } else {
-          dst[s] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const int rr = r < last ? r : last;
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + rr * D + 8 * ch));
+        const bool ok = r < rows_left;
+        dst[s] = u32x4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
       }
     }
   };
@@ -199,40 +202,45 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     }
   };
 
-  // ---- affinity: s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][jbase + 16 jb + l16]
-  auto affinity = [&](f32x4 (&s)[2][JB], const bf16* xr) {
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      bf16x8 xa[2];
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) xa[ib] = frag_c<D>(xr + (rw + 16 * ib + l16) * XRS, cs, g);
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib) s[ib][jb] = MF::run(xa[ib], mreg[jb][cs], s[ib][jb]);
-    }
+  // ---- affinity of rows 16 ib + .. with prototypes 16 jb + .. of block `mf`:
+  // s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][16 jb + l16]
+  auto pad_protos = [&](f32x4 (&s)[RB][JB], int j0) {
     if constexpr (PAD) {
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
-        const bool ok = jbase + 16 * jb + l16 < k;
+        const bool ok = j0 + 16 * jb + l16 < k;
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
+        for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
       }
     }
   };
+  auto affinity = [&](f32x4 (&s)[RB][JB], const bf16* xr) {
+#pragma unroll
+    for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      bf16x8 xa[RB];
+#pragma unroll
+      for (int ib = 0; ib < RB; ++ib) xa[ib] = frag_c<D>(xr + (rw + 16 * ib + l16) * XRS, cs, g);
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int ib = 0; ib < RB; ++ib) s[ib][jb] = MF::run(xa[ib], mreg[jb][cs], s[ib][jb]);
+    }
+    pad_protos(s, jbase);
+  };
 
-  // ---- e = 2^s' in place, this wave's row sums to xl[par], flag to flags[par]
-  auto softmax_fast = [&](f32x4 (&s)[2][JB], int par) {
-    bool bad = false;
+  // ---- e = 2^s' in place; this wave's row sums to xl[par].  After the
+  // transposing butterfly the four lanes of a quad hold the same total and
+  // store it to the same word (no branch).
+  auto softmax_fast = [&](f32x4 (&s)[RB][JB], int par) {
     float* const xlp = xl + par * (NT * WJ);
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
+    for (int ib = 0; ib < RB; ++ib) {
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -246,103 +254,139 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
         p[r] = acc;
       }
       const float z = rows4_sum_scatter(p, l16);
-      bad |= !(z >= 0x1p-100f && z <= 0x1p100f);
-      if ((l16 & 3) == 0) {
-        const int trow = rw + 16 * ib + 4 * g + ((l16 >> 3) << 1) + ((l16 >> 2) & 1);
-        xlp[trow * WJ + wj] = z;
-      }
+      const int trow = rw + 16 * ib + 4 * g + ((l16 >> 3) << 1) + ((l16 >> 2) & 1);
+      xlp[trow * WJ + wj] = z;
     }
-    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad && wave_has_protos) != 0;
-    if (lane == 0) flags[par * NW + wave] = wave_bad ? 1 : 0;
   };
 
-  auto any_flag = [&](int par) {
-    int f = 0;
+  // ---- factors 1 / sum_w l_w.  Lane (g, l16) finishes row
+  // rw + 16 ib + 4 g + r with ib = (l16 / 4) % RB, r = l16 % 4, so each row
+  // of the wave lives in the 16-lane DPP row g of the lanes that need it; the
+  // aggregation takes the factors of its rows by row broadcasts (fac_of).
+  // `bad` is set when a row total left the range of the unshifted softmax.
+  const int my_ib = (l16 >> 2) % RB, my_r = l16 & 3;
+  auto combine_fast = [&](float& f, bool& bad, int par) {
+    const float* p = xl + par * (NT * WJ) + (rw + 16 * my_ib + 4 * g + my_r) * WJ;
+    float l;
+    if constexpr (WJ % 4 == 0) {
+      f32x4 v = *reinterpret_cast<const f32x4*>(p);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) f |= flags[par * NW + w];
-    return __builtin_amdgcn_readfirstlane(f) != 0;
-  };
-
-  // ---- factors 1 / sum_w l_w of this wave's 32 rows (lane L < 32 finishes row rw + L)
-  auto combine_fast = [&](float (&fac)[2][4], int par) {
-    if (lane < kRowsPerWave) {
-      const float* p = xl + par * (NT * WJ) + (rw + lane) * WJ;
-      float l = p[0];
+      for (int w = 4; w < WJ; w += 4) v += *reinterpret_cast<const f32x4*>(p + w);
+      l = (v[0] + v[1]) + (v[2] + v[3]);
+    } else {
+      l = p[0];
 #pragma unroll
       for (int w = 1; w < WJ; ++w) l += p[w];
-      xf[lane] = __builtin_amdgcn_rcpf(l);
     }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      const f32x4 f = *reinterpret_cast<const f32x4*>(xf + 16 * ib + 4 * g);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) fac[ib][r] = f[r];
+    bad = __builtin_amdgcn_ballot_w64(!(l >= 0x1p-100f && l <= 0x1p100f)) != 0;
+    f = __builtin_amdgcn_rcpf(l);
+  };
+  // factor of row rw + 16 ib + 4 g + r from the lane that holds it
+  auto fac_of = [&](float f, int ib, int r) {
+    switch (4 * ib + r) {
+      case 0: return row_bcast<0>(f);
+      case 1: return row_bcast<1>(f);
+      case 2: return row_bcast<2>(f);
+      case 3: return row_bcast<3>(f);
+      case 4: return row_bcast<4>(f);
+      case 5: return row_bcast<5>(f);
+      case 6: return row_bcast<6>(f);
+      case 7: return row_bcast<7>(f);
+      case 8: return row_bcast<8>(f);
+      case 9: return row_bcast<9>(f);
+      case 10: return row_bcast<10>(f);
+      case 11: return row_bcast<11>(f);
+      case 12: return row_bcast<12>(f);
+      case 13: return row_bcast<13>(f);
+      case 14: return row_bcast<14>(f);
+      default: return row_bcast<15>(f);
     }
   };
 
-  // ---- exact path: recompute the tile's affinity from LDS, shift each row
-  // by its maximum over all prototypes, combine the waves' shifted sums.
-  auto softmax_exact = [&](f32x4 (&s)[2][JB], const bf16* xr, float (&fac)[2][4]) {
-    affinity(s, xr);
+  // ---- exact path of one wave (rare): for each of its row blocks, an online
+  // max / shifted-sum pass over all prototypes (M fragments from global
+  // memory), then its own prototypes' weights 2^(s' - m) with factor 1 / l.
+  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, const bf16* xr) {
+#pragma unroll 1
+    for (int ib = 0; ib < RB; ++ib) {
+      bf16x8 xa[CS];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = s[ib][0][r];
-#pragma unroll
-        for (int jb = 1; jb < JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
-        m = row16_max(m);
-        const float mu = (m == -INFINITY) ? 0.f : m;  // a wave holding only padding
-        float l = 0.f;
+      for (int cs = 0; cs < CS; ++cs) xa[cs] = frag_c<D>(xr + (rw + 16 * ib + l16) * XRS, cs, g);
+      float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      float l[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 own[JB];
+#pragma unroll 1
+      for (int w = 0; w < WJ; ++w) {
+        f32x4 sb[1][JB];
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
-          const float e = fast_exp2(s[ib][jb][r] - mu);
-          s[ib][jb][r] = e;
-          l += e;
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          const bf16* mrow = Mg + (int64_t)(w * KW + 16 * jb + l16) * D;
+#pragma unroll
+          for (int cs = 0; cs < CS; ++cs) a = MF::run(xa[cs], frag_c<D>(mrow, cs, g), a);
+          sb[0][jb] = a;
         }
-        l = row16_sum(l);
-        fac[ib][r] = m;
-        if (l16 == 0) {
-          const int trow = rw + 16 * ib + 4 * g + r;
-          xsm[trow * WJ + wj] = m;
-          xsl[trow * WJ + wj] = l;
+        if constexpr (PAD) {
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) {
+            const bool ok = w * KW + 16 * jb + l16 < k;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sb[0][jb][r] = ok ? sb[0][jb][r] : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float bm = sb[0][0][r];
+#pragma unroll
+          for (int jb = 1; jb < JB; ++jb) bm = fmaxf(bm, sb[0][jb][r]);
+          bm = row16_max(bm);
+          const float mn = fmaxf(m[r], bm);
+          if (mn != -INFINITY) {  // a block of padding only leaves the state as it is
+            float se = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) se += fast_exp2(sb[0][jb][r] - mn);
+            l[r] = l[r] * fast_exp2(m[r] - mn) + row16_sum(se);
+            m[r] = mn;
+          }
+        }
+        if (w == wj) {
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) own[jb] = sb[0][jb];
         }
       }
-    __syncthreads();
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = rw + 16 * ib + 4 * g + r;
-        float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < WJ; ++w) mx = fmaxf(mx, xsm[trow * WJ + w]);
-        float den = 0.f;
-#pragma unroll
-        for (int w = 0; w < WJ; ++w) den += xsl[trow * WJ + w] * fast_exp2(xsm[trow * WJ + w] - mx);
-        fac[ib][r] = fast_exp2(fac[ib][r] - mx) / den;
+        for (int jb = 0; jb < JB; ++jb) s[ib][jb][r] = fast_exp2(own[jb][r] - m[r]);
+        if (ib == my_ib && r == my_r) f = 1.f / l[r];
       }
+    }
   };
 
   // ---- aggregation: acc[jb][cb][r] += sum_i a[jbase+16jb+4g+r][i] X[i][16cb+l16].
-  // Reduction slot (g, e) of a lane is tile row rw + 16 (e / 4) + 4 g + e % 4,
-  // the rows the affinity layout left in that lane.
+  // Reduction slot (g, e) of k-step h is tile row rw + 32 h + 16 (e / 4) +
+  // 4 g + e % 4, the rows the affinity layout left in that lane.
   const int tr_off = (rw + 4 * g + (l16 >> 2)) * XRS + 4 * (l16 & 3);
-  auto aggregate = [&](f32x4 (&acc)[JB][CB], const f32x4 (&s)[2][JB], const float (&fac)[2][4], const bf16* xr) {
-    bf16x8 a[JB];
+  auto aggregate = [&](f32x4 (&acc)[JB][CB], const f32x4 (&s)[RB][JB], float f, const bf16* xr) {
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
+    for (int h = 0; h < RB / 2; ++h) {
+      float fac[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[jb][e] = (bf16)(s[e >> 2][jb][e & 3] * fac[e >> 2][e & 3]);
-    const bf16* const xp = xr + tr_off;
+      for (int e = 0; e < 8; ++e) fac[e] = fac_of(f, 2 * h + (e >> 2), e & 3);
+      bf16x8 a[JB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const u32x2 lo = lds_read_tr16(xp + 16 * cb);
-      const u32x2 hi = lds_read_tr16(xp + 16 * XRS + 16 * cb);
-      const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
+        for (int e = 0; e < 8; ++e) a[jb][e] = (bf16)(s[2 * h + (e >> 2)][jb][e & 3] * fac[e]);
+      const bf16* const xp = xr + tr_off + 32 * h * XRS;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const u32x2 lo = lds_read_tr16(xp + 16 * cb);
+        const u32x2 hi = lds_read_tr16(xp + 16 * XRS + 16 * cb);
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
+      }
     }
   };
 
@@ -409,34 +453,35 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     }
   }
   __syncthreads();
-  f32x4 S0[2][JB], S1[2][JB];
+  f32x4 S0[RB][JB], S1[RB][JB];
   affinity(S0, Xr);
   softmax_fast(S0, 0);
   __syncthreads();
 
   // ---- main loop, unrolled by two so the two affinity tiles swap roles
-  // without register copies.  ring index of tile t: t % 3.
-  int q0 = 0;  // t % 3
-  auto step = [&](int t, f32x4 (&Sa)[2][JB], f32x4 (&Sb)[2][JB], u32x4 (&pslot)[G::CPT]) {
+  // without register copies.  Ring index of tile t: t % 3.  Past the end of
+  // the list the staged tile is zeros and the affinity of "t+1" is computed
+  // and unused, so the hot path has no data-dependent branch but the rare
+  // exact one.
+  int q0 = 0;
+  auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT]) {
     const int q1 = q0 == 2 ? 0 : q0 + 1;
     const int q2 = q1 == 2 ? 0 : q1 + 1;
     bf16* const xr_t = Xr + q0 * G::XR_ELEMS;
     bf16* const xr_t1 = Xr + q1 * G::XR_ELEMS;
     bf16* const xr_t2 = Xr + q2 * G::XR_ELEMS;
-    const bool has1 = t + 1 < ntot;
-    if (t + 2 < ntot) {
-      store_tile(pslot, xr_t2);
-      load_tile(pslot, cl, t + 2 + PF < ntot);
-      cursor_next(cl);
-    }
-    if (has1) affinity(Sb, xr_t1);
-    float fac[2][4];
-    combine_fast(fac, t & 1);
-    if (any_flag(t & 1)) softmax_exact(Sa, xr_t, fac);
-    aggregate(acc, Sa, fac, xr_t);
-    if (has1) softmax_fast(Sb, (t + 1) & 1);
+    store_tile(pslot, xr_t2);
+    load_tile(pslot, cl, t + 2 + PF < ntot);
+    affinity(Sb, xr_t1);
+    float f;
+    bool bad;
+    combine_fast(f, bad, t & 1);
+    if (bad) exact_wave(Sa, f, xr_t);
+    aggregate(acc, Sa, f, xr_t);
+    softmax_fast(Sb, (t + 1) & 1);
     if (cc.row + NT >= cc.end) flush(acc, cc.u);
     cursor_next(cc);
+    cursor_next(cl);
     q0 = q1;
     __syncthreads();
   };
@@ -446,23 +491,24 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   }
 }
 
-template <int D, int KW, int WJ, int WI, int PF>
+template <int D, int KW, int WJ, int WI, int RB, int PF>
 hipError_t run_stream_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
   constexpr int threads = 64 * WJ * WI;
   if (p.k == p.k_pad) {
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, PF, false>,
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, false>,
                                                                  threads, 0);
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, PF, false>), dim3(groups), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, false>), dim3(groups), dim3(threads), 0, st, a);
   } else {
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, PF, true>,
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, true>,
                                                                  threads, 0);
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, PF, true>), dim3(groups), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, true>), dim3(groups), dim3(threads), 0, st, a);
   }
   return hipGetLastError();
 }
 
-#define SA_STREAM_PLAN(D_, KW_, WJ_, WI_, PF_)                                                     \
-  if (p.kind == 1 && p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.prefetch == PF_) \
-    return run_stream_plan<D_, KW_, WJ_, WI_, PF_>(p, a, groups, st, occ);
+#define SA_STREAM_PLAN(D_, KW_, WJ_, WI_, RB_, PF_)                                                \
+  if (p.kind == 1 && p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.row_blocks == RB_ && \
+      p.prefetch == PF_)                                                                            \
+    return run_stream_plan<D_, KW_, WJ_, WI_, RB_, PF_>(p, a, groups, st, occ);
 
 }  // namespace sa

@@ -5,10 +5,11 @@
 namespace sa {
 
 hipError_t dispatch_stream_d128(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
-  SA_STREAM_PLAN(128, 32, 8, 1, 2)
-  SA_STREAM_PLAN(128, 32, 8, 1, 1)
-  SA_STREAM_PLAN(128, 32, 4, 2, 2)
-  SA_STREAM_PLAN(128, 32, 2, 4, 2)
+  SA_STREAM_PLAN(128, 32, 8, 1, 4, 1)
+  SA_STREAM_PLAN(128, 32, 8, 1, 4, 2)
+  SA_STREAM_PLAN(128, 32, 8, 1, 2, 1)
+  SA_STREAM_PLAN(128, 32, 4, 2, 2, 1)
+  SA_STREAM_PLAN(128, 32, 2, 4, 2, 1)
   return hipErrorInvalidValue;
 }
 

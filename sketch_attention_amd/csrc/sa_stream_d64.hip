@@ -5,10 +5,10 @@
 namespace sa {
 
 hipError_t dispatch_stream_d64(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
-  SA_STREAM_PLAN(64, 64, 8, 1, 2)
-  SA_STREAM_PLAN(64, 32, 8, 1, 2)
-  SA_STREAM_PLAN(64, 32, 4, 2, 2)
-  SA_STREAM_PLAN(64, 32, 2, 4, 2)
+  SA_STREAM_PLAN(64, 64, 8, 1, 2, 1)
+  SA_STREAM_PLAN(64, 32, 8, 1, 4, 1)
+  SA_STREAM_PLAN(64, 32, 4, 2, 4, 1)
+  SA_STREAM_PLAN(64, 32, 2, 4, 2, 1)
   return hipErrorInvalidValue;
 }
 
