@@ -74,6 +74,9 @@ Plan make_plan(int dtype, int d, int k) {
     p.kw = (d == 64 && k > 256) ? 64 : 32;
     p.waves_k = k <= 64 ? 2 : (k <= 128 ? 4 : 8);
     p.row_blocks = (p.kw == 32 && (p.waves_k == 8 || (d == 64 && p.waves_k == 4))) ? 4 : 2;
+    // d = 128, k <= 64: two row waves (four waves per group) keep the four
+    // 64-row LDS tiles of the ring within budget
+    p.waves_rows = (d == 128 && p.waves_k == 2) ? 2 : waves / p.waves_k;
   } else if (k16 <= 16) {
     p.kw = 16; p.waves_k = 1;
   } else if (k16 <= 32) {
@@ -89,7 +92,7 @@ Plan make_plan(int dtype, int d, int k) {
   } else {
     p.kw = 128; p.waves_k = 8;
   }
-  p.waves_rows = waves / p.waves_k;
+  if (!stream) p.waves_rows = waves / p.waves_k;
   p.m_in_lds = (dtype == SA_BF16 && !stream) ? 1 : 0;
   if (const char* env = std::getenv("SA_PLAN")) {
     int kw = 0, wk = 0, wr = 0, ml = 0, kind = 0, pf = 1, rb = 2;

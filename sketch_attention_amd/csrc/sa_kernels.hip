@@ -84,47 +84,60 @@ hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hip
 // [wj][jb][cb][lane][4]; float4 number p of a slot holds prototypes
 // wj*kw + 16*jb + 4*(lane/16) + 0..3 at column 16*cb + lane%16.
 //
-// One thread per float4 of a slot, 64 threads per group (many groups, so the
-// partial reads of all users spread over the whole GPU); four running sums
-// over b = b0 + 4q + t, t = 0..3, keep four loads in flight and are added in
-// a fixed order at the end.
-constexpr int kReduceThreads = 64;
+// One thread per float4 of a slot and per share of the user's groups: a
+// work group of `shares` waves (1..8, chosen from the slots per user) covers
+// 64 float4s; wave q sums its contiguous share of the slots b0..b1 (four
+// running sums, four loads in flight), and the shares are added through LDS
+// in a fixed order, so many waves stream the partials of a user with many
+// groups while users with few groups do not pay for idle waves.
+constexpr int kReduceLanes = 64;
+constexpr int kReduceShares = 8;
 
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
+__global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(ReduceArgs a) {
+  __shared__ f32x4 part_sum[kReduceShares][kReduceLanes];
+  const int shares = blockDim.x / kReduceLanes;
   const int u = blockIdx.y;
   const int slot_f4 = a.k_pad * a.d / 4;
-  const int p = blockIdx.x * kReduceThreads + threadIdx.x;
-  if (p >= slot_f4) return;
+  const int lane = threadIdx.x % kReduceLanes;
+  const int q = threadIdx.x / kReduceLanes;
+  const int p = blockIdx.x * kReduceLanes + lane;
   const int64_t r0 = a.offsets[u], r1 = a.offsets[u + 1];
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if (r1 > r0) {
+  if (r1 > r0 && p < slot_f4) {
     const int64_t G = a.groups, R = a.rows;
     const int64_t b0 = ((r0 + 1) * G - 1) / R;
     const int64_t b1 = (r1 * G - 1) / R;
-    const f32x4* part = reinterpret_cast<const f32x4*>(a.partial) + (b0 + u) * slot_f4 + p;
     const int64_t n = b1 - b0 + 1;
+    const int64_t q0 = n * q / shares, q1 = n * (q + 1) / shares;
+    const f32x4* part = reinterpret_cast<const f32x4*>(a.partial) + (b0 + u) * slot_f4 + p;
     f32x4 t0 = s, t1 = s, t2 = s, t3 = s;
-    int64_t q = 0;
-    for (; q + 4 <= n; q += 4) {
-      t0 += __builtin_nontemporal_load(part + (q + 0) * slot_f4);
-      t1 += __builtin_nontemporal_load(part + (q + 1) * slot_f4);
-      t2 += __builtin_nontemporal_load(part + (q + 2) * slot_f4);
-      t3 += __builtin_nontemporal_load(part + (q + 3) * slot_f4);
+    int64_t i = q0;
+    for (; i + 4 <= q1; i += 4) {
+      t0 += __builtin_nontemporal_load(part + (i + 0) * slot_f4);
+      t1 += __builtin_nontemporal_load(part + (i + 1) * slot_f4);
+      t2 += __builtin_nontemporal_load(part + (i + 2) * slot_f4);
+      t3 += __builtin_nontemporal_load(part + (i + 3) * slot_f4);
     }
-    if (q + 0 < n) t0 += __builtin_nontemporal_load(part + (q + 0) * slot_f4);
-    if (q + 1 < n) t1 += __builtin_nontemporal_load(part + (q + 1) * slot_f4);
-    if (q + 2 < n) t2 += __builtin_nontemporal_load(part + (q + 2) * slot_f4);
+    if (i + 0 < q1) t0 += __builtin_nontemporal_load(part + (i + 0) * slot_f4);
+    if (i + 1 < q1) t1 += __builtin_nontemporal_load(part + (i + 1) * slot_f4);
+    if (i + 2 < q1) t2 += __builtin_nontemporal_load(part + (i + 2) * slot_f4);
     s = (t0 + t1) + (t2 + t3);
   }
-  const int lane = p & 63;
+  part_sum[q][lane] = s;
+  __syncthreads();
+  if (q != 0 || p >= slot_f4) return;
+#pragma unroll
+  for (int w = 1; w < kReduceShares; ++w)
+    if (w < shares) s += part_sum[w][lane];
   int t = p >> 6;
   const int cbs = a.d / 16, jbs = a.kw / 16;
   const int cb = t % cbs;
   t /= cbs;
   const int jb = t % jbs;
   const int wj = t / jbs;
-  const int j0 = wj * a.kw + 16 * jb + 4 * (lane >> 4);
-  const int c = 16 * cb + (lane & 15);
+  const int l = p & 63;
+  const int j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);
+  const int c = 16 * cb + (l & 15);
   float* o = a.out + (int64_t)u * a.k * a.d;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -133,8 +146,11 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   const int slot_f4 = a.k_pad * a.d / 4;
-  hipLaunchKernelGGL(reduce_kernel, dim3((slot_f4 + kReduceThreads - 1) / kReduceThreads, a.users),
-                     dim3(kReduceThreads), 0, stream, a);
+  const int64_t per_user = (a.groups + a.users) / (a.users > 0 ? a.users : 1);
+  int shares = 1;
+  while (shares < kReduceShares && 8 * 2 * shares <= per_user) shares *= 2;
+  hipLaunchKernelGGL(reduce_kernel, dim3((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users),
+                     dim3(kReduceLanes * shares), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ struct StreamGeom {
   static constexpr int KPAD = KW * WJ;
   static constexpr int XRS = D + 16;           // row stride (elements): +32 bytes, conflict-free fragment reads
   static constexpr int XR_ELEMS = NT * XRS;
-  static constexpr int NXR = 3;
+  static constexpr int NXR = 4;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int NCH = NT * CH;
   static constexpr int CPT = (NCH + THREADS - 1) / THREADS;  // chunks per thread
@@ -367,17 +367,21 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // Reduction slot (g, e) of k-step h is tile row rw + 32 h + 16 (e / 4) +
   // 4 g + e % 4, the rows the affinity layout left in that lane.
   const int tr_off = (rw + 4 * g + (l16 >> 2)) * XRS + 4 * (l16 & 3);
-  auto aggregate = [&](f32x4 (&acc)[JB][CB], const f32x4 (&s)[RB][JB], float f, const bf16* xr) {
+  auto weights = [&](bf16x8 (&a)[RB / 2][JB], const f32x4 (&s)[RB][JB], float f) {
 #pragma unroll
     for (int h = 0; h < RB / 2; ++h) {
       float fac[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) fac[e] = fac_of(f, 2 * h + (e >> 2), e & 3);
-      bf16x8 a[JB];
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[jb][e] = (bf16)(s[2 * h + (e >> 2)][jb][e & 3] * fac[e]);
+        for (int e = 0; e < 8; ++e) a[h][jb][e] = (bf16)(s[2 * h + (e >> 2)][jb][e & 3] * fac[e]);
+    }
+  };
+  auto aggregate = [&](f32x4 (&acc)[JB][CB], const bf16x8 (&a)[RB / 2][JB], const bf16* xr) {
+#pragma unroll
+    for (int h = 0; h < RB / 2; ++h) {
       const bf16* const xp = xr + tr_off + 32 * h * XRS;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
         const u32x2 hi = lds_read_tr16(xp + 16 * XRS + 16 * cb);
         const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
+        for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[h][jb], xb, acc[jb][cb]);
       }
     }
   };
@@ -434,61 +438,67 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: tiles 0 and 1 into the ring, tiles 2 .. 1+PF into registers,
-  // affinity and exponentials of tile 0.
+  // ---- prologue: tiles 0, 1, 2 into the ring, tiles 3 .. 2+PF into
+  // registers, affinity of tiles 0 and 1, exponentials of tile 0.
   Cursor cc = cursor_begin();  // tile t (aggregation, flush)
   Cursor cl = cc;              // next tile to load from HBM
   {
-    u32x4 tmp[G::CPT];
-    load_tile(tmp, cl, 0 < ntot);
-    store_tile(tmp, Xr);
-    cursor_next(cl);
-    load_tile(tmp, cl, 1 < ntot);
-    store_tile(tmp, Xr + G::XR_ELEMS);
-    cursor_next(cl);
+    // every HBM load of the prologue is issued before the first one is used
+    u32x4 tmp[3][G::CPT];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      load_tile(pre[(2 + p) % PF], cl, 2 + p < ntot);
+    for (int p = 0; p < 3; ++p) {
+      load_tile(tmp[p], cl, p < ntot);
       cursor_next(cl);
     }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      load_tile(pre[(3 + p) % PF], cl, 3 + p < ntot);
+      cursor_next(cl);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) store_tile(tmp[p], Xr + p * G::XR_ELEMS);
   }
   __syncthreads();
   f32x4 S0[RB][JB], S1[RB][JB];
   affinity(S0, Xr);
+  affinity(S1, Xr + G::XR_ELEMS);
   softmax_fast(S0, 0);
   __syncthreads();
 
-  // ---- main loop, unrolled by two so the two affinity tiles swap roles
-  // without register copies.  Ring index of tile t: t % 3.  Past the end of
-  // the list the staged tile is zeros and the affinity of "t+1" is computed
-  // and unused, so the hot path has no data-dependent branch but the rare
-  // exact one.
-  int q0 = 0;
+  // ---- main loop.  Step t: stage tile t+3, factors and weights of tile t,
+  // aggregation of tile t, affinity of tile t+2 (into the registers tile t's
+  // scores just left), exponentials of tile t+1 (its affinity came from the
+  // step before), one barrier.  The exponentials depend on no product of
+  // the same step, so matrix-core and VALU work of a step overlap freely.
+  // Unrolled by two so the two score tiles swap roles without copies.  Ring
+  // slot of tile t: t % 4.  Past the end of the list the staged tiles are
+  // zeros and the scores computed for them are unused, so the hot path has
+  // no data-dependent branch but the rare exact one.
   auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT]) {
-    const int q1 = q0 == 2 ? 0 : q0 + 1;
-    const int q2 = q1 == 2 ? 0 : q1 + 1;
-    bf16* const xr_t = Xr + q0 * G::XR_ELEMS;
-    bf16* const xr_t1 = Xr + q1 * G::XR_ELEMS;
-    bf16* const xr_t2 = Xr + q2 * G::XR_ELEMS;
-    store_tile(pslot, xr_t2);
-    load_tile(pslot, cl, t + 2 + PF < ntot);
-    affinity(Sb, xr_t1);
+    bf16* const xr_t = Xr + (t & 3) * G::XR_ELEMS;
+    bf16* const xr_t2 = Xr + ((t + 2) & 3) * G::XR_ELEMS;
+    bf16* const xr_t3 = Xr + ((t + 3) & 3) * G::XR_ELEMS;
+    store_tile(pslot, xr_t3);
+    load_tile(pslot, cl, t + 3 + PF < ntot);
     float f;
     bool bad;
     combine_fast(f, bad, t & 1);
     if (bad) exact_wave(Sa, f, xr_t);
-    aggregate(acc, Sa, f, xr_t);
+    bf16x8 a[RB / 2][JB];
+    weights(a, Sa, f);
+    aggregate(acc, a, xr_t);
+    affinity(Sa, xr_t2);
     softmax_fast(Sb, (t + 1) & 1);
     if (cc.row + NT >= cc.end) flush(acc, cc.u);
     cursor_next(cc);
     cursor_next(cl);
-    q0 = q1;
     __syncthreads();
   };
   for (int t = 0; t < ntot; t += 2) {
-    step(t, S0, S1, pre[0]);
-    if (t + 1 < ntot) step(t + 1, S1, S0, pre[PF - 1]);
+    step(t, S0, S1, pre[3 % PF]);
+    if (t + 1 < ntot) step(t + 1, S1, S0, pre[0]);
   }
+
 }
 
 template <int D, int KW, int WJ, int WI, int RB, int PF>
