@@ -49,15 +49,16 @@ constexpr double kLog2e = 1.4426950408889634073599246810019;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Plan of the fused pass for a supported (dtype, d, k).
-// bf16 with 32 < k <= 256 (d = 128) or 32 < k <= 512 (d = 64): the streamed,
-// software-pipelined pass (sa_stream.hpp), eight waves per group, 32
-// prototypes per wave (64 for d = 64 above k = 256), the folded matrix in
-// registers, 64 rows per wave and tile where LDS and registers allow.  Other
-// bf16 shapes: the lockstep pass (sa_fused.hpp), eight waves, folded matrix
-// in LDS, at most 128 accumulator registers per lane.  float32: lockstep,
-// four waves, folded matrix in registers.
-// SA_PLAN="kw,waves_k,waves_rows,m_in_lds[,kind[,prefetch[,row_blocks]]]" in
-// the environment overrides the choice when that plan is compiled.
+// bf16 with k > 32: the streamed pass (sa_stream.hpp), eight waves per group
+// (four for d = 128, k <= 64).  Up to k = 256 (d = 128) or 512 (d = 64) each
+// wave holds 32 prototypes (64 for d = 64 above k = 256), the folded matrix
+// in registers and two affinity tiles in flight; above that (k <= 512 for
+// d = 128, k <= 1024 for d = 64) each wave holds k_pad / 8 prototypes, one
+// affinity tile, and the folded matrix sits in LDS.  bf16 with k <= 32: the
+// lockstep pass (sa_fused.hpp), eight waves.  float32: lockstep, four waves,
+// folded matrix in registers.
+// SA_PLAN="kw,waves_k,waves_rows,m_in_lds[,kind[,prefetch[,row_blocks[,score_buffers]]]]"
+// in the environment overrides the choice when that plan is compiled.
 Plan make_plan(int dtype, int d, int k) {
   Plan p{};
   p.dtype = dtype;
@@ -66,14 +67,22 @@ Plan make_plan(int dtype, int d, int k) {
   p.kind = 0;
   p.prefetch = 1;
   p.row_blocks = 2;
+  p.score_buffers = 2;
   const int waves = dtype == SA_BF16 ? 8 : 4;
   const int k16 = (k + 15) / 16 * 16;
-  const bool stream = dtype == SA_BF16 && k > 32 && (d == 128 ? k <= 256 : k <= 512);
+  const bool stream = dtype == SA_BF16 && k > 32;
   if (stream) {
     p.kind = 1;
-    p.kw = (d == 64 && k > 256) ? 64 : 32;
-    p.waves_k = k <= 64 ? 2 : (k <= 128 ? 4 : 8);
-    p.row_blocks = (p.kw == 32 && (p.waves_k == 8 || (d == 64 && p.waves_k == 4))) ? 4 : 2;
+    const bool wide = d == 128 ? k > 256 : k > 512;  // folded matrix too large for registers
+    if (wide) {
+      p.kw = d == 128 ? 64 : 128;
+      p.waves_k = 8;
+      p.score_buffers = 1;
+    } else {
+      p.kw = (d == 64 && k > 256) ? 64 : 32;
+      p.waves_k = k <= 64 ? 2 : (k <= 128 ? 4 : 8);
+      p.row_blocks = (p.kw == 32 && (p.waves_k == 8 || (d == 64 && p.waves_k == 4))) ? 4 : 2;
+    }
     // d = 128, k <= 64: two row waves (four waves per group) keep the four
     // 64-row LDS tiles of the ring within budget
     p.waves_rows = (d == 128 && p.waves_k == 2) ? 2 : waves / p.waves_k;
@@ -95,12 +104,12 @@ Plan make_plan(int dtype, int d, int k) {
   if (!stream) p.waves_rows = waves / p.waves_k;
   p.m_in_lds = (dtype == SA_BF16 && !stream) ? 1 : 0;
   if (const char* env = std::getenv("SA_PLAN")) {
-    int kw = 0, wk = 0, wr = 0, ml = 0, kind = 0, pf = 1, rb = 2;
-    const int n = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &kw, &wk, &wr, &ml, &kind, &pf, &rb);
+    int kw = 0, wk = 0, wr = 0, ml = 0, kind = 0, pf = 1, rb = 2, sb = 2;
+    const int n = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &kw, &wk, &wr, &ml, &kind, &pf, &rb, &sb);
     if (n >= 4 && kw % 16 == 0 && kw > 0 && wk > 0 && wr > 0 && kw * wk >= k && (kind == 0 || kind == 1) &&
-        (pf == 1 || pf == 2) && (rb == 2 || rb == 4)) {
+        (pf == 1 || pf == 2) && (rb == 2 || rb == 4) && (sb == 1 || sb == 2)) {
       p.kw = kw; p.waves_k = wk; p.waves_rows = wr; p.m_in_lds = ml ? 1 : 0; p.kind = kind; p.prefetch = pf;
-      p.row_blocks = rb;
+      p.row_blocks = rb; p.score_buffers = sb;
     }
   }
   p.k_pad = p.kw * p.waves_k;

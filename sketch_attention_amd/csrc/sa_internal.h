@@ -29,6 +29,7 @@ struct Plan {
   int kind;         // 0 = lockstep pass (sa_fused.hpp), 1 = streamed pass (sa_stream.hpp, bf16)
   int prefetch;     // streamed pass: tiles held in registers between HBM and LDS (1 or 2)
   int row_blocks;   // streamed pass: 16-row blocks per wave and tile (2 or 4)
+  int score_buffers;  // streamed pass: affinity tiles in flight per wave (2: M in registers; 1: M in LDS)
 };
 
 // Arguments of the fused kernel (passed by value in the dispatch packet).

@@ -65,9 +65,10 @@ __device__ __forceinline__ float row_bcast(float x) {
                                                                 false));
 }
 
-template <int D, int KW, int WJ, int WI, int RB, int PF>
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
 struct StreamGeom {
-  static_assert(KW % 16 == 0 && D % 32 == 0 && (PF == 1 || PF == 2) && (RB == 2 || RB == 4), "tile shape");
+  static_assert(KW % 16 == 0 && D % 32 == 0 && (PF == 1 || PF == 2) && (RB == 2 || RB == 4) && (SB == 1 || SB == 2),
+                "tile shape");
   static constexpr int NW = WJ * WI;
   static constexpr int THREADS = 64 * NW;
   static constexpr int RW = 16 * RB;           // rows per wave and tile
@@ -78,7 +79,7 @@ struct StreamGeom {
   static constexpr int KPAD = KW * WJ;
   static constexpr int XRS = D + 16;           // row stride (elements): +32 bytes, conflict-free fragment reads
   static constexpr int XR_ELEMS = NT * XRS;
-  static constexpr int NXR = 4;
+  static constexpr int NXR = SB == 2 ? 4 : 3;   // X tiles in the LDS ring
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int NCH = NT * CH;
   static constexpr int CPT = (NCH + THREADS - 1) / THREADS;  // chunks per thread
@@ -87,13 +88,18 @@ struct StreamGeom {
   static constexpr int STAGE_BYTES = WI > 1 ? WJ * CB * 64 * 16 : 0;
   static constexpr int OFF_XL = XR_BYTES;
   static constexpr int OFF_STAGE = OFF_XL + XL_BYTES;
-  static constexpr int LDS_BYTES = OFF_STAGE + STAGE_BYTES;
+  // one score buffer: the folded matrix lives in LDS, rows of D bf16 with
+  // their 16-byte chunks XOR-swizzled (chunk c of row r at c ^ ((r / P) % CH),
+  // P rows per 256 bytes), so fragment reads are conflict-free without padding
+  static constexpr int M_BYTES = SB == 1 ? KPAD * D * 2 : 0;
+  static constexpr int OFF_M = OFF_STAGE + STAGE_BYTES;
+  static constexpr int LDS_BYTES = OFF_M + M_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
-template <int D, int KW, int WJ, int WI, int RB, int PF, bool PAD>
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args) {
-  using G = StreamGeom<D, KW, WJ, WI, RB, PF>;
+  using G = StreamGeom<D, KW, WJ, WI, RB, PF, SB>;
   using MF = Mfma<bf16>;
   constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, RW = G::RW, THREADS = G::THREADS;
   constexpr int XRS = G::XRS;
@@ -164,13 +170,28 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   };
 
   // ---- folded matrix: this wave's KW rows as B fragments, in registers
-  bf16x8 mreg[JB][CS];
+  // (two score buffers) or in the swizzled LDS copy (one score buffer)
+  constexpr int MP = 256 / (2 * D);  // rows of M per 256 bytes
+  bf16x8 mreg[SB == 2 ? JB : 1][SB == 2 ? CS : 1];
+  bf16* const Ms = reinterpret_cast<bf16*>(lds + G::OFF_M);
+  int moff[CS];  // element offset of chunk 4 cs + g of this lane's rows (the swizzle depends on l16 only)
+  if constexpr (SB == 2) {
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb) {
-    const bf16* mrow = Mg + (int64_t)(jbase + 16 * jb + l16) * D;
+    for (int jb = 0; jb < JB; ++jb) {
+      const bf16* mrow = Mg + (int64_t)(jbase + 16 * jb + l16) * D;
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+      for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+    }
+  } else {
+    for (int idx = tid; idx < G::KPAD * G::CH; idx += THREADS) {
+      const int r = idx / G::CH, c = idx % G::CH;
+      *reinterpret_cast<u32x4*>(Ms + r * D + 8 * (c ^ ((r / MP) % G::CH))) =
+          *reinterpret_cast<const u32x4*>(Mg + (int64_t)r * D + 8 * c);
+    }
+    // ordered before the first read by the prologue's barrier
   }
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) moff[cs] = 8 * ((4 * cs + g) ^ ((l16 / MP) % G::CH));
 
   // ---- staging: thread chunk s covers row (tid + s*THREADS) / CH, 16 bytes.
   // Rows past the piece (or a tile past the list) load the piece's last row,
@@ -229,7 +250,15 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int ib = 0; ib < RB; ++ib) s[ib][jb] = MF::run(xa[ib], mreg[jb][cs], s[ib][jb]);
+        for (int ib = 0; ib < RB; ++ib) {
+          bf16x8 mf;
+          if constexpr (SB == 2) {
+            mf = mreg[jb][cs];
+          } else {
+            mf = *reinterpret_cast<const bf16x8*>(Ms + (jbase + 16 * jb + l16) * D + moff[cs]);
+          }
+          s[ib][jb] = MF::run(xa[ib], mf, s[ib][jb]);
+        }
     }
     pad_protos(s, jbase);
   };
@@ -307,57 +336,42 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // max / shifted-sum pass over all prototypes (M fragments from global
   // memory), then its own prototypes' weights 2^(s' - m) with factor 1 / l.
   auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, const bf16* xr) {
-#pragma unroll 1
+#pragma unroll  // s[ib] must be indexed by constants to stay in registers
     for (int ib = 0; ib < RB; ++ib) {
       bf16x8 xa[CS];
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs) xa[cs] = frag_c<D>(xr + (rw + 16 * ib + l16) * XRS, cs, g);
       float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       float l[4] = {0.f, 0.f, 0.f, 0.f};
-      f32x4 own[JB];
 #pragma unroll 1
       for (int w = 0; w < WJ; ++w) {
-        f32x4 sb[1][JB];
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
+        for (int jb = 0; jb < JB; ++jb) {  // one 16-prototype block at a time (few live registers)
           f32x4 a = {0.f, 0.f, 0.f, 0.f};
-          const bf16* mrow = Mg + (int64_t)(w * KW + 16 * jb + l16) * D;
+          const int j0 = w * KW + 16 * jb;
+          const bf16* mrow = Mg + (int64_t)(j0 + l16) * D;
 #pragma unroll
           for (int cs = 0; cs < CS; ++cs) a = MF::run(xa[cs], frag_c<D>(mrow, cs, g), a);
-          sb[0][jb] = a;
-        }
-        if constexpr (PAD) {
+          if constexpr (PAD) {
+            const bool ok = j0 + l16 < k;
 #pragma unroll
-          for (int jb = 0; jb < JB; ++jb) {
-            const bool ok = w * KW + 16 * jb + l16 < k;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sb[0][jb][r] = ok ? sb[0][jb][r] : -INFINITY;
+            for (int r = 0; r < 4; ++r) a[r] = ok ? a[r] : -INFINITY;
           }
-        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float bm = sb[0][0][r];
-#pragma unroll
-          for (int jb = 1; jb < JB; ++jb) bm = fmaxf(bm, sb[0][jb][r]);
-          bm = row16_max(bm);
-          const float mn = fmaxf(m[r], bm);
-          if (mn != -INFINITY) {  // a block of padding only leaves the state as it is
-            float se = 0.f;
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) se += fast_exp2(sb[0][jb][r] - mn);
-            l[r] = l[r] * fast_exp2(m[r] - mn) + row16_sum(se);
-            m[r] = mn;
+          for (int r = 0; r < 4; ++r) {
+            const float mn = fmaxf(m[r], row16_max(a[r]));
+            if (mn != -INFINITY) {  // a block of padding only leaves the state as it is
+              l[r] = l[r] * fast_exp2(m[r] - mn) + row16_sum(fast_exp2(a[r] - mn));
+              m[r] = mn;
+            }
           }
-        }
-        if (w == wj) {
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb) own[jb] = sb[0][jb];
+          if (w == wj) s[ib][jb] = a;  // this wave's own scores, kept where its fast-path values were
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) s[ib][jb][r] = fast_exp2(own[jb][r] - m[r]);
+        for (int jb = 0; jb < JB; ++jb) s[ib][jb][r] = fast_exp2(s[ib][jb][r] - m[r]);
         if (ib == my_ib && r == my_r) f = 1.f / l[r];
       }
     }
@@ -438,87 +452,131 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: tiles 0, 1, 2 into the ring, tiles 3 .. 2+PF into
-  // registers, affinity of tiles 0 and 1, exponentials of tile 0.
   Cursor cc = cursor_begin();  // tile t (aggregation, flush)
   Cursor cl = cc;              // next tile to load from HBM
+  constexpr int NPRE = SB == 2 ? 3 : 2;  // tiles staged by the prologue
+
+  // ---- prologue: tiles 0 .. NPRE-1 into the ring, the next PF into
+  // registers (every HBM load issued before the first one is used), then
+  // the first affinities and exponentials.
   {
-    // every HBM load of the prologue is issued before the first one is used
-    u32x4 tmp[3][G::CPT];
+    u32x4 tmp[NPRE][G::CPT];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
+    for (int p = 0; p < NPRE; ++p) {
       load_tile(tmp[p], cl, p < ntot);
       cursor_next(cl);
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      load_tile(pre[(3 + p) % PF], cl, 3 + p < ntot);
+      load_tile(pre[(NPRE + p) % PF], cl, NPRE + p < ntot);
       cursor_next(cl);
     }
 #pragma unroll
-    for (int p = 0; p < 3; ++p) store_tile(tmp[p], Xr + p * G::XR_ELEMS);
+    for (int p = 0; p < NPRE; ++p) store_tile(tmp[p], Xr + p * G::XR_ELEMS);
   }
   __syncthreads();
-  f32x4 S0[RB][JB], S1[RB][JB];
-  affinity(S0, Xr);
-  affinity(S1, Xr + G::XR_ELEMS);
-  softmax_fast(S0, 0);
-  __syncthreads();
 
-  // ---- main loop.  Step t: stage tile t+3, factors and weights of tile t,
-  // aggregation of tile t, affinity of tile t+2 (into the registers tile t's
-  // scores just left), exponentials of tile t+1 (its affinity came from the
-  // step before), one barrier.  The exponentials depend on no product of
-  // the same step, so matrix-core and VALU work of a step overlap freely.
-  // Unrolled by two so the two score tiles swap roles without copies.  Ring
-  // slot of tile t: t % 4.  Past the end of the list the staged tiles are
-  // zeros and the scores computed for them are unused, so the hot path has
-  // no data-dependent branch but the rare exact one.
-  auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT]) {
-    bf16* const xr_t = Xr + (t & 3) * G::XR_ELEMS;
-    bf16* const xr_t2 = Xr + ((t + 2) & 3) * G::XR_ELEMS;
-    bf16* const xr_t3 = Xr + ((t + 3) & 3) * G::XR_ELEMS;
-    store_tile(pslot, xr_t3);
-    load_tile(pslot, cl, t + 3 + PF < ntot);
-    float f;
-    bool bad;
-    combine_fast(f, bad, t & 1);
-    if (bad) exact_wave(Sa, f, xr_t);
-    bf16x8 a[RB / 2][JB];
-    weights(a, Sa, f);
-    aggregate(acc, a, xr_t);
-    affinity(Sa, xr_t2);
-    softmax_fast(Sb, (t + 1) & 1);
-    if (cc.row + NT >= cc.end) flush(acc, cc.u);
-    cursor_next(cc);
-    cursor_next(cl);
+  if constexpr (SB == 2) {
+    f32x4 S0[RB][JB], S1[RB][JB];
+    affinity(S0, Xr);
+    affinity(S1, Xr + G::XR_ELEMS);
+    softmax_fast(S0, 0);
     __syncthreads();
-  };
-  for (int t = 0; t < ntot; t += 2) {
-    step(t, S0, S1, pre[3 % PF]);
-    if (t + 1 < ntot) step(t + 1, S1, S0, pre[0]);
-  }
 
+    // ---- main loop.  Step t: stage tile t+3, factors and weights of tile
+    // t, aggregation of tile t, affinity of tile t+2 (into the registers
+    // tile t's scores just left), exponentials of tile t+1 (its affinity came
+    // from the step before), one barrier.  The exponentials depend on no
+    // product of the same step, so matrix-core and VALU work of a step
+    // overlap freely.  Unrolled by two so the two score tiles swap roles
+    // without copies.  Ring slot of tile t: t % 4.  Past the end of the list
+    // the staged tiles are zeros and the scores computed for them are unused,
+    // so the hot path has no data-dependent branch but the rare exact one.
+    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT]) {
+      bf16* const xr_t = Xr + (t & 3) * G::XR_ELEMS;
+      bf16* const xr_t2 = Xr + ((t + 2) & 3) * G::XR_ELEMS;
+      bf16* const xr_t3 = Xr + ((t + 3) & 3) * G::XR_ELEMS;
+      store_tile(pslot, xr_t3);
+      load_tile(pslot, cl, t + 3 + PF < ntot);
+      float f;
+      bool bad;
+      combine_fast(f, bad, t & 1);
+      if (bad) exact_wave(Sa, f, xr_t);
+      bf16x8 a[RB / 2][JB];
+      weights(a, Sa, f);
+      aggregate(acc, a, xr_t);
+      affinity(Sa, xr_t2);
+      softmax_fast(Sb, (t + 1) & 1);
+      if (cc.row + NT >= cc.end) flush(acc, cc.u);
+      cursor_next(cc);
+      cursor_next(cl);
+      __syncthreads();
+    };
+    for (int t = 0; t < ntot; t += 2) {
+      step(t, S0, S1, pre[3 % PF]);
+      if (t + 1 < ntot) step(t + 1, S1, S0, pre[0]);
+    }
+  } else {
+    f32x4 S[RB][JB];
+    affinity(S, Xr);
+    softmax_fast(S, 0);
+    __syncthreads();
+
+    // ---- main loop, one score buffer.  Step t: stage tile t+2, factors and
+    // weights of tile t (the scores become bf16 operands, freeing S),
+    // aggregation of tile t, affinity and exponentials of tile t+1 into S,
+    // one barrier.  Ring slot of tile t: t % 3.
+    int q0 = 0;
+    auto step = [&](int t, u32x4 (&pslot)[G::CPT]) {
+      const int q1 = q0 == 2 ? 0 : q0 + 1;
+      const int q2 = q1 == 2 ? 0 : q1 + 1;
+      bf16* const xr_t = Xr + q0 * G::XR_ELEMS;
+      bf16* const xr_t1 = Xr + q1 * G::XR_ELEMS;
+      bf16* const xr_t2 = Xr + q2 * G::XR_ELEMS;
+      store_tile(pslot, xr_t2);
+      load_tile(pslot, cl, t + 2 + PF < ntot);
+      float f;
+      bool bad;
+      combine_fast(f, bad, t & 1);
+      if (bad) exact_wave(S, f, xr_t);
+      bf16x8 a[RB / 2][JB];
+      weights(a, S, f);
+      aggregate(acc, a, xr_t);
+      affinity(S, xr_t1);
+      softmax_fast(S, (t + 1) & 1);
+      if (cc.row + NT >= cc.end) flush(acc, cc.u);
+      cursor_next(cc);
+      cursor_next(cl);
+      q0 = q1;
+      __syncthreads();
+    };
+    for (int t = 0; t < ntot; t += 2) {
+      step(t, pre[2 % PF]);
+      if (t + 1 < ntot) step(t + 1, pre[3 % PF]);
+    }
+  }
 }
 
-template <int D, int KW, int WJ, int WI, int RB, int PF>
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
 hipError_t run_stream_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
   constexpr int threads = 64 * WJ * WI;
   if (p.k == p.k_pad) {
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, false>,
-                                                                 threads, 0);
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, false>), dim3(groups), dim3(threads), 0, st, a);
+    if (occ)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false>,
+                                                          threads, 0);
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false>), dim3(groups), dim3(threads), 0, st, a);
   } else {
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, true>,
-                                                                 threads, 0);
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, true>), dim3(groups), dim3(threads), 0, st, a);
+    if (occ)
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true>,
+                                                          threads, 0);
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true>), dim3(groups), dim3(threads), 0, st, a);
   }
   return hipGetLastError();
 }
 
-#define SA_STREAM_PLAN(D_, KW_, WJ_, WI_, RB_, PF_)                                                \
+#define SA_STREAM_PLAN(D_, KW_, WJ_, WI_, RB_, PF_, SB_)                                           \
   if (p.kind == 1 && p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.row_blocks == RB_ && \
-      p.prefetch == PF_)                                                                            \
-    return run_stream_plan<D_, KW_, WJ_, WI_, RB_, PF_>(p, a, groups, st, occ);
+      p.prefetch == PF_ && p.score_buffers == SB_)                                                  \
+    return run_stream_plan<D_, KW_, WJ_, WI_, RB_, PF_, SB_>(p, a, groups, st, occ);
 
 }  // namespace sa
