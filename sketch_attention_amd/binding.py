@@ -60,7 +60,7 @@ def library() -> ctypes.CDLL:
     p_f64 = ctypes.POINTER(ctypes.c_double)
     sig = {
         "sa_create": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, vp]),
-        "sa_compress_batch": (i32, [vp, vp, p_i64, i32, vp, vp]),
+        "sa_compress_batch": (i32, [vp, vp, vp, i32, vp, vp]),
         "sa_destroy": (None, [vp]),
         "sa_status_string": (ctypes.c_char_p, [i32]),
         "sa_check_config": (i32, [i32, i32, f32, i32]),
@@ -147,8 +147,15 @@ def sa_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
 
 def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
                       stream: Optional[torch.cuda.Stream] = None) -> None:
-    """Enqueue the compression of a packed batch into `out` ([U, k, d] float32)."""
-    offs = _offsets_array(offsets)
+    """Enqueue the compression of a packed batch into `out` ([U, k, d] float32).
+
+    The library selects the handle's device itself, so no device context is
+    entered here; pointers go to ctypes as plain integers."""
+    if isinstance(offsets, np.ndarray) and offsets.dtype == np.int64 and offsets.ndim == 1 and \
+            offsets.flags["C_CONTIGUOUS"]:
+        offs = offsets
+    else:
+        offs = _offsets_array(offsets)
     if offs.ndim != 1 or offs.size < 1:
         raise ValueError("offsets must be a 1-D array of length num_users + 1")
     _device_tensor(X, "X")
@@ -157,9 +164,10 @@ def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: to
         raise ValueError("out must be float32")
     if X.dim() != 2 or X.shape[0] != int(offs[-1]):
         raise ValueError("X must be [offsets[-1], d]")
-    with torch.cuda.device(X.device):
-        st = library().sa_compress_batch(handle, ctypes.c_void_p(X.data_ptr()), _i64_ptr(offs), int(offs.size - 1),
-                                         ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream, X.device))
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    st = library().sa_compress_batch(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
+                                     stream.cuda_stream)
     _check(st, "sa_compress_batch")
 
 

@@ -22,7 +22,7 @@ namespace {
 using sa::Plan;
 
 struct TimingSlot {
-  hipEvent_t ev[3];  // before fused, after fused, after reduce
+  hipEvent_t ev[4];  // fused kernel start/stop, reduction kernel start/stop (recorded by the dispatches)
   bool fused;        // false when the launch had no rows (reduce only)
 };
 
@@ -333,17 +333,12 @@ SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* of
     if (h->timing) {
       ts = take_slot(h);
       ts.fused = rows > 0;
-      if (ts.ev[0]) (void)hipEventRecord(ts.ev[0], s);
     }
     if (rows > 0) {
-      if (sa::launch_fused(plan, fa, groups, s) != hipSuccess) return SA_ERR_DEVICE;
+      if (sa::launch_fused(plan, fa, groups, s, ts.ev[0], ts.ev[1]) != hipSuccess) return SA_ERR_DEVICE;
     }
-    if (h->timing && ts.ev[1]) (void)hipEventRecord(ts.ev[1], s);
-    if (sa::launch_reduce(ra, s) != hipSuccess) return SA_ERR_DEVICE;
-    if (h->timing) {
-      if (ts.ev[2]) (void)hipEventRecord(ts.ev[2], s);
-      h->slots.push_back(ts);
-    }
+    if (sa::launch_reduce(ra, s, ts.ev[2], ts.ev[3]) != hipSuccess) return SA_ERR_DEVICE;
+    if (h->timing) h->slots.push_back(ts);
   }
   return SA_OK;
 }
@@ -370,13 +365,13 @@ SA_API sa_status sa_read_kernel_timing(sa_handle h, double* fused_ms, double* re
   int64_t n = 0;
   sa_status st = SA_OK;
   for (auto& s : h->slots) {
-    if (!s.ev[0] || !s.ev[1] || !s.ev[2] || hipEventSynchronize(s.ev[2]) != hipSuccess) {
+    if (!s.ev[0] || !s.ev[1] || !s.ev[2] || !s.ev[3] || hipEventSynchronize(s.ev[3]) != hipSuccess) {
       st = SA_ERR_DEVICE;
       continue;
     }
     float a = 0.f, b = 0.f;
-    if (hipEventElapsedTime(&a, s.ev[0], s.ev[1]) != hipSuccess ||
-        hipEventElapsedTime(&b, s.ev[1], s.ev[2]) != hipSuccess) {
+    if ((s.fused && hipEventElapsedTime(&a, s.ev[0], s.ev[1]) != hipSuccess) ||
+        hipEventElapsedTime(&b, s.ev[2], s.ev[3]) != hipSuccess) {
       st = SA_ERR_DEVICE;
       continue;
     }

@@ -39,6 +39,7 @@
 //   5. accumulators stay in registers (float32) for the whole piece.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -669,9 +670,14 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
 }
 
 template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
-hipError_t launch_fused_t(const FusedArgs& args, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>), dim3(groups), dim3(64 * WJ * WI), 0, stream,
-                     args);
+hipError_t launch_fused_t(const FusedArgs& args, const Launch& l) {
+  if (l.start || l.stop) {
+    hipExtLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>), dim3(l.groups), dim3(64 * WJ * WI), 0,
+                          l.stream, l.start, l.stop, 0, args);
+  } else {
+    hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>), dim3(l.groups), dim3(64 * WJ * WI), 0,
+                       l.stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -684,16 +690,14 @@ hipError_t occupancy_t(int* n) {
 // One plan of the fused pass: launch it, or (occ != nullptr) report how
 // many of its work groups fit on a compute unit.
 template <typename T, int D, int KW, int WJ, int WI, bool MLDS>
-hipError_t run_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+hipError_t run_plan(const Plan& p, const FusedArgs& a, const Launch& l, int* occ) {
   if (p.k == p.k_pad)
-    return occ ? occupancy_t<T, D, KW, WJ, WI, MLDS, false>(occ)
-               : launch_fused_t<T, D, KW, WJ, WI, MLDS, false>(a, groups, st);
-  return occ ? occupancy_t<T, D, KW, WJ, WI, MLDS, true>(occ)
-             : launch_fused_t<T, D, KW, WJ, WI, MLDS, true>(a, groups, st);
+    return occ ? occupancy_t<T, D, KW, WJ, WI, MLDS, false>(occ) : launch_fused_t<T, D, KW, WJ, WI, MLDS, false>(a, l);
+  return occ ? occupancy_t<T, D, KW, WJ, WI, MLDS, true>(occ) : launch_fused_t<T, D, KW, WJ, WI, MLDS, true>(a, l);
 }
 
 #define SA_PLAN(T_, D_, KW_, WJ_, WI_, MLDS_)                                                       \
   if (p.kind == 0 && p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.m_in_lds == MLDS_) \
-    return run_plan<T_, D_, KW_, WJ_, WI_, MLDS_>(p, a, groups, st, occ);
+    return run_plan<T_, D_, KW_, WJ_, WI_, MLDS_>(p, a, l, occ);
 
 }  // namespace sa

@@ -5,7 +5,7 @@
 
 namespace sa {
 
-hipError_t dispatch_bf16_d128(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+hipError_t dispatch_bf16_d128(const Plan& p, const FusedArgs& a, const Launch& l, int* occ) {
   SA_PLAN(bf16, 128, 16, 1, 8, true)
   SA_PLAN(bf16, 128, 32, 1, 8, true)
   SA_PLAN(bf16, 128, 64, 1, 8, true)

@@ -56,9 +56,13 @@ struct ReduceArgs {
   int64_t offsets[kMaxUsersPerLaunch + 1];
 };
 
-// Launchers (defined in the .hip translation units).
-hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream);
-hipError_t launch_reduce(const ReduceArgs& args, hipStream_t stream);
+// Launchers (defined in the .hip translation units).  Non-null start/stop
+// events are recorded by the kernel's own dispatch (hipExtLaunchKernelGGL):
+// they time the kernel itself and add no packets to the stream.
+hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream,
+                        hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+hipError_t launch_reduce(const ReduceArgs& args, hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 hipError_t launch_fold(int dtype, const void* P, const void* WQ, const void* WK, float scale, int k, int k_pad,
                        int d, float* tmp, void* M, hipStream_t stream);
 hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hipStream_t stream);
@@ -67,12 +71,19 @@ hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
 
 // Plan groups, one translation unit each (see sa_fused_*.hip).  With
 // occ != nullptr they report occupancy instead of launching.
-using DispatchFn = hipError_t (*)(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_bf16_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_bf16_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_f32_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_f32_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_stream_d64(const Plan&, const FusedArgs&, int, hipStream_t, int*);
-hipError_t dispatch_stream_d128(const Plan&, const FusedArgs&, int, hipStream_t, int*);
+// Launch description handed to the per-plan dispatchers.
+struct Launch {
+  int groups;
+  hipStream_t stream;
+  hipEvent_t start, stop;  // optional, recorded by the dispatch
+};
+// occ != nullptr: report how many work groups of the plan fit on a CU instead of launching.
+using DispatchFn = hipError_t (*)(const Plan&, const FusedArgs&, const Launch&, int*);
+hipError_t dispatch_bf16_d64(const Plan&, const FusedArgs&, const Launch&, int*);
+hipError_t dispatch_bf16_d128(const Plan&, const FusedArgs&, const Launch&, int*);
+hipError_t dispatch_f32_d64(const Plan&, const FusedArgs&, const Launch&, int*);
+hipError_t dispatch_f32_d128(const Plan&, const FusedArgs&, const Launch&, int*);
+hipError_t dispatch_stream_d64(const Plan&, const FusedArgs&, const Launch&, int*);
+hipError_t dispatch_stream_d128(const Plan&, const FusedArgs&, const Launch&, int*);
 
 }  // namespace sa

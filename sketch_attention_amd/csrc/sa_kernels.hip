@@ -1,5 +1,6 @@
 // Support kernels: weight fold, split-n partial reduction, and the launch
 // dispatchers of the fused pass.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -144,13 +145,16 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
     if (j0 + r < a.k) o[(int64_t)(j0 + r) * a.d + c] = s[r];
 }
 
-hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int slot_f4 = a.k_pad * a.d / 4;
   const int64_t per_user = (a.groups + a.users) / (a.users > 0 ? a.users : 1);
   int shares = 1;
   while (shares < kReduceShares && 8 * 2 * shares <= per_user) shares *= 2;
-  hipLaunchKernelGGL(reduce_kernel, dim3((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users),
-                     dim3(kReduceLanes * shares), 0, stream, a);
+  const dim3 grid((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users), block(kReduceLanes * shares);
+  if (start || stop)
+    hipExtLaunchKernelGGL(reduce_kernel, grid, block, 0, stream, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(reduce_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -172,15 +176,18 @@ static DispatchFn plan_group(const Plan& p) {
   return nullptr;
 }
 
-hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream) {
+hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
   DispatchFn f = plan_group(plan);
-  return f ? f(plan, args, groups, stream, nullptr) : hipErrorInvalidValue;
+  const Launch l{groups, stream, start, stop};
+  return f ? f(plan, args, l, nullptr) : hipErrorInvalidValue;
 }
 
 hipError_t fused_occupancy(const Plan& plan, int* n) {
   DispatchFn f = plan_group(plan);
   static const FusedArgs unused{};
-  return f ? f(plan, unused, 0, nullptr, n) : hipErrorInvalidValue;
+  const Launch l{0, nullptr, nullptr, nullptr};
+  return f ? f(plan, unused, l, n) : hipErrorInvalidValue;
 }
 
 }  // namespace sa

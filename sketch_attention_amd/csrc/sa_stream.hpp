@@ -557,26 +557,37 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   }
 }
 
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
+hipError_t launch_stream_t(const FusedArgs& a, const Launch& l) {
+  constexpr int threads = 64 * WJ * WI;
+  if (l.start || l.stop) {
+    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD>), dim3(l.groups), dim3(threads), 0,
+                          l.stream, l.start, l.stop, 0, a);
+  } else {
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD>), dim3(l.groups), dim3(threads), 0, l.stream,
+                       a);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
-hipError_t run_stream_plan(const Plan& p, const FusedArgs& a, int groups, hipStream_t st, int* occ) {
+hipError_t run_stream_plan(const Plan& p, const FusedArgs& a, const Launch& l, int* occ) {
   constexpr int threads = 64 * WJ * WI;
   if (p.k == p.k_pad) {
     if (occ)
       return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false>,
                                                           threads, 0);
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false>), dim3(groups), dim3(threads), 0, st, a);
-  } else {
-    if (occ)
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true>,
-                                                          threads, 0);
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true>), dim3(groups), dim3(threads), 0, st, a);
+    return launch_stream_t<D, KW, WJ, WI, RB, PF, SB, false>(a, l);
   }
-  return hipGetLastError();
+  if (occ)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true>,
+                                                        threads, 0);
+  return launch_stream_t<D, KW, WJ, WI, RB, PF, SB, true>(a, l);
 }
 
 #define SA_STREAM_PLAN(D_, KW_, WJ_, WI_, RB_, PF_, SB_)                                           \
   if (p.kind == 1 && p.kw == KW_ && p.waves_k == WJ_ && p.waves_rows == WI_ && p.row_blocks == RB_ && \
       p.prefetch == PF_ && p.score_buffers == SB_)                                                  \
-    return run_stream_plan<D_, KW_, WJ_, WI_, RB_, PF_, SB_>(p, a, groups, st, occ);
+    return run_stream_plan<D_, KW_, WJ_, WI_, RB_, PF_, SB_>(p, a, l, occ);
 
 }  // namespace sa
