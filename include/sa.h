@@ -125,9 +125,12 @@ sa_status sa_check_batch(int32_t k, const int64_t* offsets, int32_t num_users);
 sa_status sa_get_folded(sa_handle h, float* dst, void* stream);
 
 /*
- * Kernel timing for measurement.  While enabled, sa_compress_batch records
- * HIP events on its stream around each launch of the fused compression
- * kernel and of the partial-sum reduction.  sa_read_kernel_timing waits for
+ * Kernel timing for measurement.  While enabled, each launch of the fused
+ * compression kernel and of the partial-sum reduction made by
+ * sa_compress_batch carries a start and a stop HIP event that the kernel's
+ * own dispatch records on the caller's stream (so the durations are those of
+ * the kernels, and no extra work is queued); such launches cost the host more
+ * than plain ones.  sa_read_kernel_timing waits for
  * the recorded events, returns the summed durations in milliseconds and the
  * number of fused launches since the previous read, and starts a new count.
  * Any output pointer may be NULL.
