@@ -194,32 +194,42 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   for (int cs = 0; cs < CS; ++cs) moff[cs] = 8 * ((4 * cs + g) ^ ((l16 / MP) % G::CH));
 
   // ---- staging: thread chunk s covers row (tid + s*THREADS) / CH, 16 bytes.
-  // Rows past the piece (or a tile past the list) load the piece's last row,
-  // always in bounds, and are replaced by zeros: no branch in the hot block.
+  // A tile's loads read rows clamped to its piece (always in bounds, offsets
+  // 32-bit from the tile's first row); rows past the piece are replaced by
+  // zeros when the tile is staged, which only a piece's last tile needs.
   u32x4 pre[PF][G::CPT];
-  auto load_tile = [&](u32x4 (&dst)[G::CPT], const Cursor& c, bool valid) {
+  int pre_rows[PF];  // valid rows of the tile held in each register slot (0 past the list)
+  auto load_tile = [&](u32x4 (&dst)[G::CPT], int& dst_rows, const Cursor& c, bool valid) {
     const int64_t left = c.end - c.row;
-    const int rows_left = !valid ? 0 : (left < NT ? (int)left : NT);
+    dst_rows = !valid ? 0 : (left < NT ? (int)left : NT);
     const int last = (int)(c.end - 1 - c.row);  // -1 past the list: c.row + last = c.end - 1 >= 0
-    const bf16* tile = X + c.row * D;
+    const u32x4* tile = reinterpret_cast<const u32x4*>(X + c.row * D);
 #pragma unroll
     for (int s = 0; s < G::CPT; ++s) {
       const int ci = tid + s * THREADS;
       const int r = ci / G::CH, ch = ci % G::CH;
       if (G::NCH % THREADS == 0 || ci < G::NCH) {
         const int rr = r < last ? r : last;
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + rr * D + 8 * ch));
-        const bool ok = r < rows_left;
-        dst[s] = u32x4{ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
+        dst[s] = __builtin_nontemporal_load(tile + (rr * G::CH + ch));
       }
     }
   };
-  auto store_tile = [&](const u32x4 (&src)[G::CPT], bf16* xr) {
+  auto store_tile = [&](const u32x4 (&src)[G::CPT], int rows_valid, bf16* xr) {
+    if (rows_valid == NT) {  // uniform: every tile but a piece's last
 #pragma unroll
-    for (int s = 0; s < G::CPT; ++s) {
-      const int ci = tid + s * THREADS;
-      const int r = ci / G::CH, ch = ci % G::CH;
-      if (G::NCH % THREADS == 0 || ci < G::NCH) *reinterpret_cast<u32x4*>(xr + r * XRS + 8 * ch) = src[s];
+      for (int s = 0; s < G::CPT; ++s) {
+        const int ci = tid + s * THREADS;
+        const int r = ci / G::CH, ch = ci % G::CH;
+        if (G::NCH % THREADS == 0 || ci < G::NCH) *reinterpret_cast<u32x4*>(xr + r * XRS + 8 * ch) = src[s];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < G::CPT; ++s) {
+        const int ci = tid + s * THREADS;
+        const int r = ci / G::CH, ch = ci % G::CH;
+        if (G::NCH % THREADS == 0 || ci < G::NCH)
+          *reinterpret_cast<u32x4*>(xr + r * XRS + 8 * ch) = r < rows_valid ? src[s] : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
 
@@ -273,9 +283,11 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float acc = 0.f;
+        // the first term starts the sum (0 + e is not foldable for -0)
+        float acc = fast_exp2(s[ib][0][r]);
+        s[ib][0][r] = acc;
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
+        for (int jb = 1; jb < JB; ++jb) {
           const float e = fast_exp2(s[ib][jb][r]);
           s[ib][jb][r] = e;
           acc += e;
@@ -461,18 +473,19 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // the first affinities and exponentials.
   {
     u32x4 tmp[NPRE][G::CPT];
+    int tmp_rows[NPRE];
 #pragma unroll
     for (int p = 0; p < NPRE; ++p) {
-      load_tile(tmp[p], cl, p < ntot);
+      load_tile(tmp[p], tmp_rows[p], cl, p < ntot);
       cursor_next(cl);
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      load_tile(pre[(NPRE + p) % PF], cl, NPRE + p < ntot);
+      load_tile(pre[(NPRE + p) % PF], pre_rows[(NPRE + p) % PF], cl, NPRE + p < ntot);
       cursor_next(cl);
     }
 #pragma unroll
-    for (int p = 0; p < NPRE; ++p) store_tile(tmp[p], Xr + p * G::XR_ELEMS);
+    for (int p = 0; p < NPRE; ++p) store_tile(tmp[p], tmp_rows[p], Xr + p * G::XR_ELEMS);
   }
   __syncthreads();
 
@@ -492,12 +505,12 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     // without copies.  Ring slot of tile t: t % 4.  Past the end of the list
     // the staged tiles are zeros and the scores computed for them are unused,
     // so the hot path has no data-dependent branch but the rare exact one.
-    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT]) {
+    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT], int& prow) {
       bf16* const xr_t = Xr + (t & 3) * G::XR_ELEMS;
       bf16* const xr_t2 = Xr + ((t + 2) & 3) * G::XR_ELEMS;
       bf16* const xr_t3 = Xr + ((t + 3) & 3) * G::XR_ELEMS;
-      store_tile(pslot, xr_t3);
-      load_tile(pslot, cl, t + 3 + PF < ntot);
+      store_tile(pslot, prow, xr_t3);
+      load_tile(pslot, prow, cl, t + 3 + PF < ntot);
       float f;
       bool bad;
       combine_fast(f, bad, t & 1);
@@ -513,8 +526,8 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       __syncthreads();
     };
     for (int t = 0; t < ntot; t += 2) {
-      step(t, S0, S1, pre[3 % PF]);
-      if (t + 1 < ntot) step(t + 1, S1, S0, pre[0]);
+      step(t, S0, S1, pre[3 % PF], pre_rows[3 % PF]);
+      if (t + 1 < ntot) step(t + 1, S1, S0, pre[0], pre_rows[0]);
     }
   } else {
     f32x4 S[RB][JB];
@@ -527,14 +540,14 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     // aggregation of tile t, affinity and exponentials of tile t+1 into S,
     // one barrier.  Ring slot of tile t: t % 3.
     int q0 = 0;
-    auto step = [&](int t, u32x4 (&pslot)[G::CPT]) {
+    auto step = [&](int t, u32x4 (&pslot)[G::CPT], int& prow) {
       const int q1 = q0 == 2 ? 0 : q0 + 1;
       const int q2 = q1 == 2 ? 0 : q1 + 1;
       bf16* const xr_t = Xr + q0 * G::XR_ELEMS;
       bf16* const xr_t1 = Xr + q1 * G::XR_ELEMS;
       bf16* const xr_t2 = Xr + q2 * G::XR_ELEMS;
-      store_tile(pslot, xr_t2);
-      load_tile(pslot, cl, t + 2 + PF < ntot);
+      store_tile(pslot, prow, xr_t2);
+      load_tile(pslot, prow, cl, t + 2 + PF < ntot);
       float f;
       bool bad;
       combine_fast(f, bad, t & 1);
@@ -551,8 +564,8 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       __syncthreads();
     };
     for (int t = 0; t < ntot; t += 2) {
-      step(t, pre[2 % PF]);
-      if (t + 1 < ntot) step(t + 1, pre[3 % PF]);
+      step(t, pre[2 % PF], pre_rows[2 % PF]);
+      if (t + 1 < ntot) step(t + 1, pre[3 % PF], pre_rows[3 % PF]);
     }
   }
 }
