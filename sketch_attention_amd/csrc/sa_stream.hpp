@@ -45,6 +45,8 @@
 // memory), so no other wave waits for it.
 #pragma once
 
+#include <type_traits>
+
 #include "sa_fused.hpp"
 
 namespace sa {
@@ -56,6 +58,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ u32x2 lds_read_tr16(const bf16* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
+}
+
+// Integer sum over the 16 lanes of a DPP row (every lane gets the total).
+__device__ __forceinline__ int row16_sum_i(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  return x;
 }
 
 // Value of lane n of this lane's 16-lane row (DPP row_newbcast).
@@ -128,29 +139,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
 
-  // ---- the group's tile list: pieces (user segments) of [r_begin, r_end),
-  // each cut into tiles of NT rows.
-  int u_first;
-  {
-    int lo = 0, hi = args.users - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (args.offsets[mid] <= r_begin) lo = mid; else hi = mid - 1;
-    }
-    u_first = lo;
-  }
-  int ntot = 0;
-  {
-    int64_t r = r_begin;
-    int u = u_first;
-    while (r < r_end) {
-      const int64_t e = min(r_end, args.offsets[u + 1]);
-      ntot += (int)((e - r + NT - 1) / NT);
-      r = e;
-      ++u;
-      while (u < args.users && args.offsets[u + 1] <= r) ++u;
-    }
-  }
+  int u_first = 0, ntot = 0;
   // A cursor walks the tile list: first row of the tile, end of its piece, user.
   struct Cursor {
     int64_t row, end;
@@ -233,6 +222,39 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     }
   };
 
+  // tile 0 starts at r_begin whatever the users: its loads go out before the
+  // tile list is known (rows clamped to the group's range, masked at staging)
+  u32x4 tile0[G::CPT];
+  {
+    int unused_rows;
+    load_tile(tile0, unused_rows, Cursor{r_begin, r_end, 0}, true);
+  }
+
+  // ---- the group's tile list: pieces (user segments) of [r_begin, r_end),
+  // each cut into tiles of NT rows.  Every lane examines up to four users at
+  // once (no chain of dependent loads): u_first is the last user starting at
+  // or before r_begin (a prefix, offsets being non-decreasing; it is
+  // non-empty because offsets[u_first + 1] > r_begin), ntot the sum of the
+  // pieces' tile counts.
+  {
+    int cnt = 0, tiles = 0;
+    const int nq = (args.users + 63) / 64;
+    for (int q = 0; q < nq; ++q) {
+      const int uu = lane + 64 * q;
+      if (uu < args.users) {
+        const int64_t a = args.offsets[uu], b = args.offsets[uu + 1];
+        cnt += a <= r_begin ? 1 : 0;
+        const int64_t lo = a > r_begin ? a : r_begin, hi = b < r_end ? b : r_end;
+        if (hi > lo) tiles += (int)((hi - lo + NT - 1) / NT);
+      }
+    }
+    cnt = row16_sum_i(cnt);
+    tiles = row16_sum_i(tiles);
+    u_first = __builtin_amdgcn_readlane(cnt, 0) + __builtin_amdgcn_readlane(cnt, 16) +
+              __builtin_amdgcn_readlane(cnt, 32) + __builtin_amdgcn_readlane(cnt, 48) - 1;
+    ntot = __builtin_amdgcn_readlane(tiles, 0) + __builtin_amdgcn_readlane(tiles, 16) +
+           __builtin_amdgcn_readlane(tiles, 32) + __builtin_amdgcn_readlane(tiles, 48);
+  }
   // ---- affinity of rows 16 ib + .. with prototypes 16 jb + .. of block `mf`:
   // s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][16 jb + l16]
   auto pad_protos = [&](f32x4 (&s)[RB][JB], int j0) {
@@ -475,7 +497,11 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     u32x4 tmp[NPRE][G::CPT];
     int tmp_rows[NPRE];
 #pragma unroll
-    for (int p = 0; p < NPRE; ++p) {
+    for (int s0 = 0; s0 < G::CPT; ++s0) tmp[0][s0] = tile0[s0];
+    tmp_rows[0] = ntot > 0 ? (int)min((int64_t)NT, cl.end - cl.row) : 0;
+    cursor_next(cl);
+#pragma unroll
+    for (int p = 1; p < NPRE; ++p) {
       load_tile(tmp[p], tmp_rows[p], cl, p < ntot);
       cursor_next(cl);
     }
@@ -505,7 +531,11 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     // without copies.  Ring slot of tile t: t % 4.  Past the end of the list
     // the staged tiles are zeros and the scores computed for them are unused,
     // so the hot path has no data-dependent branch but the rare exact one.
-    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT], int& prow) {
+    // `full` (compile-time): tiles t+1 and t+2 exist, so the step has no
+    // branch but the exact one; the last two steps of a list skip the
+    // affinity and exponentials of tiles past its end.
+    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT], int& prow,
+                    auto full) {
       bf16* const xr_t = Xr + (t & 3) * G::XR_ELEMS;
       bf16* const xr_t2 = Xr + ((t + 2) & 3) * G::XR_ELEMS;
       bf16* const xr_t3 = Xr + ((t + 3) & 3) * G::XR_ELEMS;
@@ -518,17 +548,24 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       bf16x8 a[RB / 2][JB];
       weights(a, Sa, f);
       aggregate(acc, a, xr_t);
-      affinity(Sa, xr_t2);
-      softmax_fast(Sb, (t + 1) & 1);
+      if (decltype(full)::value || t + 2 < ntot) affinity(Sa, xr_t2);
+      if (decltype(full)::value || t + 1 < ntot) softmax_fast(Sb, (t + 1) & 1);
       if (cc.row + NT >= cc.end) flush(acc, cc.u);
       cursor_next(cc);
       cursor_next(cl);
       __syncthreads();
     };
-    for (int t = 0; t < ntot; t += 2) {
-      step(t, S0, S1, pre[3 % PF], pre_rows[3 % PF]);
-      if (t + 1 < ntot) step(t + 1, S1, S0, pre[0], pre_rows[0]);
+    using Full = std::integral_constant<bool, true>;
+    using Tail = std::integral_constant<bool, false>;
+    int t = 0;
+    for (; t + 3 < ntot; t += 2) {
+      step(t, S0, S1, pre[3 % PF], pre_rows[3 % PF], Full{});
+      step(t + 1, S1, S0, pre[0], pre_rows[0], Full{});
     }
+    // 0..3 steps remain; S0 holds tile t's scores
+    if (t < ntot) step(t, S0, S1, pre[3 % PF], pre_rows[3 % PF], Tail{});
+    if (t + 1 < ntot) step(t + 1, S1, S0, pre[0], pre_rows[0], Tail{});
+    if (t + 2 < ntot) step(t + 2, S0, S1, pre[3 % PF], pre_rows[3 % PF], Tail{});
   } else {
     f32x4 S[RB][JB];
     affinity(S, Xr);
