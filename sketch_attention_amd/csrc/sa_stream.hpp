@@ -491,33 +491,34 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   constexpr int NPRE = SB == 2 ? 3 : 2;  // tiles staged by the prologue
 
   // ---- prologue: tiles 0 .. NPRE-1 into the ring, the next PF into
-  // registers (every HBM load issued before the first one is used), then
-  // the first affinities and exponentials.
-  {
-    u32x4 tmp[NPRE][G::CPT];
-    int tmp_rows[NPRE];
+  // registers (every HBM load issued before the first one is used).  Tile 0
+  // is staged alone first, so its affinity runs while the other tiles arrive.
+  u32x4 tmp[NPRE - 1][G::CPT];
+  int tmp_rows[NPRE];
+  tmp_rows[0] = ntot > 0 ? (int)min((int64_t)NT, cl.end - cl.row) : 0;
+  cursor_next(cl);
 #pragma unroll
-    for (int s0 = 0; s0 < G::CPT; ++s0) tmp[0][s0] = tile0[s0];
-    tmp_rows[0] = ntot > 0 ? (int)min((int64_t)NT, cl.end - cl.row) : 0;
+  for (int p = 1; p < NPRE; ++p) {
+    load_tile(tmp[p - 1], tmp_rows[p], cl, p < ntot);
     cursor_next(cl);
-#pragma unroll
-    for (int p = 1; p < NPRE; ++p) {
-      load_tile(tmp[p], tmp_rows[p], cl, p < ntot);
-      cursor_next(cl);
-    }
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      load_tile(pre[(NPRE + p) % PF], pre_rows[(NPRE + p) % PF], cl, NPRE + p < ntot);
-      cursor_next(cl);
-    }
-#pragma unroll
-    for (int p = 0; p < NPRE; ++p) store_tile(tmp[p], tmp_rows[p], Xr + p * G::XR_ELEMS);
   }
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    load_tile(pre[(NPRE + p) % PF], pre_rows[(NPRE + p) % PF], cl, NPRE + p < ntot);
+    cursor_next(cl);
+  }
+  store_tile(tile0, tmp_rows[0], Xr);
   __syncthreads();
+  auto stage_rest = [&]() {
+#pragma unroll
+    for (int p = 1; p < NPRE; ++p) store_tile(tmp[p - 1], tmp_rows[p], Xr + p * G::XR_ELEMS);
+    __syncthreads();
+  };
 
   if constexpr (SB == 2) {
     f32x4 S0[RB][JB], S1[RB][JB];
     affinity(S0, Xr);
+    stage_rest();
     affinity(S1, Xr + G::XR_ELEMS);
     softmax_fast(S0, 0);
     __syncthreads();
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     f32x4 S[RB][JB];
     affinity(S, Xr);
     softmax_fast(S, 0);
-    __syncthreads();
+    stage_rest();  // its barrier also publishes the row sums of tile 0
 
     // ---- main loop, one score buffer.  Step t: stage tile t+2, factors and
     // weights of tile t (the scores become bf16 operands, freeing S),

@@ -121,6 +121,8 @@ SWEEP = [
     ("bf16", 128, 512, [65, 1500]),
     ("bf16", 64, 700, [1, 800]),
     ("bf16", 64, 1024, [5, 3000]),
+    ("bf16", 64, 50, [1, 300, 4099]),
+    ("bf16", 64, 400, [70, 2600]),
 ]
 
 
@@ -228,10 +230,12 @@ def _hard_bf16_workload(lengths, d, k, tau, seed, spike_rows=None):
     return W.Workload(name="hard-bf16", X=X, offsets=offs, P=P, W_Q=eye, W_K=eye.copy(), tau=tau, dtype="bf16")
 
 
-@pytest.mark.parametrize("k,wave_split", [(64, "rows"), (128, "mixed"), (256, "prototypes")])
-def test_exact_path_bf16(k, wave_split):
+@pytest.mark.parametrize("d,k,plan", [(64, 64, "rows"), (64, 128, "mixed"), (64, 256, "prototypes"),
+                                      (64, 700, "one score buffer, padded"), (64, 1024, "one score buffer"),
+                                      (128, 300, "one score buffer, d=128")])
+def test_exact_path_bf16(d, k, plan):
     """Every tile overflows the unshifted softmax and takes the exact path."""
-    wl = _hard_bf16_workload([3000, 77, 1], d=64, k=k, tau=4.0, seed=19 + k)
+    wl = _hard_bf16_workload([3000, 77, 1], d=d, k=k, tau=4.0, seed=19 + k)
     got = run_gpu(wl)
     assert np.isfinite(got).all()
     _assert_parity(wl, got)
