@@ -85,8 +85,9 @@ def cpu_baseline(wl, budget_s: float):
 
 def kernel_source_hash(dtype: str = "bf16", d: int = 128) -> str:
     """sha256 over the sources and build flags that decide the fused kernel a launch runs."""
-    files = [os.path.join(CSRC, f) for f in ("sa_fused.hpp", f"sa_fused_{dtype}_d{d}.hip", "sa_internal.h",
-                                             "sa_api.cpp")]
+    names = ["sa_fused.hpp", "sa_stream.hpp", f"sa_fused_{dtype}_d{d}.hip", f"sa_stream_d{d}.hip", "sa_kernels.hip",
+             "sa_internal.h", "sa_api.cpp"]
+    files = [os.path.join(CSRC, f) for f in names if os.path.exists(os.path.join(CSRC, f))]
     files.append(os.path.join(ROOT, "sketch_attention_amd", "build.py"))
     h = hashlib.sha256()
     for f in files:

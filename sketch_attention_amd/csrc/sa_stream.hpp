@@ -14,8 +14,7 @@
 // wave keeps two affinity tiles in flight:
 //
 //   iteration t  (one barrier at its end)
-//     stage tile t+2 from registers into the LDS ring, issue the HBM loads
-//       of tile t+2+PF
+//     issue the LDS DMA of tile t+NS-1 into the slot tile t-1 left
 //     S(t+1) = X(t+1) . M^T          matrix cores (M held in registers)
 //     factors of tile t               row sums of all waves from LDS, 1/sum,
 //                                     spread to the lanes by DPP broadcasts
@@ -28,8 +27,15 @@
 // previous one and the aggregation product overlaps the exponentials of the
 // next one.
 //
-// X is staged once, row-major, in a ring of three LDS tiles (tile t is read
-// by the aggregation while t+1 is read by the affinity and t+2 is written).
+// X goes from HBM straight into a ring of NS LDS tiles by LDS DMA
+// (global_load_lds_dwordx4: 64 lanes x 16 bytes land at consecutive LDS
+// addresses), issued NS - 1 tiles ahead and awaited with explicit vmcnt waits
+// before the barrier that publishes a tile, so no register or LDS store
+// instruction touches X on its way in.  Rows are stored unpadded with their
+// 16-byte chunks XOR-swizzled (chunk c of row r at c ^ sw(r)); each DMA lane
+// reads the global chunk that belongs at its LDS position.  The swizzle keeps
+// both read patterns free of bank conflicts: the affinity's 16-byte fragment
+// reads (16 rows, one chunk) and the aggregation's transposing reads.
 // The aggregation needs X with the row index along each lane's reduction
 // slots; gfx950's transposing LDS read (ds_read_b64_tr_b16) delivers exactly
 // that from the row-major tile: within a 16-lane group, output lane o gets
@@ -37,11 +43,12 @@
 // s of group g therefore reads row 4g + s / 4, columns 4 (s % 4) .. +3 of a
 // 16-column block, and receives one column of four consecutive rows.
 //
-// Rows past the end of a piece are staged as zeros: their affinity is 0,
-// their weights are finite and they add nothing to the sketch.  The softmax
-// takes 2^s' without a shift; when the total of a row leaves [2^-100, 2^100]
-// the wave holding it recomputes its rows with the max-shifted softmax on
-// its own (an online max/sum pass over all prototypes, M read from global
+// Rows past the end of a piece are loaded as copies of its last row (loads
+// never leave the piece) and get factor 0, so they add nothing to the sketch.
+// The softmax takes 2^s' without a shift; when the total of a row leaves
+// [2^-100, 2^100] the wave holding it recomputes its rows with the
+// max-shifted softmax on its own (an online max/sum pass over all
+// prototypes, M read from global
 // memory), so no other wave waits for it.
 #pragma once
 
@@ -54,11 +61,6 @@ namespace sa {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Four consecutive rows of one column, see the header comment.
-__device__ __forceinline__ u32x2 lds_read_tr16(const bf16* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
 
 // Integer sum over the 16 lanes of a DPP row (every lane gets the total).
 __device__ __forceinline__ int row16_sum_i(int x) {
@@ -76,9 +78,50 @@ __device__ __forceinline__ float row_bcast(float x) {
                                                                 false));
 }
 
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// LDS reads at 32-bit LDS byte addresses (constant offsets fold into the
+// instructions' offset fields); lds_tr16 returns four consecutive rows of one
+// column, see the header comment.
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t byte) { return *(const lds_bf16x8*)(size_t)byte; }
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t byte) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(size_t)byte);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// LDS DMA of one 1 KB block: lane i reads 16 bytes at sbase + voff and they
+// land at LDS byte lds_byte + 16 i.  In assembly so that the compiler does
+// not track it (it would wait for every outstanding DMA before any LDS read
+// it cannot prove disjoint); the kernel orders it with wait_vm before the
+// barrier that publishes the tile.  M0 is written one instruction ahead of
+// its use by the DMA, as the hazard rules require.  No output registers.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_byte)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt and
+// lgkmcnt left at their maxima).  Vector-memory loads complete in order, so
+// this waits for every load but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Chunk swizzle of LDS row r (16-byte chunks, D / 8 per row).  d = 128: one
+// row per 256 bytes of banks, sw = 2 (r % 8) + (r / 8) % 2; d = 64: two rows,
+// sw = 2 ((r / 2) % 4) + (r / 8) % 2.  Depends on r % 16 only.
+template <int D>
+__device__ __forceinline__ constexpr int chunk_sw(int r) {
+  return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
 struct StreamGeom {
-  static_assert(KW % 16 == 0 && D % 32 == 0 && (PF == 1 || PF == 2) && (RB == 2 || RB == 4) && (SB == 1 || SB == 2),
+  static_assert(KW % 16 == 0 && (D == 64 || D == 128) && PF >= 1 && PF <= 3 && (RB == 2 || RB == 4) &&
+                    (SB == 1 || SB == 2),
                 "tile shape");
   static constexpr int NW = WJ * WI;
   static constexpr int THREADS = 64 * NW;
@@ -88,13 +131,16 @@ struct StreamGeom {
   static constexpr int CB = D / 16;
   static constexpr int CS = D / 32;
   static constexpr int KPAD = KW * WJ;
-  static constexpr int XRS = D + 16;           // row stride (elements): +32 bytes, conflict-free fragment reads
-  static constexpr int XR_ELEMS = NT * XRS;
-  static constexpr int NXR = SB == 2 ? 4 : 3;   // X tiles in the LDS ring
   static constexpr int CH = D / 8;             // 16-byte chunks per row
-  static constexpr int NCH = NT * CH;
-  static constexpr int CPT = (NCH + THREADS - 1) / THREADS;  // chunks per thread
-  static constexpr int XR_BYTES = NXR * XR_ELEMS * 2;
+  // ring of X tiles: the tiles read by a step, the ones the affinity runs
+  // ahead of the aggregation, and PF - 1 more in flight
+  static constexpr int NS = (SB == 2 ? 4 : 3) + PF - 1;
+  static constexpr int SLOT_BYTES = NT * D * 2;
+  static constexpr int XR_BYTES = NS * SLOT_BYTES;
+  static constexpr int NI = SLOT_BYTES / 1024;  // DMA blocks per tile
+  static_assert(SLOT_BYTES % 1024 == 0, "tile of whole DMA blocks");
+  static constexpr int NIW = (NI + NW - 1) / NW;  // DMA blocks per wave and tile (some waves may have one fewer)
+  static constexpr int RPI = 1024 / (2 * D);      // rows per DMA block
   static constexpr int XL_BYTES = 2 * NT * WJ * 4;  // row sums of every wave, two parities
   static constexpr int STAGE_BYTES = WI > 1 ? WJ * CB * 64 * 16 : 0;
   static constexpr int OFF_XL = XR_BYTES;
@@ -113,10 +159,10 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   using G = StreamGeom<D, KW, WJ, WI, RB, PF, SB>;
   using MF = Mfma<bf16>;
   constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, RW = G::RW, THREADS = G::THREADS;
-  constexpr int XRS = G::XRS;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
-  bf16* const Xr = reinterpret_cast<bf16*>(lds);
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[G::LDS_BYTES];
+  const uint32_t xr0 = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;  // LDS byte address
+  auto slot_of = [&](int q) { return xr0 + (uint32_t)(q * G::SLOT_BYTES); };
   float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);  // [2][NT][WJ]
 
   const int tid = threadIdx.x;
@@ -182,52 +228,53 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) moff[cs] = 8 * ((4 * cs + g) ^ ((l16 / MP) % G::CH));
 
-  // ---- staging: thread chunk s covers row (tid + s*THREADS) / CH, 16 bytes.
-  // A tile's loads read rows clamped to its piece (always in bounds, offsets
-  // 32-bit from the tile's first row); rows past the piece are replaced by
-  // zeros when the tile is staged, which only a piece's last tile needs.
-  u32x4 pre[PF][G::CPT];
-  int pre_rows[PF];  // valid rows of the tile held in each register slot (0 past the list)
-  auto load_tile = [&](u32x4 (&dst)[G::CPT], int& dst_rows, const Cursor& c, bool valid) {
-    const int64_t left = c.end - c.row;
-    dst_rows = !valid ? 0 : (left < NT ? (int)left : NT);
-    const int last = (int)(c.end - 1 - c.row);  // -1 past the list: c.row + last = c.end - 1 >= 0
-    const u32x4* tile = reinterpret_cast<const u32x4*>(X + c.row * D);
+  // ---- LDS DMA of one tile into ring slot q: block j = wave + s NW of the
+  // tile (RPI rows) lands at slot + 1024 j; lane i of a block holds row
+  // j RPI + i / CH, LDS chunk i % CH, i.e. global chunk (i % CH) ^ sw(row).
+  // Rows past the piece read its last row (offsets stay non-negative: past
+  // the list every lane reads row c.end - 1), so every load is in bounds.
+  int dma_row[G::NIW], dma_col[G::NIW];
 #pragma unroll
-    for (int s = 0; s < G::CPT; ++s) {
-      const int ci = tid + s * THREADS;
-      const int r = ci / G::CH, ch = ci % G::CH;
-      if (G::NCH % THREADS == 0 || ci < G::NCH) {
-        const int rr = r < last ? r : last;
-        dst[s] = __builtin_nontemporal_load(tile + (rr * G::CH + ch));
+  for (int s = 0; s < G::NIW; ++s) {
+    const int j = wave + s * G::NW;
+    dma_row[s] = j * G::RPI + lane / G::CH;
+    dma_col[s] = 8 * ((lane % G::CH) ^ chunk_sw<D>(dma_row[s]));
+  }
+  auto issue_tile = [&](const auto& c, int q) {
+    const int64_t last = c.end - 1 - c.row;  // -1 past the list
+    const int64_t b0 = last < 0 ? c.end - 1 : c.row;
+    const int lim = last < 0 ? 0 : (int)(last < G::NT ? last : G::NT - 1);
+    const bf16* const base = X + b0 * D;
+    const uint32_t slot = slot_of(q);
+#pragma unroll
+    for (int s = 0; s < G::NIW; ++s) {
+      const int j = wave + s * G::NW;
+      if (G::NI % G::NW == 0 || j < G::NI) {
+        const int rr = dma_row[s] < lim ? dma_row[s] : lim;
+        dma16(base, (uint32_t)(rr * D + dma_col[s]) * 2u, slot + 1024u * (uint32_t)j);
       }
     }
   };
-  auto store_tile = [&](const u32x4 (&src)[G::CPT], int rows_valid, bf16* xr) {
-    if (rows_valid == NT) {  // uniform: every tile but a piece's last
-#pragma unroll
-      for (int s = 0; s < G::CPT; ++s) {
-        const int ci = tid + s * THREADS;
-        const int r = ci / G::CH, ch = ci % G::CH;
-        if (G::NCH % THREADS == 0 || ci < G::NCH) *reinterpret_cast<u32x4*>(xr + r * XRS + 8 * ch) = src[s];
-      }
+  // wait until every DMA block of this wave is done but those of the n most
+  // recently issued tiles
+  auto wait_tiles = [&](auto n_) {
+    constexpr int n = decltype(n_)::value;
+    if constexpr (G::NI % G::NW == 0) {
+      wait_vm<(G::NI / G::NW) * n>();
     } else {
-#pragma unroll
-      for (int s = 0; s < G::CPT; ++s) {
-        const int ci = tid + s * THREADS;
-        const int r = ci / G::CH, ch = ci % G::CH;
-        if (G::NCH % THREADS == 0 || ci < G::NCH)
-          *reinterpret_cast<u32x4*>(xr + r * XRS + 8 * ch) = r < rows_valid ? src[s] : u32x4{0u, 0u, 0u, 0u};
-      }
+      if (wave < G::NI % G::NW) wait_vm<(G::NI / G::NW + 1) * n>();
+      else wait_vm<(G::NI / G::NW) * n>();
     }
   };
 
-  // tile 0 starts at r_begin whatever the users: its loads go out before the
-  // tile list is known (rows clamped to the group's range, masked at staging)
-  u32x4 tile0[G::CPT];
+  // tile 0 starts at r_begin whatever the users: its DMA goes out before the
+  // tile list is known (rows clamped to the group's range; rows of the next
+  // user get factor 0)
   {
-    int unused_rows;
-    load_tile(tile0, unused_rows, Cursor{r_begin, r_end, 0}, true);
+    struct {
+      int64_t row, end;
+    } c0{r_begin, r_end};
+    issue_tile(c0, 0);
   }
 
   // ---- the group's tile list: pieces (user segments) of [r_begin, r_end),
@@ -269,57 +316,61 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       }
     }
   };
-  auto affinity = [&](f32x4 (&s)[RB][JB], const bf16* xr) {
+  // one reduction step (32 columns of d) of the affinity; cs = 0 starts the sums
+  // byte offset of chunk 4 cs + g of this lane's row l16 (the swizzle of rows
+  // 16 ib + l16 is that of l16)
+  uint32_t aoff[CS];
 #pragma unroll
-    for (int ib = 0; ib < RB; ++ib)
+  for (int cs = 0; cs < CS; ++cs) aoff[cs] = (uint32_t)(2 * (l16 * D + 8 * ((4 * cs + g) ^ chunk_sw<D>(l16))));
+  auto xfrag = [&](uint32_t xs, int ib, int cs) { return lds_b128(xs + aoff[cs] + (uint32_t)(2 * (rw + 16 * ib) * D)); };
+  auto affinity_cs = [&](f32x4 (&s)[RB][JB], uint32_t xs, int cs) {
+    bf16x8 xa[RB];
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb) s[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ib = 0; ib < RB; ++ib) xa[ib] = xfrag(xs, ib, cs);
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      bf16x8 xa[RB];
+    for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int ib = 0; ib < RB; ++ib) xa[ib] = frag_c<D>(xr + (rw + 16 * ib + l16) * XRS, cs, g);
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int ib = 0; ib < RB; ++ib) {
-          bf16x8 mf;
-          if constexpr (SB == 2) {
-            mf = mreg[jb][cs];
-          } else {
-            mf = *reinterpret_cast<const bf16x8*>(Ms + (jbase + 16 * jb + l16) * D + moff[cs]);
-          }
-          s[ib][jb] = MF::run(xa[ib], mf, s[ib][jb]);
+      for (int ib = 0; ib < RB; ++ib) {
+        bf16x8 mf;
+        if constexpr (SB == 2) {
+          mf = mreg[jb][cs];
+        } else {
+          mf = *reinterpret_cast<const bf16x8*>(Ms + (jbase + 16 * jb + l16) * D + moff[cs]);
         }
-    }
+        s[ib][jb] = MF::run(xa[ib], mf, cs == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[ib][jb]);
+      }
+  };
+  auto affinity = [&](f32x4 (&s)[RB][JB], uint32_t xs) {
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) affinity_cs(s, xs, cs);
     pad_protos(s, jbase);
   };
 
   // ---- e = 2^s' in place; this wave's row sums to xl[par].  After the
   // transposing butterfly the four lanes of a quad hold the same total and
   // store it to the same word (no branch).
-  auto softmax_fast = [&](f32x4 (&s)[RB][JB], int par) {
-    float* const xlp = xl + par * (NT * WJ);
+  auto softmax_ib = [&](f32x4 (&s)[RB][JB], int par, int ib) {
+    float p[4];
 #pragma unroll
-    for (int ib = 0; ib < RB; ++ib) {
-      float p[4];
+    for (int r = 0; r < 4; ++r) {
+      // the first term starts the sum (0 + e is not foldable for -0)
+      float acc = fast_exp2(s[ib][0][r]);
+      s[ib][0][r] = acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // the first term starts the sum (0 + e is not foldable for -0)
-        float acc = fast_exp2(s[ib][0][r]);
-        s[ib][0][r] = acc;
-#pragma unroll
-        for (int jb = 1; jb < JB; ++jb) {
-          const float e = fast_exp2(s[ib][jb][r]);
-          s[ib][jb][r] = e;
-          acc += e;
-        }
-        p[r] = acc;
+      for (int jb = 1; jb < JB; ++jb) {
+        const float e = fast_exp2(s[ib][jb][r]);
+        s[ib][jb][r] = e;
+        acc += e;
       }
-      const float z = rows4_sum_scatter(p, l16);
-      const int trow = rw + 16 * ib + 4 * g + ((l16 >> 3) << 1) + ((l16 >> 2) & 1);
-      xlp[trow * WJ + wj] = z;
+      p[r] = acc;
     }
+    const float z = rows4_sum_scatter(p, l16);
+    const int trow = rw + 16 * ib + 4 * g + ((l16 >> 3) << 1) + ((l16 >> 2) & 1);
+    xl[par * (NT * WJ) + trow * WJ + wj] = z;
+  };
+  auto softmax_fast = [&](f32x4 (&s)[RB][JB], int par) {
+#pragma unroll
+    for (int ib = 0; ib < RB; ++ib) softmax_ib(s, par, ib);
   };
 
   // ---- factors 1 / sum_w l_w.  Lane (g, l16) finishes row
@@ -328,6 +379,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // aggregation takes the factors of its rows by row broadcasts (fac_of).
   // `bad` is set when a row total left the range of the unshifted softmax.
   const int my_ib = (l16 >> 2) % RB, my_r = l16 & 3;
+  const int my_row = rw + 16 * my_ib + 4 * g + my_r;  // tile row whose factor this lane finishes
   auto combine_fast = [&](float& f, bool& bad, int par) {
     const float* p = xl + par * (NT * WJ) + (rw + 16 * my_ib + 4 * g + my_r) * WJ;
     float l;
@@ -369,12 +421,12 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // ---- exact path of one wave (rare): for each of its row blocks, an online
   // max / shifted-sum pass over all prototypes (M fragments from global
   // memory), then its own prototypes' weights 2^(s' - m) with factor 1 / l.
-  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, const bf16* xr) {
+  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, uint32_t xs) {
 #pragma unroll  // s[ib] must be indexed by constants to stay in registers
     for (int ib = 0; ib < RB; ++ib) {
       bf16x8 xa[CS];
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs) xa[cs] = frag_c<D>(xr + (rw + 16 * ib + l16) * XRS, cs, g);
+      for (int cs = 0; cs < CS; ++cs) xa[cs] = xfrag(xs, ib, cs);
       float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       float l[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
@@ -413,33 +465,40 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 
   // ---- aggregation: acc[jb][cb][r] += sum_i a[jbase+16jb+4g+r][i] X[i][16cb+l16].
   // Reduction slot (g, e) of k-step h is tile row rw + 32 h + 16 (e / 4) +
-  // 4 g + e % 4, the rows the affinity layout left in that lane.
-  const int tr_off = (rw + 4 * g + (l16 >> 2)) * XRS + 4 * (l16 & 3);
+  // 4 g + e % 4, the rows the affinity layout left in that lane.  This lane
+  // reads row 4 g + l16 / 4 (+ rw + 32 h + 16 e/4), columns 16 cb + 4 (l16 % 4):
+  // chunk 2 cb + (l16 / 2) % 2 at (2 cb + q) ^ sw, i.e. element offset
+  // 16 cb ^ (8 (q ^ sw) + 4 (l16 % 2)) in the row, one XOR per column block.
+  const uint32_t trb = (uint32_t)(2 * ((4 * g + (l16 >> 2)) * D + 8 * (((l16 >> 1) & 1) ^ chunk_sw<D>(4 * g + (l16 >> 2))) +
+                                       4 * (l16 & 1)));
+  auto weights_h = [&](bf16x8 (&a)[RB / 2][JB], const f32x4 (&s)[RB][JB], float f, int h) {
+    float fac[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fac[e] = fac_of(f, 2 * h + (e >> 2), e & 3);
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[h][jb][e] = (bf16)(s[2 * h + (e >> 2)][jb][e & 3] * fac[e]);
+  };
   auto weights = [&](bf16x8 (&a)[RB / 2][JB], const f32x4 (&s)[RB][JB], float f) {
 #pragma unroll
-    for (int h = 0; h < RB / 2; ++h) {
-      float fac[8];
+    for (int h = 0; h < RB / 2; ++h) weights_h(a, s, f, h);
+  };
+  auto aggregate_h = [&](f32x4 (&acc)[JB][CB], const bf16x8 (&a)[RB / 2][JB], uint32_t xs, int h) {
+    const uint32_t xp = xs + (uint32_t)(2 * rw * D) + trb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) fac[e] = fac_of(f, 2 * h + (e >> 2), e & 3);
+    for (int cb = 0; cb < CB; ++cb) {
+      const uint32_t xc = xp ^ (uint32_t)(32 * cb);  // the slot and row parts are multiples of 2 D bytes
+      const u32x2 lo = lds_tr16(xc + (uint32_t)(2 * 32 * h * D));
+      const u32x2 hi = lds_tr16(xc + (uint32_t)(2 * (32 * h + 16) * D));
+      const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[h][jb][e] = (bf16)(s[2 * h + (e >> 2)][jb][e & 3] * fac[e]);
+      for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[h][jb], xb, acc[jb][cb]);
     }
   };
-  auto aggregate = [&](f32x4 (&acc)[JB][CB], const bf16x8 (&a)[RB / 2][JB], const bf16* xr) {
+  auto aggregate = [&](f32x4 (&acc)[JB][CB], const bf16x8 (&a)[RB / 2][JB], uint32_t xs) {
 #pragma unroll
-    for (int h = 0; h < RB / 2; ++h) {
-      const bf16* const xp = xr + tr_off + 32 * h * XRS;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const u32x2 lo = lds_read_tr16(xp + 16 * cb);
-        const u32x2 hi = lds_read_tr16(xp + 16 * XRS + 16 * cb);
-        const bf16x8 xb = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[h][jb], xb, acc[jb][cb]);
-      }
-    }
+    for (int h = 0; h < RB / 2; ++h) aggregate_h(acc, a, xs, h);
   };
 
   // ---- flush one (group, user) piece: waves that split the rows add their
@@ -488,124 +547,114 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 
   Cursor cc = cursor_begin();  // tile t (aggregation, flush)
   Cursor cl = cc;              // next tile to load from HBM
-  constexpr int NPRE = SB == 2 ? 3 : 2;  // tiles staged by the prologue
+  constexpr int NS = G::NS;
 
-  // ---- prologue: tiles 0 .. NPRE-1 into the ring, the next PF into
-  // registers (every HBM load issued before the first one is used).  Tile 0
-  // is staged alone first, so its affinity runs while the other tiles arrive.
-  u32x4 tmp[NPRE - 1][G::CPT];
-  int tmp_rows[NPRE];
-  tmp_rows[0] = ntot > 0 ? (int)min((int64_t)NT, cl.end - cl.row) : 0;
+  // ---- prologue: DMA of tiles 1 .. NS-2 (tile 0 is on its way); the ring
+  // position of tile t is t % NS
   cursor_next(cl);
 #pragma unroll
-  for (int p = 1; p < NPRE; ++p) {
-    load_tile(tmp[p - 1], tmp_rows[p], cl, p < ntot);
+  for (int p = 1; p < NS - 1; ++p) {
+    issue_tile(cl, p);
     cursor_next(cl);
   }
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    load_tile(pre[(NPRE + p) % PF], pre_rows[(NPRE + p) % PF], cl, NPRE + p < ntot);
-    cursor_next(cl);
-  }
-  store_tile(tile0, tmp_rows[0], Xr);
-  __syncthreads();
-  auto stage_rest = [&]() {
-#pragma unroll
-    for (int p = 1; p < NPRE; ++p) store_tile(tmp[p - 1], tmp_rows[p], Xr + p * G::XR_ELEMS);
-    __syncthreads();
-  };
+  // factor of this lane's row of the tile at cursor c (0 for rows past its piece)
+  auto row_ok = [&](const Cursor& c) { return (int64_t)my_row < c.end - c.row; };
 
   if constexpr (SB == 2) {
     f32x4 S0[RB][JB], S1[RB][JB];
-    affinity(S0, Xr);
-    stage_rest();
-    affinity(S1, Xr + G::XR_ELEMS);
+    wait_tiles(std::integral_constant<int, NS - 2>{});
+    __syncthreads();
+    affinity(S0, slot_of(0));
+    wait_tiles(std::integral_constant<int, NS - 3>{});
+    __syncthreads();
+    affinity(S1, slot_of(1));
     softmax_fast(S0, 0);
+    wait_tiles(std::integral_constant<int, NS - 4>{});
     __syncthreads();
 
-    // ---- main loop.  Step t: stage tile t+3, factors and weights of tile
-    // t, aggregation of tile t, affinity of tile t+2 (into the registers
+    // ---- main loop.  Step t: DMA of tile t+NS-1, factors and weights of
+    // tile t, aggregation of tile t, affinity of tile t+2 (into the registers
     // tile t's scores just left), exponentials of tile t+1 (its affinity came
-    // from the step before), one barrier.  The exponentials depend on no
-    // product of the same step, so matrix-core and VALU work of a step
-    // overlap freely.  Unrolled by two so the two score tiles swap roles
-    // without copies.  Ring slot of tile t: t % 4.  Past the end of the list
-    // the staged tiles are zeros and the scores computed for them are unused,
-    // so the hot path has no data-dependent branch but the rare exact one.
+    // from the step before), wait for tile t+3, one barrier.  The
+    // exponentials depend on no product of the same step, so matrix-core and
+    // VALU work of a step overlap freely.  Unrolled by two so the two score
+    // tiles swap roles without copies.  Past the end of the list the tiles
+    // are copies of a row and the scores computed for them are unused, so
+    // the hot path has no data-dependent branch but the rare exact one.
     // `full` (compile-time): tiles t+1 and t+2 exist, so the step has no
     // branch but the exact one; the last two steps of a list skip the
     // affinity and exponentials of tiles past its end.
-    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], u32x4 (&pslot)[G::CPT], int& prow,
-                    auto full) {
-      bf16* const xr_t = Xr + (t & 3) * G::XR_ELEMS;
-      bf16* const xr_t2 = Xr + ((t + 2) & 3) * G::XR_ELEMS;
-      bf16* const xr_t3 = Xr + ((t + 3) & 3) * G::XR_ELEMS;
-      store_tile(pslot, prow, xr_t3);
-      load_tile(pslot, prow, cl, t + 3 + PF < ntot);
+    int q0 = 0;  // ring slot of tile t
+    auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], auto full) {
+      const int q2 = q0 + 2 < NS ? q0 + 2 : q0 + 2 - NS;
+      const int qn = q0 == 0 ? NS - 1 : q0 - 1;
+      issue_tile(cl, qn);
       float f;
       bool bad;
       combine_fast(f, bad, t & 1);
-      if (bad) exact_wave(Sa, f, xr_t);
+      if (bad) exact_wave(Sa, f, slot_of(q0));
+      f = row_ok(cc) ? f : 0.f;
       bf16x8 a[RB / 2][JB];
       weights(a, Sa, f);
-      aggregate(acc, a, xr_t);
-      if (decltype(full)::value || t + 2 < ntot) affinity(Sa, xr_t2);
+      aggregate(acc, a, slot_of(q0));
+      if (decltype(full)::value || t + 2 < ntot) affinity(Sa, slot_of(q2));
       if (decltype(full)::value || t + 1 < ntot) softmax_fast(Sb, (t + 1) & 1);
       if (cc.row + NT >= cc.end) flush(acc, cc.u);
       cursor_next(cc);
       cursor_next(cl);
+      q0 = q0 + 1 < NS ? q0 + 1 : 0;
+      wait_tiles(std::integral_constant<int, NS - 4>{});  // tile t+3
       __syncthreads();
     };
     using Full = std::integral_constant<bool, true>;
     using Tail = std::integral_constant<bool, false>;
     int t = 0;
     for (; t + 3 < ntot; t += 2) {
-      step(t, S0, S1, pre[3 % PF], pre_rows[3 % PF], Full{});
-      step(t + 1, S1, S0, pre[0], pre_rows[0], Full{});
+      step(t, S0, S1, Full{});
+      step(t + 1, S1, S0, Full{});
     }
     // 0..3 steps remain; S0 holds tile t's scores
-    if (t < ntot) step(t, S0, S1, pre[3 % PF], pre_rows[3 % PF], Tail{});
-    if (t + 1 < ntot) step(t + 1, S1, S0, pre[0], pre_rows[0], Tail{});
-    if (t + 2 < ntot) step(t + 2, S0, S1, pre[3 % PF], pre_rows[3 % PF], Tail{});
+    if (t < ntot) step(t, S0, S1, Tail{});
+    if (t + 1 < ntot) step(t + 1, S1, S0, Tail{});
+    if (t + 2 < ntot) step(t + 2, S0, S1, Tail{});
   } else {
     f32x4 S[RB][JB];
-    affinity(S, Xr);
+    wait_tiles(std::integral_constant<int, NS - 2>{});
+    __syncthreads();  // also publishes the folded matrix
+    affinity(S, slot_of(0));
     softmax_fast(S, 0);
-    stage_rest();  // its barrier also publishes the row sums of tile 0
+    wait_tiles(std::integral_constant<int, NS - 3>{});
+    __syncthreads();  // tile 1; row sums of tile 0
 
-    // ---- main loop, one score buffer.  Step t: stage tile t+2, factors and
-    // weights of tile t (the scores become bf16 operands, freeing S),
+    // ---- main loop, one score buffer.  Step t: DMA of tile t+NS-1, factors
+    // and weights of tile t (the scores become bf16 operands, freeing S),
     // aggregation of tile t, affinity and exponentials of tile t+1 into S,
-    // one barrier.  Ring slot of tile t: t % 3.
+    // wait for tile t+2, one barrier.
     int q0 = 0;
-    auto step = [&](int t, u32x4 (&pslot)[G::CPT], int& prow) {
-      const int q1 = q0 == 2 ? 0 : q0 + 1;
-      const int q2 = q1 == 2 ? 0 : q1 + 1;
-      bf16* const xr_t = Xr + q0 * G::XR_ELEMS;
-      bf16* const xr_t1 = Xr + q1 * G::XR_ELEMS;
-      bf16* const xr_t2 = Xr + q2 * G::XR_ELEMS;
-      store_tile(pslot, prow, xr_t2);
-      load_tile(pslot, prow, cl, t + 2 + PF < ntot);
+    auto step = [&](int t) {
+      const int q1 = q0 + 1 < NS ? q0 + 1 : 0;
+      const int qn = q0 == 0 ? NS - 1 : q0 - 1;
+      issue_tile(cl, qn);
       float f;
       bool bad;
       combine_fast(f, bad, t & 1);
-      if (bad) exact_wave(S, f, xr_t);
+      if (bad) exact_wave(S, f, slot_of(q0));
+      f = row_ok(cc) ? f : 0.f;
       bf16x8 a[RB / 2][JB];
       weights(a, S, f);
-      aggregate(acc, a, xr_t);
-      affinity(S, xr_t1);
+      aggregate(acc, a, slot_of(q0));
+      affinity(S, slot_of(q1));
       softmax_fast(S, (t + 1) & 1);
       if (cc.row + NT >= cc.end) flush(acc, cc.u);
       cursor_next(cc);
       cursor_next(cl);
       q0 = q1;
+      wait_tiles(std::integral_constant<int, NS - 3>{});  // tile t+2
       __syncthreads();
     };
-    for (int t = 0; t < ntot; t += 2) {
-      step(t, pre[2 % PF], pre_rows[2 % PF]);
-      if (t + 1 < ntot) step(t + 1, pre[3 % PF], pre_rows[3 % PF]);
-    }
+    for (int t = 0; t < ntot; ++t) step(t);
   }
+  wait_vm<0>();  // no DMA outlives the work group
 }
 
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
