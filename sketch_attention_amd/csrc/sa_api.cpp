@@ -139,11 +139,18 @@ sa_status check_batch(const int64_t* offsets, int32_t num_users) {
 }
 
 // Work groups of the fused grid for a launch of `rows` rows: at most one full
-// wave of resident groups, and no more groups than tiles.
+// wave of resident groups and no more groups than tiles.  Beyond one group
+// per compute unit, extra resident groups are used only when each still gets
+// at least kMinTilesPerGroup tiles: a short group is mostly prologue and its
+// partial sketch costs as much to write and reduce as a long one's.
+constexpr int64_t kMinTilesPerGroup = 8;
 int groups_for(const sa_handle_s* h, int64_t rows) {
   const int64_t cap = (int64_t)h->cu_count * h->groups_per_cu;
   const int64_t tiles = (rows + h->plan.tile_rows - 1) / h->plan.tile_rows;
-  int64_t g = tiles < cap ? tiles : cap;
+  int64_t g = (tiles + kMinTilesPerGroup - 1) / kMinTilesPerGroup;
+  if (g < h->cu_count) g = h->cu_count;
+  if (g > cap) g = cap;
+  if (g > tiles) g = tiles;
   return g < 1 ? 1 : (int)g;
 }
 

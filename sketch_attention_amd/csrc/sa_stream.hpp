@@ -110,12 +110,18 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Chunk swizzle of LDS row r (16-byte chunks, D / 8 per row).  d = 128: one
-// row per 256 bytes of banks, sw = 2 (r % 8) + (r / 8) % 2; d = 64: two rows,
-// sw = 2 ((r / 2) % 4) + (r / 8) % 2.  Depends on r % 16 only.
+// Chunk swizzle of LDS row r (16-byte chunks, D / 8 per row), a function of
+// r % 16.  Measured on gfx950: 16-byte reads are served 32 lanes at a time
+// over 128 four-byte banks, the 8-byte transposing reads 32 lanes at a time
+// over 64 banks.  The affinity's reads (32 lanes: rows l16 of one parity
+// class per 512 bytes, chunks c, c + 1) and the transposing reads (32 lanes:
+// rows 0..7 or 8..15, chunks 2 cb, 2 cb + 1) are then conflict-free when
+// sw / 2 takes distinct values over each of those row sets:
+//   d = 128: sw / 2 = 4 ((r ^ r / 8) % 2) + (r / 2) % 4
+//   d = 64:  sw / 2 = 2 ((r / 4) % 2) + ((r / 2 ^ r / 8) % 2)
 template <int D>
 __device__ __forceinline__ constexpr int chunk_sw(int r) {
-  return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  return D == 128 ? 8 * ((r ^ (r >> 3)) & 1) + 2 * ((r >> 1) & 3) : 4 * ((r >> 2) & 1) + 2 * (((r >> 1) ^ (r >> 3)) & 1);
 }
 
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
@@ -141,8 +147,19 @@ struct StreamGeom {
   static_assert(SLOT_BYTES % 1024 == 0, "tile of whole DMA blocks");
   static constexpr int NIW = (NI + NW - 1) / NW;  // DMA blocks per wave and tile (some waves may have one fewer)
   static constexpr int RPI = 1024 / (2 * D);      // rows per DMA block
-  static constexpr int XL_BYTES = 2 * NT * WJ * 4;  // row sums of every wave, two parities
-  static constexpr int STAGE_BYTES = WI > 1 ? WJ * CB * 64 * 16 : 0;
+  // row sums of every wave, two parities.  WJ % 4 == 0: [2][WJ / 4][NTP][4]
+  // floats, row R at padded position R + 8 (R / 32), so the 16-byte reads of
+  // the combine (32 lanes, rows 16 ib + 4 g + r) hit distinct banks; else
+  // [2][NT][WJ].
+  static constexpr int NTP = NT + 8 * ((NT + 31) / 32);
+  static constexpr int XL_BYTES = WJ % 4 == 0 ? 2 * (WJ / 4) * NTP * 16 : 2 * NT * WJ * 4;
+  // waves that split the rows add their accumulators through LDS when a
+  // piece ends: one prototype block of every wave at a time.  When that fits
+  // in a tile it uses the ring slot of the tile just aggregated (free until
+  // the next step's DMA), else a buffer of its own.
+  static constexpr int STAGE_NEED = WI > 1 ? WJ * CB * 64 * 16 : 0;
+  static constexpr bool STAGE_IN_RING = STAGE_NEED <= SLOT_BYTES;
+  static constexpr int STAGE_BYTES = STAGE_IN_RING ? 0 : STAGE_NEED;
   static constexpr int OFF_XL = XR_BYTES;
   static constexpr int OFF_STAGE = OFF_XL + XL_BYTES;
   // one score buffer: the folded matrix lives in LDS, rows of D bf16 with
@@ -163,7 +180,14 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   __shared__ __attribute__((aligned(1024))) unsigned char lds[G::LDS_BYTES];
   const uint32_t xr0 = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;  // LDS byte address
   auto slot_of = [&](int q) { return xr0 + (uint32_t)(q * G::SLOT_BYTES); };
-  float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);  // [2][NT][WJ]
+  float* const xl = reinterpret_cast<float*>(lds + G::OFF_XL);
+  // index of the row sum of tile row `row` from prototype wave w, parity par
+  auto xl_at = [&](int par, int row, int w) {
+    if constexpr (WJ % 4 == 0)
+      return ((par * (WJ / 4) + w / 4) * G::NTP + row + 8 * (row >> 5)) * 4 + (w & 3);
+    else
+      return (par * NT + row) * WJ + w;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -366,7 +390,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     }
     const float z = rows4_sum_scatter(p, l16);
     const int trow = rw + 16 * ib + 4 * g + ((l16 >> 3) << 1) + ((l16 >> 2) & 1);
-    xl[par * (NT * WJ) + trow * WJ + wj] = z;
+    xl[xl_at(par, trow, wj)] = z;
   };
   auto softmax_fast = [&](f32x4 (&s)[RB][JB], int par) {
 #pragma unroll
@@ -381,14 +405,14 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int my_ib = (l16 >> 2) % RB, my_r = l16 & 3;
   const int my_row = rw + 16 * my_ib + 4 * g + my_r;  // tile row whose factor this lane finishes
   auto combine_fast = [&](float& f, bool& bad, int par) {
-    const float* p = xl + par * (NT * WJ) + (rw + 16 * my_ib + 4 * g + my_r) * WJ;
     float l;
     if constexpr (WJ % 4 == 0) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(p);
+      f32x4 v = *reinterpret_cast<const f32x4*>(xl + xl_at(par, my_row, 0));
 #pragma unroll
-      for (int w = 4; w < WJ; w += 4) v += *reinterpret_cast<const f32x4*>(p + w);
+      for (int w = 4; w < WJ; w += 4) v += *reinterpret_cast<const f32x4*>(xl + xl_at(par, my_row, w));
       l = (v[0] + v[1]) + (v[2] + v[3]);
     } else {
+      const float* p = xl + xl_at(par, my_row, 0);
       l = p[0];
 #pragma unroll
       for (int w = 1; w < WJ; ++w) l += p[w];
@@ -504,9 +528,9 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // ---- flush one (group, user) piece: waves that split the rows add their
   // accumulators through LDS in a fixed order, then one wave per prototype
   // slice writes the slot in the lane layout [wj][jb][cb][lane][4].
-  auto flush = [&](f32x4 (&acc)[JB][CB], int u) {
+  auto flush = [&](f32x4 (&acc)[JB][CB], int u, int q) {
     if constexpr (WI > 1) {
-      float* stage = reinterpret_cast<float*>(lds + G::OFF_STAGE);
+      float* stage = reinterpret_cast<float*>(lds + (G::STAGE_IN_RING ? q * G::SLOT_BYTES : G::OFF_STAGE));
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
         for (int st = WI - 1; st >= 1; --st) {
@@ -599,7 +623,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       aggregate(acc, a, slot_of(q0));
       if (decltype(full)::value || t + 2 < ntot) affinity(Sa, slot_of(q2));
       if (decltype(full)::value || t + 1 < ntot) softmax_fast(Sb, (t + 1) & 1);
-      if (cc.row + NT >= cc.end) flush(acc, cc.u);
+      if (cc.row + NT >= cc.end) flush(acc, cc.u, q0);  // its first barrier ends every read of slot q0
       cursor_next(cc);
       cursor_next(cl);
       q0 = q0 + 1 < NS ? q0 + 1 : 0;
@@ -645,7 +669,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       aggregate(acc, a, slot_of(q0));
       affinity(S, slot_of(q1));
       softmax_fast(S, (t + 1) & 1);
-      if (cc.row + NT >= cc.end) flush(acc, cc.u);
+      if (cc.row + NT >= cc.end) flush(acc, cc.u, q0);  // its first barrier ends every read of slot q0
       cursor_next(cc);
       cursor_next(cl);
       q0 = q1;
