@@ -147,6 +147,76 @@ sa_status sa_read_kernel_timing(sa_handle h, double* fused_ms, double* reduce_ms
 sa_status sa_describe_plan(sa_handle h, int64_t total_rows, int32_t* groups, int32_t* waves_k,
                            int32_t* waves_rows, int32_t* tile_rows, int32_t* k_padded);
 
+/*
+ * Stacked refinement (SequenceO1 close-reading page, section 2.2 "Stacked
+ * Refinement and action-side fusion").  After one assignment and aggregation
+ * the k x d state carries the user's information, so it queries the same raw
+ * history again.  Starting from X~(0) = P, layer l = 1..L computes, per user,
+ *
+ *     Y      = A(l) X     with A(l) the section 2.1 assignment for the query
+ *                         X~(l-1): S = tau (X~(l-1) W_Q(l))(X W_K(l))^T,
+ *                         softmax over the prototype axis
+ *     Xbar   = LN1(X~(l-1) + Y)
+ *     X~(l)  = LN2(Xbar + FFN(Xbar)),   FFN(z) = (silu(z W_gate) * (z W_up)) W_down
+ *
+ * LN normalises each row over its d entries with the population variance and
+ * epsilon 1e-5, then applies a per-column gain and bias; silu(x) = x / (1 +
+ * e^-x).  The page lost the equations of this update: the post-norm residual
+ * form, the SwiGLU FFN (the gated form the page gives for the action fusion)
+ * and epsilon are the readings this library takes.  Every layer reads the
+ * original history; layer 1 runs the plain SA pass with the shared fold of P,
+ * later layers fold each user's state into its own k x d matrix and run the
+ * same fused pass with per-user matrices.  The aggregation is in float32
+ * from the dtype inputs; LN, FFN and the per-user folds are float32 (the
+ * folded matrices are rounded once to the dtype, as in sa_create).
+ */
+typedef struct sa_stack_s* sa_stack;
+
+/* Weights of one refinement layer: device pointers, row-major, 16-byte aligned. */
+typedef struct sa_layer_params {
+  const void* W_Q;          /* [d][d], dtype of the stack */
+  const void* W_K;          /* [d][d], dtype of the stack */
+  const float* ln1_gain;    /* [d] */
+  const float* ln1_bias;    /* [d] */
+  const float* ffn_gate;    /* [d][d_ff] */
+  const float* ffn_up;      /* [d][d_ff] */
+  const float* ffn_down;    /* [d_ff][d] */
+  const float* ln2_gain;    /* [d] */
+  const float* ln2_bias;    /* [d] */
+} sa_layer_params;
+
+/*
+ * sa_stack_create -- validate, copy every weight (the caller may free them
+ * when this returns) and fold layer 1's matrix.
+ *
+ *   out         host pointer receiving the new handle (NULL on error)
+ *   d, k, tau, dtype, P   as for sa_create (P is X~(0), shared by all users)
+ *   d_ff        FFN hidden width, a multiple of 64 in 64..8192
+ *   num_layers  1..16
+ *   params      host array of num_layers layer descriptions
+ *   stream      stream for the copies; waited for before returning
+ *
+ * Errors as sa_create; SA_ERR_UNSUPPORTED also for an unsupported d_ff,
+ * SA_ERR_INVALID_ARG for a bad layer count or a null or misaligned pointer.
+ */
+sa_status sa_stack_create(sa_stack* out, int32_t d, int32_t k, int32_t d_ff, int32_t num_layers, float tau,
+                          sa_dtype dtype, const void* P, const sa_layer_params* params, void* stream);
+
+/*
+ * sa_stack_compress_batch -- X~(L) for every user of a packed batch.
+ * Arguments, ownership, asynchrony and errors as sa_compress_batch; out is
+ * float32 [num_users][k][d].  An empty history gives Y = 0 in every layer.
+ * The handle holds per-call buffers sized for the largest batch seen (grown
+ * on demand, after waiting for the stream); the same concurrency rules as
+ * for sa_handle apply.
+ */
+sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_t* offsets, int32_t num_users, float* out,
+                                  void* stream);
+
+/* sa_stack_destroy -- release everything the handle owns; NULL is ignored.
+ * The caller must have synchronised the streams that used it. */
+void sa_stack_destroy(sa_stack h);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,7 @@ be used without it; any call into the binding fails loudly when it is absent.
 from .binding import (  # noqa: F401
     SAError,
     SketchAttention,
+    SketchStack,
     sa_check_batch,
     sa_check_config,
     sa_compress_batch,
@@ -17,5 +18,8 @@ from .binding import (  # noqa: F401
     sa_get_folded,
     sa_read_kernel_timing,
     sa_set_kernel_timing,
+    sa_stack_compress_batch,
+    sa_stack_create,
+    sa_stack_destroy,
     sa_status_string,
 )

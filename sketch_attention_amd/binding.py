@@ -32,7 +32,14 @@ _DTYPE_NAMES = {"f32": SA_F32, "bf16": SA_BF16}
 EXPORTED = (
     "sa_create", "sa_compress_batch", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
     "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
+    "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy",
 )
+
+
+class sa_layer_params(ctypes.Structure):
+    """Mirror of the C struct sa_layer_params (device pointers)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "W_Q", "W_K", "ln1_gain", "ln1_bias", "ffn_gate", "ffn_up", "ffn_down", "ln2_gain", "ln2_bias")]
 
 
 class SAError(RuntimeError):
@@ -69,6 +76,10 @@ def library() -> ctypes.CDLL:
         "sa_set_kernel_timing": (i32, [vp, i32]),
         "sa_read_kernel_timing": (i32, [vp, p_f64, p_f64, p_i64]),
         "sa_describe_plan": (i32, [vp, i64, p_i32, p_i32, p_i32, p_i32, p_i32]),
+        "sa_stack_create": (i32, [ctypes.POINTER(vp), i32, i32, i32, i32, f32, i32, vp,
+                                  ctypes.POINTER(sa_layer_params), vp]),
+        "sa_stack_compress_batch": (i32, [vp, vp, vp, i32, vp, vp]),
+        "sa_stack_destroy": (None, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -238,6 +249,107 @@ class SketchAttention:
     def close(self) -> None:
         if getattr(self, "handle", None) is not None:
             sa_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------- stacked refinement
+
+LAYER_FIELDS = ("W_Q", "W_K", "ln1_gain", "ln1_bias", "ffn_gate", "ffn_up", "ffn_down", "ln2_gain", "ln2_bias")
+
+
+def sa_stack_create(P: torch.Tensor, layers: Sequence[dict], tau: float,
+                    stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    """Copy the weights of a refinement stack into a new handle (see include/sa.h).
+
+    `layers` holds one dict per layer with the sa_layer_params fields as GPU
+    tensors: W_Q, W_K [d, d] in P's dtype; ln gains/biases [d], ffn_gate and
+    ffn_up [d, d_ff], ffn_down [d_ff, d] in float32."""
+    _device_tensor(P, "P")
+    if P.dtype not in _DTYPES or P.dim() != 2:
+        raise ValueError("P must be a [k, d] float32 or bfloat16 tensor")
+    k, d = P.shape
+    if len(layers) < 1:
+        raise ValueError("at least one layer")
+    d_ff = int(layers[0]["ffn_gate"].shape[1])
+    arr = (sa_layer_params * len(layers))()
+    for i, lay in enumerate(layers):
+        for name in LAYER_FIELDS:
+            t = lay[name]
+            _device_tensor(t, f"layers[{i}].{name}")
+            want_dtype = P.dtype if name in ("W_Q", "W_K") else torch.float32
+            if t.dtype != want_dtype:
+                raise ValueError(f"layers[{i}].{name} must be {want_dtype}")
+            shape = {"W_Q": (d, d), "W_K": (d, d), "ffn_gate": (d, d_ff), "ffn_up": (d, d_ff),
+                     "ffn_down": (d_ff, d)}.get(name, (d,))
+            if tuple(t.shape) != shape:
+                raise ValueError(f"layers[{i}].{name} must be {list(shape)}")
+            setattr(arr[i], name, t.data_ptr())
+    h = ctypes.c_void_p()
+    with torch.cuda.device(P.device):
+        st = library().sa_stack_create(ctypes.byref(h), int(d), int(k), d_ff, len(layers), float(tau), _DTYPES[P.dtype],
+                                       ctypes.c_void_p(P.data_ptr()), arr, _stream_ptr(stream, P.device))
+    _check(st, "sa_stack_create")
+    return h
+
+
+def sa_stack_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
+                            stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue X~(L) of every user of a packed batch into `out` ([U, k, d] float32)."""
+    offs = _offsets_array(offsets)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    _device_tensor(X, "X")
+    _device_tensor(out, "out")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    if X.dim() != 2 or X.shape[0] != int(offs[-1]):
+        raise ValueError("X must be [offsets[-1], d]")
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    st = library().sa_stack_compress_batch(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
+                                           stream.cuda_stream)
+    _check(st, "sa_stack_compress_batch")
+
+
+def sa_stack_destroy(handle: Optional[ctypes.c_void_p]) -> None:
+    if handle is not None and handle.value:
+        library().sa_stack_destroy(handle)
+
+
+class SketchStack:
+    """Owns one refinement-stack handle (section 2.2 of the SequenceO1 close reading)."""
+
+    def __init__(self, P: torch.Tensor, layers: Sequence[dict], tau: float,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.handle = sa_stack_create(P, layers, tau, stream)
+        self.k, self.d = int(P.shape[0]), int(P.shape[1])
+        self.dtype = P.dtype
+
+    def compress(self, X: torch.Tensor, offsets, out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        if X.dtype != self.dtype or X.dim() != 2 or X.shape[1] != self.d:
+            raise ValueError(f"X must be [N, {self.d}] {self.dtype}")
+        offs = _offsets_array(offsets)
+        if out is None:
+            out = torch.empty((offs.size - 1, self.k, self.d), dtype=torch.float32, device=X.device)
+        sa_stack_compress_batch(self.handle, X, offs, out, stream)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None:
+            sa_stack_destroy(self.handle)
             self.handle = None
 
     def __enter__(self):

@@ -30,6 +30,7 @@ SOURCES = [
     "sa_fused_f32_d128.hip",
     "sa_stream_d64.hip",
     "sa_stream_d128.hip",
+    "sa_refine.hip",
 ]
 # The bf16 plans (accumulators of at most 128 registers per lane) keep every
 # matrix-core result in VGPRs, so the softmax reads the affinity tile without

@@ -264,8 +264,12 @@ SA_API void sa_destroy(sa_handle h) {
   delete h;
 }
 
-SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users, float* out,
-                                   void* stream) {
+namespace {
+
+// One SA pass over a packed batch into out [U][k][d].  M: the folded matrix
+// shared by all users (m_stride 0) or one per user, m_stride elements apart.
+sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_t num_users, float* out, void* stream,
+                   const void* M, int64_t m_stride) {
   if (h == nullptr) return SA_ERR_INVALID_ARG;
   sa_status st = check_batch(offsets, num_users);
   if (st != SA_OK) return st;
@@ -315,7 +319,8 @@ SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* of
     sa::FusedArgs fa;
     std::memset(&fa, 0, sizeof(fa));
     fa.X = static_cast<const char*>(X) + (size_t)base * plan.d * elem;
-    fa.M = h->M;
+    fa.M = static_cast<const char*>(M) + (size_t)u0 * (size_t)m_stride * elem;
+    fa.m_stride = m_stride;
     fa.partial = h->workspace;
     fa.rows = rows;
     fa.users = nu;
@@ -348,6 +353,14 @@ SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* of
     if (h->timing) h->slots.push_back(ts);
   }
   return SA_OK;
+}
+
+}  // namespace
+
+SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users, float* out,
+                                   void* stream) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  return compress(h, X, offsets, num_users, out, stream, h->M, 0);
 }
 
 SA_API sa_status sa_get_folded(sa_handle h, float* dst, void* stream) {
@@ -404,5 +417,182 @@ SA_API sa_status sa_describe_plan(sa_handle h, int64_t total_rows, int32_t* grou
   if (waves_rows) *waves_rows = h->plan.waves_rows;
   if (tile_rows) *tile_rows = h->plan.tile_rows;
   if (k_padded) *k_padded = h->plan.k_pad;
+  return SA_OK;
+}
+
+// ---------------------------------------------------------------- stacked refinement
+// Section 2.2 of the SequenceO1 close-reading page: layer l queries the raw
+// history with the previous state (X~(0) = P), adds the aggregate and
+// normalises, then applies a residual feed-forward block and a second
+// normalisation.  Layer 1 runs the plain SA pass with the shared fold of P;
+// layers 2.. fold each user's state into its own matrix and run the same
+// pass with per-user matrices.
+
+struct sa_stack_s {
+  struct Layer {
+    float* wqk = nullptr;     // [d][d] W_Q W_K^T (layers 2..)
+    float* ln1_g = nullptr;   // [d] each
+    float* ln1_b = nullptr;
+    float* ln2_g = nullptr;
+    float* ln2_b = nullptr;
+    float* gate_t = nullptr;  // [d_ff][d]
+    float* up_t = nullptr;    // [d_ff][d]
+    float* down_t = nullptr;  // [d][d_ff]
+  };
+  int device = 0;
+  int d = 0, k = 0, d_ff = 0;
+  sa_handle_s* base = nullptr;  // plan, fold of P with layer 1's weights, workspace
+  float* P = nullptr;           // [k][d] float32 copy of the prototypes
+  std::vector<Layer> layers;
+  // per-call buffers, grown on demand
+  int64_t cap_users = 0;
+  void* Mu = nullptr;       // [U][k_pad][d] per-user folded matrices, dtype
+  float* y = nullptr;       // [U][k][d] aggregate of the current layer
+  float* xbar = nullptr;    // [U][k][d] first normalisation
+  float* state = nullptr;   // [U][k][d] X~(l)
+  float* ffn_out = nullptr; // [U][k][d]
+  float* hidden = nullptr;  // [U][k][d_ff]
+};
+
+namespace {
+
+constexpr float kLayerNormEps = 1e-5f;
+constexpr int32_t kMaxStackLayers = 16;
+
+void free_stack_buffers(sa_stack_s* h) {
+  for (void* p : {h->Mu, (void*)h->y, (void*)h->xbar, (void*)h->state, (void*)h->ffn_out, (void*)h->hidden})
+    if (p) (void)hipFree(p);
+  h->Mu = nullptr;
+  h->y = h->xbar = h->state = h->ffn_out = h->hidden = nullptr;
+  h->cap_users = 0;
+}
+
+void free_stack(sa_stack_s* h) {
+  free_stack_buffers(h);
+  for (auto& l : h->layers)
+    for (float* p : {l.wqk, l.ln1_g, l.ln1_b, l.ln2_g, l.ln2_b, l.gate_t, l.up_t, l.down_t})
+      if (p) (void)hipFree(p);
+  if (h->P) (void)hipFree(h->P);
+  if (h->base) sa_destroy(h->base);
+  delete h;
+}
+
+template <typename T>
+bool dev_alloc(T** p, size_t count) {
+  return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T)) == hipSuccess;
+}
+
+}  // namespace
+
+SA_API sa_status sa_stack_create(sa_stack* out, int32_t d, int32_t k, int32_t d_ff, int32_t num_layers, float tau,
+                                 sa_dtype dtype, const void* P, const sa_layer_params* params, void* stream) {
+  if (out == nullptr) return SA_ERR_INVALID_ARG;
+  *out = nullptr;
+  sa_status st = check_config(d, k, tau, dtype);
+  if (st != SA_OK) return st;
+  if (num_layers < 1 || num_layers > kMaxStackLayers || params == nullptr || P == nullptr) return SA_ERR_INVALID_ARG;
+  if (d_ff < 64 || d_ff > 8192 || d_ff % 64 != 0) return SA_ERR_UNSUPPORTED;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    const sa_layer_params& p = params[l];
+    for (const void* q : {p.W_Q, p.W_K, (const void*)p.ln1_gain, (const void*)p.ln1_bias, (const void*)p.ffn_gate,
+                          (const void*)p.ffn_up, (const void*)p.ffn_down, (const void*)p.ln2_gain,
+                          (const void*)p.ln2_bias})
+      if (q == nullptr || !aligned16(q)) return SA_ERR_INVALID_ARG;
+  }
+
+  sa_stack_s* h = new (std::nothrow) sa_stack_s();
+  if (h == nullptr) return SA_ERR_OUT_OF_MEMORY;
+  h->d = d;
+  h->k = k;
+  h->d_ff = d_ff;
+  st = sa_create(&h->base, d, k, tau, dtype, P, params[0].W_Q, params[0].W_K, stream);
+  if (st != SA_OK) {
+    delete h;
+    return st;
+  }
+  h->device = h->base->device;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  h->layers.resize(num_layers);
+  bool ok = dev_alloc(&h->P, (size_t)k * d) &&
+            sa::launch_unfold((int)dtype, P, k, d, h->P, s) == hipSuccess;  // a plain copy to float32
+  const size_t dd = (size_t)d * d, dv = (size_t)d, df = (size_t)d * d_ff;
+  for (int32_t l = 0; ok && l < num_layers; ++l) {
+    const sa_layer_params& p = params[l];
+    auto& L = h->layers[l];
+    ok = dev_alloc(&L.ln1_g, dv) && dev_alloc(&L.ln1_b, dv) && dev_alloc(&L.ln2_g, dv) && dev_alloc(&L.ln2_b, dv) &&
+         dev_alloc(&L.gate_t, df) && dev_alloc(&L.up_t, df) && dev_alloc(&L.down_t, df);
+    if (ok && l > 0) ok = dev_alloc(&L.wqk, dd) && sa::launch_wqk((int)dtype, p.W_Q, p.W_K, d, L.wqk, s) == hipSuccess;
+    ok = ok && hipMemcpyAsync(L.ln1_g, p.ln1_gain, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
+         hipMemcpyAsync(L.ln1_b, p.ln1_bias, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
+         hipMemcpyAsync(L.ln2_g, p.ln2_gain, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
+         hipMemcpyAsync(L.ln2_b, p.ln2_bias, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
+         sa::launch_transpose(p.ffn_gate, d, d_ff, L.gate_t, s) == hipSuccess &&
+         sa::launch_transpose(p.ffn_up, d, d_ff, L.up_t, s) == hipSuccess &&
+         sa::launch_transpose(p.ffn_down, d_ff, d, L.down_t, s) == hipSuccess;
+  }
+  if (ok) ok = hipStreamSynchronize(s) == hipSuccess;  // the caller may free its weights on return
+  if (!ok) {
+    free_stack(h);
+    return SA_ERR_DEVICE;
+  }
+  *out = h;
+  return SA_OK;
+}
+
+SA_API void sa_stack_destroy(sa_stack h) {
+  if (h == nullptr) return;
+  DeviceGuard guard(h->device);
+  free_stack(h);
+}
+
+SA_API sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_t* offsets, int32_t num_users,
+                                         float* out, void* stream) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  sa_status st = check_batch(offsets, num_users);
+  if (st != SA_OK) return st;
+  if (num_users == 0) return SA_OK;
+  if (out == nullptr || !aligned16(out)) return SA_ERR_INVALID_ARG;
+  if (offsets[num_users] > 0 && (X == nullptr || !aligned16(X))) return SA_ERR_INVALID_ARG;
+
+  DeviceGuard guard(h->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Plan& plan = h->base->plan;
+  const int d = h->d, k = h->k, d_ff = h->d_ff;
+  const size_t elem = plan.dtype == SA_BF16 ? 2 : 4;
+  if (num_users > h->cap_users) {
+    if (h->cap_users > 0 && hipStreamSynchronize(s) != hipSuccess) return SA_ERR_DEVICE;  // earlier calls may use them
+    free_stack_buffers(h);
+    const size_t rk = (size_t)num_users * k;
+    const bool ok = hipMalloc(&h->Mu, (size_t)num_users * plan.k_pad * d * elem) == hipSuccess &&
+                    dev_alloc(&h->y, rk * d) && dev_alloc(&h->xbar, rk * d) && dev_alloc(&h->state, rk * d) &&
+                    dev_alloc(&h->ffn_out, rk * d) && dev_alloc(&h->hidden, rk * d_ff);
+    if (!ok) {
+      free_stack_buffers(h);
+      return SA_ERR_OUT_OF_MEMORY;
+    }
+    h->cap_users = num_users;
+  }
+  const int64_t rows = (int64_t)num_users * k;
+  const float scale = (float)((double)h->base->tau * kLog2e);
+  const int nl = (int)h->layers.size();
+  for (int l = 0; l < nl; ++l) {
+    const auto& L = h->layers[l];
+    if (l == 0) {
+      st = compress(h->base, X, offsets, num_users, h->y, stream, h->base->M, 0);
+    } else {
+      if (sa::launch_fold_users(plan.dtype, h->state, L.wqk, scale, num_users, k, plan.k_pad, d, h->Mu, s) !=
+          hipSuccess)
+        return SA_ERR_DEVICE;
+      st = compress(h->base, X, offsets, num_users, h->y, stream, h->Mu, (int64_t)plan.k_pad * d);
+    }
+    if (st != SA_OK) return st;
+    // Xbar = LN(X~(l-1) + Y); X~(l) = LN(Xbar + FFN(Xbar)); X~(0) = P for every user
+    float* dst = l == nl - 1 ? out : h->state;
+    if (sa::launch_add_ln(l == 0 ? h->P : h->state, l == 0 ? k : 0, h->y, L.ln1_g, L.ln1_b, kLayerNormEps, rows, d,
+                          h->xbar, s) != hipSuccess ||
+        sa::launch_ffn(h->xbar, rows, d, d_ff, L.gate_t, L.up_t, L.down_t, h->hidden, h->ffn_out, s) != hipSuccess ||
+        sa::launch_add_ln(h->xbar, 0, h->ffn_out, L.ln2_g, L.ln2_b, kLayerNormEps, rows, d, dst, s) != hipSuccess)
+      return SA_ERR_DEVICE;
+  }
   return SA_OK;
 }

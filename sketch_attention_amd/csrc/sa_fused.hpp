@@ -306,23 +306,29 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
 
-  // Folded matrix: this wave's KW rows as B fragments of the affinity product.
+  // Folded matrix of user u (one shared matrix when m_stride is 0): this
+  // wave's KW rows as B fragments of the affinity product.  Called at the
+  // start of a piece, before its first barrier, which orders the LDS copy
+  // before every read; the barrier before the call (per-user matrices only)
+  // ends the reads of the previous piece.
   Frag mreg[MLDS ? 1 : JB][MLDS ? 1 : CS];
-  if constexpr (MLDS) {
-    constexpr int CH = D / 8;  // 16-byte chunks per row
-    for (int idx = tid; idx < G::KPAD * CH; idx += THREADS) {
-      const int r = idx / CH, ch = idx % CH;
-      *reinterpret_cast<u32x4*>(Ms + r * G::MS + ch * 8) = *reinterpret_cast<const u32x4*>(Mg + r * D + ch * 8);
-    }
-    // ordered before the first read by the piece's first barrier
-  } else {
+  auto load_m = [&](int u) {
+    const T* const Mu = Mg + (int64_t)u * args.m_stride;
+    if constexpr (MLDS) {
+      constexpr int CH = D / 8;  // 16-byte chunks per row
+      for (int idx = tid; idx < G::KPAD * CH; idx += THREADS) {
+        const int r = idx / CH, ch = idx % CH;
+        *reinterpret_cast<u32x4*>(Ms + r * G::MS + ch * 8) = *reinterpret_cast<const u32x4*>(Mu + r * D + ch * 8);
+      }
+    } else {
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const T* mrow = Mg + (int64_t)(jbase + 16 * jb + l16) * D;
+      for (int jb = 0; jb < JB; ++jb) {
+        const T* mrow = Mu + (int64_t)(jbase + 16 * jb + l16) * D;
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+        for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+      }
     }
-  }
+  };
 
   // ---- affinity of one tile: s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][jbase + 16 jb + l16],
   // padded prototypes set to -inf.  xfrag(ib, cs) supplies the X fragments.
@@ -550,7 +556,13 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   }
 
   int64_t row = r_begin;
+  int m_user = -1;  // user whose folded matrix is loaded
   while (row < r_end) {
+    if (m_user < 0 || (args.m_stride != 0 && m_user != u)) {
+      if (m_user >= 0) __syncthreads();  // every wave is done with the previous user's matrix
+      load_m(u);
+      m_user = u;
+    }
     const int64_t seg_end = min(r_end, args.offsets[u + 1]);
     const int ntiles = (int)((seg_end - row + NT - 1) / NT);
 

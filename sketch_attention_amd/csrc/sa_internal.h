@@ -27,7 +27,7 @@ struct Plan {
   int m_in_lds;     // folded matrix staged in LDS (1) or held in registers (0)
   int tile_rows;    // rows per tile: kRowsPerWave * waves_rows (lockstep), 16 * row_blocks * waves_rows (streamed)
   int kind;         // 0 = lockstep pass (sa_fused.hpp), 1 = streamed pass (sa_stream.hpp, bf16)
-  int prefetch;     // streamed pass: tiles held in registers between HBM and LDS (1 or 2)
+  int prefetch;     // streamed pass: LDS ring slots beyond the minimum, plus one (ring of 3 or 4 + prefetch - 1 tiles)
   int row_blocks;   // streamed pass: 16-row blocks per wave and tile (2 or 4)
   int score_buffers;  // streamed pass: affinity tiles in flight per wave (2: M in registers; 1: M in LDS)
 };
@@ -35,7 +35,8 @@ struct Plan {
 // Arguments of the fused kernel (passed by value in the dispatch packet).
 struct FusedArgs {
   const void* X;        // rows of this launch, [rows][d]
-  const void* M;        // folded matrix [k_pad][d] in the dtype
+  const void* M;        // folded matrix [k_pad][d] in the dtype, or one per user (m_stride apart)
+  int64_t m_stride;     // elements between the folded matrices of consecutive users; 0: one shared matrix
   float* partial;       // [slots][k_pad * d] float32, slot = group + user
   int64_t rows;         // rows in this launch (offsets[users])
   int32_t users;        // users in this launch (<= kMaxUsersPerLaunch)
@@ -68,6 +69,22 @@ hipError_t launch_fold(int dtype, const void* P, const void* WQ, const void* WK,
 hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hipStream_t stream);
 // Workgroups of the fused kernel that fit on one compute unit at once.
 hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
+
+// Stacked refinement (sa_refine.hip), all float32 unless noted.
+// W_QK = W_Q W_K^T (d x d) from weights in the dtype.
+hipError_t launch_wqk(int dtype, const void* WQ, const void* WK, int d, float* out, hipStream_t stream);
+// dst = src^T for a rows x cols matrix.
+hipError_t launch_transpose(const float* src, int rows, int cols, float* dst, hipStream_t stream);
+// M[u] = scale * state[u] W_QK in the dtype, [users][k_pad][d], padding rows zero.
+hipError_t launch_fold_users(int dtype, const float* state, const float* wqk, float scale, int users, int k, int k_pad,
+                             int d, void* M, hipStream_t stream);
+// out[r] = LN(a[r % a_period (or r when 0)] + b[r]) * gain + bias over d in {64, 128}.
+hipError_t launch_add_ln(const float* a, int64_t a_period, const float* b, const float* gain, const float* bias,
+                         float eps, int64_t rows, int d, float* out, hipStream_t stream);
+// H = silu(Z W_gate) * (Z W_up) [rows][d_ff], F = H W_down [rows][d]; weights given transposed
+// (gate_t, up_t: [d_ff][d]; down_t: [d][d_ff]); d and d_ff multiples of 64.
+hipError_t launch_ffn(const float* Z, int64_t rows, int d, int d_ff, const float* gate_t, const float* up_t,
+                      const float* down_t, float* H, float* F, hipStream_t stream);
 
 // Plan groups, one translation unit each (see sa_fused_*.hip).  With
 // occ != nullptr they report occupancy instead of launching.

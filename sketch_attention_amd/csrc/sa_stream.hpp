@@ -171,7 +171,10 @@ struct StreamGeom {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
 
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
+// PU: one folded matrix per user (args.m_stride apart) instead of one shared
+// matrix; a separate instantiation so the shared case carries none of its
+// bookkeeping.
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args) {
   using G = StreamGeom<D, KW, WJ, WI, RB, PF, SB>;
   using MF = Mfma<bf16>;
@@ -229,25 +232,35 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   };
 
   // ---- folded matrix: this wave's KW rows as B fragments, in registers
-  // (two score buffers) or in the swizzled LDS copy (one score buffer)
+  // (two score buffers) or in the swizzled LDS copy (one score buffer).  One
+  // matrix for all users (m_stride 0, loaded at once) or one per user,
+  // loaded when the tile whose affinity comes next belongs to another user
+  // (ensure_m below).
   constexpr int MP = 256 / (2 * D);  // rows of M per 256 bytes
   bf16x8 mreg[SB == 2 ? JB : 1][SB == 2 ? CS : 1];
   bf16* const Ms = reinterpret_cast<bf16*>(lds + G::OFF_M);
   int moff[CS];  // element offset of chunk 4 cs + g of this lane's rows (the swizzle depends on l16 only)
-  if constexpr (SB == 2) {
+  auto load_m = [&](int u) {
+    const bf16* const Mu = PU ? Mg + (int64_t)u * args.m_stride : Mg;
+    if constexpr (SB == 2) {
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const bf16* mrow = Mg + (int64_t)(jbase + 16 * jb + l16) * D;
+      for (int jb = 0; jb < JB; ++jb) {
+        const bf16* mrow = Mu + (int64_t)(jbase + 16 * jb + l16) * D;
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+        for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(mrow, cs, g);
+      }
+    } else {
+      for (int idx = tid; idx < G::KPAD * G::CH; idx += THREADS) {
+        const int r = idx / G::CH, c = idx % G::CH;
+        *reinterpret_cast<u32x4*>(Ms + r * D + 8 * (c ^ ((r / MP) % G::CH))) =
+            *reinterpret_cast<const u32x4*>(Mu + (int64_t)r * D + 8 * c);
+      }
     }
-  } else {
-    for (int idx = tid; idx < G::KPAD * G::CH; idx += THREADS) {
-      const int r = idx / G::CH, c = idx % G::CH;
-      *reinterpret_cast<u32x4*>(Ms + r * D + 8 * (c ^ ((r / MP) % G::CH))) =
-          *reinterpret_cast<const u32x4*>(Mg + (int64_t)r * D + 8 * c);
-    }
-    // ordered before the first read by the prologue's barrier
+  };
+  int m_user = -1;  // user whose matrix is loaded
+  if constexpr (!PU) {
+    load_m(0);  // LDS copy ordered before the first read by the prologue's barrier
+    m_user = 0;
   }
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) moff[cs] = 8 * ((4 * cs + g) ^ ((l16 / MP) % G::CH));
@@ -445,7 +458,8 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // ---- exact path of one wave (rare): for each of its row blocks, an online
   // max / shifted-sum pass over all prototypes (M fragments from global
   // memory), then its own prototypes' weights 2^(s' - m) with factor 1 / l.
-  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, uint32_t xs) {
+  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, uint32_t xs, int u) {
+    const bf16* const Mu = PU ? Mg + (int64_t)u * args.m_stride : Mg;
 #pragma unroll  // s[ib] must be indexed by constants to stay in registers
     for (int ib = 0; ib < RB; ++ib) {
       bf16x8 xa[CS];
@@ -459,7 +473,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
         for (int jb = 0; jb < JB; ++jb) {  // one 16-prototype block at a time (few live registers)
           f32x4 a = {0.f, 0.f, 0.f, 0.f};
           const int j0 = w * KW + 16 * jb;
-          const bf16* mrow = Mg + (int64_t)(j0 + l16) * D;
+          const bf16* mrow = Mu + (int64_t)(j0 + l16) * D;
 #pragma unroll
           for (int cs = 0; cs < CS; ++cs) a = MF::run(xa[cs], frag_c<D>(mrow, cs, g), a);
           if constexpr (PAD) {
@@ -583,15 +597,38 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   }
   // factor of this lane's row of the tile at cursor c (0 for rows past its piece)
   auto row_ok = [&](const Cursor& c) { return (int64_t)my_row < c.end - c.row; };
+  // per-user matrices: the matrix of user u before an affinity of its tile.
+  // With the LDS copy, the caller's last barrier ended the reads of the old
+  // matrix (the affinity runs once per step) and the copy is published by
+  // the barrier that follows it here or in the prologue.
+  Cursor ca = cc;  // tile whose affinity comes next (per-user matrices only)
+  auto ensure_m = [&](bool barrier_after) {
+    if constexpr (PU) {
+      if (ca.u != m_user) {
+        load_m(ca.u);
+        m_user = ca.u;
+        if constexpr (SB == 1) {
+          if (barrier_after) __syncthreads();
+        }
+      }
+    }
+  };
+  auto next_affinity_tile = [&]() {
+    if constexpr (PU) cursor_next(ca);
+  };
 
   if constexpr (SB == 2) {
     f32x4 S0[RB][JB], S1[RB][JB];
+    ensure_m(false);
     wait_tiles(std::integral_constant<int, NS - 2>{});
     __syncthreads();
     affinity(S0, slot_of(0));
+    next_affinity_tile();
+    ensure_m(false);
     wait_tiles(std::integral_constant<int, NS - 3>{});
     __syncthreads();
     affinity(S1, slot_of(1));
+    next_affinity_tile();
     softmax_fast(S0, 0);
     wait_tiles(std::integral_constant<int, NS - 4>{});
     __syncthreads();
@@ -616,12 +653,14 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       float f;
       bool bad;
       combine_fast(f, bad, t & 1);
-      if (bad) exact_wave(Sa, f, slot_of(q0));
+      if (bad) exact_wave(Sa, f, slot_of(q0), cc.u);
       f = row_ok(cc) ? f : 0.f;
       bf16x8 a[RB / 2][JB];
       weights(a, Sa, f);
       aggregate(acc, a, slot_of(q0));
+      ensure_m(false);
       if (decltype(full)::value || t + 2 < ntot) affinity(Sa, slot_of(q2));
+      next_affinity_tile();
       if (decltype(full)::value || t + 1 < ntot) softmax_fast(Sb, (t + 1) & 1);
       if (cc.row + NT >= cc.end) flush(acc, cc.u, q0);  // its first barrier ends every read of slot q0
       cursor_next(cc);
@@ -643,9 +682,11 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     if (t + 2 < ntot) step(t + 2, S0, S1, Tail{});
   } else {
     f32x4 S[RB][JB];
+    ensure_m(false);
     wait_tiles(std::integral_constant<int, NS - 2>{});
     __syncthreads();  // also publishes the folded matrix
     affinity(S, slot_of(0));
+    next_affinity_tile();
     softmax_fast(S, 0);
     wait_tiles(std::integral_constant<int, NS - 3>{});
     __syncthreads();  // tile 1; row sums of tile 0
@@ -659,15 +700,17 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       const int q1 = q0 + 1 < NS ? q0 + 1 : 0;
       const int qn = q0 == 0 ? NS - 1 : q0 - 1;
       issue_tile(cl, qn);
+      ensure_m(true);  // matrix of tile t+1's user
       float f;
       bool bad;
       combine_fast(f, bad, t & 1);
-      if (bad) exact_wave(S, f, slot_of(q0));
+      if (bad) exact_wave(S, f, slot_of(q0), cc.u);
       f = row_ok(cc) ? f : 0.f;
       bf16x8 a[RB / 2][JB];
       weights(a, S, f);
       aggregate(acc, a, slot_of(q0));
       affinity(S, slot_of(q1));
+      next_affinity_tile();
       softmax_fast(S, (t + 1) & 1);
       if (cc.row + NT >= cc.end) flush(acc, cc.u, q0);  // its first barrier ends every read of slot q0
       cursor_next(cc);
@@ -681,17 +724,22 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   wait_vm<0>();  // no DMA outlives the work group
 }
 
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
-hipError_t launch_stream_t(const FusedArgs& a, const Launch& l) {
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU>
+hipError_t launch_stream_pu(const FusedArgs& a, const Launch& l) {
   constexpr int threads = 64 * WJ * WI;
   if (l.start || l.stop) {
-    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD>), dim3(l.groups), dim3(threads), 0,
+    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU>), dim3(l.groups), dim3(threads), 0,
                           l.stream, l.start, l.stop, 0, a);
   } else {
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD>), dim3(l.groups), dim3(threads), 0, l.stream,
-                       a);
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU>), dim3(l.groups), dim3(threads), 0,
+                       l.stream, a);
   }
   return hipGetLastError();
+}
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
+hipError_t launch_stream_t(const FusedArgs& a, const Launch& l) {
+  return a.m_stride != 0 ? launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, true>(a, l)
+                         : launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false>(a, l);
 }
 
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
@@ -699,12 +747,12 @@ hipError_t run_stream_plan(const Plan& p, const FusedArgs& a, const Launch& l, i
   constexpr int threads = 64 * WJ * WI;
   if (p.k == p.k_pad) {
     if (occ)
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false>,
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false, false>,
                                                           threads, 0);
     return launch_stream_t<D, KW, WJ, WI, RB, PF, SB, false>(a, l);
   }
   if (occ)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true>,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true, false>,
                                                         threads, 0);
   return launch_stream_t<D, KW, WJ, WI, RB, PF, SB, true>(a, l);
 }

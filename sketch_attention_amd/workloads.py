@@ -256,3 +256,28 @@ def named_workload(name: str, users: Optional[int] = None,
     wl = make_workload(name=name, **args)
     wl.recipe = spec["recipe"]
     return wl
+
+
+def make_stack_layers(*, d: int, d_ff: int, layers: int, dtype: str = "bf16", seed: int = 0,
+                      w_std: Optional[float] = None) -> list:
+    """Seeded weights of a refinement stack: one dict per layer with W_Q, W_K
+    ~ N(0, w_std^2) (default 1/d variance; rounded to the dtype), layer-norm
+    gains 1 + 0.1 N(0, 1) and biases 0.1 N(0, 1), FFN gate/up ~ N(0, 1/d) and
+    down ~ N(0, 1/d_ff), all float32 numpy arrays.  Random numbers only: no
+    arithmetic of the method."""
+    rng = np.random.default_rng(np.random.PCG64(seed + 7919))
+    ws = (1.0 / np.sqrt(d)) if w_std is None else w_std
+    out = []
+    for _ in range(layers):
+        out.append({
+            "W_Q": _finish(_normal(rng, (d, d), ws), dtype),
+            "W_K": _finish(_normal(rng, (d, d), ws), dtype),
+            "ln1_gain": 1.0 + _normal(rng, (d,), 0.1),
+            "ln1_bias": _normal(rng, (d,), 0.1),
+            "ffn_gate": _normal(rng, (d, d_ff), 1.0 / np.sqrt(d)),
+            "ffn_up": _normal(rng, (d, d_ff), 1.0 / np.sqrt(d)),
+            "ffn_down": _normal(rng, (d_ff, d), 1.0 / np.sqrt(d_ff)),
+            "ln2_gain": 1.0 + _normal(rng, (d,), 0.1),
+            "ln2_bias": _normal(rng, (d,), 0.1),
+        })
+    return out

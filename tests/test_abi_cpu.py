@@ -107,6 +107,28 @@ def test_null_handle_paths_return_errors_without_device_work():
     lib.sa_destroy(None)  # NULL-safe
 
 
+def test_stack_entry_points_validate_before_device_work():
+    lib = B.library()
+    f = ctypes.c_float(0.1)
+    h = ctypes.c_void_p(99)
+    params = (B.sa_layer_params * 2)()
+    assert lib.sa_stack_create(None, 128, 16, 256, 2, f, 1, None, params, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_stack_create(ctypes.byref(h), 96, 16, 256, 2, f, 1, None, params, None) == B.SA_ERR_UNSUPPORTED
+    assert h.value is None
+    assert lib.sa_stack_create(ctypes.byref(h), 128, 16, 256, 0, f, 1, ctypes.c_void_p(16), params, None) == \
+        B.SA_ERR_INVALID_ARG
+    assert lib.sa_stack_create(ctypes.byref(h), 128, 16, 256, 2, f, 1, ctypes.c_void_p(16), None, None) == \
+        B.SA_ERR_INVALID_ARG
+    assert lib.sa_stack_create(ctypes.byref(h), 128, 16, 100, 2, f, 1, ctypes.c_void_p(16), params, None) == \
+        B.SA_ERR_UNSUPPORTED
+    # null layer pointers are rejected before anything is allocated
+    assert lib.sa_stack_create(ctypes.byref(h), 128, 16, 256, 2, f, 1, ctypes.c_void_p(16), params, None) == \
+        B.SA_ERR_INVALID_ARG
+    offs = np.array([0, 4], dtype=np.int64)
+    assert lib.sa_stack_compress_batch(None, None, offs.ctypes.data, 1, None, None) == B.SA_ERR_INVALID_ARG
+    lib.sa_stack_destroy(None)  # NULL-safe
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
