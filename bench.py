@@ -54,19 +54,27 @@ def algorithmic_bytes(rows: int, users: int, k: int, d: int, elem: int) -> float
     return float(rows) * d * elem + 4.0 * users * k * d
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, budget_s: float, layers=None):
     """Time the fp64 CPU oracle on whole users of the workload, cycling over
-    them until about budget_s seconds have passed."""
+    them until about budget_s seconds have passed (the refinement stack's
+    oracle when `layers` holds its weights)."""
     from threadpoolctl import threadpool_info
 
-    from oracle import sa_oracle
+    from oracle import refine_oracle, sa_oracle
 
+    params = None
+    if layers is not None:
+        params = [refine_oracle.LayerParams(**{k: np.asarray(v, dtype=np.float64) for k, v in lay.items()})
+                  for lay in layers]
     rows = 0
     users = 0
     t0 = time.perf_counter()
     while True:
         u = users % wl.num_users
-        sa_oracle.sketch_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau)
+        if params is None:
+            sa_oracle.sketch_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau)
+        else:
+            refine_oracle.stack_user(wl.user_rows(u), wl.P, params, wl.tau)
         rows += int(wl.offsets[u + 1] - wl.offsets[u])
         users += 1
         if time.perf_counter() - t0 > budget_s:
@@ -78,8 +86,8 @@ def cpu_baseline(wl, budget_s: float):
         "unit": "behaviors/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{users} user sketches cycling over the {wl.num_users} users of the workload ({rows} rows), "
-                  f"fp64 numpy/OpenBLAS, {dt:.2f} s",
+        "sample": f"{users} user {'sketches' if params is None else f'{len(params)}-layer stacks'} cycling over "
+                  f"the {wl.num_users} users of the workload ({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s",
     }
 
 
@@ -141,6 +149,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true", help="run plain copies only (counter scaling)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="run the stacked refinement with this many layers (0: the single SA pass)")
+    ap.add_argument("--d-ff", type=int, default=None, help="FFN width of the refinement stack (default 4 d)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -175,11 +186,27 @@ def main() -> int:
     plan = sa.plan(wl.total_rows)
     log(f"[bench] plan {plan}; input copies {copies} x {x_bytes / 1e6:.1f} MB")
     stream = torch.cuda.current_stream(dev)
+    stack_layers = None
+    passes = 1  # fused SA passes per step
+    if args.layers > 0:
+        from sketch_attention_amd import SketchStack
+        d_ff = args.d_ff or 4 * wl.d
+        stack_layers = workloads.make_stack_layers(d=wl.d, d_ff=d_ff, layers=args.layers, dtype=wl.dtype, seed=11)
+        lt = [{n: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt if n in ("W_Q", "W_K") else torch.float32)
+               for n, a in lay.items()} for lay in stack_layers]
+        stack = SketchStack(t(wl.P), lt, wl.tau)
+        passes = args.layers
+        log(f"[bench] refinement stack: {args.layers} layers, FFN width {d_ff}")
+        handle, compress = stack.handle, binding.sa_stack_compress_batch
+        set_timing, read_timing = binding.sa_stack_set_kernel_timing, binding.sa_stack_read_kernel_timing
+    else:
+        handle, compress = sa.handle, binding.sa_compress_batch
+        set_timing, read_timing = binding.sa_set_kernel_timing, binding.sa_read_kernel_timing
 
     for i in range(args.warmup):
-        binding.sa_compress_batch(sa.handle, Xs[i % copies], offs, outs[i % 2], stream)
+        compress(handle, Xs[i % copies], offs, outs[i % 2], stream)
     torch.cuda.synchronize(dev)
-    binding.sa_read_kernel_timing(sa.handle)  # discard anything recorded so far
+    read_timing(handle)  # discard anything recorded so far
 
     # Kernel durations come from HIP events that the kernels' own dispatches
     # record on the launch stream; they are taken on every TIMING_PERIOD-th
@@ -190,13 +217,13 @@ def main() -> int:
     for i in range(args.steps):
         timed = i % TIMING_PERIOD == 0
         if timed:
-            binding.sa_set_kernel_timing(sa.handle, True)
-        binding.sa_compress_batch(sa.handle, Xs[i % copies], offs, outs[i % 2], stream)
+            set_timing(handle, True)
+        compress(handle, Xs[i % copies], offs, outs[i % 2], stream)
         if timed:
-            binding.sa_set_kernel_timing(sa.handle, False)
+            set_timing(handle, False)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
-    fused_ms, reduce_ms, launches = binding.sa_read_kernel_timing(sa.handle)
+    fused_ms, reduce_ms, launches = read_timing(handle)
     log(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms")
 
     ms_per_step = elapsed * 1e3 / args.steps
@@ -206,8 +233,8 @@ def main() -> int:
     fused_avg_ms = fused_ms / max(launches, 1)
     # launches == timed steps unless the batch spans several launches; per-launch work
     timed_steps = (args.steps + TIMING_PERIOD - 1) // TIMING_PERIOD
-    per_launch_flops = flops * timed_steps / max(launches, 1)
-    per_launch_bytes = nbytes * timed_steps / max(launches, 1)
+    per_launch_flops = flops * passes * timed_steps / max(launches, 1)
+    per_launch_bytes = nbytes * passes * timed_steps / max(launches, 1)
     mfma_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     tflops = per_launch_flops / (fused_avg_ms * 1e-3) / 1e12 if fused_avg_ms > 0 else 0.0
     gbs = per_launch_bytes / (fused_avg_ms * 1e-3) / 1e9 if fused_avg_ms > 0 else 0.0
@@ -219,22 +246,24 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(wl.name, wl.dtype, wl.d) if args.users is None else None
+    roof["traffic"] = measured_traffic(wl.name, wl.dtype, wl.d) if args.users is None and not args.layers else None
     # the library runs the streamed pass for bf16 with k > 32, the lockstep pass otherwise
     roof["kernel"] = "sa_stream_kernel" if wl.dtype == "bf16" and wl.k > 32 else "sa_fused_kernel"
     roof["kernel_avg_us"] = round(fused_avg_ms * 1e3, 2)
     log(f"[bench] fused kernel avg {fused_avg_ms * 1e3:.2f} us ({tflops:.1f} TFLOP/s, {gbs:.0f} GB/s), "
         f"reduce avg {reduce_ms / max(launches, 1) * 1e3:.2f} us; whole step {ms_per_step * 1e3:.2f} us "
-        f"({flops / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s)")
+        f"({flops * passes / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s in the SA passes)")
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu = cpu_baseline(wl, args.cpu_budget, stack_layers)
         log(f"[bench] cpu baseline: {cpu}")
 
     sa.close()
+    if args.layers > 0:
+        stack.close()
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not args.layers else f"history behaviors/sec through a {args.layers}-layer refinement stack",
         "value": round(value, 1),
         "unit": "behaviors/s",
         "n_gpus": 1,
@@ -253,6 +282,7 @@ def main() -> int:
             "rows": wl.total_rows,
             "d": wl.d,
             "k": wl.k,
+            **({"layers": args.layers, "d_ff": args.d_ff or 4 * wl.d} if args.layers else {}),
             "parallelism": "single-gpu",
         },
         "roofline": roof,

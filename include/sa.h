@@ -217,6 +217,12 @@ sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_t* offs
  * The caller must have synchronised the streams that used it. */
 void sa_stack_destroy(sa_stack h);
 
+/* sa_stack_set_kernel_timing / sa_stack_read_kernel_timing -- as the sa_handle
+ * versions, for the fused passes and reductions of every layer (one fused
+ * launch per layer and launch of at most 256 users). */
+sa_status sa_stack_set_kernel_timing(sa_stack h, int32_t enable);
+sa_status sa_stack_read_kernel_timing(sa_stack h, double* fused_ms, double* reduce_ms, int64_t* fused_launches);
+
 #ifdef __cplusplus
 }
 #endif

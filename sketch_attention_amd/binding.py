@@ -32,7 +32,8 @@ _DTYPE_NAMES = {"f32": SA_F32, "bf16": SA_BF16}
 EXPORTED = (
     "sa_create", "sa_compress_batch", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
     "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
-    "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy",
+    "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy", "sa_stack_set_kernel_timing",
+    "sa_stack_read_kernel_timing",
 )
 
 
@@ -80,6 +81,8 @@ def library() -> ctypes.CDLL:
                                   ctypes.POINTER(sa_layer_params), vp]),
         "sa_stack_compress_batch": (i32, [vp, vp, vp, i32, vp, vp]),
         "sa_stack_destroy": (None, [vp]),
+        "sa_stack_set_kernel_timing": (i32, [vp, i32]),
+        "sa_stack_read_kernel_timing": (i32, [vp, p_f64, p_f64, p_i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -326,6 +329,18 @@ def sa_stack_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, o
 def sa_stack_destroy(handle: Optional[ctypes.c_void_p]) -> None:
     if handle is not None and handle.value:
         library().sa_stack_destroy(handle)
+
+
+def sa_stack_set_kernel_timing(handle: ctypes.c_void_p, enable: bool) -> None:
+    _check(library().sa_stack_set_kernel_timing(handle, 1 if enable else 0), "sa_stack_set_kernel_timing")
+
+
+def sa_stack_read_kernel_timing(handle: ctypes.c_void_p):
+    """Returns (fused_ms_total, reduce_ms_total, fused_launches) since the last read."""
+    f, r, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(library().sa_stack_read_kernel_timing(handle, ctypes.byref(f), ctypes.byref(r), ctypes.byref(n)),
+           "sa_stack_read_kernel_timing")
+    return f.value, r.value, n.value
 
 
 class SketchStack:

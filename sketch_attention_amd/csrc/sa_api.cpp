@@ -430,7 +430,7 @@ SA_API sa_status sa_describe_plan(sa_handle h, int64_t total_rows, int32_t* grou
 
 struct sa_stack_s {
   struct Layer {
-    float* wqk = nullptr;     // [d][d] W_Q W_K^T (layers 2..)
+    float* wqk_t = nullptr;   // [d][d] (W_Q W_K^T)^T (layers 2..)
     float* ln1_g = nullptr;   // [d] each
     float* ln1_b = nullptr;
     float* ln2_g = nullptr;
@@ -470,7 +470,7 @@ void free_stack_buffers(sa_stack_s* h) {
 void free_stack(sa_stack_s* h) {
   free_stack_buffers(h);
   for (auto& l : h->layers)
-    for (float* p : {l.wqk, l.ln1_g, l.ln1_b, l.ln2_g, l.ln2_b, l.gate_t, l.up_t, l.down_t})
+    for (float* p : {l.wqk_t, l.ln1_g, l.ln1_b, l.ln2_g, l.ln2_b, l.gate_t, l.up_t, l.down_t})
       if (p) (void)hipFree(p);
   if (h->P) (void)hipFree(h->P);
   if (h->base) sa_destroy(h->base);
@@ -521,7 +521,8 @@ SA_API sa_status sa_stack_create(sa_stack* out, int32_t d, int32_t k, int32_t d_
     auto& L = h->layers[l];
     ok = dev_alloc(&L.ln1_g, dv) && dev_alloc(&L.ln1_b, dv) && dev_alloc(&L.ln2_g, dv) && dev_alloc(&L.ln2_b, dv) &&
          dev_alloc(&L.gate_t, df) && dev_alloc(&L.up_t, df) && dev_alloc(&L.down_t, df);
-    if (ok && l > 0) ok = dev_alloc(&L.wqk, dd) && sa::launch_wqk((int)dtype, p.W_Q, p.W_K, d, L.wqk, s) == hipSuccess;
+    if (ok && l > 0)
+      ok = dev_alloc(&L.wqk_t, dd) && sa::launch_wqk_t((int)dtype, p.W_Q, p.W_K, d, L.wqk_t, s) == hipSuccess;
     ok = ok && hipMemcpyAsync(L.ln1_g, p.ln1_gain, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
          hipMemcpyAsync(L.ln1_b, p.ln1_bias, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
          hipMemcpyAsync(L.ln2_g, p.ln2_gain, dv * 4, hipMemcpyDeviceToDevice, s) == hipSuccess &&
@@ -563,7 +564,9 @@ SA_API sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_
     if (h->cap_users > 0 && hipStreamSynchronize(s) != hipSuccess) return SA_ERR_DEVICE;  // earlier calls may use them
     free_stack_buffers(h);
     const size_t rk = (size_t)num_users * k;
-    const bool ok = hipMalloc(&h->Mu, (size_t)num_users * plan.k_pad * d * elem) == hipSuccess &&
+    const size_t mu_bytes = (size_t)num_users * plan.k_pad * d * elem;
+    // the folds never write the padding rows k..k_pad-1: zero them once
+    const bool ok = hipMalloc(&h->Mu, mu_bytes) == hipSuccess && hipMemsetAsync(h->Mu, 0, mu_bytes, s) == hipSuccess &&
                     dev_alloc(&h->y, rk * d) && dev_alloc(&h->xbar, rk * d) && dev_alloc(&h->state, rk * d) &&
                     dev_alloc(&h->ffn_out, rk * d) && dev_alloc(&h->hidden, rk * d_ff);
     if (!ok) {
@@ -580,7 +583,7 @@ SA_API sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_
     if (l == 0) {
       st = compress(h->base, X, offsets, num_users, h->y, stream, h->base->M, 0);
     } else {
-      if (sa::launch_fold_users(plan.dtype, h->state, L.wqk, scale, num_users, k, plan.k_pad, d, h->Mu, s) !=
+      if (sa::launch_fold_users(plan.dtype, h->state, L.wqk_t, scale, num_users, k, plan.k_pad, d, h->Mu, s) !=
           hipSuccess)
         return SA_ERR_DEVICE;
       st = compress(h->base, X, offsets, num_users, h->y, stream, h->Mu, (int64_t)plan.k_pad * d);
@@ -595,4 +598,15 @@ SA_API sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_
       return SA_ERR_DEVICE;
   }
   return SA_OK;
+}
+
+SA_API sa_status sa_stack_set_kernel_timing(sa_stack h, int32_t enable) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  return sa_set_kernel_timing(h->base, enable);
+}
+
+SA_API sa_status sa_stack_read_kernel_timing(sa_stack h, double* fused_ms, double* reduce_ms,
+                                             int64_t* fused_launches) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  return sa_read_kernel_timing(h->base, fused_ms, reduce_ms, fused_launches);
 }

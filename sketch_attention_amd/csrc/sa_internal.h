@@ -71,18 +71,19 @@ hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hip
 hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
 
 // Stacked refinement (sa_refine.hip), all float32 unless noted.
-// W_QK = W_Q W_K^T (d x d) from weights in the dtype.
-hipError_t launch_wqk(int dtype, const void* WQ, const void* WK, int d, float* out, hipStream_t stream);
+// (W_Q W_K^T)^T (d x d) from weights in the dtype.
+hipError_t launch_wqk_t(int dtype, const void* WQ, const void* WK, int d, float* out, hipStream_t stream);
 // dst = src^T for a rows x cols matrix.
 hipError_t launch_transpose(const float* src, int rows, int cols, float* dst, hipStream_t stream);
-// M[u] = scale * state[u] W_QK in the dtype, [users][k_pad][d], padding rows zero.
-hipError_t launch_fold_users(int dtype, const float* state, const float* wqk, float scale, int users, int k, int k_pad,
+// M[u] = scale * state[u] W_QK in the dtype, [users][k_pad][d], from wqk_t = W_QK^T; padding rows
+// k..k_pad-1 are not written (the caller keeps them zero).
+hipError_t launch_fold_users(int dtype, const float* state, const float* wqk_t, float scale, int users, int k, int k_pad,
                              int d, void* M, hipStream_t stream);
 // out[r] = LN(a[r % a_period (or r when 0)] + b[r]) * gain + bias over d in {64, 128}.
 hipError_t launch_add_ln(const float* a, int64_t a_period, const float* b, const float* gain, const float* bias,
                          float eps, int64_t rows, int d, float* out, hipStream_t stream);
 // H = silu(Z W_gate) * (Z W_up) [rows][d_ff], F = H W_down [rows][d]; weights given transposed
-// (gate_t, up_t: [d_ff][d]; down_t: [d][d_ff]); d and d_ff multiples of 64.
+// (gate_t, up_t: [d_ff][d]; down_t: [d][d_ff]); d and d_ff multiples of 32.
 hipError_t launch_ffn(const float* Z, int64_t rows, int d, int d_ff, const float* gate_t, const float* up_t,
                       const float* down_t, float* H, float* F, hipStream_t stream);
 

@@ -22,12 +22,13 @@ namespace {
 
 // ------------------------------------------------------------ weight prep
 // W_QK[a][c] = sum_b W_Q[a][b] W_K[c][b]: the affinity (Q W_Q)(x W_K)^T of a
-// query row Q and a history row x equals (Q W_QK) x^T.
+// query row Q and a history row x equals (Q W_QK) x^T.  Stored transposed,
+// out[c][a] = W_QK[a][c], the B layout of the fold product.
 template <typename T>
-__global__ __launch_bounds__(256) void wqk_kernel(const T* WQ, const T* WK, int d, float* out) {
+__global__ __launch_bounds__(256) void wqk_t_kernel(const T* WQ, const T* WK, int d, float* out) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= d * d) return;
-  const int a = idx / d, c = idx % d;
+  const int c = idx / d, a = idx % d;
   float s = 0.f;
   for (int b = 0; b < d; ++b) s += (float)WQ[a * d + b] * (float)WK[c * d + b];
   out[idx] = s;
@@ -39,29 +40,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(const float* src, int ro
   if (idx >= rows * cols) return;
   const int r = idx / cols, c = idx % cols;
   dst[(int64_t)c * rows + r] = src[idx];
-}
-
-// ------------------------------------------------------------ per-user fold
-// M[u][j][c] = scale * sum_a state[u][j][a] W_QK[a][c] for j < k, zero for the
-// padding rows k..k_pad-1.  One thread per output element; the state row is
-// the same for a wave's lanes, the W_QK row reads are coalesced.
-template <typename T>
-__global__ __launch_bounds__(256) void fold_users_kernel(const float* state, const float* wqk, float scale, int users,
-                                                         int k, int k_pad, int d, T* M) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)users * k_pad * d;
-  if (idx >= total) return;
-  const int c = (int)(idx % d);
-  const int64_t uj = idx / d;
-  const int j = (int)(uj % k_pad);
-  const int64_t u = uj / k_pad;
-  float s = 0.f;
-  if (j < k) {
-    const float* q = state + (u * k + j) * d;
-    for (int a = 0; a < d; ++a) s += q[a] * wqk[a * d + c];
-    s *= scale;
-  }
-  M[idx] = (T)s;
 }
 
 // ------------------------------------------------------------ residual + LN
@@ -106,74 +84,92 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const float* a, int64_t a_p
   }
 }
 
-// ------------------------------------------------------------ FFN products
+// ------------------------------------------------------------ small products
 // C = A B for row-major A [M][K] and B given transposed, Bt [N][K], float32
-// matrix cores (16x16x4).  A wave owns a 32 x 32 tile, four waves a 64 x 64
-// one.  Reduction slot (g, s) of a 16-column chunk k0 is column k0 + 4 g + s
-// of both operands, so each lane reads four consecutive floats of a row.
-// Rows of A past M read zeros and are not stored.
+// matrix cores (16x16x4), one wave per work group owning a 16 x 32 tile so
+// that these small products still spread over the compute units.  Reduction
+// slot (g, s) of a 16-column chunk k0 is column k0 + 4 g + s of both
+// operands, so each lane reads four consecutive floats of a row.  Rows of A
+// past M read zeros and are not stored.  Epilogues:
+//   EPI_STORE  C[r][c] = acc
+//   EPI_GATED  C[r][c] = silu(A Bt0^T) * (A Bt1^T)      (SwiGLU hidden layer)
+//   EPI_FOLD   row r = u k + j of the per-user states -> M[u][j][c] =
+//              scale * acc rounded to T (rows k..k_pad-1 of each user are
+//              left as they are: zero from allocation)
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+enum { EPI_STORE = 0, EPI_GATED = 1, EPI_FOLD = 2 };
 
-__device__ __forceinline__ f32x4_t load_row4(const float* base, int64_t row, int64_t rows, int K, int col) {
-  if (row >= rows) return f32x4_t{0.f, 0.f, 0.f, 0.f};
-  return *reinterpret_cast<const f32x4_t*>(base + row * K + col);
-}
-
-template <bool GATED>
-__global__ __launch_bounds__(256) void ffn_gemm_kernel(const float* A, int64_t M, int K, const float* Bt0,
-                                                       const float* Bt1, int N, float* C) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int EPI, typename T>
+__global__ __launch_bounds__(64) void small_gemm_kernel(const float* A, int64_t M, int K, const float* Bt0,
+                                                        const float* Bt1, int N, T* C, float scale, int k, int k_pad) {
+  const int lane = threadIdx.x;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.y * 64 + 32 * (wave >> 1);
-  const int col0 = blockIdx.x * 64 + 32 * (wave & 1);
-  f32x4_t acc0[2][2], acc1[2][2];
+  const int64_t row0 = (int64_t)blockIdx.y * 16;
+  const int col0 = blockIdx.x * 32;
+  const int64_t arow = row0 + l16;
+  // four partial sums per block (slot s of each chunk), added at the end:
+  // four independent chains instead of one long dependent one
+  f32x4_t acc0[2][4], acc1[2][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc0[i][j] = acc1[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4; ++s) acc0[j][s] = acc1[j][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4  // loads of several chunks in flight
   for (int k0 = 0; k0 < K; k0 += 16) {
-    f32x4_t a[2], b0[2], b1[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = load_row4(A, row0 + 16 * i + l16, M, K, k0 + 4 * g);
+    const f32x4_t a = arow < M ? *reinterpret_cast<const f32x4_t*>(A + arow * K + k0 + 4 * g)
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t b0[2], b1[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       b0[j] = *reinterpret_cast<const f32x4_t*>(Bt0 + (int64_t)(col0 + 16 * j + l16) * K + k0 + 4 * g);
-      if constexpr (GATED) b1[j] = *reinterpret_cast<const f32x4_t*>(Bt1 + (int64_t)(col0 + 16 * j + l16) * K + k0 + 4 * g);
+      if constexpr (EPI == EPI_GATED)
+        b1[j] = *reinterpret_cast<const f32x4_t*>(Bt1 + (int64_t)(col0 + 16 * j + l16) * K + k0 + 4 * g);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b0[j][s], acc0[i][j], 0, 0, 0);
-          if constexpr (GATED) acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b1[j][s], acc1[i][j], 0, 0, 0);
-        }
-  }
-  // lane holds C[row0 + 16 i + 4 g + r][col0 + 16 j + l16]
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = row0 + 16 * i + 4 * g + r;
-      if (row >= M) continue;
-#pragma unroll
       for (int j = 0; j < 2; ++j) {
-        float v = acc0[i][j][r];
-        if constexpr (GATED) v = v / (1.f + expf(-v)) * acc1[i][j][r];  // silu(gate) * up
-        C[row * N + col0 + 16 * j + l16] = v;
+        acc0[j][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b0[j][s], acc0[j][s], 0, 0, 0);
+        if constexpr (EPI == EPI_GATED)
+          acc1[j][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b1[j][s], acc1[j][s], 0, 0, 0);
+      }
+  }
+  f32x4_t sum0[2], sum1[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sum0[j] = (acc0[j][0] + acc0[j][1]) + (acc0[j][2] + acc0[j][3]);
+    sum1[j] = (acc1[j][0] + acc1[j][1]) + (acc1[j][2] + acc1[j][3]);
+  }
+  // lane holds C[row0 + 4 g + r][col0 + 16 j + l16]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t row = row0 + 4 * g + r;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + 16 * j + l16;
+      float v = sum0[j][r];
+      if constexpr (EPI == EPI_GATED) {
+        v = v / (1.f + expf(-v)) * sum1[j][r];  // silu(gate) * up
+        C[row * N + col] = (T)v;
+      } else if constexpr (EPI == EPI_FOLD) {
+        const int64_t u = row / k, jj = row % k;
+        C[(u * k_pad + jj) * N + col] = (T)(scale * v);
+      } else {
+        C[row * N + col] = (T)v;
       }
     }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_wqk(int dtype, const void* WQ, const void* WK, int d, float* out, hipStream_t s) {
+hipError_t launch_wqk_t(int dtype, const void* WQ, const void* WK, int d, float* out, hipStream_t s) {
   const int blocks = (d * d + 255) / 256;
   if (dtype == 1)
-    hipLaunchKernelGGL(wqk_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)WQ, (const bf16*)WK, d, out);
+    hipLaunchKernelGGL(wqk_t_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)WQ, (const bf16*)WK, d, out);
   else
-    hipLaunchKernelGGL(wqk_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)WQ, (const float*)WK, d, out);
+    hipLaunchKernelGGL(wqk_t_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)WQ, (const float*)WK, d, out);
   return hipGetLastError();
 }
 
@@ -182,15 +178,17 @@ hipError_t launch_transpose(const float* src, int rows, int cols, float* dst, hi
   return hipGetLastError();
 }
 
-hipError_t launch_fold_users(int dtype, const float* state, const float* wqk, float scale, int users, int k, int k_pad,
+hipError_t launch_fold_users(int dtype, const float* state, const float* wqk_t, float scale, int users, int k, int k_pad,
                              int d, void* M, hipStream_t s) {
-  const int64_t total = (int64_t)users * k_pad * d;
-  const dim3 grid((unsigned)((total + 255) / 256));
+  if (d % 32 != 0) return hipErrorInvalidValue;
+  const int64_t rows = (int64_t)users * k;
+  const dim3 grid(d / 32, (unsigned)((rows + 15) / 16));
   if (dtype == 1)
-    hipLaunchKernelGGL(fold_users_kernel<bf16>, grid, dim3(256), 0, s, state, wqk, scale, users, k, k_pad, d, (bf16*)M);
+    hipLaunchKernelGGL((small_gemm_kernel<EPI_FOLD, bf16>), grid, dim3(64), 0, s, state, rows, d, wqk_t, nullptr, d,
+                       (bf16*)M, scale, k, k_pad);
   else
-    hipLaunchKernelGGL(fold_users_kernel<float>, grid, dim3(256), 0, s, state, wqk, scale, users, k, k_pad, d,
-                       (float*)M);
+    hipLaunchKernelGGL((small_gemm_kernel<EPI_FOLD, float>), grid, dim3(64), 0, s, state, rows, d, wqk_t, nullptr, d,
+                       (float*)M, scale, k, k_pad);
   return hipGetLastError();
 }
 
@@ -208,10 +206,12 @@ hipError_t launch_add_ln(const float* a, int64_t a_period, const float* b, const
 
 hipError_t launch_ffn(const float* Z, int64_t rows, int d, int d_ff, const float* gate_t, const float* up_t,
                       const float* down_t, float* H, float* F, hipStream_t s) {
-  if (d % 64 != 0 || d_ff % 64 != 0) return hipErrorInvalidValue;
-  const unsigned gy = (unsigned)((rows + 63) / 64);
-  hipLaunchKernelGGL(ffn_gemm_kernel<true>, dim3(d_ff / 64, gy), dim3(256), 0, s, Z, rows, d, gate_t, up_t, d_ff, H);
-  hipLaunchKernelGGL(ffn_gemm_kernel<false>, dim3(d / 64, gy), dim3(256), 0, s, H, rows, d_ff, down_t, nullptr, d, F);
+  if (d % 32 != 0 || d_ff % 32 != 0) return hipErrorInvalidValue;
+  const unsigned gy = (unsigned)((rows + 15) / 16);
+  hipLaunchKernelGGL((small_gemm_kernel<EPI_GATED, float>), dim3(d_ff / 32, gy), dim3(64), 0, s, Z, rows, d, gate_t,
+                     up_t, d_ff, H, 1.f, 0, 0);
+  hipLaunchKernelGGL((small_gemm_kernel<EPI_STORE, float>), dim3(d / 32, gy), dim3(64), 0, s, H, rows, d_ff, down_t,
+                     nullptr, d, F, 1.f, 0, 0);
   return hipGetLastError();
 }
 
