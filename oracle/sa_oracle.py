@@ -35,7 +35,11 @@ in every row; invariance under permuting history rows; additivity over any
 split of a user's rows; k = 2 reduces to the logistic function; n = 1 gives
 a rank-one sketch; brute-force index sums on tiny inputs; the hard-assignment
 limit; scipy's softmax on the prototype axis; planted mistakes are caught.
-No function here is left unpinned.
+The comparator (softmax over the history axis, section 3.1) is pinned in
+its own tests: rows of its assignment sum to one, n = 1 and W_K = 0 closed
+forms, invariance under duplicating every row, scipy's softmax on the
+history axis, index loops, planted mistakes.  No function here is left
+unpinned.
 """
 from __future__ import annotations
 
@@ -43,7 +47,8 @@ from typing import Iterable, Optional
 
 import numpy as np
 
-__all__ = ["affinity", "assignment", "sketch_user", "sketch_batch", "fold_reference"]
+__all__ = ["affinity", "assignment", "sketch_user", "sketch_batch", "fold_reference", "history_assignment",
+           "history_sketch_user", "history_sketch_batch"]
 
 
 def _f64(a) -> np.ndarray:
@@ -118,3 +123,41 @@ def fold_reference(P, W_Q, W_K) -> np.ndarray:
     which avoids forming the history's key projection (section 1).
     """
     return (_f64(P) @ _f64(W_Q)) @ _f64(W_K).T
+
+
+# ------------------------------------------------------------------ comparator
+def history_assignment(S) -> np.ndarray:
+    """softmax of S over the history axis (axis 1), shape (k, n).
+
+    Section 2.1 of the close reading contrasts SA with the usual latent
+    cross-attention, which normalises over history positions so that each
+    prototype selects content from the history; section 3.1 (Figure 3,
+    Table 1) compares the two with only the softmax axis changed.  Each row
+    of this assignment sums to one over the n behaviours."""
+    S = _f64(S)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def history_sketch_user(X, P, W_Q, W_K, tau: float) -> np.ndarray:
+    """The comparator's k x d summary for one user: history_assignment(S) X,
+    the same affinity and the same aggregation of the raw X as sketch_user;
+    an empty history gives zeros."""
+    X = _f64(X)
+    P = _f64(P)
+    if X.shape[0] == 0:
+        return np.zeros(P.shape, dtype=np.float64)
+    return history_assignment(affinity(X, P, W_Q, W_K, tau)) @ X
+
+
+def history_sketch_batch(X, offsets, P, W_Q, W_K, tau: float, users: Optional[Iterable[int]] = None) -> np.ndarray:
+    """history_sketch_user over a packed batch, float64 [U, k, d] (or a chosen subset)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    U = offsets.shape[0] - 1
+    sel = list(range(U)) if users is None else [int(u) for u in users]
+    P = _f64(P)
+    out = np.zeros((len(sel), P.shape[0], P.shape[1]), dtype=np.float64)
+    for slot, u in enumerate(sel):
+        out[slot] = history_sketch_user(X[int(offsets[u]):int(offsets[u + 1])], P, W_Q, W_K, tau)
+    return out
