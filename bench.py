@@ -54,7 +54,7 @@ def algorithmic_bytes(rows: int, users: int, k: int, d: int, elem: int) -> float
     return float(rows) * d * elem + 4.0 * users * k * d
 
 
-def cpu_baseline(wl, budget_s: float, layers=None):
+def cpu_baseline(wl, budget_s: float, layers=None, norm: str = "prototypes"):
     """Time the fp64 CPU oracle on whole users of the workload, cycling over
     them until about budget_s seconds have passed (the refinement stack's
     oracle when `layers` holds its weights)."""
@@ -71,7 +71,9 @@ def cpu_baseline(wl, budget_s: float, layers=None):
     t0 = time.perf_counter()
     while True:
         u = users % wl.num_users
-        if params is None:
+        if norm == "history":
+            sa_oracle.history_sketch_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau)
+        elif params is None:
             sa_oracle.sketch_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau)
         else:
             refine_oracle.stack_user(wl.user_rows(u), wl.P, params, wl.tau)
@@ -86,7 +88,7 @@ def cpu_baseline(wl, budget_s: float, layers=None):
         "unit": "behaviors/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{users} user {'sketches' if params is None else f'{len(params)}-layer stacks'} cycling over "
+        "sample": f"{users} user {'comparator summaries' if norm == 'history' else 'sketches' if params is None else f'{len(params)}-layer stacks'} cycling over "
                   f"the {wl.num_users} users of the workload ({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s",
     }
 
@@ -152,6 +154,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0,
                     help="run the stacked refinement with this many layers (0: the single SA pass)")
     ap.add_argument("--d-ff", type=int, default=None, help="FFN width of the refinement stack (default 4 d)")
+    ap.add_argument("--norm", default="prototypes", choices=["prototypes", "history"],
+                    help="softmax axis: prototypes (Sketch Attention) or history (the comparator)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -180,7 +184,10 @@ def main() -> int:
     x_bytes = wl.total_rows * wl.d * elem
     copies = max(1, math.ceil(2 * MALL_BYTES / max(x_bytes, 1)) + 1) if x_bytes < 2 * MALL_BYTES else 1
     Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
-    sa = SketchAttention(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau)
+    if args.norm == "history" and args.layers:
+        print("--norm history runs the single pass only", file=sys.stderr)
+        return 2
+    sa = SketchAttention(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau, norm=args.norm)
     outs = [torch.empty((wl.num_users, wl.k, wl.d), dtype=torch.float32, device=dev) for _ in range(2)]
     offs = np.ascontiguousarray(wl.offsets, dtype=np.int64)
     plan = sa.plan(wl.total_rows)
@@ -246,7 +253,8 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(wl.name, wl.dtype, wl.d) if args.users is None and not args.layers else None
+    roof["traffic"] = measured_traffic(wl.name, wl.dtype, wl.d) if (args.users is None and not args.layers and
+                                                                     args.norm == "prototypes") else None
     # the library runs the streamed pass for bf16 with k > 32, the lockstep pass otherwise
     roof["kernel"] = "sa_stream_kernel" if wl.dtype == "bf16" and wl.k > 32 else "sa_fused_kernel"
     roof["kernel_avg_us"] = round(fused_avg_ms * 1e3, 2)
@@ -256,14 +264,16 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_budget, stack_layers)
+        cpu = cpu_baseline(wl, args.cpu_budget, stack_layers, args.norm)
         log(f"[bench] cpu baseline: {cpu}")
 
     sa.close()
     if args.layers > 0:
         stack.close()
     line = {
-        "metric": METRIC if not args.layers else f"history behaviors/sec through a {args.layers}-layer refinement stack",
+        "metric": (METRIC if args.norm == "prototypes" else "history behaviors/sec summarised by the history-axis "
+                   "softmax comparator") if not args.layers
+        else f"history behaviors/sec through a {args.layers}-layer refinement stack",
         "value": round(value, 1),
         "unit": "behaviors/s",
         "n_gpus": 1,
@@ -283,6 +293,7 @@ def main() -> int:
             "d": wl.d,
             "k": wl.k,
             **({"layers": args.layers, "d_ff": args.d_ff or 4 * wl.d} if args.layers else {}),
+            **({"norm": "history"} if args.norm == "history" else {}),
             "parallelism": "single-gpu",
         },
         "roofline": roof,

@@ -49,6 +49,16 @@ typedef enum sa_status {
   SA_ERR_DEVICE = 4         /* a HIP call or kernel launch failed */
 } sa_status;
 
+/* Softmax axis of the assignment: SA_NORM_PROTOTYPES is Sketch Attention
+ * (section 2.1: each behaviour's weights over the k prototypes sum to one);
+ * SA_NORM_HISTORY is the comparator of section 3.1 (Figure 3, Table 1): the
+ * usual latent cross-attention, each prototype's weights over the user's n
+ * behaviours sum to one, everything else unchanged. */
+typedef enum sa_norm {
+  SA_NORM_PROTOTYPES = 0,
+  SA_NORM_HISTORY = 1
+} sa_norm;
+
 typedef enum sa_dtype {
   SA_F32 = 0,   /* float32 inputs, float32 matrix-core products */
   SA_BF16 = 1   /* bfloat16 inputs, float32 accumulation */
@@ -76,6 +86,17 @@ typedef enum sa_dtype {
  */
 sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype,
                     const void* P, const void* W_Q, const void* W_K, void* stream);
+
+/*
+ * sa_create_ex -- sa_create with a choice of softmax axis.  SA_NORM_HISTORY
+ * (the comparator) computes, per user, X~_j = sum_i a_ji x_i with
+ * a_ji = exp(S_ji) / sum_i' exp(S_ji') over the user's rows (an empty history
+ * gives zeros); it is implemented for SA_BF16 only (SA_ERR_UNSUPPORTED for
+ * SA_F32) over the same d and k range.  sa_compress_batch then computes that
+ * summary for the handle; all other behaviour is as for sa_create.
+ */
+sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype,
+                       const void* P, const void* W_Q, const void* W_K, sa_norm norm, void* stream);
 
 /*
  * sa_compress_batch -- sketches of a ragged batch of users (section 2.4).

@@ -26,11 +26,15 @@ SA_ERR_DEVICE = 4
 SA_F32 = 0
 SA_BF16 = 1
 
+SA_NORM_PROTOTYPES = 0  # Sketch Attention: softmax over the prototype axis
+SA_NORM_HISTORY = 1     # the comparator: softmax over the history axis
+_NORMS = {"prototypes": SA_NORM_PROTOTYPES, "history": SA_NORM_HISTORY}
+
 _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
 _DTYPE_NAMES = {"f32": SA_F32, "bf16": SA_BF16}
 
 EXPORTED = (
-    "sa_create", "sa_compress_batch", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
+    "sa_create", "sa_create_ex", "sa_compress_batch", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
     "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
     "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy", "sa_stack_set_kernel_timing",
     "sa_stack_read_kernel_timing",
@@ -68,6 +72,7 @@ def library() -> ctypes.CDLL:
     p_f64 = ctypes.POINTER(ctypes.c_double)
     sig = {
         "sa_create": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, vp]),
+        "sa_create_ex": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, i32, vp]),
         "sa_compress_batch": (i32, [vp, vp, vp, i32, vp, vp]),
         "sa_destroy": (None, [vp]),
         "sa_status_string": (ctypes.c_char_p, [i32]),
@@ -139,8 +144,11 @@ def sa_check_batch(k: int, offsets) -> int:
 
 
 def sa_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
-              stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
-    """Fold the weights into a new handle (see include/sa.h)."""
+              stream: Optional[torch.cuda.Stream] = None, norm: str = "prototypes") -> ctypes.c_void_p:
+    """Fold the weights into a new handle (see include/sa.h); norm "history"
+    selects the comparator (sa_create_ex with SA_NORM_HISTORY)."""
+    if norm not in _NORMS:
+        raise ValueError("norm must be 'prototypes' or 'history'")
     for t, n in ((P, "P"), (W_Q, "W_Q"), (W_K, "W_K")):
         _device_tensor(t, n)
     if P.dtype not in _DTYPES or W_Q.dtype != P.dtype or W_K.dtype != P.dtype:
@@ -152,9 +160,14 @@ def sa_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
         raise ValueError("W_Q and W_K must be [d, d]")
     h = ctypes.c_void_p()
     with torch.cuda.device(P.device):
-        st = library().sa_create(ctypes.byref(h), int(d), int(k), float(tau), _DTYPES[P.dtype],
-                                 ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
-                                 ctypes.c_void_p(W_K.data_ptr()), _stream_ptr(stream, P.device))
+        if norm == "prototypes":
+            st = library().sa_create(ctypes.byref(h), int(d), int(k), float(tau), _DTYPES[P.dtype],
+                                     ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
+                                     ctypes.c_void_p(W_K.data_ptr()), _stream_ptr(stream, P.device))
+        else:
+            st = library().sa_create_ex(ctypes.byref(h), int(d), int(k), float(tau), _DTYPES[P.dtype],
+                                        ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
+                                        ctypes.c_void_p(W_K.data_ptr()), _NORMS[norm], _stream_ptr(stream, P.device))
     _check(st, "sa_create")
     return h
 
@@ -222,8 +235,9 @@ class SketchAttention:
     """Owns one handle: the folded weights of one (P, W_Q, W_K, tau)."""
 
     def __init__(self, P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
-                 stream: Optional[torch.cuda.Stream] = None):
-        self.handle = sa_create(P, W_Q, W_K, tau, stream)
+                 stream: Optional[torch.cuda.Stream] = None, norm: str = "prototypes"):
+        self.handle = sa_create(P, W_Q, W_K, tau, stream, norm)
+        self.norm = norm
         self.k, self.d = int(P.shape[0]), int(P.shape[1])
         self.dtype = P.dtype
         self.device = P.device

@@ -33,6 +33,7 @@ struct sa_handle_s {
   int cu_count = 0;
   int groups_per_cu = 1;
   float tau = 0.f;
+  int norm = SA_NORM_PROTOTYPES;  // softmax axis
   Plan plan{};
   void* M = nullptr;           // folded matrix [k_pad][d], dtype
   float* workspace = nullptr;  // partial sketches
@@ -59,6 +60,32 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // folded matrix in registers.
 // SA_PLAN="kw,waves_k,waves_rows,m_in_lds[,kind[,prefetch[,row_blocks[,score_buffers]]]]"
 // in the environment overrides the choice when that plan is compiled.
+// The comparator (softmax over the history axis) runs the streamed pass with
+// waves that never split a tile's rows: eight waves over the prototypes,
+// 32 (d = 128, k <= 256; d = 64, k <= 256), 64 (k <= 512) or 128 (d = 64,
+// k <= 1024) prototypes each.
+Plan make_history_plan(int d, int k) {
+  Plan p{};
+  p.dtype = SA_BF16;
+  p.d = d;
+  p.k = k;
+  p.kind = 1;
+  p.prefetch = 1;
+  p.waves_k = 8;
+  p.waves_rows = 1;
+  if (k <= 256) {
+    p.kw = 32; p.row_blocks = 4; p.score_buffers = 2;
+  } else if (k <= 512) {
+    p.kw = 64; p.row_blocks = 2; p.score_buffers = d == 128 ? 1 : 2;
+  } else {
+    p.kw = 128; p.row_blocks = 2; p.score_buffers = 1;
+  }
+  p.m_in_lds = 0;
+  p.k_pad = p.kw * p.waves_k;
+  p.tile_rows = 16 * p.row_blocks;
+  return p;
+}
+
 Plan make_plan(int dtype, int d, int k) {
   Plan p{};
   p.dtype = dtype;
@@ -202,12 +229,14 @@ SA_API sa_status sa_check_batch(int32_t k, const int64_t* offsets, int32_t num_u
   return check_batch(offsets, num_users);
 }
 
-SA_API sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype, const void* P,
-                           const void* W_Q, const void* W_K, void* stream) {
+SA_API sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype, const void* P,
+                              const void* W_Q, const void* W_K, sa_norm norm, void* stream) {
   if (out == nullptr) return SA_ERR_INVALID_ARG;
   *out = nullptr;
   sa_status st = check_config(d, k, tau, dtype);
   if (st != SA_OK) return st;
+  if (norm != SA_NORM_PROTOTYPES && norm != SA_NORM_HISTORY) return SA_ERR_INVALID_ARG;
+  if (norm == SA_NORM_HISTORY && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   if (P == nullptr || W_Q == nullptr || W_K == nullptr) return SA_ERR_INVALID_ARG;
   if (!aligned16(P) || !aligned16(W_Q) || !aligned16(W_K)) return SA_ERR_INVALID_ARG;
 
@@ -215,7 +244,8 @@ SA_API sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_d
   if (h == nullptr) return SA_ERR_OUT_OF_MEMORY;
   hipStream_t s = static_cast<hipStream_t>(stream);
   h->tau = tau;
-  h->plan = make_plan((int)dtype, d, k);
+  h->norm = norm;
+  h->plan = norm == SA_NORM_HISTORY ? make_history_plan(d, k) : make_plan((int)dtype, d, k);
   const size_t elem = dtype == SA_BF16 ? 2 : 4;
   float* tmp = nullptr;
   hipDeviceProp_t prop;
@@ -252,6 +282,11 @@ SA_API sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_d
   return SA_OK;
 }
 
+SA_API sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype, const void* P,
+                           const void* W_Q, const void* W_K, void* stream) {
+  return sa_create_ex(out, d, k, tau, dtype, P, W_Q, W_K, SA_NORM_PROTOTYPES, stream);
+}
+
 SA_API void sa_destroy(sa_handle h) {
   if (h == nullptr) return;
   DeviceGuard guard(h->device);
@@ -280,7 +315,9 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
 
   const Plan& plan = h->plan;
   const size_t elem = plan.dtype == SA_BF16 ? 2 : 4;
-  const size_t slot_bytes = (size_t)plan.k_pad * plan.d * sizeof(float);
+  const bool hist = h->norm == SA_NORM_HISTORY;
+  // a partial slot: the k_pad x d accumulator, plus per-prototype maxima and sums for the comparator
+  const size_t slot_bytes = (size_t)plan.k_pad * (plan.d + (hist ? 2 : 0)) * sizeof(float);
 
   // Workspace for the largest launch of this call.
   size_t need = 0;
@@ -321,6 +358,7 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     fa.X = static_cast<const char*>(X) + (size_t)base * plan.d * elem;
     fa.M = static_cast<const char*>(M) + (size_t)u0 * (size_t)m_stride * elem;
     fa.m_stride = m_stride;
+    fa.history_softmax = hist ? 1 : 0;
     fa.partial = h->workspace;
     fa.rows = rows;
     fa.users = nu;
@@ -328,6 +366,7 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     sa::ReduceArgs ra;
     std::memset(&ra, 0, sizeof(ra));
     ra.partial = h->workspace;
+    ra.history_softmax = hist ? 1 : 0;
     ra.out = out + (size_t)u0 * plan.k * plan.d;
     ra.rows = rows;
     ra.users = nu;

@@ -37,6 +37,7 @@ struct FusedArgs {
   const void* X;        // rows of this launch, [rows][d]
   const void* M;        // folded matrix [k_pad][d] in the dtype, or one per user (m_stride apart)
   int64_t m_stride;     // elements between the folded matrices of consecutive users; 0: one shared matrix
+  int32_t history_softmax;  // 1: the comparator (softmax over the history axis); partial slots of k_pad (d + 2) floats
   float* partial;       // [slots][k_pad * d] float32, slot = group + user
   int64_t rows;         // rows in this launch (offsets[users])
   int32_t users;        // users in this launch (<= kMaxUsersPerLaunch)
@@ -46,6 +47,7 @@ struct FusedArgs {
 
 struct ReduceArgs {
   const float* partial;  // as above
+  int32_t history_softmax;  // partial slots carry (acc, max, sum) per prototype: merge and divide
   float* out;            // [users][k][d] float32
   int64_t rows;
   int32_t users;

@@ -145,9 +145,91 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
     if (j0 + r < a.k) o[(int64_t)(j0 + r) * a.d + c] = s[r];
 }
 
-hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+// Comparator (softmax over the history axis): slot s of user u holds, for
+// every prototype j, acc_s = sum_i 2^(s'_ji - m_s) x_i over its rows (lane
+// layout as above), the maximum m_s[j] it used and l_s[j] = sum_i 2^(s'_ji -
+// m_s).  The user's summary is sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M)
+// l_s with M the largest m_s; zero when no slot saw a row.  One thread per
+// float4 of the slot layout (four prototypes, one column) and per share of
+// the user's slots; each share merges its slots in order with a running
+// maximum, then share 0 merges the shares in order (fixed order throughout).
+struct HistPart {
+  float m, l, a;
+};
+__device__ __forceinline__ void hist_merge(HistPart& x, float m, float l, float a) {
+  if (m == -INFINITY) return;  // nothing seen
+  const float mn = fmaxf(x.m, m);
+  const float sa = x.m == -INFINITY ? 0.f : exp2f(x.m - mn);
+  const float sb = exp2f(m - mn);
+  x.a = x.a * sa + a * sb;
+  x.l = x.l * sa + l * sb;
+  x.m = mn;
+}
+
+__global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_kernel(ReduceArgs a) {
+  __shared__ HistPart part[kReduceShares][kReduceLanes][4];
+  const int shares = blockDim.x / kReduceLanes;
+  const int u = blockIdx.y;
   const int slot_f4 = a.k_pad * a.d / 4;
+  const int64_t slot_floats = (int64_t)a.k_pad * (a.d + 2);
+  const int lane = threadIdx.x % kReduceLanes;
+  const int q = threadIdx.x / kReduceLanes;
+  const int p = blockIdx.x * kReduceLanes + lane;
+  int t = p >> 6;
+  const int cbs = a.d / 16, jbs = a.kw / 16;
+  const int cb = t % cbs;
+  t /= cbs;
+  const int jb = t % jbs;
+  const int wj = t / jbs;
+  const int l = p & 63;
+  const int j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);
+  const int c = 16 * cb + (l & 15);
+  HistPart x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = HistPart{-INFINITY, 0.f, 0.f};
+  const int64_t r0 = a.offsets[u], r1 = a.offsets[u + 1];
+  if (r1 > r0 && p < slot_f4) {
+    const int64_t G = a.groups, R = a.rows;
+    const int64_t b0 = ((r0 + 1) * G - 1) / R;
+    const int64_t b1 = (r1 * G - 1) / R;
+    const int64_t n = b1 - b0 + 1;
+    const int64_t q0 = n * q / shares, q1 = n * (q + 1) / shares;
+    for (int64_t i = q0; i < q1; ++i) {
+      const float* slot = a.partial + (b0 + i + u) * slot_floats;
+      const f32x4 v = reinterpret_cast<const f32x4*>(slot)[p];
+      const float* stats = slot + (int64_t)a.k_pad * a.d;
+      const f32x4 ms = *reinterpret_cast<const f32x4*>(stats + j0);
+      const f32x4 ls = *reinterpret_cast<const f32x4*>(stats + a.k_pad + j0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hist_merge(x[r], ms[r], ls[r], v[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[q][lane][r] = x[r];
+  __syncthreads();
+  if (q != 0 || p >= slot_f4) return;
+  for (int w = 1; w < shares; ++w)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hist_merge(x[r], part[w][lane][r].m, part[w][lane][r].l, part[w][lane][r].a);
+  float* o = a.out + (int64_t)u * a.k * a.d;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (j0 + r < a.k) o[(int64_t)(j0 + r) * a.d + c] = x[r].l > 0.f ? x[r].a / x[r].l : 0.f;
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int64_t per_user = (a.groups + a.users) / (a.users > 0 ? a.users : 1);
+  if (a.history_softmax) {
+    int shares = 1;
+    while (shares < kReduceShares && 8 * shares < per_user) shares *= 2;
+    const dim3 grid((a.k_pad * a.d / 4 + kReduceLanes - 1) / kReduceLanes, a.users), block(kReduceLanes * shares);
+    if (start || stop)
+      hipExtLaunchKernelGGL(reduce_history_kernel, grid, block, 0, stream, start, stop, 0, a);
+    else
+      hipLaunchKernelGGL(reduce_history_kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const int slot_f4 = a.k_pad * a.d / 4;
   int shares = 1;
   while (shares < kReduceShares && 8 * 2 * shares <= per_user) shares *= 2;
   const dim3 grid((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users), block(kReduceLanes * shares);

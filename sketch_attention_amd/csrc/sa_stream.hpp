@@ -173,8 +173,9 @@ struct StreamGeom {
 
 // PU: one folded matrix per user (args.m_stride apart) instead of one shared
 // matrix; a separate instantiation so the shared case carries none of its
-// bookkeeping.
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU>
+// bookkeeping.  HS: the comparator of section 3.1, the softmax taken over the
+// history axis instead of the prototype axis (see the main loop below).
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU, bool HS = false>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args) {
   using G = StreamGeom<D, KW, WJ, WI, RB, PF, SB>;
   using MF = Mfma<bf16>;
@@ -617,7 +618,136 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     if constexpr (PU) cursor_next(ca);
   };
 
-  if constexpr (SB == 2) {
+  if constexpr (HS) {
+    // ---- comparator: A_ji = 2^(s'_ji) / sum_i' 2^(s'_ji') over the rows of
+    // the user, i.e. a softmax over the history for each prototype.  Each
+    // wave owns its prototypes for every row of a tile (no row split), so the
+    // normalisation needs no exchange between waves: per prototype a running
+    // maximum hm (raised lazily, only when a tile exceeds it by more than
+    // 2^8, which bounds every weight by 256) and per lane a partial sum hl of
+    // 2^(s' - hm) over the rows it holds; the accumulator is kept in the
+    // scale of hm.  A piece's partial carries (acc, hm, sum hl); the
+    // reduction merges the pieces of a user with their maxima.
+    static_assert(WI == 1, "the history softmax keeps whole tile columns in one wave");
+    float hm[JB], hl[JB];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      hm[jb] = -INFINITY;
+      hl[jb] = 0.f;
+    }
+    f32x4 S[RB][JB];
+    bf16x8 a[RB / 2][JB];
+    // weights of the tile at cursor c from its scores in S (rows past the piece excluded)
+    auto hs_weights = [&](const Cursor& c) {
+      const int64_t nv = c.end - c.row;
+      if (nv < NT) {
+#pragma unroll
+        for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = (int64_t)(rw + 16 * ib + 4 * g + r) < nv;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) S[ib][jb][r] = ok ? S[ib][jb][r] : -INFINITY;
+          }
+      }
+      float mnew[JB];
+      bool grow = false;
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        float tm = S[0][jb][0];
+#pragma unroll
+        for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tm = fmaxf(tm, S[ib][jb][r]);
+        tm = fmaxf(tm, __shfl_xor(tm, 16));
+        tm = fmaxf(tm, __shfl_xor(tm, 32));
+        mnew[jb] = fmaxf(hm[jb], tm);
+        grow |= mnew[jb] > hm[jb] + 8.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // a piece's first tile, or a jump of the maximum
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const float alpha = hm[jb] == -INFINITY ? 0.f : fast_exp2(hm[jb] - mnew[jb]);
+          hl[jb] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * g + r);  // factor of prototype 16 jb + 4 g + r
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[jb][cb][r] *= ar;
+          }
+          hm[jb] = mnew[jb];
+        }
+      }
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const float mu = hm[jb] == -INFINITY ? 0.f : hm[jb];  // all-padding prototypes: weights 0
+#pragma unroll
+        for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(S[ib][jb][r] - mu);
+            S[ib][jb][r] = e;
+            hl[jb] += e;
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < RB / 2; ++h)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[h][jb][e] = (bf16)S[2 * h + (e >> 2)][jb][e & 3];
+    };
+    // partial of one piece: acc in the lane layout, then the maxima and the
+    // sums of every prototype of the slot
+    auto hs_flush = [&](int u) {
+      float* dst = args.partial + (grp + u) * (int64_t)(G::KPAD * (D + 2));
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          *reinterpret_cast<f32x4*>(dst + (((wj * JB + jb) * CB + cb) * 64 + lane) * 4) = acc[jb][cb];
+          acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        float lt = hl[jb] + __shfl_xor(hl[jb], 16);
+        lt += __shfl_xor(lt, 32);
+        if (g == 0) {
+          dst[G::KPAD * D + jbase + 16 * jb + l16] = hm[jb];
+          dst[G::KPAD * D + G::KPAD + jbase + 16 * jb + l16] = lt;
+        }
+        hm[jb] = -INFINITY;
+        hl[jb] = 0.f;
+      }
+    };
+    wait_tiles(std::integral_constant<int, NS - 2>{});
+    __syncthreads();
+    affinity(S, slot_of(0));
+    hs_weights(ca);
+    cursor_next(ca);
+    wait_tiles(std::integral_constant<int, NS - 3>{});
+    __syncthreads();
+    // Step t: DMA of tile t+NS-1, aggregation of tile t with the weights made
+    // in the step before, the piece's partial when tile t ends it (before the
+    // next tile starts a new piece's maxima), affinity and weights of tile
+    // t+1, wait for tile t+2, one barrier (the ring only).
+    int q0 = 0;
+    for (int t = 0; t < ntot; ++t) {
+      const int q1 = q0 + 1 < NS ? q0 + 1 : 0;
+      const int qn = q0 == 0 ? NS - 1 : q0 - 1;
+      issue_tile(cl, qn);
+      aggregate(acc, a, slot_of(q0));
+      if (cc.row + NT >= cc.end) hs_flush(cc.u);
+      if (t + 1 < ntot) {
+        affinity(S, slot_of(q1));
+        hs_weights(ca);
+      }
+      cursor_next(ca);
+      cursor_next(cc);
+      cursor_next(cl);
+      q0 = q1;
+      wait_tiles(std::integral_constant<int, NS - 3>{});  // tile t+2
+      __syncthreads();
+    }
+  } else if constexpr (SB == 2) {
     f32x4 S0[RB][JB], S1[RB][JB];
     ensure_m(false);
     wait_tiles(std::integral_constant<int, NS - 2>{});
@@ -724,22 +854,27 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   wait_vm<0>();  // no DMA outlives the work group
 }
 
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU>
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU, bool HS>
 hipError_t launch_stream_pu(const FusedArgs& a, const Launch& l) {
   constexpr int threads = 64 * WJ * WI;
   if (l.start || l.stop) {
-    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU>), dim3(l.groups), dim3(threads), 0,
+    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU, HS>), dim3(l.groups), dim3(threads), 0,
                           l.stream, l.start, l.stop, 0, a);
   } else {
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU>), dim3(l.groups), dim3(threads), 0,
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU, HS>), dim3(l.groups), dim3(threads), 0,
                        l.stream, a);
   }
   return hipGetLastError();
 }
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
 hipError_t launch_stream_t(const FusedArgs& a, const Launch& l) {
-  return a.m_stride != 0 ? launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, true>(a, l)
-                         : launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false>(a, l);
+  if constexpr (WI == 1) {
+    if (a.history_softmax) return launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false, true>(a, l);
+  } else {
+    if (a.history_softmax) return hipErrorInvalidValue;
+  }
+  return a.m_stride != 0 ? launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, true, false>(a, l)
+                         : launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false, false>(a, l);
 }
 
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
@@ -747,12 +882,12 @@ hipError_t run_stream_plan(const Plan& p, const FusedArgs& a, const Launch& l, i
   constexpr int threads = 64 * WJ * WI;
   if (p.k == p.k_pad) {
     if (occ)
-      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false, false>,
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, false, false, false>,
                                                           threads, 0);
     return launch_stream_t<D, KW, WJ, WI, RB, PF, SB, false>(a, l);
   }
   if (occ)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true, false>,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, true, false, false>,
                                                         threads, 0);
   return launch_stream_t<D, KW, WJ, WI, RB, PF, SB, true>(a, l);
 }

@@ -107,6 +107,18 @@ def test_null_handle_paths_return_errors_without_device_work():
     lib.sa_destroy(None)  # NULL-safe
 
 
+def test_create_ex_validates_before_device_work():
+    lib = B.library()
+    f = ctypes.c_float(0.1)
+    h = ctypes.c_void_p(77)
+    assert lib.sa_create_ex(None, 128, 16, f, 1, None, None, None, 1, None) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_create_ex(ctypes.byref(h), 128, 16, f, 1, None, None, None, 7, None) == B.SA_ERR_INVALID_ARG
+    assert h.value is None
+    # the comparator is implemented for bf16 only
+    assert lib.sa_create_ex(ctypes.byref(h), 128, 16, f, 0, None, None, None, 1, None) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_create_ex(ctypes.byref(h), 96, 16, f, 1, None, None, None, 1, None) == B.SA_ERR_UNSUPPORTED
+
+
 def test_stack_entry_points_validate_before_device_work():
     lib = B.library()
     f = ctypes.c_float(0.1)
