@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Plan of the fused pass for a supported (dtype, d, k).
 // bf16 with k > 32: the streamed pass (sa_stream.hpp), eight waves per group
-// (four for d = 128, k <= 64).  Up to k = 256 (d = 128) or 512 (d = 64) each
+// (four for d = 128, k <= 128).  Up to k = 256 (d = 128) or 512 (d = 64) each
 // wave holds 32 prototypes (64 for d = 64 above k = 256), the folded matrix
 // in registers and two affinity tiles in flight; above that (k <= 512 for
 // d = 128, k <= 1024 for d = 64) each wave holds k_pad / 8 prototypes, one
@@ -61,8 +61,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // SA_PLAN="kw,waves_k,waves_rows,m_in_lds[,kind[,prefetch[,row_blocks[,score_buffers]]]]"
 // in the environment overrides the choice when that plan is compiled.
 // The comparator (softmax over the history axis) runs the streamed pass with
-// waves that never split a tile's rows: eight waves over the prototypes,
-// 32 (d = 128, k <= 256; d = 64, k <= 256), 64 (k <= 512) or 128 (d = 64,
+// waves that never split a tile's rows: four waves of 32 prototypes for
+// k <= 128, else eight waves of 32 (k <= 256), 64 (k <= 512) or 128 (d = 64,
 // k <= 1024) prototypes each.
 Plan make_history_plan(int d, int k) {
   Plan p{};
@@ -73,7 +73,9 @@ Plan make_history_plan(int d, int k) {
   p.prefetch = 1;
   p.waves_k = 8;
   p.waves_rows = 1;
-  if (k <= 256) {
+  if (k <= 128) {
+    p.kw = 32; p.waves_k = 4; p.row_blocks = 4; p.score_buffers = 2;  // four-wave groups, two per CU
+  } else if (k <= 256) {
     p.kw = 32; p.row_blocks = 4; p.score_buffers = 2;
   } else if (k <= 512) {
     p.kw = 64; p.row_blocks = 2; p.score_buffers = d == 128 ? 1 : 2;
@@ -108,11 +110,14 @@ Plan make_plan(int dtype, int d, int k) {
     } else {
       p.kw = (d == 64 && k > 256) ? 64 : 32;
       p.waves_k = k <= 64 ? 2 : (k <= 128 ? 4 : 8);
-      p.row_blocks = (p.kw == 32 && (p.waves_k == 8 || (d == 64 && p.waves_k == 4))) ? 4 : 2;
+      p.row_blocks = (p.kw == 32 && (p.waves_k == 8 || p.waves_k == 4)) ? 4 : 2;
     }
     // d = 128, k <= 64: two row waves (four waves per group) keep the four
-    // 64-row LDS tiles of the ring within budget
-    p.waves_rows = (d == 128 && p.waves_k == 2) ? 2 : waves / p.waves_k;
+    // 64-row LDS tiles of the ring within budget; d = 128, k <= 128: four
+    // waves over the prototypes and none over the rows, two groups per CU
+    // (measured faster than eight waves split 4 x 2: 248 against 273 us on
+    // the ragged workload)
+    p.waves_rows = (d == 128 && p.waves_k == 2) ? 2 : (d == 128 && p.waves_k == 4) ? 1 : waves / p.waves_k;
   } else if (k16 <= 16) {
     p.kw = 16; p.waves_k = 1;
   } else if (k16 <= 32) {

@@ -6,7 +6,7 @@
 
 namespace sa {
 
-#define SA_PLANS(X) X(128, 32, 8, 1, 4, 1, 2) X(128, 32, 8, 1, 2, 1, 2) X(128, 32, 4, 2, 2, 1, 2) X(128, 32, 2, 2, 2, 1, 2) X(128, 64, 8, 1, 2, 1, 1)
+#define SA_PLANS(X) X(128, 32, 8, 1, 4, 1, 2) X(128, 32, 4, 1, 4, 1, 2) X(128, 32, 8, 1, 2, 1, 2) X(128, 32, 4, 2, 2, 1, 2) X(128, 32, 2, 2, 2, 1, 2) X(128, 64, 8, 1, 2, 1, 1)
 
 hipError_t dispatch_stream_d128(const Plan& p, const FusedArgs& a, const Launch& l, int* occ) {
   SA_PLANS(SA_STREAM_PLAN)

@@ -5,7 +5,7 @@
 
 namespace sa {
 
-#define SA_PLANS(X) X(64, 64, 8, 1, 2, 1, 2) X(64, 32, 8, 1, 4, 1, 2) X(64, 32, 4, 2, 4, 1, 2) X(64, 32, 2, 4, 2, 1, 2) X(64, 128, 8, 1, 2, 1, 1)
+#define SA_PLANS(X) X(64, 64, 8, 1, 2, 1, 2) X(64, 32, 4, 1, 4, 1, 2) X(64, 32, 8, 1, 4, 1, 2) X(64, 32, 4, 2, 4, 1, 2) X(64, 32, 2, 4, 2, 1, 2) X(64, 128, 8, 1, 2, 1, 1)
 
 hipError_t dispatch_stream_d64(const Plan& p, const FusedArgs& a, const Launch& l, int* occ) {
   SA_PLANS(SA_STREAM_PLAN)
