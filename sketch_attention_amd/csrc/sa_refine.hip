@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const float* a, int64_t a_p
 
 // ------------------------------------------------------------ small products
 // C = A B for row-major A [M][K] and B given transposed, Bt [N][K], float32
-// matrix cores (16x16x4), one wave per work group owning a 16 x 32 tile so
+// matrix cores (16x16x4), one wave per work group owning a 16 x 16 NB tile so
 // that these small products still spread over the compute units.  Reduction
 // slot (g, s) of a 16-column chunk k0 is column k0 + 4 g + s of both
 // operands, so each lane reads four consecutive floats of a row.  Rows of A
@@ -99,28 +99,28 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const float* a, int64_t a_p
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 enum { EPI_STORE = 0, EPI_GATED = 1, EPI_FOLD = 2 };
 
-template <int EPI, typename T>
+template <int EPI, typename T, int NB = 2>
 __global__ __launch_bounds__(64) void small_gemm_kernel(const float* A, int64_t M, int K, const float* Bt0,
                                                         const float* Bt1, int N, T* C, float scale, int k, int k_pad) {
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.y * 16;
-  const int col0 = blockIdx.x * 32;
+  const int col0 = blockIdx.x * 16 * NB;
   const int64_t arow = row0 + l16;
   // four partial sums per block (slot s of each chunk), added at the end:
   // four independent chains instead of one long dependent one
-  f32x4_t acc0[2][4], acc1[2][4];
+  f32x4_t acc0[NB][4], acc1[NB][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc0[j][s] = acc1[j][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4  // loads of several chunks in flight
   for (int k0 = 0; k0 < K; k0 += 16) {
     const f32x4_t a = arow < M ? *reinterpret_cast<const f32x4_t*>(A + arow * K + k0 + 4 * g)
                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t b0[2], b1[2];
+    f32x4_t b0[NB], b1[NB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NB; ++j) {
       b0[j] = *reinterpret_cast<const f32x4_t*>(Bt0 + (int64_t)(col0 + 16 * j + l16) * K + k0 + 4 * g);
       if constexpr (EPI == EPI_GATED)
         b1[j] = *reinterpret_cast<const f32x4_t*>(Bt1 + (int64_t)(col0 + 16 * j + l16) * K + k0 + 4 * g);
@@ -128,15 +128,15 @@ __global__ __launch_bounds__(64) void small_gemm_kernel(const float* A, int64_t 
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NB; ++j) {
         acc0[j][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b0[j][s], acc0[j][s], 0, 0, 0);
         if constexpr (EPI == EPI_GATED)
           acc1[j][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b1[j][s], acc1[j][s], 0, 0, 0);
       }
   }
-  f32x4_t sum0[2], sum1[2];
+  f32x4_t sum0[NB], sum1[NB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NB; ++j) {
     sum0[j] = (acc0[j][0] + acc0[j][1]) + (acc0[j][2] + acc0[j][3]);
     sum1[j] = (acc1[j][0] + acc1[j][1]) + (acc1[j][2] + acc1[j][3]);
   }
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64) void small_gemm_kernel(const float* A, int64_t 
     const int64_t row = row0 + 4 * g + r;
     if (row >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int col = col0 + 16 * j + l16;
       float v = sum0[j][r];
       if constexpr (EPI == EPI_GATED) {
@@ -210,7 +210,8 @@ hipError_t launch_ffn(const float* Z, int64_t rows, int d, int d_ff, const float
   const unsigned gy = (unsigned)((rows + 15) / 16);
   hipLaunchKernelGGL((small_gemm_kernel<EPI_GATED, float>), dim3(d_ff / 32, gy), dim3(64), 0, s, Z, rows, d, gate_t,
                      up_t, d_ff, H, 1.f, 0, 0);
-  hipLaunchKernelGGL((small_gemm_kernel<EPI_STORE, float>), dim3(d / 32, gy), dim3(64), 0, s, H, rows, d_ff, down_t,
+  // the down projection has few output columns and a long reduction: one 16 x 16 block per wave
+  hipLaunchKernelGGL((small_gemm_kernel<EPI_STORE, float, 1>), dim3(d / 16, gy), dim3(64), 0, s, H, rows, d_ff, down_t,
                      nullptr, d, F, 1.f, 0, 0);
   return hipGetLastError();
 }
