@@ -94,15 +94,18 @@ def cpu_baseline(wl, budget_s: float, layers=None, norm: str = "prototypes"):
 
 
 def kernel_source_hash(dtype: str = "bf16", d: int = 128) -> str:
-    """sha256 over the sources and build flags that decide the fused kernel a launch runs."""
+    """sha256 over the sources and compiler options that decide the fused kernel
+    a launch runs (include paths left out: they differ between checkouts)."""
+    from sketch_attention_amd import build as _build
     names = ["sa_fused.hpp", "sa_stream.hpp", f"sa_fused_{dtype}_d{d}.hip", f"sa_stream_d{d}.hip", "sa_kernels.hip",
              "sa_internal.h", "sa_api.cpp"]
     files = [os.path.join(CSRC, f) for f in names if os.path.exists(os.path.join(CSRC, f))]
-    files.append(os.path.join(ROOT, "sketch_attention_amd", "build.py"))
     h = hashlib.sha256()
     for f in files:
         with open(f, "rb") as fh:
             h.update(fh.read())
+    flags = [f for f in _build.HIPCC_FLAGS if not f.startswith("-I")]
+    h.update(repr((flags, sorted(_build.VGPR_FORM))).encode())
     return h.hexdigest()
 
 
