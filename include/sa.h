@@ -244,6 +244,60 @@ void sa_stack_destroy(sa_stack h);
 sa_status sa_stack_set_kernel_timing(sa_stack h, int32_t enable);
 sa_status sa_stack_read_kernel_timing(sa_stack h, double* fused_ms, double* reduce_ms, int64_t* fused_launches);
 
+/*
+ * Backward pass (training miss path).  The close-reading page trains the
+ * compression end to end through the fused kernel (sections 2.2 and 2.4);
+ * the gradients follow from the definitions of section 2.1 by the chain
+ * rule.  For user u with sketch X~_u = A_u X_u and upstream gradient
+ * G_u = dL/dX~_u (k x d):
+ *   dA = G_u X_u^T, c_i = sum_j A_ji dA_ji, dS = A * (dA - c)
+ *   dX_u = A^T G_u + tau dS^T (P W_Q) W_K^T
+ *   dP = dQ W_Q^T, dW_Q = P^T dQ, dW_K = tau X^T dS^T (P W_Q), dQ = tau dS X W_K
+ * with the weight gradients summed over the users of the batch.
+ *
+ * sa_grad_check_config -- what sa_grad_create returns for these scalars:
+ * SA_BF16 only, d in {64, 128}, 1 <= k <= 256 (else SA_ERR_UNSUPPORTED or
+ * SA_ERR_INVALID_ARG as for sa_check_config).
+ *
+ * sa_grad_create -- prepare the weights once (device pointers in the dtype,
+ * as for sa_create; they are not used after the call returns).  The work is
+ * enqueued on stream and synchronised before returning.
+ */
+typedef struct sa_grad_s* sa_grad;
+sa_status sa_grad_check_config(int32_t d, int32_t k, float tau, sa_dtype dtype);
+sa_status sa_grad_create(sa_grad* out, int32_t d, int32_t k, float tau, sa_dtype dtype, const void* P,
+                         const void* W_Q, const void* W_K, void* stream);
+
+/*
+ * sa_grad_compute -- gradients of L for one ragged batch.
+ *
+ *   X            device, bf16 [offsets[num_users]][d], as for sa_compress_batch
+ *   offsets      host, int64 [num_users + 1], as for sa_compress_batch
+ *   grad_sketch  device, float32 [num_users][k][d], dL/dX~ per user
+ *   grad_X       device, bf16 [offsets[num_users]][d], fully overwritten
+ *   grad_P       device, float32 [k][d]; grad_W_Q, grad_W_K float32 [d][d];
+ *                fully overwritten (zero for a batch without rows)
+ * All device buffers 16-byte aligned; X and grad_X may be NULL when the
+ * batch has no rows.  The work is only enqueued on stream.  Calls on one
+ * handle share its workspace and must not overlap (one stream at a time).
+ * Errors: SA_ERR_INVALID_ARG for bad arguments (nothing enqueued),
+ * SA_ERR_OUT_OF_MEMORY when the workspace cannot grow, SA_ERR_DEVICE for a
+ * failed launch.
+ */
+sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offsets, int32_t num_users,
+                          const float* grad_sketch, void* grad_X, float* grad_P, float* grad_W_Q, float* grad_W_K,
+                          void* stream);
+
+/* sa_grad_set_kernel_timing / sa_grad_read_kernel_timing -- HIP events on the
+ * dispatches of the two streamed passes of the last launch of each call
+ * (read synchronises them): milliseconds summed over the calls since the
+ * last read, and the number of such calls. */
+sa_status sa_grad_set_kernel_timing(sa_grad h, int32_t enable);
+sa_status sa_grad_read_kernel_timing(sa_grad h, double* stats_ms, double* dx_ms, int64_t* calls);
+
+/* sa_grad_destroy -- free the handle (NULL allowed) after its streams are synchronised. */
+void sa_grad_destroy(sa_grad h);
+
 #ifdef __cplusplus
 }
 #endif

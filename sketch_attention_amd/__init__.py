@@ -8,6 +8,7 @@ be used without it; any call into the binding fails loudly when it is absent.
 from .binding import (  # noqa: F401
     SAError,
     SketchAttention,
+    SketchAttentionGrad,
     SketchStack,
     sa_check_batch,
     sa_check_config,
@@ -16,6 +17,10 @@ from .binding import (  # noqa: F401
     sa_describe_plan,
     sa_destroy,
     sa_get_folded,
+    sa_grad_check_config,
+    sa_grad_compute,
+    sa_grad_create,
+    sa_grad_destroy,
     sa_read_kernel_timing,
     sa_set_kernel_timing,
     sa_stack_compress_batch,

@@ -38,6 +38,8 @@ EXPORTED = (
     "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
     "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy", "sa_stack_set_kernel_timing",
     "sa_stack_read_kernel_timing",
+    "sa_grad_check_config", "sa_grad_create", "sa_grad_compute", "sa_grad_destroy", "sa_grad_set_kernel_timing",
+    "sa_grad_read_kernel_timing",
 )
 
 
@@ -88,6 +90,12 @@ def library() -> ctypes.CDLL:
         "sa_stack_destroy": (None, [vp]),
         "sa_stack_set_kernel_timing": (i32, [vp, i32]),
         "sa_stack_read_kernel_timing": (i32, [vp, p_f64, p_f64, p_i64]),
+        "sa_grad_check_config": (i32, [i32, i32, f32, i32]),
+        "sa_grad_create": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, vp]),
+        "sa_grad_compute": (i32, [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]),
+        "sa_grad_destroy": (None, [vp]),
+        "sa_grad_set_kernel_timing": (i32, [vp, i32]),
+        "sa_grad_read_kernel_timing": (i32, [vp, p_f64, p_f64, p_i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -379,6 +387,114 @@ class SketchStack:
     def close(self) -> None:
         if getattr(self, "handle", None) is not None:
             sa_stack_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------ backward pass
+def sa_grad_check_config(d: int, k: int, tau: float, dtype: Union[str, torch.dtype]) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else _DTYPE_NAMES.get(dtype, 99)
+    return int(library().sa_grad_check_config(int(d), int(k), float(tau), code))
+
+
+def sa_grad_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
+                   stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    """Prepare the weights of the backward pass (bfloat16 only; see include/sa.h)."""
+    for t, n in ((P, "P"), (W_Q, "W_Q"), (W_K, "W_K")):
+        _device_tensor(t, n)
+    if P.dtype not in _DTYPES or W_Q.dtype != P.dtype or W_K.dtype != P.dtype or P.dim() != 2:
+        raise ValueError("P [k, d], W_Q and W_K [d, d] must share one dtype")
+    k, d = P.shape
+    if tuple(W_Q.shape) != (d, d) or tuple(W_K.shape) != (d, d):
+        raise ValueError("W_Q and W_K must be [d, d]")
+    h = ctypes.c_void_p()
+    with torch.cuda.device(P.device):
+        st = library().sa_grad_create(ctypes.byref(h), int(d), int(k), float(tau), _DTYPES[P.dtype],
+                                      ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
+                                      ctypes.c_void_p(W_K.data_ptr()), _stream_ptr(stream, P.device))
+    _check(st, "sa_grad_create")
+    return h
+
+
+def sa_grad_compute(handle: ctypes.c_void_p, X: torch.Tensor, offsets, grad_sketch: torch.Tensor,
+                    grad_X: torch.Tensor, grad_P: torch.Tensor, grad_W_Q: torch.Tensor, grad_W_K: torch.Tensor,
+                    stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Enqueue the gradients of one packed batch (argument meaning as in include/sa.h)."""
+    offs = _offsets_array(offsets)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    for t, n in ((X, "X"), (grad_sketch, "grad_sketch"), (grad_X, "grad_X"), (grad_P, "grad_P"),
+                 (grad_W_Q, "grad_W_Q"), (grad_W_K, "grad_W_K")):
+        _device_tensor(t, n)
+    if X.dim() != 2 or X.shape[0] != int(offs[-1]) or tuple(grad_X.shape) != tuple(X.shape) or grad_X.dtype != X.dtype:
+        raise ValueError("X and grad_X must be [offsets[-1], d] of one dtype")
+    if grad_sketch.dtype != torch.float32 or grad_sketch.dim() != 3 or grad_sketch.shape[0] != offs.size - 1:
+        raise ValueError("grad_sketch must be float32 [num_users, k, d]")
+    for t in (grad_P, grad_W_Q, grad_W_K):
+        if t.dtype != torch.float32:
+            raise ValueError("weight gradients are float32")
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    st = library().sa_grad_compute(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, grad_sketch.data_ptr(),
+                                   grad_X.data_ptr(), grad_P.data_ptr(), grad_W_Q.data_ptr(), grad_W_K.data_ptr(),
+                                   stream.cuda_stream)
+    _check(st, "sa_grad_compute")
+
+
+def sa_grad_destroy(handle: Optional[ctypes.c_void_p]) -> None:
+    if handle is not None and handle.value:
+        library().sa_grad_destroy(handle)
+
+
+def sa_grad_set_kernel_timing(handle: ctypes.c_void_p, enable: bool) -> None:
+    _check(library().sa_grad_set_kernel_timing(handle, 1 if enable else 0), "sa_grad_set_kernel_timing")
+
+
+def sa_grad_read_kernel_timing(handle: ctypes.c_void_p):
+    """Returns (stats_ms_total, dx_ms_total, calls) since the last read."""
+    a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(library().sa_grad_read_kernel_timing(handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)),
+           "sa_grad_read_kernel_timing")
+    return a.value, b.value, n.value
+
+
+class SketchAttentionGrad:
+    """Owns one backward handle: gradients of the sketches of one (P, W_Q, W_K, tau)."""
+
+    def __init__(self, P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.handle = sa_grad_create(P, W_Q, W_K, tau, stream)
+        self.k, self.d = int(P.shape[0]), int(P.shape[1])
+        self.dtype = P.dtype
+        self.device = P.device
+
+    def backward(self, X: torch.Tensor, offsets, grad_sketch: torch.Tensor,
+                 stream: Optional[torch.cuda.Stream] = None):
+        """Returns (grad_X, grad_P, grad_W_Q, grad_W_K) as new tensors."""
+        if X.dtype != self.dtype or X.dim() != 2 or X.shape[1] != self.d:
+            raise ValueError(f"X must be [N, {self.d}] {self.dtype}")
+        dev = X.device
+        gX = torch.empty_like(X)
+        gP = torch.empty((self.k, self.d), dtype=torch.float32, device=dev)
+        gQ = torch.empty((self.d, self.d), dtype=torch.float32, device=dev)
+        gK = torch.empty((self.d, self.d), dtype=torch.float32, device=dev)
+        sa_grad_compute(self.handle, X, offsets, grad_sketch, gX, gP, gQ, gK, stream)
+        return gX, gP, gQ, gK
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None:
+            sa_grad_destroy(self.handle)
             self.handle = None
 
     def __enter__(self):

@@ -31,6 +31,8 @@ SOURCES = [
     "sa_stream_d64.hip",
     "sa_stream_d128.hip",
     "sa_refine.hip",
+    "sa_grad.hip",
+    "sa_grad_api.cpp",
 ]
 # The bf16 plans (accumulators of at most 128 registers per lane) keep every
 # matrix-core result in VGPRs, so the softmax reads the affinity tile without

@@ -1,0 +1,71 @@
+// Internal interface of the backward pass (sa_grad.hip, sa_grad_api.cpp).
+// Not part of the public ABI.
+//
+// For one user, with the folded M = tau log2(e) P W_Q W_K^T (bf16), the
+// natural-units fold Q' = tau P W_Q W_K^T (bf16), the upstream gradient
+// G = dL/dX~ (k x d) and A the prototype-axis softmax of S = Q' X^T:
+//   pass 1 (grad_stats)  per row i: m_i = max_j s'_ji (log2 units),
+//                        1/l_i, c_i = sum_j A_ji (G X^T)_ji, written out;
+//                        dQ' += dS X with dS = A * (G X^T - c), split over
+//                        groups like the forward partial sketches
+//   pass 2 (grad_dx)     dX = A^T G + dS^T Q' per row, with A and dS
+//                        recomputed from the row statistics
+//   then dQ = tau dQ' W_K, dW_K = tau dQ'^T Q, dP = dQ W_Q^T, dW_Q = P^T dQ.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+// Prototypes per wave in pass 1 and per chunk in pass 2.
+constexpr int kGradKW = 32;
+
+struct GradStatsArgs {
+  const void* X;      // bf16 rows of this launch [rows][d]
+  const void* M;      // bf16 [k_pad][d], tau log2(e) P W_Q W_K^T (padding rows zero)
+  const float* G;     // float32 [users][k][d], upstream gradient of this launch's users
+  float* stats;       // float32 [rows][4]: m_i, 1 / l_i, c_i, 0
+  float* partial;     // float32 [groups][k_pad * d] in the lane layout of the forward partials
+  int64_t rows;
+  int32_t users;
+  int32_t k;
+  int64_t offsets[kMaxUsersPerLaunch + 1];
+};
+
+struct GradDxArgs {
+  const void* X;        // bf16 [rows][d]
+  const float* stats;   // as written by pass 1
+  const void* packed;   // per user and 32-prototype chunk: M, G, G^T, Q'^T blocks (pack kernel)
+  void* dX;             // bf16 [rows][d]
+  int64_t rows;
+  int32_t users;
+  int32_t k;
+  int32_t chunks;       // k_pad / 32
+  int64_t offsets[kMaxUsersPerLaunch + 1];
+};
+
+// Bytes of one packed chunk: four 32 x d bf16 blocks.
+constexpr int grad_chunk_bytes(int d) { return 4 * kGradKW * d * 2; }
+
+// Waves per group of pass 1 for k prototypes (k_pad = 32 * waves), 0 when unsupported.
+int grad_stats_waves(int k);
+
+hipError_t launch_grad_stats(int d, int waves, const GradStatsArgs& a, int groups, hipStream_t s,
+                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+hipError_t launch_grad_dx(int d, const GradDxArgs& a, int groups, hipStream_t s, hipEvent_t start = nullptr,
+                          hipEvent_t stop = nullptr);
+hipError_t grad_occupancy(int d, int waves, int* stats_groups_per_cu, int* dx_groups_per_cu);
+// packed[u][c] for users 0..users-1 of G (float32 [users][k][d]) and the shared bf16 M and Q' [k_pad][d].
+hipError_t launch_grad_pack(const void* M, const void* Qp, const float* G, int users, int k, int chunks, int d,
+                            void* packed, hipStream_t s);
+// C[m][n] = alpha sum_t A[m * a_rs + t * a_cs] B[t * b_rs + n * b_cs], float32 out [rows][cols];
+// dtype 1: A and B bf16, 0: float32.
+hipError_t launch_small_matmul(int dtype, const void* A, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_rs,
+                               int64_t b_cs, int rows, int cols, int inner, float alpha, float* C, hipStream_t s);
+// dst[i] += src[i] for n floats.
+hipError_t launch_add(float* dst, const float* src, int64_t n, hipStream_t s);
+
+}  // namespace sa

@@ -281,3 +281,9 @@ def make_stack_layers(*, d: int, d_ff: int, layers: int, dtype: str = "bf16", se
             "ln2_bias": _normal(rng, (d,), 0.1),
         })
     return out
+
+
+def make_upstream_grad(users: int, k: int, d: int, seed: int = 0, scale: float = 1.0) -> np.ndarray:
+    """Seeded upstream gradient dL/dX~ for the backward pass: float32 [users, k, d], N(0, scale^2)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    return (rng.standard_normal((users, k, d)) * scale).astype(np.float32)

@@ -156,3 +156,26 @@ def test_product_path_does_not_reference_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f"{f} imports the oracle"
                 assert "oracle/" not in text and "sa_oracle" not in text, f"{f} reaches into the oracle"
+
+
+def test_grad_entry_points_validate_before_device_work():
+    lib = B.library()
+    assert lib.sa_grad_check_config(128, 256, 0.1, B.SA_BF16) == B.SA_OK
+    assert lib.sa_grad_check_config(64, 1, 0.1, B.SA_BF16) == B.SA_OK
+    assert lib.sa_grad_check_config(128, 257, 0.1, B.SA_BF16) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_grad_check_config(128, 64, 0.1, B.SA_F32) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_grad_check_config(96, 64, 0.1, B.SA_BF16) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_grad_check_config(128, 0, 0.1, B.SA_BF16) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_grad_check_config(128, 64, float("nan"), B.SA_BF16) == B.SA_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert lib.sa_grad_create(ctypes.byref(h), 128, 64, 0.1, B.SA_BF16, None, None, None, None) == \
+        B.SA_ERR_INVALID_ARG
+    assert lib.sa_grad_create(None, 128, 64, 0.1, B.SA_BF16, None, None, None, None) == B.SA_ERR_INVALID_ARG
+    offs = np.array([0, 4], dtype=np.int64)
+    assert lib.sa_grad_compute(None, None, offs.ctypes.data, 1, None, None, None, None, None, None) == \
+        B.SA_ERR_INVALID_ARG
+    f, g, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    assert lib.sa_grad_read_kernel_timing(None, ctypes.byref(f), ctypes.byref(g), ctypes.byref(n)) == \
+        B.SA_ERR_INVALID_ARG
+    assert lib.sa_grad_set_kernel_timing(None, 1) == B.SA_ERR_INVALID_ARG
+    lib.sa_grad_destroy(None)
