@@ -144,6 +144,91 @@ def copy_calibration(steps: int) -> None:
                       "bytes_written_per_dispatch": nbytes, "dispatches": steps}), flush=True)
 
 
+def grad_cpu_baseline(wl, G, budget_s: float):
+    """Time the fp64 gradient oracle on whole users, cycling until about budget_s seconds have passed."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import grad_oracle
+
+    rows = users = 0
+    t0 = time.perf_counter()
+    while True:
+        u = users % wl.num_users
+        grad_oracle.sketch_grad_user(wl.user_rows(u), wl.P, wl.W_Q, wl.W_K, wl.tau, G[u])
+        rows += int(wl.offsets[u + 1] - wl.offsets[u])
+        users += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": rows / dt if dt > 0 else None, "unit": "behaviors/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{users} user gradients cycling over the {wl.num_users} users of the workload ({rows} rows), "
+                      f"fp64 numpy/OpenBLAS, {dt:.2f} s"}
+
+
+def run_grad(args, wl, Xs, copies, offs, dev) -> int:
+    """Backward pass: one step = sa_grad_compute over the whole batch.  The
+    roofline is that of the longer of the two streamed passes, on its
+    algorithmic share: 6kd FLOP per row for the statistics pass (s', dA and
+    dQ' = dS X), 4kd for the dX pass (its recomputation of s' and dA, 4kd more
+    per row, is not counted)."""
+    from sketch_attention_amd import SketchAttentionGrad, binding, workloads
+
+    dt = torch.bfloat16
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+    G = workloads.make_upstream_grad(wl.num_users, wl.k, wl.d, seed=0)
+    Gd = torch.from_numpy(G).to(dev)
+    h = SketchAttentionGrad(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau)
+    gX = torch.empty_like(Xs[0])
+    gP = torch.empty((wl.k, wl.d), dtype=torch.float32, device=dev)
+    gQ = torch.empty((wl.d, wl.d), dtype=torch.float32, device=dev)
+    gK = torch.empty_like(gQ)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda i: binding.sa_grad_compute(h.handle, Xs[i % copies], offs, Gd, gX, gP, gQ, gK, stream)
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize(dev)
+    binding.sa_grad_read_kernel_timing(h.handle)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        timed = i % TIMING_PERIOD == 0
+        if timed:
+            binding.sa_grad_set_kernel_timing(h.handle, True)
+        run(i)
+        if timed:
+            binding.sa_grad_set_kernel_timing(h.handle, False)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    stats_ms, dx_ms, calls = binding.sa_grad_read_kernel_timing(h.handle)
+    h.close()
+    ms_per_step = elapsed * 1e3 / args.steps
+    n, k, d = wl.total_rows, wl.k, wl.d
+    st_us, dx_us = stats_ms * 1e3 / max(calls, 1), dx_ms * 1e3 / max(calls, 1)
+    st_tf = 6.0 * k * d * n / (st_us * 1e-6) / 1e12 if st_us > 0 else 0.0
+    dx_tf = 4.0 * k * d * n / (dx_us * 1e-6) / 1e12 if dx_us > 0 else 0.0
+    log(f"[bench] grad: statistics pass {st_us:.2f} us ({st_tf:.1f} TFLOP/s algorithmic), dX pass {dx_us:.2f} us "
+        f"({dx_tf:.1f} TFLOP/s algorithmic, {2 * dx_tf:.1f} executed); whole step {ms_per_step * 1e3:.2f} us "
+        f"({10.0 * k * d * n / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s over the 10kd FLOP per row)")
+    name, us, tf = ("grad_dx_kernel", dx_us, dx_tf) if dx_us >= st_us else ("grad_stats_kernel", st_us, st_tf)
+    roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": name, "kernel_avg_us": round(us, 2)}
+    cpu = None if args.no_cpu_baseline else grad_cpu_baseline(wl, G, args.cpu_budget)
+    if cpu:
+        log(f"[bench] cpu baseline: {cpu}")
+    line = {
+        "metric": "history behaviors/sec through the backward pass (gradients w.r.t. X, P, W_Q, W_K)",
+        "value": round(n * args.steps / elapsed, 1), "unit": "behaviors/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.num_users} users x n={n // max(wl.num_users, 1)}, d={d}, k={k}, "
+                               f"{wl.dtype}, backward", "users": wl.num_users, "rows": n, "d": d, "k": k,
+                   "pass": "backward", "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +242,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0,
                     help="run the stacked refinement with this many layers (0: the single SA pass)")
     ap.add_argument("--d-ff", type=int, default=None, help="FFN width of the refinement stack (default 4 d)")
+    ap.add_argument("--grad", action="store_true",
+                    help="time the backward pass (gradients w.r.t. X, P, W_Q, W_K) instead of the compression")
     ap.add_argument("--norm", default="prototypes", choices=["prototypes", "history"],
                     help="softmax axis: prototypes (Sketch Attention) or history (the comparator)")
     args = ap.parse_args()
@@ -190,6 +277,11 @@ def main() -> int:
     if args.norm == "history" and args.layers:
         print("--norm history runs the single pass only", file=sys.stderr)
         return 2
+    if args.grad:
+        if args.layers or args.norm != "prototypes":
+            print("--grad times the single pass's backward only", file=sys.stderr)
+            return 2
+        return run_grad(args, wl, Xs, copies, np.ascontiguousarray(wl.offsets, dtype=np.int64), dev)
     sa = SketchAttention(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau, norm=args.norm)
     outs = [torch.empty((wl.num_users, wl.k, wl.d), dtype=torch.float32, device=dev) for _ in range(2)]
     offs = np.ascontiguousarray(wl.offsets, dtype=np.int64)

@@ -61,10 +61,22 @@ hipError_t grad_occupancy(int d, int waves, int* stats_groups_per_cu, int* dx_gr
 // packed[u][c] for users 0..users-1 of G (float32 [users][k][d]) and the shared bf16 M and Q' [k_pad][d].
 hipError_t launch_grad_pack(const void* M, const void* Qp, const float* G, int users, int k, int chunks, int d,
                             void* packed, hipStream_t s);
-// C[m][n] = alpha sum_t A[m * a_rs + t * a_cs] B[t * b_rs + n * b_cs], float32 out [rows][cols];
-// dtype 1: A and B bf16, 0: float32.
-hipError_t launch_small_matmul(int dtype, const void* A, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_rs,
-                               int64_t b_cs, int rows, int cols, int inner, float alpha, float* C, hipStream_t s);
+// C[m][n] = alpha sum_t A[m * a_rs + t * a_cs] B[t * b_rs + n * b_cs], float32, C [rows][cols].
+constexpr int kMaxInner = 256;
+struct Matmul {
+  const float* A;
+  int64_t a_rs, a_cs;
+  const float* B;
+  int64_t b_rs, b_cs;
+  int rows, cols, inner;  // inner <= kMaxInner
+  float alpha;
+  float* C;
+};
+struct MatmulPair {
+  Matmul p[2];
+};
+// Both products in one launch (independent of each other).
+hipError_t launch_small_matmuls(const Matmul& a, const Matmul& b, hipStream_t stream);
 // dst[i] += src[i] for n floats.
 hipError_t launch_add(float* dst, const float* src, int64_t n, hipStream_t s);
 

@@ -38,17 +38,25 @@ namespace sa {
 namespace {
 
 // ------------------------------------------------------------ pass 1
+// X arrives by LDS DMA into a ring of NS = 4 tiles (issued three tiles
+// ahead, rows swizzled as in sa_stream.hpp).  Step t (one barrier): DMA of
+// tile t+3 into the slot tile t-1 left; merge of tile t's row statistics
+// (written by every wave in step t-1), its dS and the aggregation dQ' +=
+// dS X; s' and dA of tile t+1 and their per-wave row statistics; wait for
+// tile t+2.  So the products of tile t+1 overlap the merge of tile t.
 template <int D, int WJ>
 __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args) {
   constexpr int KW = kGradKW, JB = KW / 16, RB = 2, NT = 16 * RB, CS = D / 32, CB = D / 16, CH = D / 8;
-  constexpr int THREADS = 64 * WJ, KPAD = KW * WJ;
+  constexpr int KPAD = KW * WJ;
+  constexpr int NS = 4;
   constexpr int TILE_BYTES = NT * D * 2;
-  constexpr int NCH = NT * CH;                          // 16-byte chunks per tile
-  constexpr int CPT = (NCH + THREADS - 1) / THREADS;    // per thread
+  constexpr int NI = TILE_BYTES / 1024;     // DMA blocks per tile
+  constexpr int NIW = (NI + WJ - 1) / WJ;   // per wave (some waves may have one fewer, or none)
+  constexpr int RPI = 1024 / (2 * D);       // rows per DMA block
   using MF = Mfma<bf16>;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
-  __shared__ float xs_m[NT][WJ], xs_l[NT][WJ], xs_c[NT][WJ];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[NS * TILE_BYTES];
+  __shared__ float xs_m[2][NT][WJ], xs_l[2][NT][WJ], xs_c[2][NT][WJ];
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -81,29 +89,33 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     }
   };
 
-  // ---- X tile staging: chunk i of the tile = row i / CH, chunk i % CH, stored
-  // at chunk (i % CH) ^ sw(row) of that LDS row; rows past the piece repeat its last row
-  u32x4 pre[CPT];
-  auto load_tile = [&](const Cursor& c) {
-    const int64_t lim = c.end - 1 - c.row;
+  // ---- LDS DMA of the tile at cursor c into ring slot q: block j = wj + s WJ
+  // (RPI rows) lands at slot + 1024 j; lane i holds row j RPI + i / CH, LDS
+  // chunk i % CH = global chunk (i % CH) ^ sw(row).  Rows past the piece read
+  // its last row; past the list every lane reads row c.end - 1 (in bounds).
+  auto issue_tile = [&](const Cursor& c, int q) {
+    const int64_t last = c.end - 1 - c.row;
+    const int64_t b0 = last < 0 ? c.end - 1 : c.row;
+    const int lim = last < 0 ? 0 : (int)(last < NT ? last : NT - 1);
 #pragma unroll
-    for (int s = 0; s < CPT; ++s) {
-      const int i = tid + s * THREADS;
-      if (NCH % THREADS == 0 || i < NCH) {
-        const int r = i / CH;
-        const int64_t rr = r < lim ? r : lim;
-        pre[s] = *reinterpret_cast<const u32x4*>(X + (c.row + rr) * D + 8 * (i % CH));
+    for (int s = 0; s < NIW; ++s) {
+      const int j = wj + s * WJ;
+      if (NI % WJ == 0 || j < NI) {
+        const int r = j * RPI + lane / CH;
+        const int rr = r < lim ? r : lim;
+        dma16(X + b0 * D, (uint32_t)(rr * D + 8 * ((lane % CH) ^ chunk_sw<D>(r))) * 2u,
+              lds0 + (uint32_t)(q * TILE_BYTES + 1024 * j));
       }
     }
   };
-  auto store_tile = [&](int q) {
-#pragma unroll
-    for (int s = 0; s < CPT; ++s) {
-      const int i = tid + s * THREADS;
-      if (NCH % THREADS == 0 || i < NCH) {
-        const int r = i / CH;
-        *reinterpret_cast<u32x4*>(lds + q * TILE_BYTES + r * D * 2 + 16 * ((i % CH) ^ chunk_sw<D>(r))) = pre[s];
-      }
+  // wait until this wave's DMA blocks are done but those of the n most recent tiles
+  auto wait_tiles = [&](auto n_) {
+    constexpr int n = decltype(n_)::value;
+    if constexpr (NI % WJ == 0) {
+      wait_vm<(NI / WJ) * n>();
+    } else {
+      if (wj < NI % WJ) wait_vm<(NI / WJ + 1) * n>();
+      else wait_vm<(NI / WJ) * n>();
     }
   };
 
@@ -114,7 +126,9 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(M + (int64_t)(jbase + 16 * jb + l16) * D, cs, g);
   int g_user = -1;
-  auto load_g = [&](int u) {
+  auto ensure_g = [&](int u) {
+    if (u == g_user) return;
+    g_user = u;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       const int j = jbase + 16 * jb + l16;
@@ -141,37 +155,18 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   // transposing reads for the aggregation (see sa_stream.hpp)
   const uint32_t trb = (uint32_t)(2 * ((4 * g + (l16 >> 2)) * D + 8 * (((l16 >> 1) & 1) ^ chunk_sw<D>(4 * g + (l16 >> 2))) +
                                        4 * (l16 & 1)));
-
-  f32x4 acc[JB][CB];
-#pragma unroll
-  for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // lane (g, l16) finishes row my_row of a tile; its 16-lane DPP row holds every lane that needs it
   const int my_ib = (l16 >> 2) & 1, my_r = l16 & 3;
   const int my_row = 16 * my_ib + 4 * g + my_r;
   // row whose 16-lane totals rows4_sum_scatter leaves in this lane (per ib)
   const int sc_r = 2 * (l16 >> 3) + ((l16 >> 2) & 1);
 
-  Cursor cur{r_begin, min(r_end, args.offsets[u0 + 1]), u0};
-  load_tile(cur);
-  store_tile(0);
-  __syncthreads();
-  int q = 0;
-  while (cur.row < r_end) {
-    Cursor nxt = cur;
-    cursor_next(nxt);
-    const bool has_next = nxt.row < r_end;
-    if (has_next) load_tile(nxt);
-    if (cur.u != g_user) {
-      load_g(cur.u);
-      g_user = cur.u;
-    }
+  // s' and dA of the tile in ring slot q for this wave's prototypes
+  // (s[ib][jb][r]: row 16 ib + 4 g + r, prototype 16 jb + l16), then the
+  // per-wave row statistics m_w, sum 2^(s' - m_w), sum 2^(s' - m_w) dA into xs[par]
+  f32x4 s[RB][JB], da[RB][JB];
+  auto affinity = [&](int q, int par) {
     const uint32_t slot = lds0 + (uint32_t)(q * TILE_BYTES);
-
-    // s' and dA of this wave's prototypes: s[ib][jb][r] for row 16 ib + 4 g + r, prototype 16 jb + l16
-    f32x4 s[RB][JB], da[RB][JB];
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
       bf16x8 xa[RB];
@@ -197,8 +192,6 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
           da[ib][jb][r] = ok ? da[ib][jb][r] : 0.f;
         }
     }
-
-    // per row and wave: m_w, sum 2^(s' - m_w), sum 2^(s' - m_w) dA
 #pragma unroll
     for (int ib = 0; ib < RB; ++ib) {
       float mw[4], pl[4], pc[4];
@@ -222,29 +215,56 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
       const float zc = rows4_sum_scatter(pc, l16);
       const float zm = sc_r == 0 ? mw[0] : sc_r == 1 ? mw[1] : sc_r == 2 ? mw[2] : mw[3];
       const int trow = 16 * ib + 4 * g + sc_r;
-      xs_m[trow][wj] = zm;
-      xs_l[trow][wj] = zl;
-      xs_c[trow][wj] = zc;
+      xs_m[par][trow][wj] = zm;
+      xs_l[par][trow][wj] = zl;
+      xs_c[par][trow][wj] = zc;
     }
-    __syncthreads();
+  };
 
-    // merge the waves for row my_row
-    float m = xs_m[my_row][0];
+  f32x4 acc[JB][CB];
 #pragma unroll
-    for (int w = 1; w < WJ; ++w) m = fmaxf(m, xs_m[my_row][w]);
+  for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Cursor cc{r_begin, min(r_end, args.offsets[u0 + 1]), u0};  // tile t (merge, aggregation)
+  Cursor ca = cc;                                             // tile t + 1 (affinity)
+  Cursor cl = cc;                                             // next tile to load
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    issue_tile(cl, p);
+    cursor_next(cl);
+  }
+  wait_tiles(std::integral_constant<int, NS - 2>{});  // tile 0
+  __syncthreads();
+  ensure_g(ca.u);
+  affinity(0, 0);
+  cursor_next(ca);
+  wait_tiles(std::integral_constant<int, NS - 3>{});  // tile 1
+  __syncthreads();
+
+  int t = 0;
+  while (cc.row < r_end) {
+    issue_tile(cl, (t + NS - 1) % NS);  // the slot of tile t - 1
+    cursor_next(cl);
+    const int par = t & 1;
+    // merge the waves for row my_row of tile t
+    float m = xs_m[par][my_row][0];
+#pragma unroll
+    for (int w = 1; w < WJ; ++w) m = fmaxf(m, xs_m[par][my_row][w]);
     float l = 0.f, c = 0.f;
 #pragma unroll
     for (int w = 0; w < WJ; ++w) {
-      const float f = fast_exp2(xs_m[my_row][w] - m);  // 0 for a wave without real prototypes
-      l += xs_l[my_row][w] * f;
-      c += xs_c[my_row][w] * f;
+      const float f = fast_exp2(xs_m[par][my_row][w] - m);  // 0 for a wave without real prototypes
+      l += xs_l[par][my_row][w] * f;
+      c += xs_c[par][my_row][w] * f;
     }
     float inv = 1.f / l;
     c *= inv;
-    const bool valid = (int64_t)my_row < cur.end - cur.row;
+    const bool valid = (int64_t)my_row < cc.end - cc.row;
     if (!valid) inv = 0.f;  // rows past the piece add nothing
     if (valid && wj == 0 && l16 < 8)
-      *reinterpret_cast<f32x4*>(args.stats + (cur.row + my_row) * 4) = f32x4{m, inv, c, 0.f};
+      *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{m, inv, c, 0.f};
 
     // dS of this wave's prototypes as bf16 weights of the aggregation
     bf16x8 a[JB];
@@ -252,27 +272,27 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float mm, ii, cc;
+        float mm, ii, cv;
         switch (4 * ib + r) {
-          case 0: mm = row_bcast<0>(m); ii = row_bcast<0>(inv); cc = row_bcast<0>(c); break;
-          case 1: mm = row_bcast<1>(m); ii = row_bcast<1>(inv); cc = row_bcast<1>(c); break;
-          case 2: mm = row_bcast<2>(m); ii = row_bcast<2>(inv); cc = row_bcast<2>(c); break;
-          case 3: mm = row_bcast<3>(m); ii = row_bcast<3>(inv); cc = row_bcast<3>(c); break;
-          case 4: mm = row_bcast<4>(m); ii = row_bcast<4>(inv); cc = row_bcast<4>(c); break;
-          case 5: mm = row_bcast<5>(m); ii = row_bcast<5>(inv); cc = row_bcast<5>(c); break;
-          case 6: mm = row_bcast<6>(m); ii = row_bcast<6>(inv); cc = row_bcast<6>(c); break;
-          default: mm = row_bcast<7>(m); ii = row_bcast<7>(inv); cc = row_bcast<7>(c); break;
+          case 0: mm = row_bcast<0>(m); ii = row_bcast<0>(inv); cv = row_bcast<0>(c); break;
+          case 1: mm = row_bcast<1>(m); ii = row_bcast<1>(inv); cv = row_bcast<1>(c); break;
+          case 2: mm = row_bcast<2>(m); ii = row_bcast<2>(inv); cv = row_bcast<2>(c); break;
+          case 3: mm = row_bcast<3>(m); ii = row_bcast<3>(inv); cv = row_bcast<3>(c); break;
+          case 4: mm = row_bcast<4>(m); ii = row_bcast<4>(inv); cv = row_bcast<4>(c); break;
+          case 5: mm = row_bcast<5>(m); ii = row_bcast<5>(inv); cv = row_bcast<5>(c); break;
+          case 6: mm = row_bcast<6>(m); ii = row_bcast<6>(inv); cv = row_bcast<6>(c); break;
+          default: mm = row_bcast<7>(m); ii = row_bcast<7>(inv); cv = row_bcast<7>(c); break;
         }
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
           const float A = fast_exp2(s[ib][jb][r] - mm) * ii;
-          a[jb][4 * ib + r] = (bf16)(A * (da[ib][jb][r] - cc));
+          a[jb][4 * ib + r] = (bf16)(A * (da[ib][jb][r] - cv));
         }
       }
 
     // dQ'[j][:] += sum_i dS_ji x_i (reduction slot (g, e) = row 16 (e / 4) + 4 g + e % 4)
     {
-      const uint32_t xp = slot + trb;
+      const uint32_t xp = lds0 + (uint32_t)((t % NS) * TILE_BYTES) + trb;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const uint32_t xc = xp ^ (uint32_t)(32 * cb);
@@ -283,11 +303,18 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
         for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
       }
     }
-    if (has_next) store_tile(q ^ 1);  // that slot was last read before the exchange barrier
+    // products and statistics of tile t + 1
+    if (ca.row < r_end) {
+      ensure_g(ca.u);
+      affinity((t + 1) % NS, par ^ 1);
+    }
+    cursor_next(cc);
+    cursor_next(ca);
+    ++t;
+    wait_tiles(std::integral_constant<int, NS - 3>{});  // tile t + 1 of the new t, read by its affinity
     __syncthreads();
-    cur = nxt;
-    q ^= 1;
   }
+  wait_vm<0>();  // no DMA outlives the work group
 
   // ---- one partial per group, lane layout [wj][jb][cb][lane][4]
   float* dst = args.partial + grp * (int64_t)(KPAD * D);
@@ -345,12 +372,13 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
   constexpr int KW = kGradKW, NT = 32 * W2, CS = D / 32, DB = D / 16;
   constexpr int BLK = KW * D * 2;        // bytes of one block of a chunk
   constexpr int CHUNK = 4 * BLK;
-  constexpr int NBLK = CHUNK / 1024;     // DMA blocks per chunk
+  constexpr int CPS = 2;                 // chunks per step (the prototype count is a multiple of 64)
+  constexpr int NBLK = CPS * CHUNK / 1024;  // DMA blocks per step
   static_assert(NBLK % W2 == 0, "DMA blocks split evenly over the waves");
   constexpr int BPW = NBLK / W2;
   using MF = Mfma<bf16>;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * CHUNK];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * CPS * CHUNK];
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
@@ -382,13 +410,14 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
     }
   };
 
-  // LDS DMA of chunk c of user u into buffer b: block j = wave + W2 s lands at 1024 j
-  auto issue_chunk = [&](int u, int c, int b) {
+  // LDS DMA of chunks c .. c + CPS - 1 of user u (adjacent in the packed
+  // layout) into buffer b: block j = wave + W2 s lands at 1024 j
+  auto issue_chunks = [&](int u, int c, int b) {
     const unsigned char* src = packed + ((int64_t)u * chunks + c) * CHUNK;
 #pragma unroll
     for (int s = 0; s < BPW; ++s) {
       const int j = wave + W2 * s;
-      dma16(src, (uint32_t)(1024 * j + 16 * lane), lds0 + (uint32_t)(b * CHUNK + 1024 * j));
+      dma16(src, (uint32_t)(1024 * j + 16 * lane), lds0 + (uint32_t)(b * CPS * CHUNK + 1024 * j));
     }
   };
 
@@ -400,7 +429,7 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
   const uint32_t toff = (uint32_t)(2 * (l16 * KW + 8 * (g ^ (2 * ((l16 >> 3) & 1)))));
 
   Cursor cur{r_begin, min(r_end, args.offsets[u0 + 1]), u0};
-  issue_chunk(cur.u, 0, 0);
+  issue_chunks(cur.u, 0, 0);
   wait_vm<0>();
   __syncthreads();
   int q = 0;
@@ -411,6 +440,7 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
     // this wave's rows: X fragments (B operand of s' = M x, rows along the
     // lanes) and the statistics of rows 16 ib + l16
     const int64_t lim = cur.end - 1 - cur.row;
+    const bool busy = rw <= lim;  // the wave has rows in this tile (wave-uniform)
     bf16x8 xr[2][CS];
     float sm[2], si[2], sc[2];
     bool valid[2];
@@ -432,10 +462,14 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[ib][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int c = 0; c < chunks; ++c) {
-      if (c + 1 < chunks) issue_chunk(cur.u, c + 1, q ^ 1);
-      else if (has_next) issue_chunk(nxt.u, 0, q ^ 1);
-      const uint32_t buf = lds0 + (uint32_t)(q * CHUNK);
+    for (int c0 = 0; c0 < chunks; c0 += CPS) {
+      if (c0 + CPS < chunks) issue_chunks(cur.u, c0 + CPS, q ^ 1);
+      else if (has_next) issue_chunks(nxt.u, 0, q ^ 1);
+      if (busy) {
+#pragma unroll
+      for (int h = 0; h < CPS; ++h) {
+      const int c = c0 + h;
+      const uint32_t buf = lds0 + (uint32_t)((q * CPS + h) * CHUNK);
 
       // s'[jb][ib][r] and dA for prototype 16 jb + 4 g + r of the chunk, row 16 ib + l16
       f32x4 s[2][2], da[2][2];
@@ -476,7 +510,9 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
           acc[ib][db] = MF::run(qt, wd[ib], acc[ib][db]);
         }
       }
-      wait_vm<0>();  // the next chunk's DMA (and this tile's loads) are done
+      }
+      }
+      wait_vm<0>();  // the next step's DMA (and this tile's loads) are done
       __syncthreads();
       q ^= 1;
     }
@@ -501,21 +537,49 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
 }
 
 // ------------------------------------------------------------ small products
-template <typename T>
-__device__ __forceinline__ float ld_f32(const T* p, int64_t i) {
-  return (float)p[i];
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void small_matmul_kernel(const T* A, int64_t a_rs, int64_t a_cs, const T* B,
-                                                           int64_t b_rs, int64_t b_cs, int rows, int cols, int inner,
-                                                           float alpha, float* C) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)rows * cols) return;
-  const int m = (int)(idx / cols), n = (int)(idx % cols);
-  float s = 0.f;
-  for (int t = 0; t < inner; ++t) s = fmaf(ld_f32(A, m * a_rs + t * a_cs), ld_f32(B, t * b_rs + n * b_cs), s);
-  C[idx] = alpha * s;
+// Two independent small products per launch (blockIdx.z picks one), one
+// 16 x 16 tile of C per work group.  The whole inner dimension (<= 256) of
+// the tile's operands is staged in LDS with all loads in flight at once, so a
+// tile costs one memory latency; operands are read with arbitrary strides, so
+// transposed views need no copy.
+__global__ __launch_bounds__(256) void small_matmul_kernel(MatmulPair pr) {
+  __shared__ float As[16][kMaxInner + 1], Bs[kMaxInner][17];
+  const Matmul& p = pr.p[blockIdx.z];
+  const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 16;
+  if (m0 >= p.rows || n0 >= p.cols) return;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  // consecutive threads walk the operand's unit-stride dimension (coalesced loads)
+  const bool a_rows_fast = p.a_rs < p.a_cs, b_rows_fast = p.b_rs < p.b_cs;
+  constexpr int PER = 16 * kMaxInner / 256;  // elements of each operand per thread, all loaded before any store
+  float av[PER], bv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    av[i] = bv[i] = 0.f;
+    if (e < 16 * p.inner) {
+      const int mm = a_rows_fast ? e & 15 : e / p.inner, tt = a_rows_fast ? e >> 4 : e % p.inner;
+      if (m0 + mm < p.rows) av[i] = p.A[(m0 + mm) * p.a_rs + tt * p.a_cs];
+      const int tb = b_rows_fast ? e % p.inner : e >> 4, nn = b_rows_fast ? e / p.inner : e & 15;
+      if (n0 + nn < p.cols) bv[i] = p.B[tb * p.b_rs + (n0 + nn) * p.b_cs];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    if (e < 16 * p.inner) {
+      As[a_rows_fast ? e & 15 : e / p.inner][a_rows_fast ? e >> 4 : e % p.inner] = av[i];
+      Bs[b_rows_fast ? e % p.inner : e >> 4][b_rows_fast ? e / p.inner : e & 15] = bv[i];
+    }
+  }
+  __syncthreads();
+  float s0 = 0.f, s1 = 0.f;
+  int t = 0;
+  for (; t + 2 <= p.inner; t += 2) {
+    s0 = fmaf(As[ty][t], Bs[t][tx], s0);
+    s1 = fmaf(As[ty][t + 1], Bs[t + 1][tx], s1);
+  }
+  if (t < p.inner) s0 = fmaf(As[ty][t], Bs[t][tx], s0);
+  if (m0 + ty < p.rows && n0 + tx < p.cols) p.C[(int64_t)(m0 + ty) * p.cols + n0 + tx] = p.alpha * (s0 + s1);
 }
 
 __global__ __launch_bounds__(256) void add_kernel(float* dst, const float* src, int64_t n) {
@@ -611,15 +675,12 @@ hipError_t launch_grad_pack(const void* M, const void* Qp, const float* G, int u
   return hipGetLastError();
 }
 
-hipError_t launch_small_matmul(int dtype, const void* A, int64_t a_rs, int64_t a_cs, const void* B, int64_t b_rs,
-                               int64_t b_cs, int rows, int cols, int inner, float alpha, float* C, hipStream_t s) {
-  const dim3 grid((unsigned)(((int64_t)rows * cols + 255) / 256));
-  if (dtype == 1)
-    hipLaunchKernelGGL(small_matmul_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)A, a_rs, a_cs, (const bf16*)B,
-                       b_rs, b_cs, rows, cols, inner, alpha, C);
-  else
-    hipLaunchKernelGGL(small_matmul_kernel<float>, grid, dim3(256), 0, s, (const float*)A, a_rs, a_cs,
-                       (const float*)B, b_rs, b_cs, rows, cols, inner, alpha, C);
+hipError_t launch_small_matmuls(const Matmul& a, const Matmul& b, hipStream_t s) {
+  for (const Matmul* p : {&a, &b})
+    if (p->inner < 1 || p->inner > kMaxInner || p->rows < 1 || p->cols < 1) return hipErrorInvalidValue;
+  const int rows = a.rows > b.rows ? a.rows : b.rows, cols = a.cols > b.cols ? a.cols : b.cols;
+  const dim3 grid((unsigned)((cols + 15) / 16), (unsigned)((rows + 15) / 16), 2);
+  hipLaunchKernelGGL(small_matmul_kernel, grid, dim3(256), 0, s, MatmulPair{{a, b}});
   return hipGetLastError();
 }
 

@@ -198,7 +198,8 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
   }
   bool timed = false;
 
-  hipError_t e = hipMemsetAsync(dq_sum, 0, kd * sizeof(float), s);
+  hipError_t e = hipSuccess;
+  bool have_dq = false;  // dq_sum written by a launch
   for (int32_t u0 = 0; e == hipSuccess && u0 < num_users; u0 += sa::kMaxUsersPerLaunch) {
     const int32_t u1 = u0 + sa::kMaxUsersPerLaunch < num_users ? u0 + sa::kMaxUsersPerLaunch : num_users;
     const int32_t users = u1 - u0;
@@ -228,7 +229,7 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     sa::ReduceArgs r{};
     r.partial = h->partial;
     r.history_softmax = 0;
-    r.out = dq_one;
+    r.out = have_dq ? dq_one : dq_sum;
     r.rows = rows;
     r.users = 1;  // one slot per group covering every user: the weights are shared
     r.groups = g1;
@@ -239,8 +240,9 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     r.offsets[0] = 0;
     r.offsets[1] = rows;
     e = sa::launch_reduce(r, s);
-    if (e == hipSuccess) e = sa::launch_add(dq_sum, dq_one, (int64_t)kd, s);
+    if (e == hipSuccess && have_dq) e = sa::launch_add(dq_sum, dq_one, (int64_t)kd, s);
     if (e != hipSuccess) break;
+    have_dq = true;
 
     sa::GradDxArgs a2{};
     a2.X = a1.X;
@@ -258,11 +260,14 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     e = sa::launch_grad_dx(d, a2, g2, s, time_it ? ev.ev[2] : nullptr, time_it ? ev.ev[3] : nullptr);
     timed = timed || (time_it && e == hipSuccess);
   }
+  if (e == hipSuccess && !have_dq) e = hipMemsetAsync(dq_sum, 0, kd * sizeof(float), s);  // no rows: zero gradients
   // dQ = tau dQ' W_K, dW_K = tau dQ'^T Q, dP = dQ W_Q^T, dW_Q = P^T dQ
-  if (e == hipSuccess) e = sa::launch_small_matmul(0, dq_sum, d, 1, h->WK32, d, 1, k, d, d, h->tau, dQ, s);
-  if (e == hipSuccess) e = sa::launch_small_matmul(0, dq_sum, 1, d, h->Q, d, 1, d, d, k, h->tau, grad_W_K, s);
-  if (e == hipSuccess) e = sa::launch_small_matmul(0, dQ, d, 1, h->WQ32, 1, d, k, d, d, 1.f, grad_P, s);
-  if (e == hipSuccess) e = sa::launch_small_matmul(0, h->P32, 1, d, dQ, d, 1, d, d, k, 1.f, grad_W_Q, s);
+  if (e == hipSuccess)
+    e = sa::launch_small_matmuls({dq_sum, d, 1, h->WK32, d, 1, k, d, d, h->tau, dQ},
+                                 {dq_sum, 1, d, h->Q, d, 1, d, d, k, h->tau, grad_W_K}, s);
+  if (e == hipSuccess)
+    e = sa::launch_small_matmuls({dQ, d, 1, h->WQ32, 1, d, k, d, d, 1.f, grad_P},
+                                 {h->P32, 1, d, dQ, d, 1, d, d, k, 1.f, grad_W_Q}, s);
   if (h->timing && max_rows > 0) (timed ? h->pending : h->spare).push_back(ev);
   return e == hipSuccess ? SA_OK : SA_ERR_DEVICE;
 }
