@@ -44,7 +44,7 @@ namespace {
 // (written by every wave in step t-1), its dS and the aggregation dQ' +=
 // dS X; s' and dA of tile t+1 and their per-wave row statistics; wait for
 // tile t+2.  So the products of tile t+1 overlap the merge of tile t.
-template <int D, int WJ>
+template <int D, int WJ, bool PAD>
 __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args) {
   constexpr int KW = kGradKW, JB = KW / 16, RB = 2, NT = 16 * RB, CS = D / 32, CB = D / 16, CH = D / 8;
   constexpr int KPAD = KW * WJ;
@@ -127,23 +127,21 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     for (int cs = 0; cs < CS; ++cs) mreg[jb][cs] = frag_c<D>(M + (int64_t)(jbase + 16 * jb + l16) * D, cs, g);
   int g_user = -1;
   auto ensure_g = [&](int u) {
+    u = __builtin_amdgcn_readfirstlane(u);  // uniform: a branch, not a masked block in every step
     if (u == g_user) return;
     g_user = u;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       const int j = jbase + 16 * jb + l16;
       const float* grow = args.G + ((int64_t)u * k + (j < k ? j : 0)) * D;
+      const float keep = j < k ? 1.f : 0.f;  // padding prototypes get zero rows
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(grow + 32 * cs + 8 * g);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(grow + 32 * cs + 8 * g + 4);
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = (bf16)(j < k ? a[e] : 0.f);
-          v[4 + e] = (bf16)(j < k ? b[e] : 0.f);
-        }
-        greg[jb][cs] = v;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(grow + 32 * cs + 8 * g) * keep;
+        const f32x4 b = *reinterpret_cast<const f32x4*>(grow + 32 * cs + 8 * g + 4) * keep;
+        typedef float f32x8 __attribute__((ext_vector_type(8)));
+        const f32x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        greg[jb][cs] = __builtin_convertvector(ab, bf16x8);
       }
     }
   };
@@ -162,10 +160,9 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   const int sc_r = 2 * (l16 >> 3) + ((l16 >> 2) & 1);
 
   // s' and dA of the tile in ring slot q for this wave's prototypes
-  // (s[ib][jb][r]: row 16 ib + 4 g + r, prototype 16 jb + l16), then the
-  // per-wave row statistics m_w, sum 2^(s' - m_w), sum 2^(s' - m_w) dA into xs[par]
+  // (s[ib][jb][r]: row 16 ib + 4 g + r, prototype 16 jb + l16)
   f32x4 s[RB][JB], da[RB][JB];
-  auto affinity = [&](int q, int par) {
+  auto affinity = [&](int q) {
     const uint32_t slot = lds0 + (uint32_t)(q * TILE_BYTES);
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
@@ -181,17 +178,23 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
           da[ib][jb] = MF::run(xa[ib], greg[jb][cs], cs == 0 ? z : da[ib][jb]);
         }
     }
+    if constexpr (PAD) {
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const bool ok = jbase + 16 * jb + l16 < k;
+      for (int jb = 0; jb < JB; ++jb) {
+        const bool ok = jbase + 16 * jb + l16 < k;
 #pragma unroll
-      for (int ib = 0; ib < RB; ++ib)
+        for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
-          da[ib][jb][r] = ok ? da[ib][jb][r] : 0.f;
-        }
+          for (int r = 0; r < 4; ++r) {
+            s[ib][jb][r] = ok ? s[ib][jb][r] : -INFINITY;
+            da[ib][jb][r] = ok ? da[ib][jb][r] : 0.f;
+          }
+      }
     }
+  };
+  // per-wave row statistics of the scores in s, da: m_w, sum 2^(s' - m_w),
+  // sum 2^(s' - m_w) dA into xs[par]
+  auto row_stats = [&](int par) {
 #pragma unroll
     for (int ib = 0; ib < RB; ++ib) {
       float mw[4], pl[4], pc[4];
@@ -238,7 +241,8 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   wait_tiles(std::integral_constant<int, NS - 2>{});  // tile 0
   __syncthreads();
   ensure_g(ca.u);
-  affinity(0, 0);
+  affinity(0);
+  row_stats(0);
   cursor_next(ca);
   wait_tiles(std::integral_constant<int, NS - 3>{});  // tile 1
   __syncthreads();
@@ -267,7 +271,9 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
       *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{m, inv, c, 0.f};
 
     // dS of this wave's prototypes as bf16 weights of the aggregation
-    bf16x8 a[JB];
+    // (computed in float first and converted in element order, so that
+    // consecutive pairs become single packed conversions)
+    float dsv[JB][8];
 #pragma unroll
     for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
@@ -286,9 +292,14 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
           const float A = fast_exp2(s[ib][jb][r] - mm) * ii;
-          a[jb][4 * ib + r] = (bf16)(A * (da[ib][jb][r] - cv));
+          dsv[jb][4 * ib + r] = A * (da[ib][jb][r] - cv);
         }
       }
+    bf16x8 a[JB];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[jb][e] = (bf16)dsv[jb][e];
 
     // dQ'[j][:] += sum_i dS_ji x_i (reduction slot (g, e) = row 16 (e / 4) + 4 g + e % 4)
     {
@@ -303,10 +314,11 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
         for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
       }
     }
-    // products and statistics of tile t + 1
+    // products and row statistics of tile t + 1
     if (ca.row < r_end) {
       ensure_g(ca.u);
-      affinity((t + 1) % NS, par ^ 1);
+      affinity((t + 1) % NS);
+      row_stats(par ^ 1);
     }
     cursor_next(cc);
     cursor_next(ca);
@@ -587,14 +599,20 @@ __global__ __launch_bounds__(256) void add_kernel(float* dst, const float* src, 
   if (i < n) dst[i] += src[i];
 }
 
+template <int D, int WJ, bool PAD>
+hipError_t stats_p(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
+  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_stats_kernel<D, WJ, PAD>, 64 * WJ, 0);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((grad_stats_kernel<D, WJ, PAD>), dim3(groups), dim3(64 * WJ), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((grad_stats_kernel<D, WJ, PAD>), dim3(groups), dim3(64 * WJ), 0, s, a);
+  return hipGetLastError();
+}
+// padding prototypes (k below 32 WJ) need their scores masked; the occupancy is that of the padded form
 template <int D, int WJ>
 hipError_t stats_t(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
-  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_stats_kernel<D, WJ>, 64 * WJ, 0);
-  if (e0 || e1)
-    hipExtLaunchKernelGGL((grad_stats_kernel<D, WJ>), dim3(groups), dim3(64 * WJ), 0, s, e0, e1, 0, a);
-  else
-    hipLaunchKernelGGL((grad_stats_kernel<D, WJ>), dim3(groups), dim3(64 * WJ), 0, s, a);
-  return hipGetLastError();
+  if (occ || a.k != kGradKW * WJ) return stats_p<D, WJ, true>(a, groups, s, e0, e1, occ);
+  return stats_p<D, WJ, false>(a, groups, s, e0, e1, occ);
 }
 
 template <int D>
