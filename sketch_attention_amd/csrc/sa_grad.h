@@ -4,8 +4,8 @@
 // For one user, with the folded M = tau log2(e) P W_Q W_K^T (bf16), the
 // natural-units fold Q' = tau P W_Q W_K^T (bf16), the upstream gradient
 // G = dL/dX~ (k x d) and A the prototype-axis softmax of S = Q' X^T:
-//   pass 1 (grad_stats)  per row i: m_i = max_j s'_ji (log2 units),
-//                        1/l_i, c_i = sum_j A_ji (G X^T)_ji, written out;
+//   pass 1 (grad_stats)  per row i: lse_i = log2 sum_j 2^s'_ji (s' in log2
+//                        units), c_i = sum_j A_ji (G X^T)_ji, written out;
 //                        dQ' += dS X with dS = A * (G X^T - c), split over
 //                        groups like the forward partial sketches
 //   pass 2 (grad_dx)     dX = A^T G + dS^T Q' per row, with A and dS
@@ -27,11 +27,12 @@ struct GradStatsArgs {
   const void* X;      // bf16 rows of this launch [rows][d]
   const void* M;      // bf16 [k_pad][d], tau log2(e) P W_Q W_K^T (padding rows zero)
   const float* G;     // float32 [users][k][d], upstream gradient of this launch's users
-  float* stats;       // float32 [rows][4]: m_i, 1 / l_i, c_i, 0
+  float* stats;       // float32 [rows][4]: lse_i = m_i + log2 l_i (log2 units), c_i, 0, 0
   float* partial;     // float32 [groups][k_pad * d] in the lane layout of the forward partials
   int64_t rows;
   int32_t users;
   int32_t k;
+  int32_t force_shift;  // 1: every row block takes the shifted (row maximum) path
   int64_t offsets[kMaxUsersPerLaunch + 1];
 };
 

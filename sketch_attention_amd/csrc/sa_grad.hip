@@ -194,29 +194,55 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   };
   // per-wave row statistics of the scores in s, da: m_w, sum 2^(s' - m_w),
   // sum 2^(s' - m_w) dA into xs[par]
+  // Unshifted first: 2^s' needs no row maximum while a row's sum over the
+  // wave's prototypes stays within [2^-100, 2^100]; a wave that sees a row
+  // outside it (huge scores, or all of its prototypes far below) redoes that
+  // row block with its own row maxima m_w.  The merge takes any mix of shifts.
+  const bool real_protos = jbase < k;  // wave-uniform: false for a wave of padding prototypes only
   auto row_stats = [&](int par) {
 #pragma unroll
     for (int ib = 0; ib < RB; ++ib) {
-      float mw[4], pl[4], pc[4];
+      float zm = 0.f, zl = 0.f, zc = 0.f;
+      if (real_protos) {
+        float pl[4], pc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = s[ib][0][r];
+        for (int r = 0; r < 4; ++r) {
+          pl[r] = 0.f;
+          pc[r] = 0.f;
 #pragma unroll
-        for (int jb = 1; jb < JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
-        mw[r] = row16_max(m);
-        const float ms = mw[r] == -INFINITY ? 0.f : mw[r];  // a wave of padding prototypes only
-        pl[r] = 0.f;
-        pc[r] = 0.f;
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-          const float e = fast_exp2(s[ib][jb][r] - ms);
-          pl[r] += e;
-          pc[r] += e * da[ib][jb][r];
+          for (int jb = 0; jb < JB; ++jb) {
+            const float e = fast_exp2(s[ib][jb][r]);
+            pl[r] += e;
+            pc[r] += e * da[ib][jb][r];
+          }
         }
+        zl = rows4_sum_scatter(pl, l16);
+        zc = rows4_sum_scatter(pc, l16);
+        if (args.force_shift ||
+            __builtin_amdgcn_ballot_w64(!(zl >= 0x1p-100f && zl <= 0x1p100f) || !(fabsf(zc) <= 0x1p120f)) != 0) {
+          float mw[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float m = s[ib][0][r];
+#pragma unroll
+            for (int jb = 1; jb < JB; ++jb) m = fmaxf(m, s[ib][jb][r]);
+            mw[r] = row16_max(m);
+            pl[r] = 0.f;
+            pc[r] = 0.f;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) {
+              const float e = fast_exp2(s[ib][jb][r] - mw[r]);
+              pl[r] += e;
+              pc[r] += e * da[ib][jb][r];
+            }
+          }
+          zl = rows4_sum_scatter(pl, l16);
+          zc = rows4_sum_scatter(pc, l16);
+          zm = sc_r == 0 ? mw[0] : sc_r == 1 ? mw[1] : sc_r == 2 ? mw[2] : mw[3];
+        }
+      } else {
+        zm = -INFINITY;  // contributes nothing to the merge
       }
-      const float zl = rows4_sum_scatter(pl, l16);
-      const float zc = rows4_sum_scatter(pc, l16);
-      const float zm = sc_r == 0 ? mw[0] : sc_r == 1 ? mw[1] : sc_r == 2 ? mw[2] : mw[3];
       const int trow = 16 * ib + 4 * g + sc_r;
       xs_m[par][trow][wj] = zm;
       xs_l[par][trow][wj] = zl;
@@ -263,12 +289,13 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
       l += xs_l[par][my_row][w] * f;
       c += xs_c[par][my_row][w] * f;
     }
-    float inv = 1.f / l;
-    c *= inv;
+    c *= 1.f / l;
+    // log-sum-exp of the row in log2 units: A = 2^(s' - lse)
+    float lse = m + __builtin_amdgcn_logf(l);
     const bool valid = (int64_t)my_row < cc.end - cc.row;
-    if (!valid) inv = 0.f;  // rows past the piece add nothing
     if (valid && wj == 0 && l16 < 8)
-      *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{m, inv, c, 0.f};
+      *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{lse, c, 0.f, 0.f};
+    if (!valid) lse = INFINITY;  // rows past the piece add nothing
 
     // dS of this wave's prototypes as bf16 weights of the aggregation
     // (computed in float first and converted in element order, so that
@@ -278,20 +305,20 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float mm, ii, cv;
+        float mm, cv;
         switch (4 * ib + r) {
-          case 0: mm = row_bcast<0>(m); ii = row_bcast<0>(inv); cv = row_bcast<0>(c); break;
-          case 1: mm = row_bcast<1>(m); ii = row_bcast<1>(inv); cv = row_bcast<1>(c); break;
-          case 2: mm = row_bcast<2>(m); ii = row_bcast<2>(inv); cv = row_bcast<2>(c); break;
-          case 3: mm = row_bcast<3>(m); ii = row_bcast<3>(inv); cv = row_bcast<3>(c); break;
-          case 4: mm = row_bcast<4>(m); ii = row_bcast<4>(inv); cv = row_bcast<4>(c); break;
-          case 5: mm = row_bcast<5>(m); ii = row_bcast<5>(inv); cv = row_bcast<5>(c); break;
-          case 6: mm = row_bcast<6>(m); ii = row_bcast<6>(inv); cv = row_bcast<6>(c); break;
-          default: mm = row_bcast<7>(m); ii = row_bcast<7>(inv); cv = row_bcast<7>(c); break;
+          case 0: mm = row_bcast<0>(lse); cv = row_bcast<0>(c); break;
+          case 1: mm = row_bcast<1>(lse); cv = row_bcast<1>(c); break;
+          case 2: mm = row_bcast<2>(lse); cv = row_bcast<2>(c); break;
+          case 3: mm = row_bcast<3>(lse); cv = row_bcast<3>(c); break;
+          case 4: mm = row_bcast<4>(lse); cv = row_bcast<4>(c); break;
+          case 5: mm = row_bcast<5>(lse); cv = row_bcast<5>(c); break;
+          case 6: mm = row_bcast<6>(lse); cv = row_bcast<6>(c); break;
+          default: mm = row_bcast<7>(lse); cv = row_bcast<7>(c); break;
         }
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) {
-          const float A = fast_exp2(s[ib][jb][r] - mm) * ii;
+          const float A = fast_exp2(s[ib][jb][r] - mm);
           dsv[jb][4 * ib + r] = A * (da[ib][jb][r] - cv);
         }
       }
@@ -379,7 +406,7 @@ __global__ __launch_bounds__(256) void grad_pack_kernel(const bf16* M, const bf1
   packed[(uc * 4 + part) * BLK + pos] = v;
 }
 
-template <int D, int W2>
+template <int D, int W2, bool PAD>
 __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
   constexpr int KW = kGradKW, NT = 32 * W2, CS = D / 32, DB = D / 16;
   constexpr int BLK = KW * D * 2;        // bytes of one block of a chunk
@@ -454,7 +481,7 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
     const int64_t lim = cur.end - 1 - cur.row;
     const bool busy = rw <= lim;  // the wave has rows in this tile (wave-uniform)
     bf16x8 xr[2][CS];
-    float sm[2], si[2], sc[2];
+    float sl[2], sc[2];  // log-sum-exp (log2 units, +inf past the piece) and c of rows 16 ib + l16
     bool valid[2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
@@ -464,9 +491,8 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs) xr[ib][cs] = frag_c<D>(X + row * D, cs, g);
       const f32x4 st = *reinterpret_cast<const f32x4*>(args.stats + row * 4);
-      sm[ib] = st[0];
-      si[ib] = valid[ib] ? st[1] : 0.f;
-      sc[ib] = st[2];
+      sl[ib] = valid[ib] ? st[0] : INFINITY;
+      sc[ib] = st[1];
     }
     f32x4 acc[2][DB];
 #pragma unroll
@@ -506,8 +532,8 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int jb = e >> 2, r = e & 3;
-          const bool ok = KW * c + 16 * jb + 4 * g + r < k;
-          const float A = ok ? fast_exp2(s[jb][ib][r] - sm[ib]) * si[ib] : 0.f;
+          const bool ok = !PAD || KW * c + 16 * jb + 4 * g + r < k;
+          const float A = ok ? fast_exp2(s[jb][ib][r] - sl[ib]) : 0.f;
           wa[ib][e] = (bf16)A;
           wd[ib][e] = (bf16)(A * (da[jb][ib][r] - sc[ib]));
         }
@@ -628,14 +654,20 @@ hipError_t stats_d(int waves, const GradStatsArgs& a, int groups, hipStream_t s,
 
 constexpr int kDxWaves = 8;
 
+template <int D, bool PAD>
+hipError_t dx_p(const GradDxArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
+  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_dx_kernel<D, kDxWaves, PAD>, 64 * kDxWaves, 0);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((grad_dx_kernel<D, kDxWaves, PAD>), dim3(groups), dim3(64 * kDxWaves), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((grad_dx_kernel<D, kDxWaves, PAD>), dim3(groups), dim3(64 * kDxWaves), 0, s, a);
+  return hipGetLastError();
+}
+// padding prototypes (k below 32 chunks) need their weights masked; the occupancy is that of the padded form
 template <int D>
 hipError_t dx_t(const GradDxArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
-  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_dx_kernel<D, kDxWaves>, 64 * kDxWaves, 0);
-  if (e0 || e1)
-    hipExtLaunchKernelGGL((grad_dx_kernel<D, kDxWaves>), dim3(groups), dim3(64 * kDxWaves), 0, s, e0, e1, 0, a);
-  else
-    hipLaunchKernelGGL((grad_dx_kernel<D, kDxWaves>), dim3(groups), dim3(64 * kDxWaves), 0, s, a);
-  return hipGetLastError();
+  if (occ || a.k != kGradKW * a.chunks) return dx_p<D, true>(a, groups, s, e0, e1, occ);
+  return dx_p<D, false>(a, groups, s, e0, e1, occ);
 }
 
 }  // namespace

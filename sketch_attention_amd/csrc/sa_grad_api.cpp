@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <new>
 #include <vector>
 
@@ -219,6 +220,10 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     a1.rows = rows;
     a1.users = users;
     a1.k = k;
+    // SA_GRAD_FORCE_SHIFT=1 routes every row block through the shifted path
+    // of the statistics pass (that path otherwise runs only for extreme scores)
+    const char* fs = std::getenv("SA_GRAD_FORCE_SHIFT");
+    a1.force_shift = fs != nullptr && fs[0] == '1';
     for (int32_t u = 0; u <= users; ++u) a1.offsets[u] = offsets[u0 + u] - base;
     const int g1 = (int)(rows < stats_groups_max ? rows : stats_groups_max);
     const bool last = u1 == num_users;

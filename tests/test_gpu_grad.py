@@ -73,6 +73,43 @@ def test_grad_parity(case):
     _check(wl, G, _run(wl, G))
 
 
+def test_grad_spike_rows_take_the_shifted_path():
+    """Rows scaled by 100 give scores of several hundred (log2 units): their
+    unshifted sums overflow in the waves holding the top prototypes and
+    underflow in the others, so the statistics pass redoes them with row
+    maxima.  dX is compared at the usual tolerance (the spike rows' top two
+    scores are >= 10 log2 units apart, so their assignment is well
+    conditioned).  The weight gradients are not: dQ' weighs each spike row by
+    |x|^2 = 10^4 times a runner-up weight <= 2^-10 whose relative error from
+    the bf16 rounding of a score of ~400 (about 1 log2 unit) is O(1); they are
+    only required to be finite here, and the shifted path's weight gradients
+    are checked at normal scale by the forced-shift test below."""
+    wl = W.make_workload(lengths=[3000, 500, 64], d=128, k=256, dtype="bf16", seed=13, name="spikes")
+    # rows whose two best prototypes are >= 10 log2 units apart (checked against the oracle's scores)
+    for r in (0, 1, 100, 102, 2999, 3000, 3002, 3499, 3500, 3563):
+        wl.X[r] = W.round_to_bf16(wl.X[r] * 100.0)
+    G = W.make_upstream_grad(3, 256, 128, seed=17)
+    got = _run(wl, G)
+    want = GO.sketch_grad_batch(wl.X, wl.offsets, wl.P, wl.W_Q, wl.W_K, wl.tau, G)
+    e = _nerr(got[0], want["dX"])
+    print(f"[grad] spikes dX {e:.3e}", flush=True)
+    assert e <= TOL["bf16"], e
+    for t in got[1:]:
+        assert np.all(np.isfinite(t))
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("k256_d128", "k200_d128_pad", "k100_d64_pad",
+                                                                 "k256_hot")], ids=lambda c: c[0])
+def test_grad_forced_shift_path(case, monkeypatch):
+    """Every row block through the statistics pass's shifted path (its fallback
+    for extreme scores), at normal scale, all four gradients at tolerance."""
+    monkeypatch.setenv("SA_GRAD_FORCE_SHIFT", "1")
+    name, d, k, lengths, extra = case
+    wl = W.make_workload(lengths=lengths, d=d, k=k, dtype="bf16", seed=31, name=name + "_shift", **extra)
+    G = W.make_upstream_grad(len(lengths), k, d, seed=5)
+    _check(wl, G, _run(wl, G))
+
+
 def test_grad_many_users_two_launches():
     rng = np.random.default_rng(3)
     lengths = [int(x) for x in rng.integers(0, 60, size=300)]
