@@ -586,28 +586,26 @@ __global__ __launch_bounds__(256) void small_matmul_kernel(MatmulPair pr) {
   const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 16;
   if (m0 >= p.rows || n0 >= p.cols) return;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  // consecutive threads walk the operand's unit-stride dimension (coalesced loads)
-  const bool a_rows_fast = p.a_rs < p.a_cs, b_rows_fast = p.b_rs < p.b_cs;
-  constexpr int PER = 16 * kMaxInner / 256;  // elements of each operand per thread, all loaded before any store
-  float av[PER], bv[PER];
+  // all loads in flight before any store; index arithmetic by shifts only
+  // (a runtime division per element costs more than the loads)
+  float av[16], bv[kMaxInner / 16];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + 256 * i;
-    av[i] = bv[i] = 0.f;
-    if (e < 16 * p.inner) {
-      const int mm = a_rows_fast ? e & 15 : e / p.inner, tt = a_rows_fast ? e >> 4 : e % p.inner;
-      if (m0 + mm < p.rows) av[i] = p.A[(m0 + mm) * p.a_rs + tt * p.a_cs];
-      const int tb = b_rows_fast ? e % p.inner : e >> 4, nn = b_rows_fast ? e / p.inner : e & 15;
-      if (n0 + nn < p.cols) bv[i] = p.B[tb * p.b_rs + (n0 + nn) * p.b_cs];
-    }
+  for (int mm = 0; mm < 16; ++mm) {
+    const int tt = threadIdx.x;
+    av[mm] = tt < p.inner && m0 + mm < p.rows ? p.A[(m0 + mm) * p.a_rs + tt * p.a_cs] : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < kMaxInner / 16; ++i) {
+    const int e = threadIdx.x + 256 * i, tb = e >> 4, nn = e & 15;
+    bv[i] = tb < p.inner && n0 + nn < p.cols ? p.B[tb * p.b_rs + (n0 + nn) * p.b_cs] : 0.f;
+  }
+#pragma unroll
+  for (int mm = 0; mm < 16; ++mm)
+    if (threadIdx.x < p.inner) As[mm][threadIdx.x] = av[mm];
+#pragma unroll
+  for (int i = 0; i < kMaxInner / 16; ++i) {
     const int e = threadIdx.x + 256 * i;
-    if (e < 16 * p.inner) {
-      As[a_rows_fast ? e & 15 : e / p.inner][a_rows_fast ? e >> 4 : e % p.inner] = av[i];
-      Bs[b_rows_fast ? e % p.inner : e >> 4][b_rows_fast ? e / p.inner : e & 15] = bv[i];
-    }
+    if ((e >> 4) < p.inner) Bs[e >> 4][e & 15] = bv[i];
   }
   __syncthreads();
   float s0 = 0.f, s1 = 0.f;
