@@ -298,6 +298,49 @@ sa_status sa_grad_read_kernel_timing(sa_grad h, double* stats_ms, double* dx_ms,
 /* sa_grad_destroy -- free the handle (NULL allowed) after its streams are synchronised. */
 void sa_grad_destroy(sa_grad h);
 
+/*
+ * Action fusion (section 2.2): the history row of behaviour i is built from
+ * the item embedding e_i and the embedding a_i of its action type,
+ *   x_i = e_i + (silu(z_i W_gate) * (z_i W_up)) W_down,  z_i = [e_i ; a_i],
+ * silu(v) = v / (1 + exp(-v)), no biases.  The page gives neither the action
+ * embedding width nor the FFN width: here a_i = action_table[action_i] with
+ * d_a columns and the gated layer has d_ff columns (parameters).
+ *
+ * sa_action_check_config -- SA_BF16 only, d in {64, 128}, d_a a multiple of 8
+ * with d + d_a <= 256, d_ff a multiple of 64 (of 32 when d + d_a > 192 for
+ * d = 128) and at most 4096, 1 <= n_actions <= 2^20; else SA_ERR_UNSUPPORTED
+ * or SA_ERR_INVALID_ARG.
+ *
+ * sa_action_create -- device pointers in the dtype, row-major, 16-byte
+ * aligned: action_table [n_actions][d_a] (may be NULL when d_a == 0),
+ * W_gate and W_up [d + d_a][d_ff], W_down [d_ff][d].  Copied and packed
+ * (the caller's buffers are not used after the call); synchronises stream.
+ */
+typedef struct sa_action_s* sa_action;
+sa_status sa_action_check_config(int32_t d, int32_t d_a, int32_t d_ff, int32_t n_actions, sa_dtype dtype);
+sa_status sa_action_create(sa_action* out, int32_t d, int32_t d_a, int32_t d_ff, int32_t n_actions, sa_dtype dtype,
+                           const void* action_table, const void* W_gate, const void* W_up, const void* W_down,
+                           void* stream);
+
+/*
+ * sa_action_fuse -- X[i] = x_i for rows i < rows (enqueued on stream).
+ *   E        device, bf16 [rows][d], 16-byte aligned
+ *   actions  device, int32 [rows], 4-byte aligned; ids outside
+ *            [0, n_actions) are clamped into it (the device cannot report them)
+ *   X        device, bf16 [rows][d], 16-byte aligned, fully overwritten; it is
+ *            the history input of sa_compress_batch
+ * rows == 0 is a no-op.  Calls on one handle may overlap (no workspace).
+ */
+sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actions, int64_t rows, void* X, void* stream);
+
+/* HIP events on the pass's dispatch (as for sa_set_kernel_timing): total
+ * milliseconds and launches since the last read. */
+sa_status sa_action_set_kernel_timing(sa_action h, int32_t enable);
+sa_status sa_action_read_kernel_timing(sa_action h, double* ms, int64_t* launches);
+
+/* sa_action_destroy -- free the handle (NULL allowed) after its streams are synchronised. */
+void sa_action_destroy(sa_action h);
+
 #ifdef __cplusplus
 }
 #endif

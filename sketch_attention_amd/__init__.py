@@ -6,10 +6,15 @@ workloads.  The library itself is loaded on first use, so the workloads can
 be used without it; any call into the binding fails loudly when it is absent.
 """
 from .binding import (  # noqa: F401
+    ActionFusion,
     SAError,
     SketchAttention,
     SketchAttentionGrad,
     SketchStack,
+    sa_action_check_config,
+    sa_action_create,
+    sa_action_destroy,
+    sa_action_fuse,
     sa_check_batch,
     sa_check_config,
     sa_compress_batch,

@@ -40,6 +40,8 @@ EXPORTED = (
     "sa_stack_read_kernel_timing",
     "sa_grad_check_config", "sa_grad_create", "sa_grad_compute", "sa_grad_destroy", "sa_grad_set_kernel_timing",
     "sa_grad_read_kernel_timing",
+    "sa_action_check_config", "sa_action_create", "sa_action_fuse", "sa_action_destroy",
+    "sa_action_set_kernel_timing", "sa_action_read_kernel_timing",
 )
 
 
@@ -96,6 +98,12 @@ def library() -> ctypes.CDLL:
         "sa_grad_destroy": (None, [vp]),
         "sa_grad_set_kernel_timing": (i32, [vp, i32]),
         "sa_grad_read_kernel_timing": (i32, [vp, p_f64, p_f64, p_i64]),
+        "sa_action_check_config": (i32, [i32, i32, i32, i32, i32]),
+        "sa_action_create": (i32, [ctypes.POINTER(vp), i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "sa_action_fuse": (i32, [vp, vp, vp, i64, vp, vp]),
+        "sa_action_destroy": (None, [vp]),
+        "sa_action_set_kernel_timing": (i32, [vp, i32]),
+        "sa_action_read_kernel_timing": (i32, [vp, p_f64, p_i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -495,6 +503,104 @@ class SketchAttentionGrad:
     def close(self) -> None:
         if getattr(self, "handle", None) is not None:
             sa_grad_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------ action fusion
+def sa_action_check_config(d: int, d_a: int, d_ff: int, n_actions: int, dtype: Union[str, torch.dtype]) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else _DTYPE_NAMES.get(dtype, 99)
+    return int(library().sa_action_check_config(int(d), int(d_a), int(d_ff), int(n_actions), code))
+
+
+def sa_action_create(table: Optional[torch.Tensor], W_gate: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor,
+                     n_actions: int, stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    """Pack the action-fusion weights (see include/sa.h); table may be None when d_a == 0."""
+    for t, n in ((W_gate, "W_gate"), (W_up, "W_up"), (W_down, "W_down")):
+        _device_tensor(t, n)
+    if table is not None:
+        _device_tensor(table, "action_table")
+    d_ff, d = W_down.shape
+    k_in = W_gate.shape[0]
+    d_a = k_in - d
+    if tuple(W_up.shape) != (k_in, d_ff) or W_gate.shape[1] != d_ff or d_a < 0:
+        raise ValueError("W_gate, W_up must be [d + d_a, d_ff] and W_down [d_ff, d]")
+    if d_a > 0 and (table is None or tuple(table.shape) != (n_actions, d_a)):
+        raise ValueError("action_table must be [n_actions, d_a]")
+    dt = W_down.dtype
+    if dt not in _DTYPES or any(t.dtype != dt for t in (W_gate, W_up) + ((table,) if d_a > 0 else ())):
+        raise ValueError("weights and table must share one dtype")
+    h = ctypes.c_void_p()
+    dev = W_down.device
+    with torch.cuda.device(dev):
+        st = library().sa_action_create(ctypes.byref(h), int(d), int(d_a), int(d_ff), int(n_actions), _DTYPES[dt],
+                                        ctypes.c_void_p(table.data_ptr() if d_a > 0 else 0),
+                                        ctypes.c_void_p(W_gate.data_ptr()), ctypes.c_void_p(W_up.data_ptr()),
+                                        ctypes.c_void_p(W_down.data_ptr()), _stream_ptr(stream, dev))
+    _check(st, "sa_action_create")
+    return h
+
+
+def sa_action_fuse(handle: ctypes.c_void_p, E: torch.Tensor, actions: torch.Tensor, X: torch.Tensor,
+                   stream: Optional[torch.cuda.Stream] = None) -> None:
+    for t, n in ((E, "E"), (actions, "actions"), (X, "X")):
+        _device_tensor(t, n)
+    if actions.dtype != torch.int32 or actions.dim() != 1 or actions.shape[0] != E.shape[0]:
+        raise ValueError("actions must be int32 [rows]")
+    if tuple(X.shape) != tuple(E.shape) or X.dtype != E.dtype:
+        raise ValueError("X must match E")
+    if stream is None:
+        stream = torch.cuda.current_stream(E.device)
+    _check(library().sa_action_fuse(handle, E.data_ptr(), actions.data_ptr(), int(E.shape[0]), X.data_ptr(),
+                                    stream.cuda_stream), "sa_action_fuse")
+
+
+def sa_action_destroy(handle: Optional[ctypes.c_void_p]) -> None:
+    if handle is not None and handle.value:
+        library().sa_action_destroy(handle)
+
+
+def sa_action_set_kernel_timing(handle: ctypes.c_void_p, enable: bool) -> None:
+    _check(library().sa_action_set_kernel_timing(handle, 1 if enable else 0), "sa_action_set_kernel_timing")
+
+
+def sa_action_read_kernel_timing(handle: ctypes.c_void_p):
+    """Returns (ms_total, launches) since the last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(library().sa_action_read_kernel_timing(handle, ctypes.byref(ms), ctypes.byref(n)),
+           "sa_action_read_kernel_timing")
+    return ms.value, n.value
+
+
+class ActionFusion:
+    """Owns one action-fusion handle: x = e + SwiGLU-FFN([e; table[action]]) (section 2.2)."""
+
+    def __init__(self, table: Optional[torch.Tensor], W_gate: torch.Tensor, W_up: torch.Tensor,
+                 W_down: torch.Tensor, n_actions: int, stream: Optional[torch.cuda.Stream] = None):
+        self.handle = sa_action_create(table, W_gate, W_up, W_down, n_actions, stream)
+        self.d = int(W_down.shape[1])
+
+    def fuse(self, E: torch.Tensor, actions: torch.Tensor, out: Optional[torch.Tensor] = None,
+             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(E)
+        sa_action_fuse(self.handle, E, actions, out, stream)
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None:
+            sa_action_destroy(self.handle)
             self.handle = None
 
     def __enter__(self):

@@ -33,6 +33,8 @@ SOURCES = [
     "sa_refine.hip",
     "sa_grad.hip",
     "sa_grad_api.cpp",
+    "sa_action.hip",
+    "sa_action_api.cpp",
 ]
 # The bf16 plans (accumulators of at most 128 registers per lane) keep every
 # matrix-core result in VGPRs, so the softmax reads the affinity tile without

@@ -1,0 +1,290 @@
+// Action fusion on gfx950 (bf16 operands, float32 accumulation):
+// SequenceO1 close-reading page, section 2.2 -- each history row is
+//
+//   x_i = e_i + (silu(z_i W_gate) * (z_i W_up)) W_down,   z_i = [e_i ; a_i],
+//
+// e_i the item embedding, a_i = table[action_i] the action-type embedding.
+// One pass over the rows; waves own rows, the weights stream through LDS:
+//
+//   8 waves x 32 rows per 256-row tile.  z for the wave's rows is built in
+//   registers as matrix-core B operands (rows along the lanes, 8 consecutive
+//   features per lane group): fragments of e_i from HBM, of a_i from the
+//   (cache-resident) table, zero past d + d_a (K padded to a multiple of 64).
+//   The FFN width is walked in chunks of 32 whose weights (W_gate and W_up
+//   transposed, W_down transposed with its rows permuted) are packed once
+//   and arrive by LDS DMA, double-buffered.  Per chunk:
+//     gate^T, up^T  = W^T z^T        (A = weight rows, B = z: rows on lanes)
+//     H = silu(gate) * up            in registers, already in the B-operand
+//                                    layout of the next product: the 16x16
+//                                    output puts chunk column 16 (e/4) + 4 g
+//                                    + e%4 in slot (g, e) of row l16
+//     x^T          += W_down^T H^T   (A = W_down^T rows permuted to match)
+//   and x = e + (x^T)^T is stored in bf16, four columns per lane.
+#include <hip/hip_runtime.h>
+
+#include "sa_action.h"
+#include "sa_stream.hpp"
+
+namespace sa {
+
+namespace {
+
+constexpr int kActWaves = 8;
+
+// Byte layout of one packed chunk (32 FFN columns): W_gate^T block [32][KP],
+// W_up^T block [32][KP] (16-byte chunk h of row f at h ^ (f % 8)), then the
+// W_down^T block [D][32] (row c holds W_down[32 c0 + perm(pos)][c] at
+// position pos = 8 g + e, perm = 16 (e / 4) + 4 g + e % 4; chunk g stored at
+// g ^ 2 ((c / 8) % 2)).
+template <int D, int KP>
+struct ActGeom {
+  static constexpr int W_BYTES = 32 * KP * 2;
+  static constexpr int D_BYTES = D * 32 * 2;
+  static constexpr int CHUNK = 2 * W_BYTES + D_BYTES;
+  static constexpr int CPS = 4 * CHUNK <= 144 * 1024 ? 2 : 1;  // chunks per step (two steps' buffers in LDS)
+  static constexpr int STEP = CPS * CHUNK;
+  static_assert(STEP % 1024 == 0, "whole DMA blocks");
+  static constexpr int NBLK = STEP / 1024;
+  static constexpr int BPW = (NBLK + kActWaves - 1) / kActWaves;
+};
+
+template <int D, int KP>
+__global__ __launch_bounds__(256) void action_pack_kernel(const bf16* Wg, const bf16* Wu, const bf16* Wd, int kin,
+                                                          int d_ff, bf16* packed) {
+  using G = ActGeom<D, KP>;
+  constexpr int CH_ELEMS = G::CHUNK / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int chunks = d_ff / 32;
+  if (idx >= (int64_t)chunks * CH_ELEMS) return;
+  const int c = (int)(idx / CH_ELEMS), w = (int)(idx % CH_ELEMS);
+  bf16 v;
+  int pos;
+  if (w < 2 * 32 * KP) {
+    const bf16* W = w < 32 * KP ? Wg : Wu;
+    const int ww = w % (32 * KP), f = ww / KP, kk = ww % KP;
+    v = kk < kin ? W[(int64_t)kk * d_ff + 32 * c + f] : (bf16)0.f;
+    pos = (w / (32 * KP)) * 32 * KP + f * KP + 8 * ((kk >> 3) ^ (f & 7)) + (kk & 7);
+  } else {
+    const int ww = w - 2 * 32 * KP, col = ww / 32, p = ww % 32, gg = p >> 3, e = p & 7;
+    const int f = 32 * c + 16 * (e >> 2) + 4 * gg + (e & 3);
+    v = Wd[(int64_t)f * D + col];
+    pos = 2 * 32 * KP + col * 32 + 8 * (gg ^ (2 * ((col >> 3) & 1))) + e;
+  }
+  packed[(int64_t)c * CH_ELEMS + pos] = v;
+}
+
+template <int D, int KP>
+__global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs args) {
+  using G = ActGeom<D, KP>;
+  using MF = Mfma<bf16>;
+  constexpr int NT = 32 * kActWaves, KS = KP / 32, CB = D / 16, CPS = G::CPS;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * G::STEP];
+  const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = 32 * wave;
+  const bf16* const E = static_cast<const bf16*>(args.E);
+  const bf16* const T = static_cast<const bf16*>(args.table);
+  const unsigned char* const packed = static_cast<const unsigned char*>(args.packed);
+  bf16* const X = static_cast<bf16*>(args.X);
+  const int chunks = args.chunks, steps = chunks / CPS;
+
+  const int64_t rows = args.rows, ngroups = gridDim.x, grp = blockIdx.x;
+  const int64_t r_begin = grp * rows / ngroups, r_end = (grp + 1) * rows / ngroups;
+  if (r_begin >= r_end) return;
+
+  auto issue_step = [&](int s, int b) {
+    const unsigned char* src = packed + (int64_t)s * G::STEP;
+#pragma unroll
+    for (int i = 0; i < G::BPW; ++i) {
+      const int j = wave + kActWaves * i;
+      if (G::NBLK % kActWaves == 0 || j < G::NBLK)
+        dma16(src, (uint32_t)(1024 * j + 16 * lane), lds0 + (uint32_t)(b * G::STEP + 1024 * j));
+    }
+  };
+  // fragment offsets: weight row 16 fb + l16, chunk 4 ks + g (swizzled by the row's low bits);
+  // W_down^T row 16 cb + l16, chunk g
+  uint32_t woff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) woff[ks] = (uint32_t)(2 * (l16 * KP + 8 * ((4 * ks + g) ^ (l16 & 7))));
+  const uint32_t doff = (uint32_t)(2 * 2 * 32 * KP + 2 * (l16 * 32 + 8 * (g ^ (2 * ((l16 >> 3) & 1)))));
+
+  int q = 0;
+  issue_step(0, 0);
+  wait_vm<0>();
+  __syncthreads();
+  for (int64_t t0 = r_begin; t0 < r_end; t0 += NT) {
+    const int64_t lim = r_end - 1 - t0;
+    const bool busy = rw <= lim;  // wave-uniform
+    // z = [e ; a ; 0] for rows 16 ib + l16 of this wave, K slots 32 ks + 8 g ..
+    bf16x8 zf[2][KS];
+    bool valid[2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int r = rw + 16 * ib + l16;
+      valid[ib] = r <= lim;
+      const int64_t row = t0 + (r <= lim ? r : lim);
+      int act = args.actions[row];
+      act = act < 0 ? 0 : (act >= args.n_actions ? args.n_actions - 1 : act);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int k0 = 32 * ks + 8 * g;
+        if (k0 < D) {
+          zf[ib][ks] = *reinterpret_cast<const bf16x8*>(E + row * D + k0);
+        } else if (k0 < D + args.d_a) {
+          zf[ib][ks] = *reinterpret_cast<const bf16x8*>(T + (int64_t)act * args.d_a + (k0 - D));
+        } else {
+          zf[ib][ks] = bf16x8{};
+        }
+      }
+    }
+    f32x4 acc[2][CB];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < steps; ++s) {
+      const bool last_tile = t0 + NT >= r_end;
+      if (s + 1 < steps) issue_step(s + 1, q ^ 1);
+      else if (!last_tile) issue_step(0, q ^ 1);
+      if (busy) {
+#pragma unroll
+        for (int h = 0; h < CPS; ++h) {
+          const uint32_t buf = lds0 + (uint32_t)(q * G::STEP + h * G::CHUNK);
+          // gate^T and up^T: [fb][ib] holds column 16 fb + 4 g + r of the chunk for row 16 ib + l16
+          f32x4 ga[2][2], ua[2][2];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb) {
+              const uint32_t o = woff[ks] + (uint32_t)(2 * 16 * fb * KP);
+              const bf16x8 wg = lds_b128(buf + o);
+              const bf16x8 wu = lds_b128(buf + (uint32_t)G::W_BYTES + o);
+#pragma unroll
+              for (int ib = 0; ib < 2; ++ib) {
+                const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+                ga[fb][ib] = MF::run(wg, zf[ib][ks], ks == 0 ? z : ga[fb][ib]);
+                ua[fb][ib] = MF::run(wu, zf[ib][ks], ks == 0 ? z : ua[fb][ib]);
+              }
+            }
+          }
+          // H = silu(gate) * up, slot (g, e) <-> column 16 (e / 4) + 4 g + e % 4
+          bf16x8 hf[2];
+#pragma unroll
+          for (int ib = 0; ib < 2; ++ib) {
+            float hv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float gv = ga[e >> 2][ib][e & 3];
+              hv[e] = gv * __builtin_amdgcn_rcpf(1.f + fast_exp2(-1.4426950408889634f * gv)) * ua[e >> 2][ib][e & 3];
+            }
+            typedef float f32x8 __attribute__((ext_vector_type(8)));
+            hf[ib] = __builtin_convertvector((f32x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]}), bf16x8);
+          }
+          // x^T[16 cb + 4 g + r][row 16 ib + l16] += W_down^T H^T over the chunk
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            const bf16x8 wd = lds_b128(buf + doff + (uint32_t)(2 * 16 * cb * 32));
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) acc[ib][cb] = MF::run(wd, hf[ib], acc[ib][cb]);
+          }
+        }
+      }
+      wait_vm<0>();
+      __syncthreads();
+      q ^= 1;
+    }
+    // x = e + FFN: this lane holds columns 16 cb + 4 g .. + 3 of row 16 ib + l16
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      if (!valid[ib]) continue;
+      const int64_t row = t0 + rw + 16 * ib + l16;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 ev = *reinterpret_cast<const bf16x4*>(E + row * D + 16 * cb + 4 * g);
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)((float)ev[r] + acc[ib][cb][r]);
+        *reinterpret_cast<bf16x4*>(X + row * D + 16 * cb + 4 * g) = v;
+      }
+    }
+  }
+  wait_vm<0>();
+}
+
+template <int D, int KP>
+hipError_t fuse_t(const ActionArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
+  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, action_fuse_kernel<D, KP>, 64 * kActWaves, 0);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((action_fuse_kernel<D, KP>), dim3(groups), dim3(64 * kActWaves), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((action_fuse_kernel<D, KP>), dim3(groups), dim3(64 * kActWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t fuse_d(int kp, const ActionArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
+  switch (kp) {
+    case 64: return D == 64 ? fuse_t<64, 64>(a, groups, s, e0, e1, occ) : hipErrorInvalidValue;
+    case 128: return fuse_t<D, 128>(a, groups, s, e0, e1, occ);
+    case 192: return fuse_t<D, 192>(a, groups, s, e0, e1, occ);
+    case 256: return fuse_t<D, 256>(a, groups, s, e0, e1, occ);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int KP>
+hipError_t pack_t(const void* Wg, const void* Wu, const void* Wd, int kin, int d_ff, void* packed, hipStream_t s) {
+  const int64_t total = (int64_t)(d_ff / 32) * (ActGeom<D, KP>::CHUNK / 2);
+  hipLaunchKernelGGL((action_pack_kernel<D, KP>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     (const bf16*)Wg, (const bf16*)Wu, (const bf16*)Wd, kin, d_ff, (bf16*)packed);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int action_kpad(int d, int d_a) { return 64 * ((d + d_a + 63) / 64); }
+
+size_t action_packed_bytes(int d, int kp, int d_ff) {
+  return (size_t)(d_ff / 32) * (size_t)(2 * 32 * kp * 2 + d * 32 * 2);
+}
+
+hipError_t launch_action_pack(int d, int kp, const void* Wg, const void* Wu, const void* Wd, int d_a, int d_ff,
+                              void* packed, hipStream_t s) {
+  const int kin = d + d_a;
+  if (d == 128) {
+    if (kp == 128) return pack_t<128, 128>(Wg, Wu, Wd, kin, d_ff, packed, s);
+    if (kp == 192) return pack_t<128, 192>(Wg, Wu, Wd, kin, d_ff, packed, s);
+    if (kp == 256) return pack_t<128, 256>(Wg, Wu, Wd, kin, d_ff, packed, s);
+  } else if (d == 64) {
+    if (kp == 64) return pack_t<64, 64>(Wg, Wu, Wd, kin, d_ff, packed, s);
+    if (kp == 128) return pack_t<64, 128>(Wg, Wu, Wd, kin, d_ff, packed, s);
+    if (kp == 192) return pack_t<64, 192>(Wg, Wu, Wd, kin, d_ff, packed, s);
+    if (kp == 256) return pack_t<64, 256>(Wg, Wu, Wd, kin, d_ff, packed, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_action_fuse(int d, int kp, const ActionArgs& a, int groups, hipStream_t s, hipEvent_t start,
+                              hipEvent_t stop) {
+  if (d == 128) return fuse_d<128>(kp, a, groups, s, start, stop, nullptr);
+  if (d == 64) return fuse_d<64>(kp, a, groups, s, start, stop, nullptr);
+  return hipErrorInvalidValue;
+}
+
+hipError_t action_occupancy(int d, int kp, int* groups_per_cu) {
+  static const ActionArgs unused{};
+  if (d == 128) return fuse_d<128>(kp, unused, 0, nullptr, nullptr, nullptr, groups_per_cu);
+  if (d == 64) return fuse_d<64>(kp, unused, 0, nullptr, nullptr, nullptr, groups_per_cu);
+  return hipErrorInvalidValue;
+}
+
+int action_chunks_per_step(int d, int kp) {
+  const int chunk = 2 * 32 * kp * 2 + d * 32 * 2;
+  return 4 * chunk <= 144 * 1024 ? 2 : 1;
+}
+
+}  // namespace sa

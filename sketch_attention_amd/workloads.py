@@ -287,3 +287,20 @@ def make_upstream_grad(users: int, k: int, d: int, seed: int = 0, scale: float =
     """Seeded upstream gradient dL/dX~ for the backward pass: float32 [users, k, d], N(0, scale^2)."""
     rng = np.random.Generator(np.random.PCG64(seed + 7919))
     return (rng.standard_normal((users, k, d)) * scale).astype(np.float32)
+
+
+def make_action_inputs(rows: int, d: int, d_a: int, d_ff: int, n_actions: int, seed: int = 0) -> dict:
+    """Seeded inputs of the action fusion: item embeddings E [rows, d] ~ N(0, 1),
+    action ids [rows] uniform over n_actions (int32), an action table
+    [n_actions, d_a] ~ N(0, 1), W_gate and W_up [d + d_a, d_ff] ~ N(0, 1/(d + d_a)),
+    W_down [d_ff, d] ~ N(0, 1/d_ff); floating arrays rounded to bf16, float32."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    k_in = d + d_a
+    return {
+        "E": round_to_bf16(_normal(rng, (rows, d))),
+        "actions": rng.integers(0, n_actions, size=rows).astype(np.int32),
+        "table": round_to_bf16(_normal(rng, (n_actions, d_a))),
+        "W_gate": round_to_bf16(_normal(rng, (k_in, d_ff), 1.0 / math.sqrt(k_in))),
+        "W_up": round_to_bf16(_normal(rng, (k_in, d_ff), 1.0 / math.sqrt(k_in))),
+        "W_down": round_to_bf16(_normal(rng, (d_ff, d), 1.0 / math.sqrt(d_ff))),
+    }

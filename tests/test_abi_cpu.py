@@ -179,3 +179,26 @@ def test_grad_entry_points_validate_before_device_work():
         B.SA_ERR_INVALID_ARG
     assert lib.sa_grad_set_kernel_timing(None, 1) == B.SA_ERR_INVALID_ARG
     lib.sa_grad_destroy(None)
+
+
+def test_action_entry_points_validate_before_device_work():
+    lib = B.library()
+    ok = B.SA_OK
+    assert lib.sa_action_check_config(128, 64, 256, 8, B.SA_BF16) == ok
+    assert lib.sa_action_check_config(128, 0, 64, 1, B.SA_BF16) == ok
+    assert lib.sa_action_check_config(64, 192, 128, 4, B.SA_BF16) == ok
+    assert lib.sa_action_check_config(128, 128, 32, 4, B.SA_BF16) == ok       # d + d_a = 256: chunks of 32
+    assert lib.sa_action_check_config(128, 64, 32, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED  # needs a multiple of 64
+    assert lib.sa_action_check_config(128, 136, 64, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED  # d + d_a > 256
+    assert lib.sa_action_check_config(128, 12, 64, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED   # d_a % 8
+    assert lib.sa_action_check_config(96, 32, 64, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_action_check_config(128, 32, 64, 4, B.SA_F32) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_action_check_config(128, 32, 64, 0, B.SA_BF16) == B.SA_ERR_INVALID_ARG
+    assert lib.sa_action_check_config(128, -8, 64, 4, B.SA_BF16) == B.SA_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert lib.sa_action_create(ctypes.byref(h), 128, 32, 64, 4, B.SA_BF16, None, None, None, None, None) == \
+        B.SA_ERR_INVALID_ARG
+    assert lib.sa_action_fuse(None, None, None, 10, None, None) == B.SA_ERR_INVALID_ARG
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.sa_action_read_kernel_timing(None, ctypes.byref(ms), ctypes.byref(n)) == B.SA_ERR_INVALID_ARG
+    lib.sa_action_destroy(None)
