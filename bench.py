@@ -229,6 +229,105 @@ def run_grad(args, wl, Xs, copies, offs, dev) -> int:
     return 0
 
 
+def action_cpu_baseline(inp, wl, budget_s: float):
+    """Time the fp64 oracles (action fusion, then the sketch) on whole users, cycling until about budget_s."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import action_oracle, sa_oracle
+
+    rows = users = 0
+    t0 = time.perf_counter()
+    while True:
+        u = users % wl.num_users
+        a, b = int(wl.offsets[u]), int(wl.offsets[u + 1])
+        x = action_oracle.action_fuse(inp["E"][a:b], inp["actions"][a:b], inp["table"], inp["W_gate"], inp["W_up"],
+                                      inp["W_down"])
+        sa_oracle.sketch_user(x, wl.P, wl.W_Q, wl.W_K, wl.tau)
+        rows += b - a
+        users += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": rows / dt if dt > 0 else None, "unit": "behaviors/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{users} users (action fusion + sketch) cycling over the {wl.num_users} users of the workload "
+                      f"({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s"}
+
+
+def run_actions(args, wl, dev) -> int:
+    """One step = the action fusion over every row (E, action ids -> X in HBM)
+    followed by one compression of X.  The roofline is the fusion pass's, on
+    2 (2 (d + d_a) d_ff + d_ff d) FLOP per row; the two passes are separate
+    launches (X is written once and read once)."""
+    from sketch_attention_amd import ActionFusion, SketchAttention, binding, workloads
+
+    d, d_a, d_ff, n_act = wl.d, args.d_a, args.d_ff or 2 * wl.d, args.n_actions
+    inp = workloads.make_action_inputs(wl.total_rows, d, d_a, d_ff, n_act, seed=1)
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)
+    e_bytes = wl.total_rows * d * 2
+    copies = max(1, math.ceil(2 * MALL_BYTES / max(e_bytes, 1)) + 1) if e_bytes < 2 * MALL_BYTES else 1
+    Es = [t(inp["E"])]
+    Es += [Es[0].clone() for _ in range(copies - 1)]
+    acts = t(inp["actions"], torch.int32)
+    X = torch.empty_like(Es[0])
+    af = ActionFusion(t(inp["table"]) if d_a else None, t(inp["W_gate"]), t(inp["W_up"]), t(inp["W_down"]), n_act)
+    sa = SketchAttention(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau)
+    out = torch.empty((wl.num_users, wl.k, d), dtype=torch.float32, device=dev)
+    offs = np.ascontiguousarray(wl.offsets, dtype=np.int64)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        binding.sa_action_fuse(af.handle, Es[i % copies], acts, X, stream)
+        binding.sa_compress_batch(sa.handle, X, offs, out, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    binding.sa_action_read_kernel_timing(af.handle)
+    binding.sa_read_kernel_timing(sa.handle)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        timed = i % TIMING_PERIOD == 0
+        if timed:
+            binding.sa_action_set_kernel_timing(af.handle, True)
+            binding.sa_set_kernel_timing(sa.handle, True)
+        step(i)
+        if timed:
+            binding.sa_action_set_kernel_timing(af.handle, False)
+            binding.sa_set_kernel_timing(sa.handle, False)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    a_ms, a_n = binding.sa_action_read_kernel_timing(af.handle)
+    f_ms, _, f_n = binding.sa_read_kernel_timing(sa.handle)
+    af.close()
+    sa.close()
+    n = wl.total_rows
+    a_us, f_us = a_ms * 1e3 / max(a_n, 1), f_ms * 1e3 / max(f_n, 1)
+    a_flop = 2.0 * (2.0 * (d + d_a) * d_ff + d_ff * d) * n
+    a_tf = a_flop / (a_us * 1e-6) / 1e12 if a_us > 0 else 0.0
+    ms_per_step = elapsed * 1e3 / args.steps
+    log(f"[bench] actions: fusion pass {a_us:.2f} us ({a_tf:.1f} TFLOP/s), fused SA pass {f_us:.2f} us; whole step "
+        f"{ms_per_step * 1e3:.2f} us (d_a={d_a}, d_ff={d_ff}, {n_act} action types)")
+    roof = {"bound": "mfma", "achieved": round(a_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "action_fuse_kernel",
+            "kernel_avg_us": round(a_us, 2)}
+    cpu = None if args.no_cpu_baseline else action_cpu_baseline(inp, wl, args.cpu_budget)
+    if cpu:
+        log(f"[bench] cpu baseline: {cpu}")
+    line = {
+        "metric": "history behaviors/sec through the action fusion and the compression",
+        "value": round(n * args.steps / elapsed, 1), "unit": "behaviors/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.num_users} users x n={n // max(wl.num_users, 1)}, d={d}, k={wl.k}, "
+                               f"{wl.dtype}, action fusion d_a={d_a} d_ff={d_ff}", "users": wl.num_users, "rows": n,
+                   "d": d, "k": wl.k, "d_a": d_a, "d_ff": d_ff, "n_actions": n_act, "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,7 +340,12 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true", help="run plain copies only (counter scaling)")
     ap.add_argument("--layers", type=int, default=0,
                     help="run the stacked refinement with this many layers (0: the single SA pass)")
-    ap.add_argument("--d-ff", type=int, default=None, help="FFN width of the refinement stack (default 4 d)")
+    ap.add_argument("--d-ff", type=int, default=None,
+                    help="FFN width of the refinement stack (default 4 d) or of the action fusion (default 2 d)")
+    ap.add_argument("--actions", action="store_true",
+                    help="build the rows by the action fusion (x = e + SwiGLU-FFN([e; a])) before each compression")
+    ap.add_argument("--d-a", type=int, default=64, help="action embedding width for --actions")
+    ap.add_argument("--n-actions", type=int, default=8, help="action types for --actions")
     ap.add_argument("--grad", action="store_true",
                     help="time the backward pass (gradients w.r.t. X, P, W_Q, W_K) instead of the compression")
     ap.add_argument("--norm", default="prototypes", choices=["prototypes", "history"],
@@ -277,6 +381,11 @@ def main() -> int:
     if args.norm == "history" and args.layers:
         print("--norm history runs the single pass only", file=sys.stderr)
         return 2
+    if args.actions:
+        if args.layers or args.norm != "prototypes" or args.grad:
+            print("--actions times the action fusion plus the single pass only", file=sys.stderr)
+            return 2
+        return run_actions(args, wl, dev)
     if args.grad:
         if args.layers or args.norm != "prototypes":
             print("--grad times the single pass's backward only", file=sys.stderr)
