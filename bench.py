@@ -356,6 +356,16 @@ def main() -> int:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         return 2
+    conflict = None
+    if args.norm == "history" and args.layers:
+        conflict = "--norm history runs the single pass only"
+    elif args.actions and (args.layers or args.norm != "prototypes" or args.grad):
+        conflict = "--actions times the action fusion plus the single pass only"
+    elif args.grad and (args.layers or args.norm != "prototypes"):
+        conflict = "--grad times the single pass's backward only"
+    if conflict:
+        print(conflict, file=sys.stderr)
+        return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
@@ -378,18 +388,9 @@ def main() -> int:
     x_bytes = wl.total_rows * wl.d * elem
     copies = max(1, math.ceil(2 * MALL_BYTES / max(x_bytes, 1)) + 1) if x_bytes < 2 * MALL_BYTES else 1
     Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
-    if args.norm == "history" and args.layers:
-        print("--norm history runs the single pass only", file=sys.stderr)
-        return 2
     if args.actions:
-        if args.layers or args.norm != "prototypes" or args.grad:
-            print("--actions times the action fusion plus the single pass only", file=sys.stderr)
-            return 2
         return run_actions(args, wl, dev)
     if args.grad:
-        if args.layers or args.norm != "prototypes":
-            print("--grad times the single pass's backward only", file=sys.stderr)
-            return 2
         return run_grad(args, wl, Xs, copies, np.ascontiguousarray(wl.offsets, dtype=np.int64), dev)
     sa = SketchAttention(t(wl.P), t(wl.W_Q), t(wl.W_K), wl.tau, norm=args.norm)
     outs = [torch.empty((wl.num_users, wl.k, wl.d), dtype=torch.float32, device=dev) for _ in range(2)]

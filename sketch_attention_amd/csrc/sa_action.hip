@@ -153,23 +153,37 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
 #pragma unroll
         for (int h = 0; h < CPS; ++h) {
           const uint32_t buf = lds0 + (uint32_t)(q * G::STEP + h * G::CHUNK);
-          // gate^T and up^T: [fb][ib] holds column 16 fb + 4 g + r of the chunk for row 16 ib + l16
+          // gate^T and up^T: [fb][ib] holds column 16 fb + 4 g + r of the chunk for row 16 ib + l16.
+          // Unit p = 2 ks + fb (its W_gate^T and W_up^T fragments, four MFMAs),
+          // fragments loaded PD units ahead behind scheduling fences, so the
+          // LDS latency hides under the MFMAs of the units in between.
+          constexpr int NU = 2 * KS, PD = 3;
           f32x4 ga[2][2], ua[2][2];
+          bf16x8 wg[NU], wu[NU];
+          auto load = [&](int p) {
+            const uint32_t o = woff[p >> 1] + (uint32_t)(2 * 16 * (p & 1) * KP);
+            wg[p] = lds_b128(buf + o);
+            wu[p] = lds_b128(buf + (uint32_t)G::W_BYTES + o);
+          };
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
+          for (int p = 0; p < PD; ++p) load(p);
 #pragma unroll
-            for (int fb = 0; fb < 2; ++fb) {
-              const uint32_t o = woff[ks] + (uint32_t)(2 * 16 * fb * KP);
-              const bf16x8 wg = lds_b128(buf + o);
-              const bf16x8 wu = lds_b128(buf + (uint32_t)G::W_BYTES + o);
+          for (int p = 0; p < NU; ++p) {
+            if (p + PD < NU) load(p + PD);
+            __builtin_amdgcn_sched_barrier(0);
+            const int ks = p >> 1, fb = p & 1;
 #pragma unroll
-              for (int ib = 0; ib < 2; ++ib) {
-                const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-                ga[fb][ib] = MF::run(wg, zf[ib][ks], ks == 0 ? z : ga[fb][ib]);
-                ua[fb][ib] = MF::run(wu, zf[ib][ks], ks == 0 ? z : ua[fb][ib]);
-              }
+            for (int ib = 0; ib < 2; ++ib) {
+              const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+              ga[fb][ib] = MF::run(wg[p], zf[ib][ks], ks == 0 ? z : ga[fb][ib]);
+              ua[fb][ib] = MF::run(wu[p], zf[ib][ks], ks == 0 ? z : ua[fb][ib]);
             }
+            __builtin_amdgcn_sched_barrier(0);
           }
+          // the W_down^T fragments of this chunk, issued before the H arithmetic
+          bf16x8 wd[CB];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) wd[cb] = lds_b128(buf + doff + (uint32_t)(2 * 16 * cb * 32));
           // H = silu(gate) * up, slot (g, e) <-> column 16 (e / 4) + 4 g + e % 4
           bf16x8 hf[2];
 #pragma unroll
@@ -185,11 +199,9 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
           }
           // x^T[16 cb + 4 g + r][row 16 ib + l16] += W_down^T H^T over the chunk
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const bf16x8 wd = lds_b128(buf + doff + (uint32_t)(2 * 16 * cb * 32));
+          for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) acc[ib][cb] = MF::run(wd, hf[ib], acc[ib][cb]);
-          }
+            for (int ib = 0; ib < 2; ++ib) acc[ib][cb] = MF::run(wd[cb], hf[ib], acc[ib][cb]);
         }
       }
       wait_vm<0>();

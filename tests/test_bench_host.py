@@ -5,6 +5,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -48,3 +49,12 @@ def test_stack_weights_are_seeded():
     b = W.make_stack_layers(d=64, d_ff=128, layers=2, dtype="bf16", seed=3)
     assert all(np.array_equal(x[k], y[k]) for x, y in zip(a, b) for k in x)
     assert a[0]["W_Q"].dtype == np.float32 and a[0]["ffn_down"].shape == (128, 64)
+
+
+@pytest.mark.parametrize("flags", [["--actions", "--grad"], ["--actions", "--layers", "2"], ["--grad", "--norm", "history"],
+                                   ["--norm", "history", "--layers", "2"]])
+def test_conflicting_modes_are_refused_before_any_gpu_work(flags):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "only" in r.stderr and r.stdout == ""
