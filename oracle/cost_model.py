@@ -2,11 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (imported by the tests; never by the product path).
 
-Source: SequenceO1 close-reading page, section 2.4 (cost formulas, whose
-display equations were lost in extraction) and section 3.5 / Figure 1 (top
-panels), which prints the resulting per-target GFLOP counts at n = 100K.
-The formulas below are a reconstruction, chosen because they reproduce every
-printed Figure 1 number to all printed digits:
+Source: SequenceO1 close-reading page, section 2.4 (cost formulas) and
+section 3.5 / Figure 1 (top panels), which prints the resulting per-target
+GFLOP counts at n = 100K.  The formulas below are this model's reading of
+section 2.4, chosen because they reproduce every printed Figure 1 number to
+all printed digits:
 
   SA miss cost per user   C_SA     = N_sa (2 n d^2 + 2 k d^2 + 4 k n d + 12 k d^2)
   per-target interaction  C_target = N_stca (4 h k D + 20 D^2)

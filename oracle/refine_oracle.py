@@ -16,8 +16,7 @@ adding the history aggregate and normalising, layer normalisation (LN) and
 a feed-forward network (FFN); every layer reads the original X, and the
 final configuration uses two layers.
 
-Readings taken where the equations were lost (each one is listed in the
-design notes):
+Readings taken where the page leaves the update open:
 
 * layer l uses its own projections W_Q(l), W_K(l) and the previous state
   as the query: S(l) = tau * (X~(l-1) W_Q(l))(X W_K(l))^T, assignment over

@@ -11,11 +11,9 @@ Recommendation with Low-Rank Caching"), section 2.1 "Sketch Attention":
 
 * a user's history X (n x d) and the k shared prototypes P (k x d);
 * an affinity S (k x n) between every prototype j and every behaviour i,
-  built from two projections W_Q, W_K (d x d): S = tau * (P W_Q)(X W_K)^T.
-  The page's display equations were lost; the page keeps the symbol list
-  (S, W_Q, W_K, i indexes behaviours, j indexes prototypes).  The placement
-  of tau and the row-vector convention (x @ W) are the readings this build
-  takes for the lost equations;
+  built from two projections W_Q, W_K (d x d): S = tau * (P W_Q)(X W_K)^T
+  (i indexes behaviours, j prototypes).  The placement of tau and the
+  row-vector convention (x @ W) are the readings this oracle takes;
 * an assignment A (k x n) obtained by normalising S over the prototype
   index: the page states that the denominator sums over j, so every
   behaviour's weights over the k prototypes add up to one;
