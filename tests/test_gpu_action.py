@@ -90,3 +90,13 @@ def test_action_rows_feed_the_compression():
     for g, w in zip(got, want):
         den = max(float(np.abs(w).max()), 1e-30)
         assert float(np.abs(g - w).max()) / den <= TOL["bf16"]
+
+
+def test_action_fusion_is_bitwise_deterministic():
+    inp = W.make_action_inputs(2000, 128, 64, 256, 8, seed=9)
+    with ActionFusion(_dev(inp["table"]), _dev(inp["W_gate"]), _dev(inp["W_up"]), _dev(inp["W_down"]), 8) as af:
+        E, acts = _dev(inp["E"]), _dev(inp["actions"], torch.int32)
+        a = af.fuse(E, acts).clone()
+        b = af.fuse(E, acts)
+        torch.cuda.synchronize()
+    assert torch.equal(a, b)

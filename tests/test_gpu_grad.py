@@ -144,3 +144,17 @@ def test_grad_long_full():
     wl = W.named_workload("long")
     G = W.make_upstream_grad(wl.num_users, wl.P.shape[0], wl.P.shape[1], seed=0)
     _check(wl, G, _run(wl, G))
+
+
+def test_grad_is_bitwise_deterministic():
+    """Fixed-order reductions: two calls on the same inputs give identical bits."""
+    wl = W.make_workload(lengths=[5000, 1, 2500], d=128, k=200, dtype="bf16", seed=44, name="det")
+    G = W.make_upstream_grad(3, 200, 128, seed=45)
+    X, P, WQ, WK = to_device(wl)
+    Gd = torch.from_numpy(G).cuda()
+    with SketchAttentionGrad(P, WQ, WK, wl.tau) as h:
+        a = [t.clone() for t in h.backward(X, wl.offsets, Gd)]
+        b = h.backward(X, wl.offsets, Gd)
+        torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
