@@ -622,25 +622,31 @@ SA_API sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_
   const int64_t rows = (int64_t)num_users * k;
   const float scale = (float)((double)h->base->tau * kLog2e);
   const int nl = (int)h->layers.size();
+  // Xbar = LN1(X~(l-1) + Y); X~(l) = LN2(Xbar + FFN(Xbar)); X~(0) = P for every user.  Each residual + layer
+  // norm runs as the prologue of the product that reads it (LN1 before the FFN, LN2 of layer l before the
+  // fold of layer l + 1), except the last layer's LN2, which writes the output.
   for (int l = 0; l < nl; ++l) {
     const auto& L = h->layers[l];
     if (l == 0) {
       st = compress(h->base, X, offsets, num_users, h->y, stream, h->base->M, 0);
     } else {
-      if (sa::launch_fold_users(plan.dtype, h->state, L.wqk_t, scale, num_users, k, plan.k_pad, d, h->Mu, s) !=
+      const auto& Lp = h->layers[l - 1];
+      const sa::LnPrologue ln2{h->xbar, 0, h->ffn_out, Lp.ln2_g, Lp.ln2_b, kLayerNormEps, h->state};
+      if (sa::launch_fold_users(plan.dtype, &ln2, nullptr, L.wqk_t, scale, num_users, k, plan.k_pad, d, h->Mu, s) !=
           hipSuccess)
         return SA_ERR_DEVICE;
       st = compress(h->base, X, offsets, num_users, h->y, stream, h->Mu, (int64_t)plan.k_pad * d);
     }
     if (st != SA_OK) return st;
-    // Xbar = LN(X~(l-1) + Y); X~(l) = LN(Xbar + FFN(Xbar)); X~(0) = P for every user
-    float* dst = l == nl - 1 ? out : h->state;
-    if (sa::launch_add_ln(l == 0 ? h->P : h->state, l == 0 ? k : 0, h->y, L.ln1_g, L.ln1_b, kLayerNormEps, rows, d,
-                          h->xbar, s) != hipSuccess ||
-        sa::launch_ffn(h->xbar, rows, d, d_ff, L.gate_t, L.up_t, L.down_t, h->hidden, h->ffn_out, s) != hipSuccess ||
-        sa::launch_add_ln(h->xbar, 0, h->ffn_out, L.ln2_g, L.ln2_b, kLayerNormEps, rows, d, dst, s) != hipSuccess)
+    const sa::LnPrologue ln1{l == 0 ? h->P : h->state, l == 0 ? k : 0, h->y, L.ln1_g, L.ln1_b, kLayerNormEps,
+                             h->xbar};
+    if (sa::launch_ffn(&ln1, nullptr, rows, d, d_ff, L.gate_t, L.up_t, L.down_t, h->hidden, h->ffn_out, s) !=
+        hipSuccess)
       return SA_ERR_DEVICE;
   }
+  if (sa::launch_add_ln(h->xbar, 0, h->ffn_out, h->layers[nl - 1].ln2_g, h->layers[nl - 1].ln2_b, kLayerNormEps, rows,
+                        d, out, s) != hipSuccess)
+    return SA_ERR_DEVICE;
   return SA_OK;
 }
 

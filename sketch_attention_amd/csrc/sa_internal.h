@@ -77,17 +77,30 @@ hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
 hipError_t launch_wqk_t(int dtype, const void* WQ, const void* WK, int d, float* out, hipStream_t stream);
 // dst = src^T for a rows x cols matrix.
 hipError_t launch_transpose(const float* src, int rows, int cols, float* dst, hipStream_t stream);
+// Residual + layer norm computed as the prologue of a product whose A operand it forms:
+// A[r] = LN(a[r % a_period (or r when 0)] + b[r]) * gain + bias over d, also stored to out.
+struct LnPrologue {
+  const float* a;
+  int64_t a_period;
+  const float* b;
+  const float* gain;
+  const float* bias;
+  float eps;
+  float* out;
+};
 // M[u] = scale * state[u] W_QK in the dtype, [users][k_pad][d], from wqk_t = W_QK^T; padding rows
-// k..k_pad-1 are not written (the caller keeps them zero).
-hipError_t launch_fold_users(int dtype, const float* state, const float* wqk_t, float scale, int users, int k, int k_pad,
-                             int d, void* M, hipStream_t stream);
+// k..k_pad-1 are not written (the caller keeps them zero).  With ln, state is ln->a and the rows are
+// formed (and stored to ln->out) by the layer norm first.
+hipError_t launch_fold_users(int dtype, const LnPrologue* ln, const float* state, const float* wqk_t, float scale,
+                             int users, int k, int k_pad, int d, void* M, hipStream_t stream);
 // out[r] = LN(a[r % a_period (or r when 0)] + b[r]) * gain + bias over d in {64, 128}.
 hipError_t launch_add_ln(const float* a, int64_t a_period, const float* b, const float* gain, const float* bias,
                          float eps, int64_t rows, int d, float* out, hipStream_t stream);
 // H = silu(Z W_gate) * (Z W_up) [rows][d_ff], F = H W_down [rows][d]; weights given transposed
-// (gate_t, up_t: [d_ff][d]; down_t: [d][d_ff]); d and d_ff multiples of 32.
-hipError_t launch_ffn(const float* Z, int64_t rows, int d, int d_ff, const float* gate_t, const float* up_t,
-                      const float* down_t, float* H, float* F, hipStream_t stream);
+// (gate_t, up_t: [d_ff][d]; down_t: [d][d_ff]); d and d_ff multiples of 32.  With ln, Z is ln->a
+// and its rows are formed (and stored to ln->out) by the layer norm first.
+hipError_t launch_ffn(const LnPrologue* ln, const float* Z, int64_t rows, int d, int d_ff, const float* gate_t,
+                      const float* up_t, const float* down_t, float* H, float* F, hipStream_t stream);
 
 // Plan groups, one translation unit each (see sa_fused_*.hip).  With
 // occ != nullptr they report occupancy instead of launching.
