@@ -33,9 +33,13 @@ constexpr int kActWaves = 8;
 
 // Byte layout of one packed chunk (32 FFN columns): W_gate^T block [32][KP],
 // W_up^T block [32][KP] (16-byte chunk h of row f at h ^ (f % 8)), then the
-// W_down^T block [D][32] (row c holds W_down[32 c0 + perm(pos)][c] at
-// position pos = 8 g + e, perm = 16 (e / 4) + 4 g + e % 4; chunk g stored at
-// g ^ 2 ((c / 8) % 2)).
+// W_down^T block [D][32]: row 16 cb + i holds output column
+// oc = 32 (cb / 2) + 4 (cb % 2) + 8 (i / 4) + i % 4, W_down[32 c0 + perm(pos)][oc]
+// at position pos = 8 g + e, perm = 16 (e / 4) + 4 g + e % 4; chunk g stored
+// at g ^ 2 ((row / 8) % 2).  The row order puts output column 32 ks + 8 g + e
+// in accumulator (cb = 2 ks + e / 4, register e % 4) of lane group g: the
+// lane's z fragment for K slots 32 ks + 8 g .. + 7, so the residual e_i is
+// added from registers and stored as 16-byte pieces.
 template <int D, int KP>
 struct ActGeom {
   static constexpr int W_BYTES = 32 * KP * 2;
@@ -67,7 +71,10 @@ __global__ __launch_bounds__(256) void action_pack_kernel(const bf16* Wg, const 
   } else {
     const int ww = w - 2 * 32 * KP, col = ww / 32, p = ww % 32, gg = p >> 3, e = p & 7;
     const int f = 32 * c + 16 * (e >> 2) + 4 * gg + (e & 3);
-    v = Wd[(int64_t)f * D + col];
+    // packed row col = 16 cb + i holds output column 32 (cb / 2) + 4 (cb % 2) + 8 (i / 4) + i % 4
+    const int cb = col >> 4, i = col & 15;
+    const int oc = 32 * (cb >> 1) + 4 * (cb & 1) + 8 * (i >> 2) + (i & 3);
+    v = Wd[(int64_t)f * D + oc];
     pos = 2 * 32 * KP + col * 32 + 8 * (gg ^ (2 * ((col >> 3) & 1))) + e;
   }
   packed[(int64_t)c * CH_ELEMS + pos] = v;
@@ -110,6 +117,35 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
   for (int ks = 0; ks < KS; ++ks) woff[ks] = (uint32_t)(2 * (l16 * KP + 8 * ((4 * ks + g) ^ (l16 & 7))));
   const uint32_t doff = (uint32_t)(2 * 2 * 32 * KP + 2 * (l16 * 32 + 8 * (g ^ (2 * ((l16 >> 3) & 1)))));
 
+  // action ids of a tile's rows (this lane's rows 16 ib + l16 of the wave), loaded a tile ahead so that the
+  // table rows they select do not wait for them
+  auto load_actions = [&](int64_t t, int (&ids)[2]) {
+    const int64_t lm = r_end - 1 - t;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int r = rw + 16 * ib + l16;
+      ids[ib] = args.actions[t + (r <= lm ? r : lm)];
+    }
+  };
+  int act_next[2];
+  load_actions(r_begin, act_next);
+  // the E fragments (K slots below D) of the next tile too, where the registers allow (all but d = 128 with
+  // K padded to 256)
+  constexpr int KE = D / 32;
+  constexpr bool PF = !(D == 128 && KP == 256);
+  bf16x8 ze[2][KE];
+  auto load_e = [&](int64_t t) {
+    const int64_t lm = r_end - 1 - t;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const int r = rw + 16 * ib + l16;
+      const int64_t row = t + (r <= lm ? r : lm);
+#pragma unroll
+      for (int ks = 0; ks < KE; ++ks) ze[ib][ks] = *reinterpret_cast<const bf16x8*>(E + row * D + 32 * ks + 8 * g);
+    }
+  };
+  if constexpr (PF) load_e(r_begin);
+
   int q = 0;
   issue_step(0, 0);
   wait_vm<0>();
@@ -117,6 +153,7 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
   for (int64_t t0 = r_begin; t0 < r_end; t0 += NT) {
     const int64_t lim = r_end - 1 - t0;
     const bool busy = rw <= lim;  // wave-uniform
+    int acts[2] = {act_next[0], act_next[1]};
     // z = [e ; a ; 0] for rows 16 ib + l16 of this wave, K slots 32 ks + 8 g ..
     bf16x8 zf[2][KS];
     bool valid[2];
@@ -125,19 +162,23 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
       const int r = rw + 16 * ib + l16;
       valid[ib] = r <= lim;
       const int64_t row = t0 + (r <= lim ? r : lim);
-      int act = args.actions[row];
+      int act = acts[ib];
       act = act < 0 ? 0 : (act >= args.n_actions ? args.n_actions - 1 : act);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int k0 = 32 * ks + 8 * g;
-        if (k0 < D) {
-          zf[ib][ks] = *reinterpret_cast<const bf16x8*>(E + row * D + k0);
+        if (ks < KE) {
+          zf[ib][ks] = PF ? ze[ib][ks] : *reinterpret_cast<const bf16x8*>(E + row * D + k0);
         } else if (k0 < D + args.d_a) {
           zf[ib][ks] = *reinterpret_cast<const bf16x8*>(T + (int64_t)act * args.d_a + (k0 - D));
         } else {
           zf[ib][ks] = bf16x8{};
         }
       }
+    }
+    if (t0 + NT < r_end) {
+      load_actions(t0 + NT, act_next);
+      if constexpr (PF) load_e(t0 + NT);
     }
     f32x4 acc[2][CB];
 #pragma unroll
@@ -208,19 +249,18 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
       __syncthreads();
       q ^= 1;
     }
-    // x = e + FFN: this lane holds columns 16 cb + 4 g .. + 3 of row 16 ib + l16
+    // x = e + FFN: this lane holds columns 32 ks + 8 g .. + 7 of row 16 ib + l16, the FFN part in
+    // accumulators 2 ks and 2 ks + 1, e_i in z fragment ks
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       if (!valid[ib]) continue;
       const int64_t row = t0 + rw + 16 * ib + l16;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 ev = *reinterpret_cast<const bf16x4*>(E + row * D + 16 * cb + 4 * g);
-        bf16x4 v;
+      for (int ks = 0; ks < D / 32; ++ks) {
+        bf16x8 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bf16)((float)ev[r] + acc[ib][cb][r]);
-        *reinterpret_cast<bf16x4*>(X + row * D + 16 * cb + 4 * g) = v;
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)zf[ib][ks][e] + acc[ib][2 * ks + (e >> 2)][e & 3]);
+        *reinterpret_cast<bf16x8*>(X + row * D + 32 * ks + 8 * g) = v;
       }
     }
   }
