@@ -100,3 +100,40 @@ def test_action_fusion_is_bitwise_deterministic():
         b = af.fuse(E, acts)
         torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+FULL_CASES = [
+    # name, rows, d, d_a, d_ff, n_actions: row counts large enough that every work group walks several
+    # 256-row tiles (the action ids and E rows of the next tile are loaded while the current one runs)
+    ("bench_shape_400k", 400_000, 128, 64, 256, 8),   # the shape bench.py --actions times
+    ("ragged_300007", 300_007, 128, 64, 256, 8),
+    ("d128_da128_ff96_100003", 100_003, 128, 128, 96, 5),  # K 256: one chunk per step, no E prefetch
+    ("d64_da64_ff128_70001", 70_001, 64, 64, 128, 16),
+]
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+def test_action_full_size(case):
+    """Every row of a full-size pass against the oracle (computed in blocks of rows), with the normwise
+    bound of the small cases; the device output starts as NaN so that a row the pass never wrote fails."""
+    name, rows, d, d_a, d_ff, n_act = case
+    inp = W.make_action_inputs(rows, d, d_a, d_ff, n_act, seed=rows % 1000)
+    with ActionFusion(_dev(inp["table"]), _dev(inp["W_gate"]), _dev(inp["W_up"]), _dev(inp["W_down"]),
+                      n_act) as af:
+        X = torch.full((rows, d), float("nan"), device="cuda", dtype=torch.bfloat16)
+        af.fuse(_dev(inp["E"]), _dev(inp["actions"], torch.int32), out=X)
+        torch.cuda.synchronize()
+    got = X.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    err = f_max = x_max = 0.0
+    for r0 in range(0, rows, 65536):
+        sl = slice(r0, min(r0 + 65536, rows))
+        want = AO.action_fuse(inp["E"][sl], inp["actions"][sl], inp["table"], inp["W_gate"], inp["W_up"],
+                              inp["W_down"])
+        f_want = want - inp["E"][sl]
+        err = max(err, float(np.abs(got[sl].astype(np.float64) - inp["E"][sl] - f_want).max()))
+        f_max = max(f_max, float(np.abs(f_want).max()))
+        x_max = max(x_max, float(np.abs(want).max()))
+    bound = TOL["bf16"] * f_max + 2.0 ** -8 * x_max
+    print(f"[action] {name} rows={rows} err={err:.3e} bound={bound:.3e}", flush=True)
+    assert err <= bound, (err, bound)
