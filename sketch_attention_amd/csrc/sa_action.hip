@@ -19,7 +19,10 @@
 //                                    output puts chunk column 16 (e/4) + 4 g
 //                                    + e%4 in slot (g, e) of row l16
 //     x^T          += W_down^T H^T   (A = W_down^T rows permuted to match)
-//   and x = e + (x^T)^T is stored in bf16, four columns per lane.
+//   and x = e + (x^T)^T is stored in bf16, eight columns per lane, e_i taken
+//   from the z fragments (the W_down^T row order lines the output columns up
+//   with them).  A tile's action ids and, where the registers allow, its E
+//   fragments are loaded while the previous tile runs.
 #include <hip/hip_runtime.h>
 
 #include "sa_action.h"
