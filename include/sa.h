@@ -29,6 +29,13 @@
  *     touched.  Nothing throws across this boundary.
  *   - A handle must not be used from two host threads at once, nor by two
  *     streams whose work can overlap (its workspace is shared).
+ *   - The compute entry points (sa_compress_batch, sa_stack_compress_batch,
+ *     sa_grad_compute, sa_action_fuse) allocate and synchronise only when a
+ *     batch is larger than any the handle has seen (its buffers then grow).
+ *     Otherwise a call enqueues kernel launches only, no memset or copy
+ *     nodes, so it can be recorded by stream capture into a HIP graph and
+ *     replayed: make one call with the largest batch first.  Kernel timing
+ *     (the *_set_kernel_timing calls) records events and is for eager use.
  */
 #ifndef SA_H
 #define SA_H

@@ -80,5 +80,7 @@ struct MatmulPair {
 hipError_t launch_small_matmuls(const Matmul& a, const Matmul& b, hipStream_t stream);
 // dst[i] += src[i] for n floats.
 hipError_t launch_add(float* dst, const float* src, int64_t n, hipStream_t s);
+// dst[i] = 0 for n floats (a kernel, not a memset).
+hipError_t launch_zero(float* dst, int64_t n, hipStream_t s);
 
 }  // namespace sa

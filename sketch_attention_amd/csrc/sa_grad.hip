@@ -623,6 +623,12 @@ __global__ __launch_bounds__(256) void add_kernel(float* dst, const float* src, 
   if (i < n) dst[i] += src[i];
 }
 
+// dst[i] = 0 for n floats (a kernel rather than a memset node, so that the call can be captured in a graph)
+__global__ __launch_bounds__(256) void zero_kernel(float* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = 0.f;
+}
+
 template <int D, int WJ, bool PAD>
 hipError_t stats_p(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
   if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_stats_kernel<D, WJ, PAD>, 64 * WJ, 0);
@@ -735,6 +741,12 @@ hipError_t launch_small_matmuls(const Matmul& a, const Matmul& b, hipStream_t s)
 hipError_t launch_add(float* dst, const float* src, int64_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(add_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* dst, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dst, n);
   return hipGetLastError();
 }
 

@@ -265,7 +265,7 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     e = sa::launch_grad_dx(d, a2, g2, s, time_it ? ev.ev[2] : nullptr, time_it ? ev.ev[3] : nullptr);
     timed = timed || (time_it && e == hipSuccess);
   }
-  if (e == hipSuccess && !have_dq) e = hipMemsetAsync(dq_sum, 0, kd * sizeof(float), s);  // no rows: zero gradients
+  if (e == hipSuccess && !have_dq) e = sa::launch_zero(dq_sum, (int64_t)kd, s);  // no rows: zero gradients
   // dQ = tau dQ' W_K, dW_K = tau dQ'^T Q, dP = dQ W_Q^T, dW_Q = P^T dQ
   if (e == hipSuccess)
     e = sa::launch_small_matmuls({dq_sum, d, 1, h->WK32, d, 1, k, d, d, h->tau, dQ},
