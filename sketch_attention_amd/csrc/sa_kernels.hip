@@ -158,12 +158,16 @@ struct HistPart {
 };
 __device__ __forceinline__ void hist_merge(HistPart& x, float m, float l, float a) {
   if (m == -INFINITY) return;  // nothing seen
-  const float mn = fmaxf(x.m, m);
-  const float sa = x.m == -INFINITY ? 0.f : exp2f(x.m - mn);
-  const float sb = exp2f(m - mn);
-  x.a = x.a * sa + a * sb;
-  x.l = x.l * sa + l * sb;
-  x.m = mn;
+  if (m <= x.m) {
+    const float sb = __builtin_amdgcn_exp2f(m - x.m);
+    x.a += a * sb;
+    x.l += l * sb;
+  } else {
+    const float sa = __builtin_amdgcn_exp2f(x.m - m);  // 0 when x saw nothing (x.m = -inf)
+    x.a = x.a * sa + a;
+    x.l = x.l * sa + l;
+    x.m = m;
+  }
 }
 
 __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_kernel(ReduceArgs a) {
