@@ -274,7 +274,8 @@ __global__ __launch_bounds__(64 * KS) void small_gemm_kernel(const GemmArgs args
       const int col = col0 + 16 * j + l16;
       float v = sum0[j][r];
       if constexpr (EPI == EPI_GATED) {
-        v = v / (1.f + expf(-v)) * sum1[j][r];  // silu(gate) * up
+        // silu(gate) * up, with the hardware exp2 and reciprocal (about 1 ulp each)
+        v = v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v)) * sum1[j][r];
         C[row * N + col] = (T)v;
       } else if constexpr (EPI == EPI_FOLD) {
         const int64_t u = row / args.k, jj = row % args.k;
