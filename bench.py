@@ -34,7 +34,40 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MALL_BYTES = 256 * 2 ** 20
-TIMING_PERIOD = 8  # kernel durations are taken on every 8th timed step
+MEDIAN_STEPS = 50  # steps of the separate per-step pass whose median is reported beside the mean
+
+
+def timing_period(steps: int) -> int:
+    """Kernel durations are taken on every step of a short timed region
+    (fewer than 50 steps) and on every 8th step of a long one, where
+    event-carrying launches would cost the host enough to starve small batches."""
+    return 1 if steps < 50 else 8
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def median_step_us(run, steps: int) -> float:
+    """Median over `steps` single steps, each bracketed by events on the launch
+    stream (torch's current stream, which is the stream every call uses)."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run(i)
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    return float(np.median(times))
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sketch_attention_amd", "csrc")
 METRIC = "history behaviors/sec compressed (n=100K,k=256,d=128); % bf16 MFMA/HBM peak"
@@ -87,6 +120,7 @@ def cpu_baseline(wl, budget_s: float, layers=None, norm: str = "prototypes"):
         "value": rows / dt if dt > 0 else None,
         "unit": "behaviors/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{users} user {'comparator summaries' if norm == 'history' else 'sketches' if params is None else f'{len(params)}-layer stacks'} cycling over "
                   f"the {wl.num_users} users of the workload ({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s",
@@ -161,7 +195,7 @@ def grad_cpu_baseline(wl, G, budget_s: float):
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": rows / dt if dt > 0 else None, "unit": "behaviors/s", "cores": int(threads), "kind": "oracle",
+    return {"value": rows / dt if dt > 0 else None, "unit": "behaviors/s", "cores": int(threads), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{users} user gradients cycling over the {wl.num_users} users of the workload ({rows} rows), "
                       f"fp64 numpy/OpenBLAS, {dt:.2f} s"}
 
@@ -190,8 +224,9 @@ def run_grad(args, wl, Xs, copies, offs, dev) -> int:
     torch.cuda.synchronize(dev)
     binding.sa_grad_read_kernel_timing(h.handle)
     t0 = time.perf_counter()
+    period = timing_period(args.steps)
     for i in range(args.steps):
-        timed = i % TIMING_PERIOD == 0
+        timed = i % period == 0
         if timed:
             binding.sa_grad_set_kernel_timing(h.handle, True)
         run(i)
@@ -249,7 +284,7 @@ def action_cpu_baseline(inp, wl, budget_s: float):
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": rows / dt if dt > 0 else None, "unit": "behaviors/s", "cores": int(threads), "kind": "oracle",
+    return {"value": rows / dt if dt > 0 else None, "unit": "behaviors/s", "cores": int(threads), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{users} users (action fusion + sketch) cycling over the {wl.num_users} users of the workload "
                       f"({rows} rows), fp64 numpy/OpenBLAS, {dt:.2f} s"}
 
@@ -286,8 +321,9 @@ def run_actions(args, wl, dev) -> int:
     binding.sa_action_read_kernel_timing(af.handle)
     binding.sa_read_kernel_timing(sa.handle)
     t0 = time.perf_counter()
+    period = timing_period(args.steps)
     for i in range(args.steps):
-        timed = i % TIMING_PERIOD == 0
+        timed = i % period == 0
         if timed:
             binding.sa_action_set_kernel_timing(af.handle, True)
             binding.sa_set_kernel_timing(sa.handle, True)
@@ -421,13 +457,12 @@ def main() -> int:
     read_timing(handle)  # discard anything recorded so far
 
     # Kernel durations come from HIP events that the kernels' own dispatches
-    # record on the launch stream; they are taken on every TIMING_PERIOD-th
-    # step of the timed region, since event-carrying launches cost the host
-    # more than plain ones and would otherwise starve the GPU on small batches.
+    # record on the launch stream (see timing_period for which steps carry them).
+    period = timing_period(args.steps)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        timed = i % TIMING_PERIOD == 0
+        timed = i % period == 0
         if timed:
             set_timing(handle, True)
         compress(handle, Xs[i % copies], offs, outs[i % 2], stream)
@@ -444,7 +479,7 @@ def main() -> int:
     nbytes = algorithmic_bytes(wl.total_rows, wl.num_users, wl.k, wl.d, elem)
     fused_avg_ms = fused_ms / max(launches, 1)
     # launches == timed steps unless the batch spans several launches; per-launch work
-    timed_steps = (args.steps + TIMING_PERIOD - 1) // TIMING_PERIOD
+    timed_steps = (args.steps + period - 1) // period
     per_launch_flops = flops * passes * timed_steps / max(launches, 1)
     per_launch_bytes = nbytes * passes * timed_steps / max(launches, 1)
     mfma_peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -467,6 +502,10 @@ def main() -> int:
         f"reduce avg {reduce_ms / max(launches, 1) * 1e3:.2f} us; whole step {ms_per_step * 1e3:.2f} us "
         f"({flops * passes / (ms_per_step * 1e-3) / 1e12:.1f} TFLOP/s in the SA passes)")
 
+    med_us = median_step_us(lambda i: compress(handle, Xs[i % copies], offs, outs[i % 2], stream),
+                            max(MEDIAN_STEPS, args.steps))
+    log(f"[bench] median of {max(MEDIAN_STEPS, args.steps)} single steps: {med_us:.2f} us")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_budget, stack_layers, args.norm)
@@ -485,6 +524,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "median_step_us": round(med_us, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

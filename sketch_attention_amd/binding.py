@@ -59,6 +59,27 @@ class SAError(RuntimeError):
 
 _lib = None
 
+# Shape and dtype of every live handle, keyed by its address: the C ABI takes
+# plain pointers and cannot check buffer sizes, so the binding checks every
+# tensor against the handle it is used with before anything is enqueued.
+_HANDLES: dict = {}
+
+
+def _remember(handle: ctypes.c_void_p, kind: str, **info) -> None:
+    _HANDLES[int(handle.value)] = dict(kind=kind, **info)
+
+
+def _info(handle, kind: str) -> dict:
+    key = handle.value if isinstance(handle, ctypes.c_void_p) else handle
+    got = _HANDLES.get(int(key or 0))
+    if got is None or got["kind"] != kind:
+        raise ValueError(f"not a live {kind} handle")
+    return got
+
+
+def _forget(handle: ctypes.c_void_p) -> None:
+    _HANDLES.pop(int(handle.value or 0), None)
+
 
 def library() -> ctypes.CDLL:
     """Load libsa.so (once; SA_LIB_PATH selects another build).  Raises if it is missing."""
@@ -185,6 +206,7 @@ def sa_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
                                         ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
                                         ctypes.c_void_p(W_K.data_ptr()), _NORMS[norm], _stream_ptr(stream, P.device))
     _check(st, "sa_create")
+    _remember(h, "sa", k=int(k), d=int(d), dtype=P.dtype)
     return h
 
 
@@ -201,12 +223,8 @@ def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: to
         offs = _offsets_array(offsets)
     if offs.ndim != 1 or offs.size < 1:
         raise ValueError("offsets must be a 1-D array of length num_users + 1")
-    _device_tensor(X, "X")
-    _device_tensor(out, "out")
-    if out.dtype != torch.float32:
-        raise ValueError("out must be float32")
-    if X.dim() != 2 or X.shape[0] != int(offs[-1]):
-        raise ValueError("X must be [offsets[-1], d]")
+    info = _info(handle, "sa")
+    _check_batch_tensors(info, X, offs, out)
     if stream is None:
         stream = torch.cuda.current_stream(X.device)
     st = library().sa_compress_batch(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
@@ -214,15 +232,31 @@ def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: to
     _check(st, "sa_compress_batch")
 
 
+def _check_batch_tensors(info: dict, X: torch.Tensor, offs: np.ndarray, out: torch.Tensor) -> None:
+    """X [offsets[-1], d] in the handle's dtype, out float32 [U, k, d], both contiguous on the GPU
+    (shapes are checked first, so a wrong size is reported as such)."""
+    k, d = info["k"], info["d"]
+    if X.dim() != 2 or X.shape[0] != int(offs[-1]) or X.shape[1] != d:
+        raise ValueError(f"X must be [offsets[-1], {d}]")
+    if X.dtype != info["dtype"]:
+        raise ValueError(f"X dtype {X.dtype} differs from the handle's {info['dtype']}")
+    if out.dtype != torch.float32 or tuple(out.shape) != (offs.size - 1, k, d):
+        raise ValueError(f"out must be float32 [{offs.size - 1}, {k}, {d}]")
+    _device_tensor(X, "X")
+    _device_tensor(out, "out")
+
+
 def sa_destroy(handle: Optional[ctypes.c_void_p]) -> None:
     if handle is not None and handle.value:
+        _forget(handle)
         library().sa_destroy(handle)
 
 
 def sa_get_folded(handle: ctypes.c_void_p, dst: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> None:
+    info = _info(handle, "sa")
+    if dst.dtype != torch.float32 or tuple(dst.shape) != (info["k"], info["d"]):
+        raise ValueError(f"dst must be float32 [{info['k']}, {info['d']}]")
     _device_tensor(dst, "dst")
-    if dst.dtype != torch.float32:
-        raise ValueError("dst must be float32 [k, d]")
     with torch.cuda.device(dst.device):
         _check(library().sa_get_folded(handle, ctypes.c_void_p(dst.data_ptr()), _stream_ptr(stream, dst.device)),
                "sa_get_folded")
@@ -334,6 +368,7 @@ def sa_stack_create(P: torch.Tensor, layers: Sequence[dict], tau: float,
         st = library().sa_stack_create(ctypes.byref(h), int(d), int(k), d_ff, len(layers), float(tau), _DTYPES[P.dtype],
                                        ctypes.c_void_p(P.data_ptr()), arr, _stream_ptr(stream, P.device))
     _check(st, "sa_stack_create")
+    _remember(h, "stack", k=int(k), d=int(d), dtype=P.dtype)
     return h
 
 
@@ -343,12 +378,7 @@ def sa_stack_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, o
     offs = _offsets_array(offsets)
     if offs.ndim != 1 or offs.size < 1:
         raise ValueError("offsets must be a 1-D array of length num_users + 1")
-    _device_tensor(X, "X")
-    _device_tensor(out, "out")
-    if out.dtype != torch.float32:
-        raise ValueError("out must be float32")
-    if X.dim() != 2 or X.shape[0] != int(offs[-1]):
-        raise ValueError("X must be [offsets[-1], d]")
+    _check_batch_tensors(_info(handle, "stack"), X, offs, out)
     if stream is None:
         stream = torch.cuda.current_stream(X.device)
     st = library().sa_stack_compress_batch(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
@@ -358,6 +388,7 @@ def sa_stack_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, o
 
 def sa_stack_destroy(handle: Optional[ctypes.c_void_p]) -> None:
     if handle is not None and handle.value:
+        _forget(handle)
         library().sa_stack_destroy(handle)
 
 
@@ -432,6 +463,7 @@ def sa_grad_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: f
                                       ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
                                       ctypes.c_void_p(W_K.data_ptr()), _stream_ptr(stream, P.device))
     _check(st, "sa_grad_create")
+    _remember(h, "grad", k=int(k), d=int(d), dtype=P.dtype)
     return h
 
 
@@ -442,16 +474,20 @@ def sa_grad_compute(handle: ctypes.c_void_p, X: torch.Tensor, offsets, grad_sket
     offs = _offsets_array(offsets)
     if offs.ndim != 1 or offs.size < 1:
         raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    info = _info(handle, "grad")
+    k, d, U = info["k"], info["d"], offs.size - 1
+    if X.dim() != 2 or X.shape[0] != int(offs[-1]) or X.shape[1] != d or X.dtype != info["dtype"]:
+        raise ValueError(f"X must be [offsets[-1], {d}] {info['dtype']}")
+    if tuple(grad_X.shape) != tuple(X.shape) or grad_X.dtype != X.dtype:
+        raise ValueError("grad_X must match X")
+    if grad_sketch.dtype != torch.float32 or tuple(grad_sketch.shape) != (U, k, d):
+        raise ValueError(f"grad_sketch must be float32 [{U}, {k}, {d}]")
+    for t, n, shape in ((grad_P, "grad_P", (k, d)), (grad_W_Q, "grad_W_Q", (d, d)), (grad_W_K, "grad_W_K", (d, d))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape:
+            raise ValueError(f"{n} must be float32 {list(shape)}")
     for t, n in ((X, "X"), (grad_sketch, "grad_sketch"), (grad_X, "grad_X"), (grad_P, "grad_P"),
                  (grad_W_Q, "grad_W_Q"), (grad_W_K, "grad_W_K")):
         _device_tensor(t, n)
-    if X.dim() != 2 or X.shape[0] != int(offs[-1]) or tuple(grad_X.shape) != tuple(X.shape) or grad_X.dtype != X.dtype:
-        raise ValueError("X and grad_X must be [offsets[-1], d] of one dtype")
-    if grad_sketch.dtype != torch.float32 or grad_sketch.dim() != 3 or grad_sketch.shape[0] != offs.size - 1:
-        raise ValueError("grad_sketch must be float32 [num_users, k, d]")
-    for t in (grad_P, grad_W_Q, grad_W_K):
-        if t.dtype != torch.float32:
-            raise ValueError("weight gradients are float32")
     if stream is None:
         stream = torch.cuda.current_stream(X.device)
     st = library().sa_grad_compute(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, grad_sketch.data_ptr(),
@@ -462,6 +498,7 @@ def sa_grad_compute(handle: ctypes.c_void_p, X: torch.Tensor, offsets, grad_sket
 
 def sa_grad_destroy(handle: Optional[ctypes.c_void_p]) -> None:
     if handle is not None and handle.value:
+        _forget(handle)
         library().sa_grad_destroy(handle)
 
 
@@ -549,17 +586,21 @@ def sa_action_create(table: Optional[torch.Tensor], W_gate: torch.Tensor, W_up: 
                                         ctypes.c_void_p(W_gate.data_ptr()), ctypes.c_void_p(W_up.data_ptr()),
                                         ctypes.c_void_p(W_down.data_ptr()), _stream_ptr(stream, dev))
     _check(st, "sa_action_create")
+    _remember(h, "action", d=int(d), dtype=dt)
     return h
 
 
 def sa_action_fuse(handle: ctypes.c_void_p, E: torch.Tensor, actions: torch.Tensor, X: torch.Tensor,
                    stream: Optional[torch.cuda.Stream] = None) -> None:
-    for t, n in ((E, "E"), (actions, "actions"), (X, "X")):
-        _device_tensor(t, n)
+    info = _info(handle, "action")
+    if E.dim() != 2 or E.shape[1] != info["d"] or E.dtype != info["dtype"]:
+        raise ValueError(f"E must be [rows, {info['d']}] {info['dtype']}")
     if actions.dtype != torch.int32 or actions.dim() != 1 or actions.shape[0] != E.shape[0]:
         raise ValueError("actions must be int32 [rows]")
     if tuple(X.shape) != tuple(E.shape) or X.dtype != E.dtype:
         raise ValueError("X must match E")
+    for t, n in ((E, "E"), (actions, "actions"), (X, "X")):
+        _device_tensor(t, n)
     if stream is None:
         stream = torch.cuda.current_stream(E.device)
     _check(library().sa_action_fuse(handle, E.data_ptr(), actions.data_ptr(), int(E.shape[0]), X.data_ptr(),
@@ -568,6 +609,7 @@ def sa_action_fuse(handle: ctypes.c_void_p, E: torch.Tensor, actions: torch.Tens
 
 def sa_action_destroy(handle: Optional[ctypes.c_void_p]) -> None:
     if handle is not None and handle.value:
+        _forget(handle)
         library().sa_action_destroy(handle)
 
 

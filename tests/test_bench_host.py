@@ -58,3 +58,14 @@ def test_conflicting_modes_are_refused_before_any_gpu_work(flags):
                        timeout=120)
     assert r.returncode == 2
     assert "only" in r.stderr and r.stdout == ""
+
+
+def test_short_runs_time_every_step():
+    # the driver's short runs (e.g. 20 steps) take a kernel duration on every step
+    assert bench.timing_period(20) == 1
+    assert bench.timing_period(49) == 1
+    assert bench.timing_period(400) == 8
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model() != ""
