@@ -369,7 +369,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="long", choices=["tiny", "recent", "long", "many_proto", "ragged"])
+    ap.add_argument("--workload", default="long", choices=["tiny", "recent", "long", "many_proto", "ragged", "final"])
     ap.add_argument("--users", type=int, default=None, help="change the number of users (same per-user shape)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

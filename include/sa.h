@@ -31,11 +31,15 @@
  *     streams whose work can overlap (its workspace is shared).
  *   - The compute entry points (sa_compress_batch, sa_stack_compress_batch,
  *     sa_grad_compute, sa_action_fuse) allocate and synchronise only when a
- *     batch is larger than any the handle has seen (its buffers then grow).
- *     Otherwise a call enqueues kernel launches only, no memset or copy
- *     nodes, so it can be recorded by stream capture into a HIP graph and
- *     replayed: make one call with the largest batch first.  Kernel timing
- *     (the *_set_kernel_timing calls) records events and is for eager use.
+ *     call needs more workspace than the handle holds (more work groups plus
+ *     users in one launch, more rows, or more users for the stack); the
+ *     buffers then grow by freeing the old ones.  Otherwise a call enqueues
+ *     kernel launches only, no memset or copy nodes, so it can be recorded
+ *     by stream capture into a HIP graph and replayed -- but a graph captured
+ *     before a later growth still points at the freed buffers and must not be
+ *     replayed after it: make the call with the largest workspace need first.
+ *     Kernel timing (the *_set_kernel_timing calls) records events and is for
+ *     eager use.
  */
 #ifndef SA_H
 #define SA_H

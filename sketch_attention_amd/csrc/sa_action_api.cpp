@@ -143,7 +143,8 @@ SA_API sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actio
       h->spare.pop_back();
       e0 = h->spare.back();
       h->spare.pop_back();
-    } else if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    } else if (hipEventCreateWithFlags(&e0, hipEventDisableSystemFence) != hipSuccess ||
+               hipEventCreateWithFlags(&e1, hipEventDisableSystemFence) != hipSuccess) {
       return SA_ERR_DEVICE;
     }
   }

@@ -22,8 +22,11 @@ namespace {
 using sa::Plan;
 
 struct TimingSlot {
-  hipEvent_t ev[4];  // fused kernel start/stop, reduction kernel start/stop (recorded by the dispatches)
-  bool fused;        // false when the launch had no rows (reduce only)
+  // fused kernel start/stop, reduction kernel start/stop, first phase start/stop of a two-phase pass
+  // (recorded by the dispatches)
+  hipEvent_t ev[6];
+  bool fused;      // false when the launch had no rows (reduce only)
+  bool two_phase;  // ev[4], ev[5] were recorded too
 };
 
 }  // namespace
@@ -85,6 +88,7 @@ Plan make_history_plan(int d, int k) {
   p.m_in_lds = 0;
   p.k_pad = p.kw * p.waves_k;
   p.tile_rows = 16 * p.row_blocks;
+  p.blocks = 1;
   return p;
 }
 
@@ -100,6 +104,21 @@ Plan make_plan(int dtype, int d, int k) {
   const int waves = dtype == SA_BF16 ? 8 : 4;
   const int k16 = (k + 15) / 16 * 16;
   const bool stream = dtype == SA_BF16 && k > 32;
+  p.blocks = 1;
+  if (dtype == SA_BF16 && d == 128 && k > 512) {
+    // two-phase pass over blocks of 8 x 32 prototypes (the folded matrix of
+    // more prototypes fits neither one group's registers nor its LDS)
+    p.kind = 1;
+    p.kw = 32;
+    p.waves_k = 8;
+    p.waves_rows = 1;
+    p.row_blocks = 4;
+    p.blocks = (k + 255) / 256;
+    p.k_pad = p.blocks * 256;
+    p.tile_rows = 64;
+    p.m_in_lds = 0;
+    return p;
+  }
   if (stream) {
     p.kind = 1;
     const bool wide = d == 128 ? k > 256 : k > 512;  // folded matrix too large for registers
@@ -154,7 +173,7 @@ sa_status check_config(int32_t d, int32_t k, float tau, sa_dtype dtype) {
   if (!std::isfinite(tau)) return SA_ERR_INVALID_ARG;
   if (k < 1 || d < 1) return SA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SA_ERR_UNSUPPORTED;
-  if (dtype == SA_BF16 && (k > 1024 || (int64_t)k * d > 65536)) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_BF16 && k > 1024) return SA_ERR_UNSUPPORTED;
   if (dtype == SA_F32 && k > 256) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
@@ -207,7 +226,8 @@ TimingSlot take_slot(sa_handle_s* h) {
   }
   TimingSlot s{};
   for (auto& e : s.ev) {
-    if (hipEventCreate(&e) != hipSuccess) e = nullptr;
+    // timing only: no system-scope fence (a cache writeback and invalidation) when it is recorded
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) e = nullptr;
   }
   return s;
 }
@@ -241,7 +261,7 @@ SA_API sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, s
   sa_status st = check_config(d, k, tau, dtype);
   if (st != SA_OK) return st;
   if (norm != SA_NORM_PROTOTYPES && norm != SA_NORM_HISTORY) return SA_ERR_INVALID_ARG;
-  if (norm == SA_NORM_HISTORY && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (norm == SA_NORM_HISTORY && (dtype != SA_BF16 || (int64_t)k * d > 65536)) return SA_ERR_UNSUPPORTED;
   if (P == nullptr || W_Q == nullptr || W_K == nullptr) return SA_ERR_INVALID_ARG;
   if (!aligned16(P) || !aligned16(W_Q) || !aligned16(W_K)) return SA_ERR_INVALID_ARG;
 
@@ -308,8 +328,16 @@ namespace {
 
 // One SA pass over a packed batch into out [U][k][d].  M: the folded matrix
 // shared by all users (m_stride 0) or one per user, m_stride elements apart.
+// Users go to launches of at most kMaxUsersPerLaunch; a launch is the fused
+// pass plus the reduction of its partial sketches, or, for a two-phase plan
+// (plan.blocks > 1), the statistics phase, their merge, the aggregation
+// phase and the reduction.
+// fixed_ws (fixed_bytes long): a workspace that must not grow.  Launches are
+// then formed greedily so that each fits (at least one work group per
+// prototype block and launch); if one user alone does not fit, nothing is
+// enqueued and SA_ERR_UNSUPPORTED is returned.  No event is recorded.
 sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_t num_users, float* out, void* stream,
-                   const void* M, int64_t m_stride) {
+                   const void* M, int64_t m_stride, float* fixed_ws = nullptr, size_t fixed_bytes = 0) {
   if (h == nullptr) return SA_ERR_INVALID_ARG;
   sa_status st = check_batch(offsets, num_users);
   if (st != SA_OK) return st;
@@ -321,23 +349,51 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
   const Plan& plan = h->plan;
   const size_t elem = plan.dtype == SA_BF16 ? 2 : 4;
   const bool hist = h->norm == SA_NORM_HISTORY;
-  // a partial slot: the k_pad x d accumulator, plus per-prototype maxima and sums for the comparator
-  const size_t slot_bytes = (size_t)plan.k_pad * (plan.d + (hist ? 2 : 0)) * sizeof(float);
+  const int nb = plan.blocks > 1 ? plan.blocks : 1;
+  const int block_k = plan.kw * plan.waves_k;  // prototypes per block (one partial slot)
+  // a partial slot: the block_k x d accumulator, plus per-prototype maxima and sums for the comparator
+  const size_t slot_bytes = (size_t)block_k * (plan.d + (hist ? 2 : 0)) * sizeof(float);
+  // two-phase statistics: per-block and merged log-sum-exp of every row
+  auto stats_bytes = [&](int64_t rows) { return nb > 1 ? (size_t)(nb + 1) * (size_t)rows * sizeof(float) : 0; };
+  // work groups per prototype block for a launch of `rows` rows (the grid is nb times that)
+  auto launch_groups = [&](int64_t rows) {
+    if (rows <= 0) return 0;
+    const int g = groups_for(h, rows);
+    return nb > 1 ? (g + nb - 1) / nb : g;
+  };
 
-  // Workspace for the largest launch of this call.
-  size_t need = 0;
-  for (int32_t u0 = 0; u0 < num_users; u0 += sa::kMaxUsersPerLaunch) {
-    const int32_t nu = num_users - u0 < sa::kMaxUsersPerLaunch ? num_users - u0 : sa::kMaxUsersPerLaunch;
-    const int64_t rows = offsets[u0 + nu] - offsets[u0];
-    if (rows > 0) {
-      const size_t b = (size_t)(groups_for(h, rows) + nu) * slot_bytes;
-      if (b > need) need = b;
+  struct LaunchPlan {
+    int32_t u0, nu;
+    int groups;
+    size_t bytes;  // partials + statistics
+  };
+  std::vector<LaunchPlan> launches;
+  for (int32_t u0 = 0; u0 < num_users;) {
+    int32_t nu = num_users - u0 < sa::kMaxUsersPerLaunch ? num_users - u0 : sa::kMaxUsersPerLaunch;
+    int64_t rows = offsets[u0 + nu] - offsets[u0];
+    int g = launch_groups(rows);
+    auto bytes_of = [&](int gg, int32_t n, int64_t r) { return (size_t)nb * (gg + n) * slot_bytes + stats_bytes(r); };
+    if (fixed_ws != nullptr) {
+      // the most users (up to the launch limit) that fit with at least one group each
+      while (nu > 1 && bytes_of(1, nu, rows) > fixed_bytes) {
+        nu = nu / 2;
+        rows = offsets[u0 + nu] - offsets[u0];
+      }
+      if (bytes_of(rows > 0 ? 1 : 0, nu, rows) > fixed_bytes) return SA_ERR_UNSUPPORTED;
+      g = launch_groups(rows);
+      const int64_t room = (int64_t)((fixed_bytes - stats_bytes(rows)) / slot_bytes) / nb - nu;
+      if (g > room) g = (int)room;
     }
+    launches.push_back({u0, nu, g, bytes_of(g, nu, rows)});
+    u0 += nu;
   }
 
   DeviceGuard guard(h->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (need > h->workspace_bytes) {
+  // Workspace for the largest launch of this call.
+  size_t need = 0;
+  for (const auto& L : launches) need = L.bytes > need ? L.bytes : need;
+  if (fixed_ws == nullptr && need > h->workspace_bytes) {
     // Earlier launches on this stream may still read the old workspace.
     if (h->workspace) {
       if (hipStreamSynchronize(s) != hipSuccess) return SA_ERR_DEVICE;
@@ -352,11 +408,15 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     h->workspace_bytes = need;
   }
 
-  for (int32_t u0 = 0; u0 < num_users; u0 += sa::kMaxUsersPerLaunch) {
-    const int32_t nu = num_users - u0 < sa::kMaxUsersPerLaunch ? num_users - u0 : sa::kMaxUsersPerLaunch;
+  float* const partial = fixed_ws != nullptr ? fixed_ws : h->workspace;
+  for (const auto& L : launches) {
+    const int32_t u0 = L.u0, nu = L.nu;
     const int64_t base = offsets[u0];
     const int64_t rows = offsets[u0 + nu] - base;
-    const int groups = rows > 0 ? groups_for(h, rows) : 0;
+    const int groups = L.groups;
+    // statistics after this launch's partial slots
+    float* const stats_b = partial + (size_t)nb * (groups + nu) * (slot_bytes / sizeof(float));
+    float* const stats_m = stats_b + (size_t)nb * rows;
 
     sa::FusedArgs fa;
     std::memset(&fa, 0, sizeof(fa));
@@ -364,13 +424,14 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     fa.M = static_cast<const char*>(M) + (size_t)u0 * (size_t)m_stride * elem;
     fa.m_stride = m_stride;
     fa.history_softmax = hist ? 1 : 0;
-    fa.partial = h->workspace;
+    fa.partial = partial;
     fa.rows = rows;
     fa.users = nu;
     fa.k = plan.k;
+    fa.blocks = nb;
     sa::ReduceArgs ra;
     std::memset(&ra, 0, sizeof(ra));
-    ra.partial = h->workspace;
+    ra.partial = partial;
     ra.history_softmax = hist ? 1 : 0;
     ra.out = out + (size_t)u0 * plan.k * plan.d;
     ra.rows = rows;
@@ -379,22 +440,34 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     ra.k = plan.k;
     ra.d = plan.d;
     ra.kw = plan.kw;
-    ra.k_pad = plan.k_pad;
+    ra.k_pad = block_k;
+    ra.blocks = nb;
     for (int32_t i = 0; i <= nu; ++i) {
       fa.offsets[i] = offsets[u0 + i] - base;
       ra.offsets[i] = fa.offsets[i];
     }
 
     TimingSlot ts{};
-    if (h->timing) {
+    const bool timed = h->timing && fixed_ws == nullptr;
+    if (timed) {
       ts = take_slot(h);
       ts.fused = rows > 0;
+      ts.two_phase = nb > 1;
     }
     if (rows > 0) {
-      if (sa::launch_fused(plan, fa, groups, s, ts.ev[0], ts.ev[1]) != hipSuccess) return SA_ERR_DEVICE;
+      if (nb > 1) {
+        // statistics phase, merge, aggregation phase (the aggregation carries events ev[0], ev[1])
+        fa.lse_mode = 1;
+        fa.stats = stats_b;
+        if (sa::launch_fused(plan, fa, nb * groups, s, ts.ev[4], ts.ev[5]) != hipSuccess) return SA_ERR_DEVICE;
+        if (sa::launch_lse_merge(stats_b, rows, nb, stats_m, s) != hipSuccess) return SA_ERR_DEVICE;
+        fa.lse_mode = 2;
+        fa.stats = stats_m;
+      }
+      if (sa::launch_fused(plan, fa, nb * groups, s, ts.ev[0], ts.ev[1]) != hipSuccess) return SA_ERR_DEVICE;
     }
     if (sa::launch_reduce(ra, s, ts.ev[2], ts.ev[3]) != hipSuccess) return SA_ERR_DEVICE;
-    if (h->timing) h->slots.push_back(ts);
+    if (timed) h->slots.push_back(ts);
   }
   return SA_OK;
 }
@@ -433,14 +506,15 @@ SA_API sa_status sa_read_kernel_timing(sa_handle h, double* fused_ms, double* re
       st = SA_ERR_DEVICE;
       continue;
     }
-    float a = 0.f, b = 0.f;
+    float a = 0.f, b = 0.f, c = 0.f;
     if ((s.fused && hipEventElapsedTime(&a, s.ev[0], s.ev[1]) != hipSuccess) ||
+        (s.fused && s.two_phase && (!s.ev[4] || !s.ev[5] || hipEventElapsedTime(&c, s.ev[4], s.ev[5]) != hipSuccess)) ||
         hipEventElapsedTime(&b, s.ev[2], s.ev[3]) != hipSuccess) {
       st = SA_ERR_DEVICE;
       continue;
     }
     if (s.fused) {
-      f += a;
+      f += a + c;  // both phases of a two-phase pass
       ++n;
     }
     r += b;
@@ -610,7 +684,7 @@ SA_API sa_status sa_stack_compress_batch(sa_stack h, const void* X, const int64_
     const size_t rk = (size_t)num_users * k;
     const size_t mu_bytes = (size_t)num_users * plan.k_pad * d * elem;
     // the folds never write the padding rows k..k_pad-1: zero them once
-    const bool ok = hipMalloc(&h->Mu, mu_bytes) == hipSuccess && hipMemsetAsync(h->Mu, 0, mu_bytes, s) == hipSuccess &&
+    const bool ok = hipMalloc(&h->Mu, mu_bytes) == hipSuccess && sa::launch_zero(h->Mu, mu_bytes, s) == hipSuccess &&
                     dev_alloc(&h->y, rk * d) && dev_alloc(&h->xbar, rk * d) && dev_alloc(&h->state, rk * d) &&
                     dev_alloc(&h->ffn_out, rk * d) && dev_alloc(&h->hidden, rk * d_ff);
     if (!ok) {

@@ -194,7 +194,7 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
       h->spare.pop_back();
     } else {
       for (auto& x : ev.ev)
-        if (hipEventCreate(&x) != hipSuccess) return SA_ERR_DEVICE;
+        if (hipEventCreateWithFlags(&x, hipEventDisableSystemFence) != hipSuccess) return SA_ERR_DEVICE;
     }
   }
   bool timed = false;

@@ -30,6 +30,7 @@ struct Plan {
   int prefetch;     // streamed pass: LDS ring slots beyond the minimum, plus one (ring of 3 or 4 + prefetch - 1 tiles)
   int row_blocks;   // streamed pass: 16-row blocks per wave and tile (2 or 4)
   int score_buffers;  // streamed pass: affinity tiles in flight per wave (2: M in registers; 1: M in LDS)
+  int blocks;       // prototype blocks of kw * waves_k each (k_pad = blocks * kw * waves_k); > 1: two-phase pass
 };
 
 // Arguments of the fused kernel (passed by value in the dispatch packet).
@@ -42,6 +43,14 @@ struct FusedArgs {
   int64_t rows;         // rows in this launch (offsets[users])
   int32_t users;        // users in this launch (<= kMaxUsersPerLaunch)
   int32_t k;            // real prototype count (rows k..k_pad-1 of M are padding)
+  // Two-phase pass (prototypes in `blocks` blocks of the plan's kw * waves_k
+  // rows of M): lse_mode 1 writes each row's log2 sum_j 2^s'_ji over every
+  // block into stats [blocks][rows]; lse_mode 2 reads the row's log2 sum over
+  // all prototypes from stats [rows] and aggregates 2^(s' - that); 0: the
+  // one-pass kernel.  Work group g handles block g % blocks.
+  int32_t lse_mode;
+  int32_t blocks;
+  float* stats;
   int64_t offsets[kMaxUsersPerLaunch + 1];  // relative to this launch's first row
 };
 
@@ -55,7 +64,8 @@ struct ReduceArgs {
   int32_t k;
   int32_t d;
   int32_t kw;
-  int32_t k_pad;
+  int32_t k_pad;      // prototypes of one block (one partial slot)
+  int32_t blocks;     // prototype blocks; block b's slots follow the (groups + users) slots of block b - 1
   int64_t offsets[kMaxUsersPerLaunch + 1];
 };
 
@@ -69,8 +79,13 @@ hipError_t launch_reduce(const ReduceArgs& args, hipStream_t stream, hipEvent_t 
 hipError_t launch_fold(int dtype, const void* P, const void* WQ, const void* WK, float scale, int k, int k_pad,
                        int d, float* tmp, void* M, hipStream_t stream);
 hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hipStream_t stream);
+// L[i] = log2 sum_b 2^Lb[b][i] for i < rows (the two-phase pass's merge of its per-block statistics).
+hipError_t launch_lse_merge(const float* Lb, int64_t rows, int blocks, float* L, hipStream_t stream);
+// Zero bytes / 4 words at p (a kernel, never a memset node).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 // Workgroups of the fused kernel that fit on one compute unit at once.
 hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
+
 
 // Stacked refinement (sa_refine.hip), all float32 unless noted.
 // (W_Q W_K^T)^T (d x d) from weights in the dtype.

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -75,6 +76,21 @@ hipError_t launch_unfold(int dtype, const void* M, int k, int d, float* dst, hip
   return hipGetLastError();
 }
 
+// Zero fill of a device buffer (a kernel rather than a memset node, so a
+// stream capture of the calling code records only kernels).
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words == 0) return hipSuccess;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
 // --------------------------------------------------------------- reduce
 // out[u] = sum over the work groups b that touched user u of partial[b + u],
 // in a fixed order (so results are bitwise reproducible).  Work
@@ -98,6 +114,7 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
   __shared__ f32x4 part_sum[kReduceShares][kReduceLanes];
   const int shares = blockDim.x / kReduceLanes;
   const int u = blockIdx.y;
+  const int blk = blockIdx.z;  // prototype block (two-phase pass; 0 otherwise)
   const int slot_f4 = a.k_pad * a.d / 4;
   const int lane = threadIdx.x % kReduceLanes;
   const int q = threadIdx.x / kReduceLanes;
@@ -110,7 +127,8 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
     const int64_t b1 = (r1 * G - 1) / R;
     const int64_t n = b1 - b0 + 1;
     const int64_t q0 = n * q / shares, q1 = n * (q + 1) / shares;
-    const f32x4* part = reinterpret_cast<const f32x4*>(a.partial) + (b0 + u) * slot_f4 + p;
+    const f32x4* part =
+        reinterpret_cast<const f32x4*>(a.partial) + ((int64_t)blk * (G + a.users) + b0 + u) * slot_f4 + p;
     f32x4 t0 = s, t1 = s, t2 = s, t3 = s;
     int64_t i = q0;
     for (; i + 4 <= q1; i += 4) {
@@ -137,12 +155,30 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
   const int jb = t % jbs;
   const int wj = t / jbs;
   const int l = p & 63;
-  const int j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);
+  const int j0 = blk * a.k_pad + wj * a.kw + 16 * jb + 4 * (l >> 4);
   const int c = 16 * cb + (l & 15);
   float* o = a.out + (int64_t)u * a.k * a.d;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (j0 + r < a.k) o[(int64_t)(j0 + r) * a.d + c] = s[r];
+}
+
+// Merge of the two-phase pass's per-block statistics: L[i] = log2 sum_b
+// 2^Lb[b][i] (a log-sum-exp over the blocks, shifted by their maximum).
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* Lb, int64_t rows, int blocks, float* L) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows) return;
+  float m = -INFINITY;
+  for (int b = 0; b < blocks; ++b) m = fmaxf(m, Lb[(int64_t)b * rows + i]);
+  float s = 0.f;
+  for (int b = 0; b < blocks; ++b) s += exp2f(Lb[(int64_t)b * rows + i] - m);
+  L[i] = m + log2f(s);
+}
+
+hipError_t launch_lse_merge(const float* Lb, int64_t rows, int blocks, float* L, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, Lb, rows, blocks, L);
+  return hipGetLastError();
 }
 
 // Comparator (softmax over the history axis): slot s of user u holds, for
@@ -236,7 +272,8 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t sta
   const int slot_f4 = a.k_pad * a.d / 4;
   int shares = 1;
   while (shares < kReduceShares && 8 * 2 * shares <= per_user) shares *= 2;
-  const dim3 grid((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users), block(kReduceLanes * shares);
+  const dim3 grid((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users, a.blocks > 1 ? a.blocks : 1),
+      block(kReduceLanes * shares);
   if (start || stop)
     hipExtLaunchKernelGGL(reduce_kernel, grid, block, 0, stream, start, stop, 0, a);
   else

@@ -14,7 +14,7 @@ is packed row-wise into one matrix with an int64 offsets array of length U+1
 accept such unequal-length batches (section 2.4).
 
 The pages publish no dataset for this path (their data is proprietary), so
-the five named workloads below are synthetic stand-ins with the paper's
+the named workloads below are synthetic stand-ins with the paper's
 shapes: SA width d = 128 and about a thousand prototypes (section 3.2), and
 histories up to 100K behaviours (section 2.1).
 
@@ -205,8 +205,9 @@ def _ragged_lengths(seed: int, users: int, lo: int, hi: int) -> list:
     return rng.integers(lo, hi + 1, size=users).tolist()
 
 
-# The five workloads: tiny fp32 check, recent-branch scale, full long history
-# (the headline shape n=100K, k=256, d=128), many prototypes, ragged batch.
+# The workloads: tiny fp32 check, recent-branch scale, full long history
+# (the headline shape n=100K, k=256, d=128), many prototypes, ragged batch,
+# and the page's final configuration (k = 1024 at d = 128).
 NAMED_WORKLOADS = {
     "tiny": dict(
         recipe="1 user, n=1024, d=64, k=16, fp32; X,P ~ N(0,1); W ~ N(0,1/d); tau=1/sqrt(d)",
@@ -232,6 +233,14 @@ NAMED_WORKLOADS = {
                 "20% of rows exact copies of earlier rows; W ~ N(0,1/d); tau=1/sqrt(d)"),
         args=dict(d=128, k=128, dtype="bf16", seed=1005, dup_fraction=0.2),
         lengths=lambda: _ragged_lengths(2005, 64, 1000, 100000),
+    ),
+    # the final configuration of the SequenceO1 page (about a thousand
+    # prototypes at width 128, section 3.2), on the long workload's histories
+    "final": dict(
+        recipe=("4 users x n=100000, d=128, k=1024, bf16; X = per-user mixture of 64 "
+                "N(0,I) centres + 0.3 N(0,I); P ~ N(0,1); W ~ N(0,1/d); tau=1/sqrt(d)"),
+        args=dict(lengths=[100000] * 4, d=128, k=1024, dtype="bf16", seed=1006,
+                  x_kind="clusters", clusters=64, cluster_sigma=0.3),
     ),
 }
 

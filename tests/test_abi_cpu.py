@@ -56,7 +56,9 @@ def test_status_strings():
     (128, 1, 0.0, "bf16", B.SA_OK),
     (128, 512, -3.0, "bf16", B.SA_OK),
     (64, 256, 1.0, "f32", B.SA_OK),
-    (128, 1024, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),   # k*d > 65536
+    (128, 1024, 0.1, "bf16", B.SA_OK),                # two-phase pass (blocks of 256 prototypes)
+    (128, 513, 0.1, "bf16", B.SA_OK),
+    (128, 1025, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),
     (64, 1025, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),
     (64, 257, 0.1, "f32", B.SA_ERR_UNSUPPORTED),
     (96, 16, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),

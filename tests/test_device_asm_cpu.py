@@ -6,8 +6,9 @@ compiler does not save or restore a reserved register around inline assembly,
 so the helper is only sound while the compiler itself keeps no value in M0
 across it.  This test compiles every translation unit that uses the helper to
 gfx950 assembly with the library's own flags and checks that each reference to
-M0 is the helper's sequence: the move of the LDS address into M0, then the
-global_load_lds_dwordx4 that reads it.
+M0 is one of the helpers' sequence: the move of the LDS address into M0, then
+the global_load_lds_dwordx4 (or, for the per-row statistics of the two-phase
+pass, global_load_lds_dword) that reads it.
 """
 import concurrent.futures
 import os
@@ -44,9 +45,9 @@ def test_m0_is_written_only_by_the_dma_helper(tmp_path):
             if not re.search(r"\bm0\b", l):
                 continue
             assert re.fullmatch(r"s_mov_b32 m0, s\d+", l), (unit, l)
-            # the helper: s_mov_b32 m0, sN ; s_nop 0 ; global_load_lds_dwordx4 v, s[..]
-            assert lines[i + 1] == "s_nop 0" and lines[i + 2].startswith("global_load_lds_dwordx4"), (
+            # the helpers: s_mov_b32 m0, sN ; s_nop 0 ; global_load_lds_dword[x4] v, s[..]
+            assert lines[i + 1] == "s_nop 0" and re.match(r"global_load_lds_dword(x4)? ", lines[i + 2]), (
                 unit, lines[i:i + 3])
             dmas += 1
-        n_lds = sum(1 for l in lines if l.startswith("global_load_lds_dwordx4"))
+        n_lds = sum(1 for l in lines if l.startswith("global_load_lds_dword"))
         assert dmas > 0 and n_lds == dmas, (unit, dmas, n_lds)

@@ -58,6 +58,7 @@ CASES = [
     ("bf16", 128, 64, 256, 2, [1, 200, 3000, 0, 77]),        # streamed, matrix in registers, 4-wave groups
     ("bf16", 128, 256, 512, 2, [1500, 10, 4097]),            # streamed, eight waves (the long workload's plan)
     ("bf16", 128, 300, 256, 3, [50, 2000]),                  # streamed, matrix in LDS
+    ("bf16", 128, 1000, 256, 2, [1200, 0, 3000, 1]),         # two-phase pass (the page's final configuration)
     ("bf16", 64, 700, 128, 2, [300, 2, 1000]),               # streamed, matrix in LDS, d = 64
     ("bf16", 64, 16, 128, 2, [5, 100, 0]),                   # lockstep, matrix in LDS
     ("f32", 64, 16, 64, 2, [1, 100, 33]),                    # lockstep float32, matrix in registers
