@@ -37,7 +37,8 @@
  *     kernel launches only, no memset or copy nodes, so it can be recorded
  *     by stream capture into a HIP graph and replayed -- but a graph captured
  *     before a later growth still points at the freed buffers and must not be
- *     replayed after it: make the call with the largest workspace need first.
+ *     replayed after it: make the call with the largest workspace need first,
+ *     or capture sa_compress_batch_noalloc, whose workspace never moves.
  *     Kernel timing (the *_set_kernel_timing calls) records events and is for
  *     eager use.
  */
@@ -129,6 +130,30 @@ sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype
  */
 sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users,
                             float* out, void* stream);
+
+/*
+ * sa_compress_batch_noalloc -- sa_compress_batch for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, result (bitwise, for the
+ * same launch split) and errors as sa_compress_batch, but the call never
+ * allocates, frees or synchronises: its partial sketches live in a fixed
+ * device array of 64 MiB built into the library, one per GPU, held until the
+ * process ends.  A launch needs (groups + users) partial slots per prototype
+ * block (k_pad * d floats for up to 512 prototypes at d = 128, blocks of 256
+ * prototypes above; plus 2 k_pad for SA_NORM_HISTORY) and, for more than 512
+ * prototypes at d = 128, 4 (blocks + 1) bytes per row of statistics; users
+ * go to launches greedily (at most 256, halved until the launch fits with
+ * one work group per block) and the groups are capped to what fits.  If one
+ * user alone does not fit (more than about 3 million rows at k = 1024,
+ * d = 128), nothing is enqueued and SA_ERR_UNSUPPORTED is returned; every
+ * other supported case runs.  Kernel timing is not recorded for it.  All
+ * calls on one GPU share the array: calls that can overlap on one GPU (other
+ * streams, other handles, other host threads) race and must be serialised by
+ * the caller.  The array's device address is looked up on the first call on
+ * each GPU (SA_ERR_DEVICE if that fails).
+ */
+sa_status sa_compress_batch_noalloc(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users,
+                                    float* out, void* stream);
 
 /*
  * sa_destroy -- free the handle and its device memory.  NULL is allowed.

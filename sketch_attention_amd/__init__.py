@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     sa_check_batch,
     sa_check_config,
     sa_compress_batch,
+    sa_compress_batch_noalloc,
     sa_create,
     sa_describe_plan,
     sa_destroy,

@@ -34,7 +34,7 @@ _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
 _DTYPE_NAMES = {"f32": SA_F32, "bf16": SA_BF16}
 
 EXPORTED = (
-    "sa_create", "sa_create_ex", "sa_compress_batch", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
+    "sa_create", "sa_create_ex", "sa_compress_batch", "sa_compress_batch_noalloc", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
     "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
     "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy", "sa_stack_set_kernel_timing",
     "sa_stack_read_kernel_timing",
@@ -99,6 +99,7 @@ def library() -> ctypes.CDLL:
         "sa_create": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, vp]),
         "sa_create_ex": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, i32, vp]),
         "sa_compress_batch": (i32, [vp, vp, vp, i32, vp, vp]),
+        "sa_compress_batch_noalloc": (i32, [vp, vp, vp, i32, vp, vp]),
         "sa_destroy": (None, [vp]),
         "sa_status_string": (ctypes.c_char_p, [i32]),
         "sa_check_config": (i32, [i32, i32, f32, i32]),
@@ -230,6 +231,21 @@ def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: to
     st = library().sa_compress_batch(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
                                      stream.cuda_stream)
     _check(st, "sa_compress_batch")
+
+
+def sa_compress_batch_noalloc(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
+                              stream: Optional[torch.cuda.Stream] = None) -> None:
+    """As sa_compress_batch, through the entry point that allocates nothing
+    (its workspace is the library's fixed per-GPU array; see include/sa.h)."""
+    offs = _offsets_array(offsets)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    _check_batch_tensors(_info(handle, "sa"), X, offs, out)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    st = library().sa_compress_batch_noalloc(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
+                                             stream.cuda_stream)
+    _check(st, "sa_compress_batch_noalloc")
 
 
 def _check_batch_tensors(info: dict, X: torch.Tensor, offs: np.ndarray, out: torch.Tensor) -> None:

@@ -480,6 +480,18 @@ SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* of
   return compress(h, X, offsets, num_users, out, stream, h->M, 0);
 }
 
+SA_API sa_status sa_compress_batch_noalloc(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users,
+                                           float* out, void* stream) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  sa_status st = check_batch(offsets, num_users);
+  if (st != SA_OK) return st;
+  if (num_users == 0) return SA_OK;
+  DeviceGuard guard(h->device);
+  float* ws = nullptr;
+  if (sa::noalloc_scratch(h->device, &ws) != hipSuccess) return SA_ERR_DEVICE;
+  return compress(h, X, offsets, num_users, out, stream, h->M, 0, ws, sa::kNoAllocScratchBytes);
+}
+
 SA_API sa_status sa_get_folded(sa_handle h, float* dst, void* stream) {
   if (h == nullptr || dst == nullptr) return SA_ERR_INVALID_ARG;
   DeviceGuard guard(h->device);

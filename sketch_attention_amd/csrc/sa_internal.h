@@ -86,6 +86,11 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 // Workgroups of the fused kernel that fit on one compute unit at once.
 hipError_t fused_occupancy(const Plan& plan, int* groups_per_cu);
 
+// Bytes of the fixed per-device workspace of sa_compress_batch_noalloc.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of that workspace on `device`, which must be the current
+// device (looked up on the first call per device, then cached).
+hipError_t noalloc_scratch(int device, float** ptr);
 
 // Stacked refinement (sa_refine.hip), all float32 unless noted.
 // (W_Q W_K^T)^T (d x d) from weights in the dtype.

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "sa_internal.h"
 
@@ -304,6 +305,37 @@ hipError_t launch_fused(const Plan& plan, const FusedArgs& args, int groups, hip
   DispatchFn f = plan_group(plan);
   const Launch l{groups, stream, start, stop};
   return f ? f(plan, args, l, nullptr) : hipErrorInvalidValue;
+}
+
+// ------------------------------------------------- allocation-free workspace
+// Partial sketches of sa_compress_batch_noalloc: a fixed device array that
+// the code object brings with it, so that call never allocates.  Every GPU
+// the library runs on holds its own copy at its own address until the
+// process ends; all calls on one GPU share it.  In host code `scratch` names
+// a host-side stand-in, never the device memory: its device address is taken
+// once per device with hipGetSymbolAddress (that device current) and only
+// that address is handed to kernels.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(int device, float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[device] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;  // the caller makes `device` current first
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[device] = static_cast<float*>(p);
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 hipError_t fused_occupancy(const Plan& plan, int* n) {
