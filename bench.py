@@ -373,6 +373,7 @@ def main() -> int:
     ap.add_argument("--users", type=int, default=None, help="change the number of users (same per-user shape)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the on-device ceiling measurements")
     ap.add_argument("--copy-calibration", action="store_true", help="run plain copies only (counter scaling)")
     ap.add_argument("--layers", type=int, default=0,
                     help="run the stacked refinement with this many layers (0: the single SA pass)")
@@ -506,6 +507,11 @@ def main() -> int:
                             max(MEDIAN_STEPS, args.steps))
     log(f"[bench] median of {max(MEDIAN_STEPS, args.steps)} single steps: {med_us:.2f} us")
 
+    ceil = None
+    if not args.no_ceilings:
+        ceil = measured_ceilings()
+        log(f"[bench] ceilings: {ceil}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_budget, stack_layers, args.norm)
@@ -542,10 +548,27 @@ def main() -> int:
             "parallelism": "single-gpu",
         },
         "roofline": roof,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def measured_ceilings() -> dict:
+    """On-device ceilings beside the published peaks (the fractions in
+    `roofline` stay against the published ones)."""
+    from sketch_attention_amd import binding
+    c = binding.sa_measure_ceilings()
+    return {
+        "mfma_bf16_16x16x32_tflops": round(c["mfma_bf16_tflops"], 1),
+        "mfma_bf16_32x32x16_tflops": round(c["mfma_bf16_32x32_tflops"], 1), "mfma_bf16_spec_tflops": PEAK_BF16_TFLOPS,
+        "hbm_copy_gbs": round(c["copy_gbs"], 1), "hbm_spec_gbs": PEAK_HBM_GBS,
+        "valu_fp32_fma_tflops": round(c["valu_fma_tflops"], 1), "valu_fp32_spec_tflops": 157.3,
+        "exp2_per_sec": float(f"{c['exp2_per_sec']:.4g}"),
+        "how": "bf16 matrix-core loops of 16x16x32 and of 32x32x16 products; fp32 FMA and hardware exp2 loops of independent chains; "
+               "streaming copy of 1 GiB (read + write counted)",
+    }
 
 
 if __name__ == "__main__":

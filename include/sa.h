@@ -205,6 +205,21 @@ sa_status sa_describe_plan(sa_handle h, int64_t total_rows, int32_t* groups, int
                            int32_t* waves_rows, int32_t* tile_rows, int32_t* k_padded);
 
 /*
+ * sa_measure_ceilings -- measured ceilings of the current device, against
+ * which the kernels' roofline fractions can be read beside the published
+ * peaks: bf16 matrix-core TFLOP/s for loops of independent 16x16x32 and of
+ * independent 32x32x16 products on every compute unit (the two instruction
+ * shapes do not reach the same rate), float32 FMA TFLOP/s and hardware exp2 evaluations
+ * per second on the vector ALUs (loops of independent chains), and the GB/s
+ * of a streaming copy (1 GiB read plus 1 GiB written per pass, larger than
+ * every cache).  Allocates 2 GiB and a few bytes of scratch, runs on stream
+ * and synchronises it; any output pointer may be NULL.  Returns
+ * SA_ERR_OUT_OF_MEMORY or SA_ERR_DEVICE on failure.
+ */
+sa_status sa_measure_ceilings(double* mfma_bf16_tflops, double* mfma_bf16_32x32_tflops, double* valu_fma_tflops,
+                              double* exp2_per_sec, double* copy_gbs, void* stream);
+
+/*
  * Stacked refinement (SequenceO1 close-reading page, section 2.2 "Stacked
  * Refinement and action-side fusion").  After one assignment and aggregation
  * the k x d state carries the user's information, so it queries the same raw

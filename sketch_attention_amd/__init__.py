@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     sa_grad_compute,
     sa_grad_create,
     sa_grad_destroy,
+    sa_measure_ceilings,
     sa_read_kernel_timing,
     sa_set_kernel_timing,
     sa_stack_compress_batch,

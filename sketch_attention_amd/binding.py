@@ -42,6 +42,7 @@ EXPORTED = (
     "sa_grad_read_kernel_timing",
     "sa_action_check_config", "sa_action_create", "sa_action_fuse", "sa_action_destroy",
     "sa_action_set_kernel_timing", "sa_action_read_kernel_timing",
+    "sa_measure_ceilings",
 )
 
 
@@ -126,6 +127,7 @@ def library() -> ctypes.CDLL:
         "sa_action_destroy": (None, [vp]),
         "sa_action_set_kernel_timing": (i32, [vp, i32]),
         "sa_action_read_kernel_timing": (i32, [vp, p_f64, p_i64]),
+        "sa_measure_ceilings": (i32, [p_f64, p_f64, p_f64, p_f64, p_f64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -672,3 +674,16 @@ class ActionFusion:
             self.close()
         except Exception:
             pass
+
+
+# ------------------------------------------------------------ device ceilings
+def sa_measure_ceilings(stream: Optional[torch.cuda.Stream] = None) -> dict:
+    """Measured ceilings of the current GPU (see include/sa.h): bf16 matrix-core
+    TFLOP/s (16x16x32 and 32x32x16 products), float32 FMA TFLOP/s, hardware exp2
+    per second, streaming-copy GB/s."""
+    vals = [ctypes.c_double() for _ in range(5)]
+    dev = torch.device("cuda", torch.cuda.current_device())
+    _check(library().sa_measure_ceilings(*[ctypes.byref(v) for v in vals], _stream_ptr(stream, dev)),
+           "sa_measure_ceilings")
+    keys = ("mfma_bf16_tflops", "mfma_bf16_32x32_tflops", "valu_fma_tflops", "exp2_per_sec", "copy_gbs")
+    return {k: v.value for k, v in zip(keys, vals)}

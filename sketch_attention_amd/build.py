@@ -35,6 +35,7 @@ SOURCES = [
     "sa_grad_api.cpp",
     "sa_action.hip",
     "sa_action_api.cpp",
+    "sa_ceilings.hip",
 ]
 # The bf16 plans (accumulators of at most 128 registers per lane) keep every
 # matrix-core result in VGPRs, so the softmax reads the affinity tile without
