@@ -107,8 +107,9 @@ Plan make_plan(int dtype, int d, int k) {
   p.blocks = 1;
   if (dtype == SA_BF16 && d == 128 && k > 512) {
     // two-phase pass over blocks of 8 x 32 prototypes (the folded matrix of
-    // more prototypes fits neither one group's registers nor its LDS)
-    p.kind = 1;
+    // more prototypes fits neither one group's registers nor its LDS), on
+    // 32x32x16 products
+    p.kind = 2;
     p.kw = 32;
     p.waves_k = 8;
     p.waves_rows = 1;
@@ -152,19 +153,19 @@ Plan make_plan(int dtype, int d, int k) {
   } else {
     p.kw = 128; p.waves_k = 8;
   }
-  if (!stream) p.waves_rows = waves / p.waves_k;
+  if (!stream && p.kind == 0) p.waves_rows = waves / p.waves_k;
   p.m_in_lds = (dtype == SA_BF16 && !stream) ? 1 : 0;
   if (const char* env = std::getenv("SA_PLAN")) {
     int kw = 0, wk = 0, wr = 0, ml = 0, kind = 0, pf = 1, rb = 2, sb = 2;
     const int n = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &kw, &wk, &wr, &ml, &kind, &pf, &rb, &sb);
-    if (n >= 4 && kw % 16 == 0 && kw > 0 && wk > 0 && wr > 0 && kw * wk >= k && (kind == 0 || kind == 1) &&
+    if (n >= 4 && kw % 16 == 0 && kw > 0 && wk > 0 && wr > 0 && kw * wk >= k && kind >= 0 && kind <= 2 &&
         (pf == 1 || pf == 2) && (rb == 2 || rb == 4) && (sb == 1 || sb == 2)) {
       p.kw = kw; p.waves_k = wk; p.waves_rows = wr; p.m_in_lds = ml ? 1 : 0; p.kind = kind; p.prefetch = pf;
       p.row_blocks = rb; p.score_buffers = sb;
     }
   }
   p.k_pad = p.kw * p.waves_k;
-  p.tile_rows = p.kind == 1 ? 16 * p.row_blocks * p.waves_rows : sa::kRowsPerWave * p.waves_rows;
+  p.tile_rows = p.kind >= 1 ? 16 * p.row_blocks * p.waves_rows : sa::kRowsPerWave * p.waves_rows;
   return p;
 }
 
@@ -442,6 +443,7 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     ra.kw = plan.kw;
     ra.k_pad = block_k;
     ra.blocks = nb;
+    ra.layout = plan.kind == 2 ? 1 : 0;
     for (int32_t i = 0; i <= nu; ++i) {
       fa.offsets[i] = offsets[u0 + i] - base;
       ra.offsets[i] = fa.offsets[i];

@@ -149,15 +149,29 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
 #pragma unroll
   for (int w = 1; w < kReduceShares; ++w)
     if (w < shares) s += part_sum[w][lane];
-  int t = p >> 6;
-  const int cbs = a.d / 16, jbs = a.kw / 16;
-  const int cb = t % cbs;
-  t /= cbs;
-  const int jb = t % jbs;
-  const int wj = t / jbs;
+  int j0, c;
   const int l = p & 63;
-  const int j0 = blk * a.k_pad + wj * a.kw + 16 * jb + 4 * (l >> 4);
-  const int c = 16 * cb + (l & 15);
+  if (a.layout == 1) {
+    // 32x32 products: float4 ((wj CB + cb) (kw / 8) + vq) 64 + lane holds prototypes
+    // wj kw + 8 vq + 4 (lane / 32) + 0..3 at column 32 cb + lane % 32
+    int t = p >> 6;
+    const int vqs = a.kw / 8, cbs = a.d / 32;
+    const int vq = t % vqs;
+    t /= vqs;
+    const int cb = t % cbs;
+    const int wj = t / cbs;
+    j0 = blk * a.k_pad + wj * a.kw + 8 * vq + 4 * (l >> 5);
+    c = 32 * cb + (l & 31);
+  } else {
+    int t = p >> 6;
+    const int cbs = a.d / 16, jbs = a.kw / 16;
+    const int cb = t % cbs;
+    t /= cbs;
+    const int jb = t % jbs;
+    const int wj = t / jbs;
+    j0 = blk * a.k_pad + wj * a.kw + 16 * jb + 4 * (l >> 4);
+    c = 16 * cb + (l & 15);
+  }
   float* o = a.out + (int64_t)u * a.k * a.d;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -284,6 +298,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t sta
 
 // ------------------------------------------------------------ dispatch
 static DispatchFn plan_group(const Plan& p) {
+  if (p.kind == 2) return p.dtype == 1 && p.d == 128 ? dispatch_stream_d128 : nullptr;
   if (p.kind == 1) {
     if (p.dtype != 1) return nullptr;
     if (p.d == 64) return dispatch_stream_d64;

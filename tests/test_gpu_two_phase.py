@@ -83,3 +83,15 @@ def test_two_phase_is_bitwise_deterministic():
         b = sa.compress(X, wl.offsets)
         torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("k,lengths", [(256, [1, 63, 64, 65, 3000, 0]), (200, [700, 129, 5])])
+def test_wide_products_one_pass(k, lengths, monkeypatch):
+    """The 32x32x16 pass (the one both phases above run on) as a one-pass
+    kernel for d = 128, k <= 256, selected by the plan override: parity with
+    the oracle, padded and full prototype counts, ragged users."""
+    monkeypatch.setenv("SA_PLAN", "32,8,1,0,2,1,4,2")
+    wl = W.make_workload(lengths=lengths, d=128, k=k, dtype="bf16", seed=5 * k, name=f"wide-one-pass-{k}")
+    got = run_gpu(wl)
+    _assert_parity(wl, got)
+    _assert_mass_identity(wl, got)
