@@ -152,15 +152,15 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_kernel(Re
   int j0, c;
   const int l = p & 63;
   if (a.layout == 1) {
-    // 32x32 products: float4 ((wj CB + cb) (kw / 8) + vq) 64 + lane holds prototypes
-    // wj kw + 8 vq + 4 (lane / 32) + 0..3 at column 32 cb + lane % 32
+    // 32x32 products: float4 ((jb CB + cb) 4 + vq) 64 + lane holds prototypes
+    // 32 jb + 8 vq + 4 (lane / 32) + 0..3 at column 32 cb + lane % 32
     int t = p >> 6;
-    const int vqs = a.kw / 8, cbs = a.d / 32;
-    const int vq = t % vqs;
-    t /= vqs;
+    const int cbs = a.d / 32;
+    const int vq = t & 3;
+    t >>= 2;
     const int cb = t % cbs;
-    const int wj = t / cbs;
-    j0 = blk * a.k_pad + wj * a.kw + 8 * vq + 4 * (l >> 5);
+    const int jb = t / cbs;
+    j0 = blk * a.k_pad + 32 * jb + 8 * vq + 4 * (l >> 5);
     c = 32 * cb + (l & 31);
   } else {
     int t = p >> 6;

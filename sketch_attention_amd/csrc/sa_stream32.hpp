@@ -36,13 +36,14 @@
 // 128 banks; 8-byte transposing reads: 32 lanes over 64 banks; stores: 32
 // banks, 16 lanes at a time for 8 bytes, 32 for 4 bytes).
 //
-// Each step (one barrier): DMA of tile t+3, the row sums of tile t from LDS
-// (all waves'), meanwhile the exponentials and row sums of tile t+1, the
-// factors and weights of tile t to LDS, the affinity of tile t+2 (its
-// products cover the weights' round trip through LDS), the aggregation of
-// tile t.  A row whose
-// sum leaves [2^-100, 2^100] sends the wave through an exact pass (a running
-// maximum over all prototypes, M from global memory).  The two-phase modes
+// Each step (one barrier): DMA of tile t+3; the row sums of tile t from LDS
+// (all waves'); the affinity of tile t+1, and in the shadow of its products
+// the factors and weights of tile t (to LDS); the aggregation of tile t, and
+// in the shadow of its products the exponentials and row sums of tile t+1.
+// The operands of each product are read ahead of it (one d-chunk for the
+// affinity, one row step for the aggregation).  A row whose sum leaves
+// [2^-100, 2^100] sends the wave through an exact pass (a running maximum
+// over all prototypes, M from global memory).  The two-phase modes
 // (FusedArgs::lse_mode) are those of sa_stream.hpp.
 #pragma once
 
@@ -91,6 +92,15 @@ __device__ __forceinline__ float pair32_max(float x) {
   float a, b;
   halves_of(x, a, b);
   return fmaxf(a, b);
+}
+
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 template <bool PAD, bool PU, int LM>
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
   };
   // fragments are read one d-chunk ahead of their products (scheduling fences
   // keep the compiler from hoisting all sixteen reads at once)
-  auto affinity_with = [&](f32x16 (&s)[2], uint32_t xs, auto mfrag) {
+  auto affinity_with = [&](f32x16 (&s)[2], uint32_t xs, auto mfrag, auto hook) {
     bf16x8 x[2][2];
     x[0][0] = lds_b128(aoff[0] + xs);
     x[0][1] = lds_b128(aoff[0] + xs + (uint32_t)(2 * 32 * D));
@@ -265,11 +275,13 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
       const f32x16 z = {};
       s[0] = mfma32(mf, x[kc & 1][0], kc == 0 ? z : s[0]);
       s[1] = mfma32(mf, x[kc & 1][1], kc == 0 ? z : s[1]);
+      hook(kc);  // independent vector work issued in the products' shadow
       if (SA32_FENCES) __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto affinity = [&](f32x16 (&s)[2], uint32_t xs) {
-    affinity_with(s, xs, [&](int kc) { return mreg[kc]; });
+  auto no_hook = [](int) {};
+  auto affinity = [&](f32x16 (&s)[2], uint32_t xs, auto hook) {
+    affinity_with(s, xs, [&](int kc) { return mreg[kc]; }, hook);
     pad_protos(s, jbase);
   };
 
@@ -307,6 +319,42 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
       }
       // lane l writes the partial of row 32 h + l32 (the half-waves hold both rows' sums)
       xl[xl_at(par, wj, 32 * h + l32)] = h ? sum[1] : sum[0];
+    }
+  };
+
+  // the same in eight slices of four products (slice i: row block i / 4,
+  // products 4 (i % 4) .. + 3, summed in the order above), so that the
+  // pieces can be issued between the products of another tile
+  float sm_a[2], sm_sum[2], sm_L = 0.f;
+  auto softmax_slice = [&](f32x16 (&s)[2], int i, int par, int q) {
+    const int rb = i >> 2, v0 = 4 * (i & 3);
+    if constexpr (LM == 2) {
+      if ((i & 3) == 0) {
+        const float* Lq = reinterpret_cast<const float*>(lds + OFF_L) + q * NT;
+        const float L = Lq[32 * rb + l32];
+        sm_L = (int64_t)(32 * rb + l32) < cx.end - cx.row ? L : INFINITY;
+      }
+#pragma unroll
+      for (int v = v0; v < v0 + 4; ++v) s[rb][v] = fast_exp2(s[rb][v] - sm_L);
+      if (i == 7) cursor_next(cx);
+    } else {
+      const float e0 = fast_exp2(s[rb][v0]), e1 = fast_exp2(s[rb][v0 + 1]);
+      const float e2 = fast_exp2(s[rb][v0 + 2]), e3 = fast_exp2(s[rb][v0 + 3]);
+      s[rb][v0] = e0;
+      s[rb][v0 + 1] = e1;
+      s[rb][v0 + 2] = e2;
+      s[rb][v0 + 3] = e3;
+      if ((i & 3) == 0) {
+        sm_a[0] = e0;
+        sm_a[1] = e1;
+      } else {
+        sm_a[0] += e0;
+        sm_a[1] += e1;
+      }
+      sm_a[0] += e2;
+      sm_a[1] += e3;
+      if ((i & 3) == 3) sm_sum[rb] = pair32_sum(sm_a[0] + sm_a[1]);
+      if (i == 7) xl[xl_at(par, wj, 32 * h + l32)] = h ? sm_sum[1] : sm_sum[0];
     }
   };
 
@@ -388,17 +436,20 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
     const int row = 32 * rb + l32;
     wst[rb] = eb + (uint32_t)(row * 64 + 8 * (h ^ ((row >> 1) & 7)));
   }
+  // part p of four: row block p / 2, prototypes 16 (p % 2) .. + 15
+  auto weights_part = [&](const f32x16 (&s)[2], const float (&f)[2], int p) {
+    const int rb = p >> 1;
+#pragma unroll
+    for (int b = 2 * (p & 1); b < 2 * (p & 1) + 2; ++b) {
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (bf16)(s[rb][4 * b + r] * f[rb]);
+      *(lds_u32x2*)(size_t)(wst[rb] ^ (uint32_t)(16 * b)) = __builtin_bit_cast(u32x2, w);
+    }
+  };
   auto weights_store = [&](const f32x16 (&s)[2], const float (&f)[2]) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        bf16x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (bf16)(s[rb][4 * b + r] * f[rb]);
-        *(lds_u32x2*)(size_t)(wst[rb] ^ (uint32_t)(16 * b)) = __builtin_bit_cast(u32x2, w);
-      }
-    }
+    for (int p = 0; p < 4; ++p) weights_part(s, f, p);
   };
 
   // ---- aggregation of tile t: acc[cb][v] += sum over the tile's rows of
@@ -418,20 +469,28 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
       const int c0 = 2 * (g16 & 1) + ((s16 & 3) >> 1);
       xb[qp][rr] = (uint32_t)(row * 256 + 16 * (c0 ^ chunk_sw32(row)) + 8 * (s16 & 1));
     }
-  auto aggregate = [&](f32x16 (&acc)[CBK], uint32_t xs) {
-#pragma unroll
-    for (int q = 0; q < NT / 16; ++q) {
+  // operands of row step q are read while the products of step q - 1 run
+  auto aggregate = [&](f32x16 (&acc)[CBK], uint32_t xs, auto hook) {
+    auto load = [&](int q, bf16x8& A, bf16x8 (&B)[CBK]) {
       const int qp = q & 1;
       const uint32_t qo_e = (uint32_t)((q >> 1) * 32 * 64), qo_x = (uint32_t)((q >> 1) * 32 * 256);
       const u32x2 a0 = lds_tr16(ea[qp][0] + qo_e), a1 = lds_tr16(ea[qp][1] + qo_e);
-      const bf16x8 A = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
+      A = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
 #pragma unroll
       for (int cb = 0; cb < CBK; ++cb) {
         const u32x2 b0 = lds_tr16((xb[qp][0] ^ (uint32_t)(64 * cb)) + xs + qo_x);
         const u32x2 b1 = lds_tr16((xb[qp][1] ^ (uint32_t)(64 * cb)) + xs + qo_x);
-        const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y});
-        acc[cb] = mfma32(A, B, acc[cb]);
+        B[cb] = __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y});
       }
+    };
+    bf16x8 A[2], B[2][CBK];
+    load(0, A[0], B[0]);
+#pragma unroll
+    for (int q = 0; q < NT / 16; ++q) {
+      if (q + 1 < NT / 16) load(q + 1, A[(q + 1) & 1], B[(q + 1) & 1]);
+#pragma unroll
+      for (int cb = 0; cb < CBK; ++cb) acc[cb] = mfma32(A[q & 1], B[q & 1][cb], acc[cb]);
+      hook(q);  // independent vector work issued in the products' shadow
       if (SA32_FENCES) __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -474,90 +533,115 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
     }
   };
 
+  // prologue: affinity and exponentials of tile 0
   f32x16 S0[2], S1[2];
   ensure_m();
   wait_tiles(std::integral_constant<int, NS - 2>{});
   __syncthreads();
-  affinity(S0, slot_of(0));
-  cursor_next(ca);
-  ensure_m();
-  wait_tiles(std::integral_constant<int, NS - 3>{});
-  __syncthreads();
-  affinity(S1, slot_of(1));
+  affinity(S0, slot_of(0), no_hook);
   cursor_next(ca);
   softmax_next(S0, 0, 0);
-  wait_tiles(std::integral_constant<int, NS - 4>{});
+  wait_tiles(std::integral_constant<int, NS - 3>{});  // tile 1
   __syncthreads();
 
-  // ring slot of tile t is t % NS: the main loop is unrolled by NS so every
-  // slot offset is a compile-time constant
+  // Step t (one barrier): DMA of tile t+3; the row sums of tile t from LDS
+  // (all waves'); the affinity of tile t+1, and in its shadow the factors and
+  // weights of tile t to LDS; the aggregation of tile t, and in its shadow the
+  // exponentials and row sums of tile t+1.  Sa holds tile t's exponentials,
+  // Sb receives tile t+1's scores.
   auto step = [&](int t, f32x16 (&Sa)[2], f32x16 (&Sb)[2], auto full, auto q0_) {
-    constexpr int q0 = decltype(q0_)::value;
-    constexpr int q1 = (q0 + 1) % NS, q2 = (q0 + 2) % NS, qn = (q0 + NS - 1) % NS;
+    const int q0 = q0_;  // a compile-time constant in the unrolled loop, t % NS in the tail
+    const int q1 = q0 + 1 < NS ? q0 + 1 : q0 + 1 - NS;
+    const int qn = q0 > 0 ? q0 - 1 : NS - 1;
+    constexpr bool F = decltype(full)::value;
     issue_tile(cl, qn);
-    // factors of tile t: reads issued now, the exponentials of tile t+1 cover their latency
+    const bool nxt = F || t + 1 < ntot;
     f32x4 pv[2][WJ / 4];
     if constexpr (LM != 2) combine_issue(pv, t & 1);
-    if (decltype(full)::value || t + 1 < ntot) softmax_next(Sb, (t + 1) & 1, q1);
-    if constexpr (LM == 1) {
-      float f[2], l[2], lse[2];
-      bool bad;
-      combine_finish(pv, f, l, bad);
-      lse[0] = __log2f(l[0]);
-      lse[1] = __log2f(l[1]);
-      if (bad) exact_wave(Sa, f, lse, slot_of(q0), cc.u);
-      const int row = 32 * h + l32;
-      if (wj == 0 && row_ok(cc, row)) args.stats[(int64_t)blk * rows + cc.row + row] = h ? lse[1] : lse[0];
-      ensure_m();
-      if (decltype(full)::value || t + 2 < ntot) affinity(Sa, slot_of(q2));
-      cursor_next(ca);
-    } else {
-      float f[2];
-      if constexpr (LM == 2) {
-        f[0] = f[1] = 1.f;  // the exponentials already carry the normalisation
-      } else {
-        float l[2], lse[2];
-        bool bad;
+    float f[2] = {1.f, 1.f}, l[2], lse[2];
+    bool bad = false;
+    // factors of tile t once their reads are in (two products later), then
+    // its weights in four parts; a wave with a row out of range takes the
+    // exact pass after the products instead
+    auto factors = [&]() {
+      if constexpr (LM != 2) {
         combine_finish(pv, f, l, bad);
-        if (bad) exact_wave(Sa, f, lse, slot_of(q0), cc.u);
+        if constexpr (LM == 1) {
+          lse[0] = __log2f(l[0]);
+          lse[1] = __log2f(l[1]);
+        } else {
+          f[0] = row_ok(cc, l32) ? f[0] : 0.f;
+          f[1] = row_ok(cc, 32 + l32) ? f[1] : 0.f;
+        }
+      }
+      // in the second phase the exponentials already carry the normalisation
+    };
+    auto shadow_a = [&](int kc) {
+      if (kc == 1) factors();
+      if constexpr (LM != 1) {
+        if (kc >= 2 && kc < 6 && !bad) weights_part(Sa, f, kc - 2);
+      }
+    };
+    ensure_m();
+    if (nxt) {
+      affinity(Sb, slot_of(q1), shadow_a);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) shadow_a(kc);
+    }
+    cursor_next(ca);
+    if (bad) {
+      exact_wave(Sa, f, lse, slot_of(q0), cc.u);
+      if constexpr (LM == 0) {
         f[0] = row_ok(cc, l32) ? f[0] : 0.f;
         f[1] = row_ok(cc, 32 + l32) ? f[1] : 0.f;
       }
-      weights_store(Sa, f);
-      // affinity of tile t+2 into the registers the weights just left: its
-      // products cover the latency of the weights' round trip through LDS
-      ensure_m();
-      if (decltype(full)::value || t + 2 < ntot) affinity(Sa, slot_of(q2));
-      cursor_next(ca);
-      aggregate(acc, slot_of(q0));
+      if constexpr (LM != 1) weights_store(Sa, f);
+    }
+    if constexpr (LM == 1) {
+      const int row = 32 * h + l32;
+      if (wj == 0 && row_ok(cc, row)) args.stats[(int64_t)blk * rows + cc.row + row] = h ? lse[1] : lse[0];
+      if (nxt) softmax_next(Sb, (t + 1) & 1, q1);
+    } else {
+      auto shadow_g = [&](int q) {
+        if (nxt) {
+          softmax_slice(Sb, 2 * q, (t + 1) & 1, q1);
+          softmax_slice(Sb, 2 * q + 1, (t + 1) & 1, q1);
+        }
+      };
+      aggregate(acc, slot_of(q0), shadow_g);
       if (cc.row + NT >= cc.end) flush(acc, cc.u);
     }
     cursor_next(cc);
     cursor_next(cl);
-    wait_tiles(std::integral_constant<int, NS - 4>{});  // tile t+3
+    wait_tiles(std::integral_constant<int, NS - 3>{});  // tile t+2
     __syncthreads();
   };
   using Full = std::integral_constant<bool, true>;
   using Tail = std::integral_constant<bool, false>;
-  using Q0 = std::integral_constant<int, 0>;
-  using Q1 = std::integral_constant<int, 1>;
-  using Q2 = std::integral_constant<int, 2>;
-  using Q3 = std::integral_constant<int, 3>;
-  static_assert(NS == 4, "the unrolled loop walks a ring of four slots");
+  static_assert(NS % 2 == 0, "an unrolled pass over the ring leaves the score buffers where it found them");
+  // ring slot of tile t is t % NS: the main loop is unrolled by NS so every
+  // slot offset is a compile-time constant; the tail (at most NS steps, which
+  // check at run time whether tile t+1 exists) computes it
   int t = 0;
-  for (; t + 5 < ntot; t += 4) {
-    step(t, S0, S1, Full{}, Q0{});
-    step(t + 1, S1, S0, Full{}, Q1{});
-    step(t + 2, S0, S1, Full{}, Q2{});
-    step(t + 3, S1, S0, Full{}, Q3{});
+  for (; t + NS < ntot; t += NS) {
+    static_for<0, NS>([&](auto i_) {
+      constexpr int i = decltype(i_)::value;
+      if constexpr (i % 2 == 0)
+        step(t + i, S0, S1, Full{}, i_);
+      else
+        step(t + i, S1, S0, Full{}, i_);
+    });
   }
-  // 0..5 steps remain (t % 4 == 0, S0 holds tile t's scores); these check at
-  // run time which of the tiles after t exist
-  if (t < ntot) step(t, S0, S1, Tail{}, Q0{});
-  if (t + 1 < ntot) step(t + 1, S1, S0, Tail{}, Q1{});
-  if (t + 2 < ntot) step(t + 2, S0, S1, Tail{}, Q2{});
-  if (t + 3 < ntot) step(t + 3, S1, S0, Tail{}, Q3{});
-  if (t + 4 < ntot) step(t + 4, S0, S1, Tail{}, Q0{});
+  int q = 0;  // t % NS here
+  while (t < ntot) {
+    step(t, S0, S1, Tail{}, q);
+    q = q + 1 < NS ? q + 1 : 0;
+    if (++t >= ntot) break;
+    step(t, S1, S0, Tail{}, q);
+    q = q + 1 < NS ? q + 1 : 0;
+    ++t;
+  }
   wait_vm<0>();  // no DMA outlives the work group
 }
 

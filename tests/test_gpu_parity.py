@@ -50,6 +50,9 @@ def _assert_mass_identity(wl, got, tol=None):
     worst = 0.0
     for u in range(wl.num_users):
         rows = wl.user_rows(u).astype(np.float64)
+        if rows.shape[0] == 0:  # no behaviours: the sketch is all zeros
+            assert not np.any(got[u]), u
+            continue
         want = rows.sum(axis=0)
         have = got[u].astype(np.float64).sum(axis=0)
         scale = max(float(np.abs(want).max()), float(np.abs(rows).max()) * math.sqrt(max(rows.shape[0], 1)), 1e-30)
