@@ -81,8 +81,9 @@ typedef enum sa_dtype {
  *
  *   out    host pointer receiving the new handle (set to NULL on error)
  *   d      history / prototype width; supported: 64 or 128
- *   k      number of prototypes; supported: 1..1024 with k*d <= 65536 for
- *          SA_BF16, 1..256 for SA_F32
+ *   k      number of prototypes; supported: 1..1024 for SA_BF16 (beyond
+ *          512 at d = 128 the pass runs in two phases over blocks of 256
+ *          prototypes), 1..256 for SA_F32
  *   tau    affinity scale, finite (any sign, zero allowed)
  *   dtype  element type of P, W_Q, W_K and of every X passed later
  *   P      device, [k][d] prototypes (section 2.1: P^(0), shared by all users)
@@ -307,8 +308,10 @@ sa_status sa_stack_read_kernel_timing(sa_stack h, double* fused_ms, double* redu
  * with the weight gradients summed over the users of the batch.
  *
  * sa_grad_check_config -- what sa_grad_create returns for these scalars:
- * SA_BF16 only, d in {64, 128}, 1 <= k <= 256 (else SA_ERR_UNSUPPORTED or
- * SA_ERR_INVALID_ARG as for sa_check_config).
+ * SA_BF16 only, d in {64, 128}, 1 <= k <= 1024 (else SA_ERR_UNSUPPORTED or
+ * SA_ERR_INVALID_ARG as for sa_check_config).  Beyond 256 prototypes the
+ * row statistics are gathered over blocks of 256 in a first pass, merged,
+ * and the gradient of the folded matrix formed in a second pass per block.
  *
  * sa_grad_create -- prepare the weights once (device pointers in the dtype,
  * as for sa_create; they are not used after the call returns).  The work is

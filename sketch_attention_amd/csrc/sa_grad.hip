@@ -61,12 +61,17 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int wj = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jbase = wj * KW;
+  // prototype block (phases 1 and 2): prototypes KPAD blk .. of M and G
+  const int nblk = args.phase ? args.blocks : 1;
+  const int blk = args.phase ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  const int phase = args.phase;
+  const int jbase = wj * KW;                // within the block
+  const int jg = blk * KPAD + jbase;        // first global prototype of this wave
   const int k = args.k;
   const bf16* const X = static_cast<const bf16*>(args.X);
-  const bf16* const M = static_cast<const bf16*>(args.M);
+  const bf16* const M = static_cast<const bf16*>(args.M) + (int64_t)blk * KPAD * D;
 
-  const int64_t rows = args.rows, ngroups = gridDim.x, grp = blockIdx.x;
+  const int64_t rows = args.rows, ngroups = gridDim.x / nblk, grp = blockIdx.x / nblk;
   const int64_t r_begin = grp * rows / ngroups, r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;  // the host launches at most one group per row
 
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     g_user = u;
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
-      const int j = jbase + 16 * jb + l16;
+      const int j = jg + 16 * jb + l16;
       const float* grow = args.G + ((int64_t)u * k + (j < k ? j : 0)) * D;
       const float keep = j < k ? 1.f : 0.f;  // padding prototypes get zero rows
 #pragma unroll
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     if constexpr (PAD) {
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
-        const bool ok = jbase + 16 * jb + l16 < k;
+        const bool ok = jg + 16 * jb + l16 < k;
 #pragma unroll
         for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   // wave's prototypes stays within [2^-100, 2^100]; a wave that sees a row
   // outside it (huge scores, or all of its prototypes far below) redoes that
   // row block with its own row maxima m_w.  The merge takes any mix of shifts.
-  const bool real_protos = jbase < k;  // wave-uniform: false for a wave of padding prototypes only
+  const bool real_protos = jg < k;  // wave-uniform: false for a wave of padding prototypes only
   auto row_stats = [&](int par) {
 #pragma unroll
     for (int ib = 0; ib < RB; ++ib) {
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   __syncthreads();
   ensure_g(ca.u);
   affinity(0);
-  row_stats(0);
+  if (phase != 2) row_stats(0);
   cursor_next(ca);
   wait_tiles(std::integral_constant<int, NS - 3>{});  // tile 1
   __syncthreads();
@@ -278,23 +283,39 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     issue_tile(cl, (t + NS - 1) % NS);  // the slot of tile t - 1
     cursor_next(cl);
     const int par = t & 1;
-    // merge the waves for row my_row of tile t
-    float m = xs_m[par][my_row][0];
-#pragma unroll
-    for (int w = 1; w < WJ; ++w) m = fmaxf(m, xs_m[par][my_row][w]);
-    float l = 0.f, c = 0.f;
-#pragma unroll
-    for (int w = 0; w < WJ; ++w) {
-      const float f = fast_exp2(xs_m[par][my_row][w] - m);  // 0 for a wave without real prototypes
-      l += xs_l[par][my_row][w] * f;
-      c += xs_c[par][my_row][w] * f;
-    }
-    c *= 1.f / l;
-    // log-sum-exp of the row in log2 units: A = 2^(s' - lse)
-    float lse = m + __builtin_amdgcn_logf(l);
     const bool valid = (int64_t)my_row < cc.end - cc.row;
-    if (valid && wj == 0 && l16 < 8)
-      *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{lse, c, 0.f, 0.f};
+    float lse, c;
+    if (phase == 2) {
+      // the merged statistics of all blocks (the lanes of a row read the same 8 bytes)
+      const float* st = args.stats + (valid ? (cc.row + my_row) * 4 : 0);
+      lse = st[0];
+      c = st[1];
+    } else {
+      // merge the waves for row my_row of tile t
+      float m = xs_m[par][my_row][0];
+#pragma unroll
+      for (int w = 1; w < WJ; ++w) m = fmaxf(m, xs_m[par][my_row][w]);
+      float l = 0.f;
+      c = 0.f;
+#pragma unroll
+      for (int w = 0; w < WJ; ++w) {
+        const float f = fast_exp2(xs_m[par][my_row][w] - m);  // 0 for a wave without real prototypes
+        l += xs_l[par][my_row][w] * f;
+        c += xs_c[par][my_row][w] * f;
+      }
+      if (phase == 1) {
+        // this block's share: (m, l, sum over its prototypes of 2^(s' - m) dA)
+        if (valid && wj == 0 && l16 < 8)
+          *reinterpret_cast<f32x4*>(args.stats + ((int64_t)blk * rows + cc.row + my_row) * 4) = f32x4{m, l, c, 0.f};
+      } else {
+        c *= 1.f / l;
+        // log-sum-exp of the row in log2 units: A = 2^(s' - lse)
+        lse = m + __builtin_amdgcn_logf(l);
+        if (valid && wj == 0 && l16 < 8)
+          *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{lse, c, 0.f, 0.f};
+      }
+    }
+    if (phase != 1) {
     if (!valid) lse = INFINITY;  // rows past the piece add nothing
 
     // dS of this wave's prototypes as bf16 weights of the aggregation
@@ -341,11 +362,12 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
         for (int jb = 0; jb < JB; ++jb) acc[jb][cb] = MF::run(a[jb], xb, acc[jb][cb]);
       }
     }
+    }  // phase != 1
     // products and row statistics of tile t + 1
     if (ca.row < r_end) {
       ensure_g(ca.u);
       affinity((t + 1) % NS);
-      row_stats(par ^ 1);
+      if (phase != 2) row_stats(par ^ 1);
     }
     cursor_next(cc);
     cursor_next(ca);
@@ -355,8 +377,11 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   }
   wait_vm<0>();  // no DMA outlives the work group
 
-  // ---- one partial per group, lane layout [wj][jb][cb][lane][4]
-  float* dst = args.partial + grp * (int64_t)(KPAD * D);
+  if (phase == 1) return;  // statistics only
+  // ---- one partial per group, lane layout [wj][jb][cb][lane][4]; block b's
+  // slots follow the ngroups + 1 slots of block b - 1 (the reduction's layout
+  // for one user)
+  float* dst = args.partial + ((int64_t)blk * (ngroups + 1) + grp) * (int64_t)(KPAD * D);
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -574,47 +599,70 @@ __global__ __launch_bounds__(64 * W2) void grad_dx_kernel(GradDxArgs args) {
   wait_vm<0>();
 }
 
+// ------------------------------------------------------------ block merge
+// Row i's statistics over all prototype blocks from the blocks' (m_b, l_b,
+// c_b): m = max m_b, l = sum l_b 2^(m_b - m), c = sum c_b 2^(m_b - m) / l,
+// written as (m + log2 l, c).
+__global__ __launch_bounds__(256) void grad_merge_kernel(const f32x4* bstats, int64_t rows, int blocks, f32x4* stats) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows) return;
+  float m = -INFINITY;
+  for (int b = 0; b < blocks; ++b) m = fmaxf(m, bstats[(int64_t)b * rows + i][0]);
+  float l = 0.f, c = 0.f;
+  for (int b = 0; b < blocks; ++b) {
+    const f32x4 v = bstats[(int64_t)b * rows + i];
+    const float f = exp2f(v[0] - m);  // 0 for a block of padding prototypes only (m_b = -inf)
+    l += v[1] * f;
+    c += v[2] * f;
+  }
+  stats[i] = f32x4{m + log2f(l), c / l, 0.f, 0.f};
+}
+
 // ------------------------------------------------------------ small products
 // Two independent small products per launch (blockIdx.z picks one), one
-// 16 x 16 tile of C per work group.  The whole inner dimension (<= 256) of
-// the tile's operands is staged in LDS with all loads in flight at once, so a
-// tile costs one memory latency; operands are read with arbitrary strides, so
-// transposed views need no copy.
+// 16 x 16 tile of C per work group.  The inner dimension is staged in LDS 256
+// at a time with all loads of a stage in flight at once, so a stage costs one
+// memory latency; operands are read with arbitrary strides, so transposed
+// views need no copy.
 __global__ __launch_bounds__(256) void small_matmul_kernel(MatmulPair pr) {
-  __shared__ float As[16][kMaxInner + 1], Bs[kMaxInner][17];
+  __shared__ float As[16][kInnerStage + 1], Bs[kInnerStage][17];
   const Matmul& p = pr.p[blockIdx.z];
   const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 16;
   if (m0 >= p.rows || n0 >= p.cols) return;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  // all loads in flight before any store; index arithmetic by shifts only
-  // (a runtime division per element costs more than the loads)
-  float av[16], bv[kMaxInner / 16];
-#pragma unroll
-  for (int mm = 0; mm < 16; ++mm) {
-    const int tt = threadIdx.x;
-    av[mm] = tt < p.inner && m0 + mm < p.rows ? p.A[(m0 + mm) * p.a_rs + tt * p.a_cs] : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxInner / 16; ++i) {
-    const int e = threadIdx.x + 256 * i, tb = e >> 4, nn = e & 15;
-    bv[i] = tb < p.inner && n0 + nn < p.cols ? p.B[tb * p.b_rs + (n0 + nn) * p.b_cs] : 0.f;
-  }
-#pragma unroll
-  for (int mm = 0; mm < 16; ++mm)
-    if (threadIdx.x < p.inner) As[mm][threadIdx.x] = av[mm];
-#pragma unroll
-  for (int i = 0; i < kMaxInner / 16; ++i) {
-    const int e = threadIdx.x + 256 * i;
-    if ((e >> 4) < p.inner) Bs[e >> 4][e & 15] = bv[i];
-  }
-  __syncthreads();
   float s0 = 0.f, s1 = 0.f;
-  int t = 0;
-  for (; t + 2 <= p.inner; t += 2) {
-    s0 = fmaf(As[ty][t], Bs[t][tx], s0);
-    s1 = fmaf(As[ty][t + 1], Bs[t + 1][tx], s1);
+  for (int t0 = 0; t0 < p.inner; t0 += kInnerStage) {
+    const int n = p.inner - t0 < kInnerStage ? p.inner - t0 : kInnerStage;
+    // all loads in flight before any store; index arithmetic by shifts only
+    // (a runtime division per element costs more than the loads)
+    float av[16], bv[kInnerStage / 16];
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm) {
+      const int tt = threadIdx.x;
+      av[mm] = tt < n && m0 + mm < p.rows ? p.A[(m0 + mm) * p.a_rs + (t0 + tt) * p.a_cs] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kInnerStage / 16; ++i) {
+      const int e = threadIdx.x + 256 * i, tb = e >> 4, nn = e & 15;
+      bv[i] = tb < n && n0 + nn < p.cols ? p.B[(t0 + tb) * p.b_rs + (n0 + nn) * p.b_cs] : 0.f;
+    }
+    if (t0 > 0) __syncthreads();  // the previous stage's reads are done
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm)
+      if (threadIdx.x < n) As[mm][threadIdx.x] = av[mm];
+#pragma unroll
+    for (int i = 0; i < kInnerStage / 16; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      if ((e >> 4) < n) Bs[e >> 4][e & 15] = bv[i];
+    }
+    __syncthreads();
+    int t = 0;
+    for (; t + 2 <= n; t += 2) {
+      s0 = fmaf(As[ty][t], Bs[t][tx], s0);
+      s1 = fmaf(As[ty][t + 1], Bs[t + 1][tx], s1);
+    }
+    if (t < n) s0 = fmaf(As[ty][t], Bs[t][tx], s0);
   }
-  if (t < p.inner) s0 = fmaf(As[ty][t], Bs[t][tx], s0);
   if (m0 + ty < p.rows && n0 + tx < p.cols) p.C[(int64_t)(m0 + ty) * p.cols + n0 + tx] = p.alpha * (s0 + s1);
 }
 
@@ -641,7 +689,7 @@ hipError_t stats_p(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t
 // padding prototypes (k below 32 WJ) need their scores masked; the occupancy is that of the padded form
 template <int D, int WJ>
 hipError_t stats_t(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
-  if (occ || a.k != kGradKW * WJ) return stats_p<D, WJ, true>(a, groups, s, e0, e1, occ);
+  if (occ || a.k != kGradKW * WJ * (a.phase ? a.blocks : 1)) return stats_p<D, WJ, true>(a, groups, s, e0, e1, occ);
   return stats_p<D, WJ, false>(a, groups, s, e0, e1, occ);
 }
 
@@ -680,8 +728,15 @@ int grad_stats_waves(int k) {
   if (k < 1) return 0;
   if (k <= 2 * kGradKW) return 2;
   if (k <= 4 * kGradKW) return 4;
-  if (k <= 8 * kGradKW) return 8;
+  if (k <= 4 * kGradBlock) return 8;  // one block of 256, or up to four walked in two phases
   return 0;
+}
+
+hipError_t launch_grad_merge(const float* bstats, int64_t rows, int blocks, float* stats, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(grad_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const f32x4*>(bstats), rows, blocks, reinterpret_cast<f32x4*>(stats));
+  return hipGetLastError();
 }
 
 hipError_t launch_grad_stats(int d, int waves, const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t start,
@@ -731,7 +786,7 @@ hipError_t launch_grad_pack(const void* M, const void* Qp, const float* G, int u
 
 hipError_t launch_small_matmuls(const Matmul& a, const Matmul& b, hipStream_t s) {
   for (const Matmul* p : {&a, &b})
-    if (p->inner < 1 || p->inner > kMaxInner || p->rows < 1 || p->cols < 1) return hipErrorInvalidValue;
+    if (p->inner < 1 || p->rows < 1 || p->cols < 1) return hipErrorInvalidValue;
   const int rows = a.rows > b.rows ? a.rows : b.rows, cols = a.cols > b.cols ? a.cols : b.cols;
   const dim3 grid((unsigned)((cols + 15) / 16), (unsigned)((rows + 15) / 16), 2);
   hipLaunchKernelGGL(small_matmul_kernel, grid, dim3(256), 0, s, MatmulPair{{a, b}});

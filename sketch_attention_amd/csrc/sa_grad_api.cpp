@@ -44,6 +44,7 @@ struct sa_grad_s {
   int device = 0;
   int cu_count = 0;
   int d = 0, k = 0, k_pad = 0, waves = 0;
+  int blocks = 1;  // prototype blocks of pass 1 (k_pad = blocks * waves * 32)
   int stats_per_cu = 1, dx_per_cu = 1;
   float tau = 0.f;
   void* M = nullptr;     // bf16 [k_pad][d], tau log2(e) P W_Q W_K^T
@@ -56,6 +57,8 @@ struct sa_grad_s {
   // workspace, grown on demand
   float* stats = nullptr;
   size_t stats_rows = 0;
+  float* bstats = nullptr;  // per-block statistics of pass 1 (more than one block)
+  size_t bstats_floats = 0;
   float* partial = nullptr;
   size_t partial_floats = 0;
   void* packed = nullptr;
@@ -79,7 +82,7 @@ bool grow(T*& p, size_t& have, size_t need, size_t elem) {
 
 void free_handle(sa_grad_s* h) {
   for (void* p : {(void*)h->M, (void*)h->Qp, (void*)h->Q, (void*)h->P32, (void*)h->WQ32, (void*)h->WK32,
-                  (void*)h->dq, (void*)h->stats, (void*)h->partial, h->packed})
+                  (void*)h->dq, (void*)h->stats, (void*)h->bstats, (void*)h->partial, h->packed})
     if (p) (void)hipFree(p);
   for (auto* v : {&h->pending, &h->spare})
     for (auto& e : *v)
@@ -112,7 +115,8 @@ SA_API sa_status sa_grad_create(sa_grad* out, int32_t d, int32_t k, float tau, s
   h->k = k;
   h->tau = tau;
   h->waves = sa::grad_stats_waves(k);
-  h->k_pad = sa::kGradKW * h->waves;
+  h->blocks = sa::grad_stats_blocks(k);
+  h->k_pad = sa::kGradKW * h->waves * h->blocks;
   hipDeviceProp_t prop;
   if (hipGetDevice(&h->device) != hipSuccess || hipGetDeviceProperties(&prop, h->device) != hipSuccess ||
       sa::grad_occupancy(d, h->waves, &h->stats_per_cu, &h->dx_per_cu) != hipSuccess || h->stats_per_cu < 1 ||
@@ -164,6 +168,7 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
   DeviceGuard guard(h->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int d = h->d, k = h->k, k_pad = h->k_pad, chunks = k_pad / sa::kGradKW;
+  const int nb = h->blocks, kb = sa::kGradKW * h->waves;  // blocks of pass 1 and prototypes per block
   const size_t kd = (size_t)k * d;
   float* const dq_sum = h->dq;
   float* const dq_one = h->dq + kd;
@@ -181,7 +186,8 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
   if (max_rows > 0) {
     const int64_t g1 = max_rows < stats_groups_max ? max_rows : stats_groups_max;
     if (!grow(h->stats, h->stats_rows, (size_t)max_rows * 4, sizeof(float)) ||
-        !grow(h->partial, h->partial_floats, (size_t)g1 * k_pad * d, sizeof(float)) ||
+        !grow(h->partial, h->partial_floats, (size_t)nb * (g1 + 1) * kb * d, sizeof(float)) ||
+        (nb > 1 && !grow(h->bstats, h->bstats_floats, (size_t)nb * max_rows * 4, sizeof(float))) ||
         !grow(reinterpret_cast<unsigned char*&>(h->packed), h->packed_bytes,
               (size_t)max_users * chunks * sa::grad_chunk_bytes(d), 1))
       return SA_ERR_OUT_OF_MEMORY;
@@ -228,7 +234,20 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     const int g1 = (int)(rows < stats_groups_max ? rows : stats_groups_max);
     const bool last = u1 == num_users;
     const bool time_it = h->timing && last;
-    e = sa::launch_grad_stats(d, h->waves, a1, g1, s, time_it ? ev.ev[0] : nullptr, time_it ? ev.ev[1] : nullptr);
+    if (nb == 1) {
+      e = sa::launch_grad_stats(d, h->waves, a1, g1, s, time_it ? ev.ev[0] : nullptr, time_it ? ev.ev[1] : nullptr);
+    } else {
+      // blocks of 256 prototypes: their statistics, the merge, then the aggregation with the merged values
+      a1.blocks = nb;
+      a1.phase = 1;
+      a1.stats = h->bstats;
+      e = sa::launch_grad_stats(d, h->waves, a1, g1 * nb, s, time_it ? ev.ev[0] : nullptr, nullptr);
+      if (e == hipSuccess) e = sa::launch_grad_merge(h->bstats, rows, nb, h->stats, s);
+      a1.phase = 2;
+      a1.stats = h->stats;
+      if (e == hipSuccess)
+        e = sa::launch_grad_stats(d, h->waves, a1, g1 * nb, s, nullptr, time_it ? ev.ev[1] : nullptr);
+    }
     if (e != hipSuccess) break;
 
     sa::ReduceArgs r{};
@@ -241,7 +260,8 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
     r.k = k;
     r.d = d;
     r.kw = sa::kGradKW;
-    r.k_pad = k_pad;
+    r.k_pad = kb;
+    r.blocks = nb;
     r.offsets[0] = 0;
     r.offsets[1] = rows;
     e = sa::launch_reduce(r, s);

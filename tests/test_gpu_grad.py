@@ -5,6 +5,7 @@ the batch's users) over the whole tensor; <= 2e-2 (bfloat16 operands,
 float32 accumulation; the upstream gradient is rounded to bfloat16 on the
 device).
 Cases: every wave count of the statistics pass (k <= 64, <= 128, <= 256),
+two to four blocks of 256 prototypes walked in two phases (k up to 1024),
 both widths, padded prototype counts, ragged and empty users, users shorter
 than a tile, peaked assignments, more users than one launch carries, an empty
 batch, repeated calls on one handle, and the full long workload."""
@@ -74,6 +75,12 @@ CASES = [
     ("k100_d64_pad", 64, 100, [777, 333], {}),
     ("k256_hot", 128, 256, [1200, 800], dict(x_scale=6.0)),
     ("k256_clusters_dup", 128, 256, [2048, 600], dict(x_kind="clusters", dup_fraction=0.3)),
+    ("k300_d128_pad", 128, 300, [900, 3, 0, 1500], {}),
+    ("k512_d128", 128, 512, [1100, 640], {}),
+    ("k1000_d128_pad", 128, 1000, [700, 1, 1300], {}),
+    ("k1024_d128", 128, 1024, [1500, 33], {}),
+    ("k1024_d64", 64, 1024, [600, 0, 900], {}),
+    ("k1000_clusters", 128, 1000, [1600, 500], dict(x_kind="clusters")),
 ]
 
 
@@ -85,7 +92,8 @@ def test_grad_parity(case):
     _check(wl, G, _run(wl, G))
 
 
-def test_grad_spike_rows_take_the_shifted_path():
+@pytest.mark.parametrize("k", [256, 1000])
+def test_grad_spike_rows_take_the_shifted_path(k):
     """Rows scaled by 100 give scores of several hundred (log2 units): their
     unshifted sums overflow in the waves holding the top prototypes and
     underflow in the others, so the statistics pass redoes them with row
@@ -100,7 +108,7 @@ def test_grad_spike_rows_take_the_shifted_path():
     four gradients are compared at the usual tolerance."""
     from oracle import sa_oracle as SO
 
-    wl = W.make_workload(lengths=[3000, 500, 64], d=128, k=256, dtype="bf16", seed=13, name="spikes")
+    wl = W.make_workload(lengths=[3000, 500, 64], d=128, k=k, dtype="bf16", seed=13, name=f"spikes{k}")
     s = np.sort(SO.affinity(wl.X, wl.P, wl.W_Q, wl.W_K, wl.tau), axis=0) / np.log(2.0)
     gap = s[-1] - s[-2]
     rows = []
@@ -112,12 +120,13 @@ def test_grad_spike_rows_take_the_shifted_path():
         wl.X[r] = W.round_to_bf16(wl.X[r] * 100.0)
     top = (np.sort(SO.affinity(wl.X[rows], wl.P, wl.W_Q, wl.W_K, wl.tau), axis=0) / np.log(2.0))[-1]
     assert np.all(top > 300.0), top  # far outside the unshifted range [2^-100, 2^100]
-    G = W.make_upstream_grad(3, 256, 128, seed=17)
+    G = W.make_upstream_grad(3, k, 128, seed=17)
     _check(wl, G, _run(wl, G))
 
 
 @pytest.mark.parametrize("case", [c for c in CASES if c[0] in ("k256_d128", "k200_d128_pad", "k100_d64_pad",
-                                                                 "k256_hot")], ids=lambda c: c[0])
+                                                                 "k256_hot", "k1000_d128_pad", "k1024_d64")],
+                         ids=lambda c: c[0])
 def test_grad_forced_shift_path(case, monkeypatch):
     """Every row block through the statistics pass's shifted path (its fallback
     for extreme scores), at normal scale, all four gradients at tolerance."""
@@ -162,6 +171,37 @@ def test_grad_long_full():
     wl = W.named_workload("long")
     G = W.make_upstream_grad(wl.num_users, wl.P.shape[0], wl.P.shape[1], seed=0)
     _check(wl, G, _run(wl, G))
+
+
+def test_grad_many_proto_full_sampled():
+    """The many-prototype workload at full size (32 users x 100K rows, d = 64,
+    k = 1024: four blocks of 256 prototypes in two phases).  dX of two users
+    against the oracle on those users; the weight gradients, sums over all
+    3.2M rows, through additivity over users (the batch's gradients equal the
+    sum of those of its two halves, each run on its own), which holds at any
+    size."""
+    wl = W.named_workload("many_proto")
+    k, d = wl.P.shape
+    G = W.make_upstream_grad(wl.num_users, k, d, seed=3)
+    X, P, WQ, WK = to_device(wl)
+    Gd = torch.from_numpy(G).cuda()
+    users = [0, wl.num_users - 1]
+    half = wl.num_users // 2
+    off = np.asarray(wl.offsets, dtype=np.int64)
+    with SketchAttentionGrad(P, WQ, WK, wl.tau) as h:
+        full = [t.float().cpu().numpy() for t in h.backward(X, off, Gd)]
+        lo = [t.float().cpu().numpy() for t in h.backward(X[: off[half]], off[: half + 1], Gd[:half])]
+        hi = [t.float().cpu().numpy() for t in h.backward(X[off[half]:], off[half:] - off[half], Gd[half:])]
+        torch.cuda.synchronize()
+    want = GO.sketch_grad_batch(wl.X, wl.offsets, wl.P, wl.W_Q, wl.W_K, wl.tau, G, users=users)
+    e_dx = _dx_err(wl, full[0], want["dX"], users)
+    e_add = [_nerr(f, a + b) for f, a, b in zip(full[1:], lo[1:], hi[1:])]
+    e_dx_half = _nerr(full[0], np.concatenate([lo[0], hi[0]]))
+    print(f"[grad] many_proto dX(sampled)={e_dx:.3e} additivity={e_add} dX halves={e_dx_half:.3e}", flush=True)
+    assert e_dx <= TOL["bf16"]
+    assert e_dx_half == 0.0  # a user's rows see the same kernels either way
+    for e in e_add:
+        assert e <= 1e-5, e_add  # float32 sums in another order
 
 
 def test_grad_is_bitwise_deterministic():
