@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     sa_check_batch,
     sa_check_config,
     sa_compress_batch,
+    sa_compress_batch_bound,
     sa_compress_batch_noalloc,
     sa_create,
     sa_describe_plan,
@@ -31,6 +32,7 @@ from .binding import (  # noqa: F401
     sa_read_kernel_timing,
     sa_set_kernel_timing,
     sa_stack_compress_batch,
+    sa_stack_compress_batch_bound,
     sa_stack_create,
     sa_stack_destroy,
     sa_status_string,

@@ -235,6 +235,33 @@ def sa_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: to
     _check(st, "sa_compress_batch")
 
 
+def _bound_call(fn, name: str, args: tuple, keep: tuple):
+    """A callable that re-issues fn(*args) and raises on a non-OK status; keep
+    holds the objects whose memory the pointers in args refer to."""
+    def run() -> None:
+        st = fn(*args)
+        if st != 0:
+            _check(st, name)
+    run.keep = keep
+    return run
+
+
+def sa_compress_batch_bound(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
+                            stream: Optional[torch.cuda.Stream] = None):
+    """Check the arguments of sa_compress_batch once and return a callable that
+    enqueues that same call again (same buffers, offsets and stream) with no
+    further Python-side work: for loops that re-run one batch layout over
+    buffers that stay alive (the callable keeps X, out and the offsets)."""
+    offs = np.array(_offsets_array(offsets), dtype=np.int64, copy=True)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    _check_batch_tensors(_info(handle, "sa"), X, offs, out)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    args = (handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(), stream.cuda_stream)
+    return _bound_call(library().sa_compress_batch, "sa_compress_batch", args, (X, offs, out, stream))
+
+
 def sa_compress_batch_noalloc(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
                               stream: Optional[torch.cuda.Stream] = None) -> None:
     """As sa_compress_batch, through the entry point that allocates nothing
@@ -402,6 +429,19 @@ def sa_stack_compress_batch(handle: ctypes.c_void_p, X: torch.Tensor, offsets, o
     st = library().sa_stack_compress_batch(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
                                            stream.cuda_stream)
     _check(st, "sa_stack_compress_batch")
+
+
+def sa_stack_compress_batch_bound(handle: ctypes.c_void_p, X: torch.Tensor, offsets, out: torch.Tensor,
+                                  stream: Optional[torch.cuda.Stream] = None):
+    """As sa_compress_batch_bound, for sa_stack_compress_batch."""
+    offs = np.array(_offsets_array(offsets), dtype=np.int64, copy=True)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    _check_batch_tensors(_info(handle, "stack"), X, offs, out)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    args = (handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(), stream.cuda_stream)
+    return _bound_call(library().sa_stack_compress_batch, "sa_stack_compress_batch", args, (X, offs, out, stream))
 
 
 def sa_stack_destroy(handle: Optional[ctypes.c_void_p]) -> None:

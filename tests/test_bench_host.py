@@ -60,11 +60,11 @@ def test_conflicting_modes_are_refused_before_any_gpu_work(flags):
     assert "only" in r.stderr and r.stdout == ""
 
 
-def test_short_runs_time_every_step():
-    # the driver's short runs (e.g. 20 steps) take a kernel duration on every step
-    assert bench.timing_period(20) == 1
-    assert bench.timing_period(49) == 1
-    assert bench.timing_period(400) == 8
+def test_kernel_timing_pass_is_long_enough():
+    # the driver's short runs (e.g. 20 steps) still average the kernel durations over >= 50 launches
+    assert bench.kernel_timing_steps(20) == 50
+    assert bench.kernel_timing_steps(400) == 400
+    assert bench.timing_period(20) == 1 and bench.timing_period(400) == 8  # the secondary modes
 
 
 def test_cpu_model_is_named():
