@@ -89,5 +89,40 @@ def build_library(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB_PATH
 
 
+# Host-side sanitizer check (tests/sanitize/sa_host_check.cpp): the library's
+# host translation units and the driver are built with AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host side only (each -fsanitize= behind
+# -Xarch_host), then linked with the library's unsanitized device objects.
+HOST_SOURCES = ["sa_api.cpp", "sa_grad_api.cpp", "sa_action_api.cpp"]
+HOST_CHECK = os.path.join(LIB_DIR, "sa_host_check")
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """The sanitized host-check executable; needs the device objects of build_library."""
+    cc = hipcc()
+    san_dir = os.path.join(BUILD_DIR, "sanitize")
+    os.makedirs(san_dir, exist_ok=True)
+    objs, cmds = [], []
+    driver = os.path.join(ROOT, "tests", "sanitize", "sa_host_check.cpp")
+    for src in HOST_SOURCES + [driver]:
+        obj = os.path.join(san_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+        objs.append(obj)
+        path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+        cmds.append([cc, *HIPCC_FLAGS, *SANITIZE, "-c", path, "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        for fut in [ex.submit(_run, c, verbose) for c in cmds]:
+            fut.result()
+    dev_objs = [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES if src.endswith(".hip")]
+    for o in dev_objs:
+        if not os.path.exists(o):
+            raise RuntimeError(f"missing {o}: build the library first")
+    tmp = HOST_CHECK + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", *SANITIZE, "-o", tmp, *objs, *dev_objs], verbose)
+    os.replace(tmp, HOST_CHECK)
+    return HOST_CHECK
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
