@@ -44,7 +44,7 @@ namespace {
 // (written by every wave in step t-1), its dS and the aggregation dQ' +=
 // dS X; s' and dA of tile t+1 and their per-wave row statistics; wait for
 // tile t+2.  So the products of tile t+1 overlap the merge of tile t.
-template <int D, int WJ, bool PAD>
+template <int D, int WJ, bool PAD, int PHASE>
 __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args) {
   constexpr int KW = kGradKW, JB = KW / 16, RB = 2, NT = 16 * RB, CS = D / 32, CB = D / 16, CH = D / 8;
   constexpr int KPAD = KW * WJ;
@@ -62,9 +62,9 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int wj = __builtin_amdgcn_readfirstlane(tid >> 6);
   // prototype block (phases 1 and 2): prototypes KPAD blk .. of M and G
-  const int nblk = args.phase ? args.blocks : 1;
-  const int blk = args.phase ? (int)(blockIdx.x % (unsigned)nblk) : 0;
-  const int phase = args.phase;
+  constexpr int phase = PHASE;  // args.phase, as a template parameter: one block compiles as before
+  const int nblk = phase ? args.blocks : 1;
+  const int blk = phase ? (int)(blockIdx.x % (unsigned)nblk) : 0;
   const int jbase = wj * KW;                // within the block
   const int jg = blk * KPAD + jbase;        // first global prototype of this wave
   const int k = args.k;
@@ -624,6 +624,7 @@ __global__ __launch_bounds__(256) void grad_merge_kernel(const f32x4* bstats, in
 // at a time with all loads of a stage in flight at once, so a stage costs one
 // memory latency; operands are read with arbitrary strides, so transposed
 // views need no copy.
+template <bool STAGES>  // false: the inner dimension fits one stage (<= 256)
 __global__ __launch_bounds__(256) void small_matmul_kernel(MatmulPair pr) {
   __shared__ float As[16][kInnerStage + 1], Bs[kInnerStage][17];
   const Matmul& p = pr.p[blockIdx.z];
@@ -631,8 +632,8 @@ __global__ __launch_bounds__(256) void small_matmul_kernel(MatmulPair pr) {
   if (m0 >= p.rows || n0 >= p.cols) return;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   float s0 = 0.f, s1 = 0.f;
-  for (int t0 = 0; t0 < p.inner; t0 += kInnerStage) {
-    const int n = p.inner - t0 < kInnerStage ? p.inner - t0 : kInnerStage;
+  for (int t0 = 0; t0 < (STAGES ? p.inner : 1); t0 += kInnerStage) {
+    const int n = STAGES ? (p.inner - t0 < kInnerStage ? p.inner - t0 : kInnerStage) : p.inner;
     // all loads in flight before any store; index arithmetic by shifts only
     // (a runtime division per element costs more than the loads)
     float av[16], bv[kInnerStage / 16];
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(256) void small_matmul_kernel(MatmulPair pr) {
       const int e = threadIdx.x + 256 * i, tb = e >> 4, nn = e & 15;
       bv[i] = tb < n && n0 + nn < p.cols ? p.B[(t0 + tb) * p.b_rs + (n0 + nn) * p.b_cs] : 0.f;
     }
-    if (t0 > 0) __syncthreads();  // the previous stage's reads are done
+    if (STAGES && t0 > 0) __syncthreads();  // the previous stage's reads are done
 #pragma unroll
     for (int mm = 0; mm < 16; ++mm)
       if (threadIdx.x < n) As[mm][threadIdx.x] = av[mm];
@@ -677,14 +678,24 @@ __global__ __launch_bounds__(256) void zero_kernel(float* dst, int64_t n) {
   if (i < n) dst[i] = 0.f;
 }
 
+template <int D, int WJ, bool PAD, int PHASE>
+hipError_t stats_ph(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
+  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_stats_kernel<D, WJ, PAD, PHASE>, 64 * WJ, 0);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((grad_stats_kernel<D, WJ, PAD, PHASE>), dim3(groups), dim3(64 * WJ), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((grad_stats_kernel<D, WJ, PAD, PHASE>), dim3(groups), dim3(64 * WJ), 0, s, a);
+  return hipGetLastError();
+}
+// the two phases over blocks exist for the eight-wave plan only (k > 256)
 template <int D, int WJ, bool PAD>
 hipError_t stats_p(const GradStatsArgs& a, int groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* occ) {
-  if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, grad_stats_kernel<D, WJ, PAD>, 64 * WJ, 0);
-  if (e0 || e1)
-    hipExtLaunchKernelGGL((grad_stats_kernel<D, WJ, PAD>), dim3(groups), dim3(64 * WJ), 0, s, e0, e1, 0, a);
-  else
-    hipLaunchKernelGGL((grad_stats_kernel<D, WJ, PAD>), dim3(groups), dim3(64 * WJ), 0, s, a);
-  return hipGetLastError();
+  if (occ || a.phase == 0) return stats_ph<D, WJ, PAD, 0>(a, groups, s, e0, e1, occ);
+  if constexpr (WJ == 8) {
+    if (a.phase == 1) return stats_ph<D, WJ, PAD, 1>(a, groups, s, e0, e1, occ);
+    if (a.phase == 2) return stats_ph<D, WJ, PAD, 2>(a, groups, s, e0, e1, occ);
+  }
+  return hipErrorInvalidValue;
 }
 // padding prototypes (k below 32 WJ) need their scores masked; the occupancy is that of the padded form
 template <int D, int WJ>
@@ -789,7 +800,10 @@ hipError_t launch_small_matmuls(const Matmul& a, const Matmul& b, hipStream_t s)
     if (p->inner < 1 || p->rows < 1 || p->cols < 1) return hipErrorInvalidValue;
   const int rows = a.rows > b.rows ? a.rows : b.rows, cols = a.cols > b.cols ? a.cols : b.cols;
   const dim3 grid((unsigned)((cols + 15) / 16), (unsigned)((rows + 15) / 16), 2);
-  hipLaunchKernelGGL(small_matmul_kernel, grid, dim3(256), 0, s, MatmulPair{{a, b}});
+  if (a.inner > kInnerStage || b.inner > kInnerStage)
+    hipLaunchKernelGGL(small_matmul_kernel<true>, grid, dim3(256), 0, s, MatmulPair{{a, b}});
+  else
+    hipLaunchKernelGGL(small_matmul_kernel<false>, grid, dim3(256), 0, s, MatmulPair{{a, b}});
   return hipGetLastError();
 }
 
