@@ -48,6 +48,10 @@ def test_compress_rejects_mismatched_tensors(handles, fn, X, out, what):
     call = B.sa_compress_batch if fn == "sa" else B.sa_stack_compress_batch
     with pytest.raises(ValueError, match=what):
         call(handles[fn], X, OFFS, out)
+    # the bound form (arguments checked once, then re-issued) checks the same things up front
+    bind = B.sa_compress_batch_bound if fn == "sa" else B.sa_stack_compress_batch_bound
+    with pytest.raises(ValueError, match=what):
+        bind(handles[fn], X, OFFS, out)
 
 
 def test_compress_shapes_ok_reach_device_check(handles):

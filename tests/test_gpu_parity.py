@@ -173,6 +173,25 @@ def test_deterministic_bitwise():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_bound_call_matches_direct_call():
+    """sa_compress_batch_bound (arguments checked once, the C call re-issued):
+    the same bits as sa_compress_batch, and the offsets are the bound call's own
+    copy (changing the caller's array afterwards changes nothing)."""
+    wl = W.make_workload(lengths=[700, 0, 1500, 33], d=128, k=256, dtype="bf16", seed=71, name="bound")
+    X, P, WQ, WK = to_device(wl)
+    offs = np.array(wl.offsets, dtype=np.int64)
+    with SketchAttention(P, WQ, WK, wl.tau) as sa:
+        a = sa.compress(X, offs).clone()
+        out = torch.empty_like(a)
+        run = B.sa_compress_batch_bound(sa.handle, X, offs, out)
+        offs[1:] = 0  # the caller's array is not read again
+        for _ in range(3):
+            out.zero_()
+            run()
+            torch.cuda.synchronize()
+            assert torch.equal(out, a)
+
+
 def test_additivity_across_users():
     """One user of n rows equals the sum of the same rows split into two users."""
     base = W.make_workload(lengths=[3001], d=128, k=128, dtype="bf16", seed=11, name="add")
