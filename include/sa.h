@@ -81,9 +81,9 @@ typedef enum sa_dtype {
  *
  *   out    host pointer receiving the new handle (set to NULL on error)
  *   d      history / prototype width; supported: 64 or 128
- *   k      number of prototypes; supported: 1..1024 for SA_BF16 (beyond
- *          512 at d = 128 the pass runs in two phases over blocks of 256
- *          prototypes), 1..256 for SA_F32
+ *   k      number of prototypes; supported: 1..1024 (beyond 512 at d = 128
+ *          for SA_BF16, and beyond 256 for SA_F32, the pass runs in two
+ *          phases over blocks of 256 prototypes)
  *   tau    affinity scale, finite (any sign, zero allowed)
  *   dtype  element type of P, W_Q, W_K and of every X passed later
  *   P      device, [k][d] prototypes (section 2.1: P^(0), shared by all users)

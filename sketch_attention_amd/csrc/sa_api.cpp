@@ -120,6 +120,18 @@ Plan make_plan(int dtype, int d, int k) {
     p.m_in_lds = 0;
     return p;
   }
+  if (dtype == SA_F32 && k > 256) {
+    // float32 beyond 256 prototypes: the four-wave plan of 4 x 64 prototypes in
+    // two phases over blocks of 256 (its folded matrix lives in registers)
+    p.kw = 64;
+    p.waves_k = 4;
+    p.waves_rows = 1;
+    p.m_in_lds = 0;
+    p.blocks = (k + 255) / 256;
+    p.k_pad = p.blocks * 256;
+    p.tile_rows = sa::kRowsPerWave;
+    return p;
+  }
   if (stream) {
     p.kind = 1;
     const bool wide = d == 128 ? k > 256 : k > 512;  // folded matrix too large for registers
@@ -175,7 +187,7 @@ sa_status check_config(int32_t d, int32_t k, float tau, sa_dtype dtype) {
   if (k < 1 || d < 1) return SA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SA_ERR_UNSUPPORTED;
   if (dtype == SA_BF16 && k > 1024) return SA_ERR_UNSUPPORTED;
-  if (dtype == SA_F32 && k > 256) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_F32 && k > 1024) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
 

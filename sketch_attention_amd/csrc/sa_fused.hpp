@@ -266,7 +266,12 @@ __device__ __forceinline__ float frag_c_t(const float* xt, int xts, int row, int
 }
 
 // -------------------------------------------------------------- kernel
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
+// LM (two-phase modes, FusedArgs::lse_mode): 0 one pass; 1 each row's log2
+// sum over this block's prototypes into stats[block][row], no aggregation;
+// 2 weights 2^(s' - L) with L the row's log2 sum over every block from
+// stats[row] (no row sums, no exact path).  Work group g takes prototype
+// block g % blocks in modes 1 and 2.
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD, int LM = 0>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) {
   using G = FusedGeom<T, D, KW, WJ, WI, MLDS>;
   using MF = Mfma<T>;
@@ -293,15 +298,17 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   const int wj = wave % WJ;
   const int wi = wave / WJ;
   const int rw = wi * kRowsPerWave;  // first tile row of this wave
-  const int jbase = wj * KW;         // first prototype of this wave
+  const int jbase = wj * KW;         // first prototype of this wave (within the block)
+  const int nblk = LM ? args.blocks : 1;
+  const int blk = LM ? (int)(blockIdx.x % (unsigned)nblk) : 0;
   const T* const X = static_cast<const T*>(args.X);
-  const T* const Mg = static_cast<const T*>(args.M);
-  const int k = args.k;
+  const T* const Mg = static_cast<const T*>(args.M) + (int64_t)blk * G::KPAD * D;
+  const int k = args.k - blk * G::KPAD;  // real prototypes of this block (may exceed KPAD)
   const bool wave_has_protos = jbase < k;
 
   const int64_t rows = args.rows;
-  const int64_t ngroups = gridDim.x;
-  const int64_t grp = blockIdx.x;
+  const int64_t ngroups = gridDim.x / nblk;
+  const int64_t grp = blockIdx.x / nblk;
   const int64_t r_begin = grp * rows / ngroups;
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
@@ -375,6 +382,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   // the exact shifted path recomputes the tile).
   auto softmax_fast = [&](f32x4 (&s)[2][JB]) {
     bool bad = false;
+    if constexpr (LM == 2) return;  // exponentials are taken against the stored log-sum-exp in finish_tile
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       float p[4];
@@ -421,6 +429,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   };
 
   auto any_flag = [&]() {
+    if constexpr (LM == 2) return false;
     int f = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) f |= flags[w];
@@ -484,7 +493,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   // tile's rows read again from global memory,
   // shift each row by this wave's maximum, and combine the waves with the
   // usual max/sum rescaling.  Every wave takes it together (it has a barrier).
-  auto softmax_exact = [&](f32x4 (&s)[2][JB], const T* tile, int rows_left, float (&fac)[2][4]) {
+  auto softmax_exact = [&](f32x4 (&s)[2][JB], const T* tile, int rows_left, float (&fac)[2][4], float (&lse)[2][4]) {
     affinity_from(s, [&](int ib, int cs) {
       const int rr = rw + 16 * ib + l16;
       Frag f = frag_c<D>(tile + (int64_t)(rr < rows_left ? rr : rows_left - 1) * D, cs, g);
@@ -528,6 +537,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
 #pragma unroll
         for (int w = 0; w < WJ; ++w) den += xsl[trow * WJ + w] * fast_exp2(xsm[trow * WJ + w] - mx);
         fac[ib][r] = fast_exp2(fac[ib][r] - mx) / den;
+        lse[ib][r] = mx + __log2f(den);  // the row's log2 sum over the block's prototypes
       }
   };
 
@@ -535,12 +545,48 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   // aggregation (exact path in the rare tiles that need it).
   auto finish_tile = [&](f32x4 (&acc)[JB][CB], f32x4 (&sc)[2][JB], const T* xt, int64_t t0, int rows_left) {
     float fac[2][4];
+    if constexpr (LM == 2) {
+      // 2^(s' - L) with the row's log-sum-exp over all blocks; rows past the piece weigh 0
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const int r0 = rw + 16 * ib + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float Lr = r0 + r < rows_left ? args.stats[t0 + r0 + r] : INFINITY;
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb) sc[ib][jb][r] = fast_exp2(sc[ib][jb][r] - Lr);
+          fac[ib][r] = 1.f;
+        }
+      }
+      aggregate(acc, sc, fac, xt);
+      return;
+    }
     if (any_flag()) {
-      softmax_exact(sc, X + t0 * D, rows_left, fac);
+      float lse[2][4];
+      softmax_exact(sc, X + t0 * D, rows_left, fac, lse);
+      if constexpr (LM == 1) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int trow = rw + 16 * ib + 4 * g + r;
+            if (l16 == 0 && wj == 0 && trow < rows_left) args.stats[(int64_t)blk * rows + t0 + trow] = lse[ib][r];
+          }
+      }
     } else {
       combine_fast(fac);
+      if constexpr (LM == 1) {
+        // the row's log2 sum over the block (its unshifted sum is within range here)
+        if (wj == 0 && lane < kRowsPerWave && rw + lane < rows_left) {
+          const float* p = xl + (rw + lane) * WJ;
+          float l = p[0];
+#pragma unroll
+          for (int w = 1; w < WJ; ++w) l += p[w];
+          args.stats[(int64_t)blk * rows + t0 + rw + lane] = __log2f(l);
+        }
+      }
     }
-    aggregate(acc, sc, fac, xt);
+    if constexpr (LM != 1) aggregate(acc, sc, fac, xt);
   };
 
   // First user touched: the largest u with offsets[u] <= r_begin.  It is
@@ -666,8 +712,8 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
         }
       }
     }
-    if (wi == 0) {
-      float* dst = args.partial + (grp + u) * (int64_t)(G::KPAD * D);
+    if (LM != 1 && wi == 0) {
+      float* dst = args.partial + ((int64_t)blk * (ngroups + args.users) + grp + u) * (int64_t)(G::KPAD * D);
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -681,16 +727,27 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   }
 }
 
-template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
-hipError_t launch_fused_t(const FusedArgs& args, const Launch& l) {
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD, int LM = 0>
+hipError_t launch_fused_lm(const FusedArgs& args, const Launch& l) {
   if (l.start || l.stop) {
-    hipExtLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>), dim3(l.groups), dim3(64 * WJ * WI), 0,
+    hipExtLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD, LM>), dim3(l.groups), dim3(64 * WJ * WI), 0,
                           l.stream, l.start, l.stop, 0, args);
   } else {
-    hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD>), dim3(l.groups), dim3(64 * WJ * WI), 0,
+    hipLaunchKernelGGL((sa_fused_kernel<T, D, KW, WJ, WI, MLDS, PAD, LM>), dim3(l.groups), dim3(64 * WJ * WI), 0,
                        l.stream, args);
   }
   return hipGetLastError();
+}
+// The two-phase modes are compiled for the float32 plan of 4 x 64 prototypes
+// per block only (float32 beyond 256 prototypes).
+template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
+hipError_t launch_fused_t(const FusedArgs& args, const Launch& l) {
+  if constexpr (sizeof(T) == 4 && KW == 64 && WJ == 4 && WI == 1 && !MLDS) {
+    if (args.lse_mode == 1) return launch_fused_lm<T, D, KW, WJ, WI, MLDS, PAD, 1>(args, l);
+    if (args.lse_mode == 2) return launch_fused_lm<T, D, KW, WJ, WI, MLDS, PAD, 2>(args, l);
+  }
+  if (args.lse_mode != 0) return hipErrorInvalidValue;
+  return launch_fused_lm<T, D, KW, WJ, WI, MLDS, PAD, 0>(args, l);
 }
 
 template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>

@@ -60,7 +60,9 @@ def test_status_strings():
     (128, 513, 0.1, "bf16", B.SA_OK),
     (128, 1025, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),
     (64, 1025, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),
-    (64, 257, 0.1, "f32", B.SA_ERR_UNSUPPORTED),
+    (64, 257, 0.1, "f32", B.SA_OK),                   # float32 in two phases beyond 256 prototypes
+    (128, 1024, 0.1, "f32", B.SA_OK),
+    (128, 1025, 0.1, "f32", B.SA_ERR_UNSUPPORTED),
     (96, 16, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),
     (256, 16, 0.1, "bf16", B.SA_ERR_UNSUPPORTED),
     (128, 0, 0.1, "bf16", B.SA_ERR_INVALID_ARG),

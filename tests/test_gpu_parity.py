@@ -235,6 +235,33 @@ def test_large_tau_hard_assignment():
     _assert_parity(wl, got)
 
 
+@pytest.mark.parametrize("d,k,lengths", [
+    (64, 257, [1, 300, 0, 65]),
+    (128, 300, [700, 31, 33]),
+    (64, 512, [129, 1000]),
+    (128, 700, [40, 0, 999]),
+    (128, 1000, [513, 64]),
+    (64, 1024, [2, 777]),
+])
+def test_f32_beyond_256_two_phase(d, k, lengths):
+    """float32 beyond 256 prototypes: the four-wave plan in two phases over
+    blocks of 256 (per-block log-sum-exp, merge, aggregation with 2^(s' - L));
+    parity at the float32 tolerance, padded and full blocks, ragged users."""
+    wl = W.make_workload(lengths=lengths, d=d, k=k, dtype="f32", seed=3 * k + d, name=f"f32-{d}-{k}")
+    got = run_gpu(wl)
+    _assert_parity(wl, got)
+    _assert_mass_identity(wl, got)
+
+
+def test_f32_two_phase_hard_assignment():
+    """Scores far outside exp's range in both phases of the float32 two-phase
+    pass: the statistics phase takes its exact path, the aggregation needs none."""
+    wl = W.make_workload(lengths=[3000, 17], d=128, k=600, dtype="f32", seed=16, tau=40.0, name="hard-f32-600")
+    got = run_gpu(wl)
+    assert np.isfinite(got).all()
+    _assert_parity(wl, got)
+
+
 def _hard_bf16_workload(lengths, d, k, tau, seed, spike_rows=None):
     """bf16-exact weights (P = 8 I, W_Q = W_K = I) and rows with one dominant
     coordinate: scores reach several hundred (far past exp2's range), yet the
