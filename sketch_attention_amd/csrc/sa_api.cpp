@@ -80,15 +80,18 @@ Plan make_history_plan(int d, int k) {
     p.kw = 32; p.waves_k = 4; p.row_blocks = 4; p.score_buffers = 2;  // four-wave groups, two per CU
   } else if (k <= 256) {
     p.kw = 32; p.row_blocks = 4; p.score_buffers = 2;
-  } else if (k <= 512) {
+  } else if (k <= 512 || d == 128) {
     p.kw = 64; p.row_blocks = 2; p.score_buffers = d == 128 ? 1 : 2;
   } else {
     p.kw = 128; p.row_blocks = 2; p.score_buffers = 1;
   }
   p.m_in_lds = 0;
-  p.k_pad = p.kw * p.waves_k;
   p.tile_rows = 16 * p.row_blocks;
-  p.blocks = 1;
+  // d = 128 beyond 512 prototypes: blocks of 8 x 64 prototypes, each its own
+  // work groups (the softmax over rows is per prototype, so the blocks are
+  // independent and need no second phase)
+  p.blocks = (k + p.kw * p.waves_k - 1) / (p.kw * p.waves_k);
+  p.k_pad = p.kw * p.waves_k * p.blocks;
   return p;
 }
 
@@ -274,7 +277,7 @@ SA_API sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, s
   sa_status st = check_config(d, k, tau, dtype);
   if (st != SA_OK) return st;
   if (norm != SA_NORM_PROTOTYPES && norm != SA_NORM_HISTORY) return SA_ERR_INVALID_ARG;
-  if (norm == SA_NORM_HISTORY && (dtype != SA_BF16 || (int64_t)k * d > 65536)) return SA_ERR_UNSUPPORTED;
+  if (norm == SA_NORM_HISTORY && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   if (P == nullptr || W_Q == nullptr || W_K == nullptr) return SA_ERR_INVALID_ARG;
   if (!aligned16(P) || !aligned16(W_Q) || !aligned16(W_K)) return SA_ERR_INVALID_ARG;
 
@@ -367,7 +370,9 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
   // a partial slot: the block_k x d accumulator, plus per-prototype maxima and sums for the comparator
   const size_t slot_bytes = (size_t)block_k * (plan.d + (hist ? 2 : 0)) * sizeof(float);
   // two-phase statistics: per-block and merged log-sum-exp of every row
-  auto stats_bytes = [&](int64_t rows) { return nb > 1 ? (size_t)(nb + 1) * (size_t)rows * sizeof(float) : 0; };
+  auto stats_bytes = [&](int64_t rows) {
+    return nb > 1 && !hist ? (size_t)(nb + 1) * (size_t)rows * sizeof(float) : 0;
+  };
   // work groups per prototype block for a launch of `rows` rows (the grid is nb times that)
   auto launch_groups = [&](int64_t rows) {
     if (rows <= 0) return 0;
@@ -466,10 +471,10 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     if (timed) {
       ts = take_slot(h);
       ts.fused = rows > 0;
-      ts.two_phase = nb > 1;
+      ts.two_phase = nb > 1 && !hist;
     }
     if (rows > 0) {
-      if (nb > 1) {
+      if (nb > 1 && !hist) {
         // statistics phase, merge, aggregation phase (the aggregation carries events ev[0], ev[1])
         fa.lse_mode = 1;
         fa.stats = stats_b;

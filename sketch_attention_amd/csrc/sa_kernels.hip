@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_k
   __shared__ HistPart part[kReduceShares][kReduceLanes][4];
   const int shares = blockDim.x / kReduceLanes;
   const int u = blockIdx.y;
+  const int blk = blockIdx.z;  // prototype block (its slots follow the groups + users slots of block blk - 1)
   const int slot_f4 = a.k_pad * a.d / 4;
   const int64_t slot_floats = (int64_t)a.k_pad * (a.d + 2);
   const int lane = threadIdx.x % kReduceLanes;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_k
   const int jb = t % jbs;
   const int wj = t / jbs;
   const int l = p & 63;
-  const int j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);
+  const int j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);  // within the block
   const int c = 16 * cb + (l & 15);
   HistPart x[4];
 #pragma unroll
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_k
     const int64_t n = b1 - b0 + 1;
     const int64_t q0 = n * q / shares, q1 = n * (q + 1) / shares;
     for (int64_t i = q0; i < q1; ++i) {
-      const float* slot = a.partial + (b0 + i + u) * slot_floats;
+      const float* slot = a.partial + ((int64_t)blk * (G + a.users) + b0 + i + u) * slot_floats;
       const f32x4 v = reinterpret_cast<const f32x4*>(slot)[p];
       const float* stats = slot + (int64_t)a.k_pad * a.d;
       const f32x4 ms = *reinterpret_cast<const f32x4*>(stats + j0);
@@ -267,9 +268,10 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_k
 #pragma unroll
     for (int r = 0; r < 4; ++r) hist_merge(x[r], part[w][lane][r].m, part[w][lane][r].l, part[w][lane][r].a);
   float* o = a.out + (int64_t)u * a.k * a.d;
+  const int jg = blk * a.k_pad + j0;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (j0 + r < a.k) o[(int64_t)(j0 + r) * a.d + c] = x[r].l > 0.f ? x[r].a / x[r].l : 0.f;
+    if (jg + r < a.k) o[(int64_t)(jg + r) * a.d + c] = x[r].l > 0.f ? x[r].a / x[r].l : 0.f;
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -277,7 +279,8 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t sta
   if (a.history_softmax) {
     int shares = 1;
     while (shares < kReduceShares && 8 * shares < per_user) shares *= 2;
-    const dim3 grid((a.k_pad * a.d / 4 + kReduceLanes - 1) / kReduceLanes, a.users), block(kReduceLanes * shares);
+    const dim3 grid((a.k_pad * a.d / 4 + kReduceLanes - 1) / kReduceLanes, a.users, a.blocks > 1 ? a.blocks : 1),
+        block(kReduceLanes * shares);
     if (start || stop)
       hipExtLaunchKernelGGL(reduce_history_kernel, grid, block, 0, stream, start, stop, 0, a);
     else

@@ -225,10 +225,12 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int wi = wave / WJ;
   const int rw = wi * RW;     // first tile row of this wave
   const int jbase = wj * KW;  // first prototype of this wave
-  // two-phase pass: work group g handles prototype block g % blocks (consecutive
-  // groups read the same rows at about the same time) for row range g / blocks
-  const int nblk = LM ? args.blocks : 1;
-  const int blk = LM ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  // two-phase pass, and the comparator beyond one block of prototypes (its
+  // softmax is per prototype, so blocks need no merge): work group g handles
+  // prototype block g % blocks (consecutive groups read the same rows at about
+  // the same time) for row range g / blocks
+  const int nblk = (LM || HS) ? args.blocks : 1;
+  const int blk = (LM || HS) ? (int)(blockIdx.x % (unsigned)nblk) : 0;
   const bf16* const X = static_cast<const bf16*>(args.X);
   const bf16* const Mg = static_cast<const bf16*>(args.M) + (int64_t)blk * G::KPAD * D;
   const int k = args.k - blk * G::KPAD;  // real prototypes of this block (may exceed KPAD)
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     // partial of one piece: acc in the lane layout, then the maxima and the
     // sums of every prototype of the slot
     auto hs_flush = [&](int u) {
-      float* dst = args.partial + (grp + u) * (int64_t)(G::KPAD * (D + 2));
+      float* dst = args.partial + ((int64_t)blk * (ngroups + args.users) + grp + u) * (int64_t)(G::KPAD * (D + 2));
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) {
 #pragma unroll

@@ -2,7 +2,8 @@
 reading section 3.1) through the C ABI with the fp64 CPU oracle: normwise
 error per user within 2e-2 (bfloat16 inputs).  Covers every plan the
 comparator runs on (32, 64 and 128 prototypes per wave, the folded matrix in
-registers and in LDS, padded prototypes), several users per work group,
+registers and in LDS, padded prototypes, and at d = 128 beyond 512 prototypes
+independent blocks of 512, each its own work groups), several users per work group,
 tiles cut by piece ends, maxima that jump between tiles, and the invariance
 the comparator has and Sketch Attention has not: duplicating every row of a
 history changes nothing."""
@@ -44,6 +45,10 @@ CASES = [
     (64, 400, [300, 64]),                       # d = 64, 64 per wave, matrix in registers
     (64, 700, [1, 900]),                        # d = 64, 128 per wave, matrix in LDS
     (64, 16, [40, 3]),
+    (128, 600, [3, 1200, 0, 65]),               # d = 128 beyond 512: two independent blocks of 512 prototypes
+    (128, 1000, [900, 1]),
+    (128, 1024, [2048, 31]),
+    (64, 1024, [333, 1000]),
 ]
 
 
