@@ -63,6 +63,7 @@ CASES = [
     ("bf16", 64, 16, 128, 2, [5, 100, 0]),                   # lockstep, matrix in LDS
     ("f32", 64, 16, 64, 2, [1, 100, 33]),                    # lockstep float32, matrix in registers
     ("f32", 128, 100, 128, 1, [7, 300]),                     # one layer
+    ("f32", 128, 600, 128, 2, [400, 0, 97]),                 # float32 two-phase pass, per-user matrices
 ]
 
 
