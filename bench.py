@@ -139,7 +139,7 @@ def kernel_source_hash(dtype: str = "bf16", d: int = 128) -> str:
     """sha256 over the sources and compiler options that decide the fused kernel
     a launch runs (include paths left out: they differ between checkouts)."""
     from sketch_attention_amd import build as _build
-    names = ["sa_fused.hpp", "sa_stream.hpp", "sa_stream32.hpp", f"sa_fused_{dtype}_d{d}.hip", f"sa_stream_d{d}.hip",
+    names = ["sa_fused.hpp", "sa_stream.hpp", "sa_stream32.hpp", "sa_wide.hpp", f"sa_fused_{dtype}_d{d}.hip", f"sa_stream_d{d}.hip",
              "sa_kernels.hip", "sa_internal.h", "sa_api.cpp"]
     files = [os.path.join(CSRC, f) for f in names if os.path.exists(os.path.join(CSRC, f))]
     h = hashlib.sha256()

@@ -58,7 +58,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // wave holds 32 prototypes (64 for d = 64 above k = 256), the folded matrix
 // in registers and two affinity tiles in flight; above that (k <= 512 for
 // d = 128, k <= 1024 for d = 64) each wave holds k_pad / 8 prototypes, one
-// affinity tile, and the folded matrix sits in LDS.  bf16 with k <= 32: the
+// affinity tile, and the folded matrix sits in LDS; d = 128 with 128 < k <=
+// 256 runs the 32x32x16 pass of sa_wide.hpp instead.  bf16 with k <= 32: the
 // lockstep pass (sa_fused.hpp), eight waves.  float32: lockstep, four waves,
 // folded matrix in registers.
 // SA_PLAN="kw,waves_k,waves_rows,m_in_lds[,kind[,prefetch[,row_blocks[,score_buffers]]]]"
@@ -153,6 +154,10 @@ Plan make_plan(int dtype, int d, int k) {
     // (measured faster than eight waves split 4 x 2: 248 against 273 us on
     // the ragged workload)
     p.waves_rows = (d == 128 && p.waves_k == 2) ? 2 : (d == 128 && p.waves_k == 4) ? 1 : waves / p.waves_k;
+    // d = 128, 128 < k <= 256: eight waves of 32 prototypes on 32x32x16
+    // products with the prototypes along the lanes (measured 2-3 % faster on
+    // the long workload than the 16x16x32 plan of the same shape)
+    if (d == 128 && p.kw == 32 && p.waves_k == 8 && p.waves_rows == 1) p.kind = 3;
   } else if (k16 <= 16) {
     p.kw = 16; p.waves_k = 1;
   } else if (k16 <= 32) {
@@ -173,7 +178,7 @@ Plan make_plan(int dtype, int d, int k) {
   if (const char* env = std::getenv("SA_PLAN")) {
     int kw = 0, wk = 0, wr = 0, ml = 0, kind = 0, pf = 1, rb = 2, sb = 2;
     const int n = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &kw, &wk, &wr, &ml, &kind, &pf, &rb, &sb);
-    if (n >= 4 && kw % 16 == 0 && kw > 0 && wk > 0 && wr > 0 && kw * wk >= k && kind >= 0 && kind <= 2 &&
+    if (n >= 4 && kw % 16 == 0 && kw > 0 && wk > 0 && wr > 0 && kw * wk >= k && kind >= 0 && kind <= 3 &&
         (pf == 1 || pf == 2) && (rb == 2 || rb == 4) && (sb == 1 || sb == 2)) {
       p.kw = kw; p.waves_k = wk; p.waves_rows = wr; p.m_in_lds = ml ? 1 : 0; p.kind = kind; p.prefetch = pf;
       p.row_blocks = rb; p.score_buffers = sb;
@@ -460,7 +465,7 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     ra.kw = plan.kw;
     ra.k_pad = block_k;
     ra.blocks = nb;
-    ra.layout = plan.kind == 2 ? 1 : 0;
+    ra.layout = plan.kind >= 2 ? 1 : 0;
     for (int32_t i = 0; i <= nu; ++i) {
       fa.offsets[i] = offsets[u0 + i] - base;
       ra.offsets[i] = fa.offsets[i];

@@ -27,7 +27,8 @@ struct Plan {
   int m_in_lds;     // folded matrix staged in LDS (1) or held in registers (0)
   int tile_rows;    // rows per tile: kRowsPerWave * waves_rows (lockstep), 16 * row_blocks * waves_rows (streamed)
   int kind;         // 0 = lockstep pass (sa_fused.hpp), 1 = streamed pass (sa_stream.hpp, bf16),
-                    // 2 = streamed pass on 32x32x16 products (sa_stream32.hpp: bf16, d = 128, 8 x 32 prototypes)
+                    // 2 = streamed pass on 32x32x16 products (sa_stream32.hpp: bf16, d = 128, 8 x 32 prototypes),
+                    // 3 = the same products with the prototypes along the lanes (sa_wide.hpp)
   int prefetch;     // streamed pass: LDS ring slots beyond the minimum, plus one (ring of 3 or 4 + prefetch - 1 tiles)
   int row_blocks;   // streamed pass: 16-row blocks per wave and tile (2 or 4)
   int score_buffers;  // streamed pass: affinity tiles in flight per wave (2: M in registers; 1: M in LDS)
@@ -67,7 +68,7 @@ struct ReduceArgs {
   int32_t kw;
   int32_t k_pad;      // prototypes of one block (one partial slot)
   int32_t blocks;     // prototype blocks; block b's slots follow the (groups + users) slots of block b - 1
-  int32_t layout;     // slot layout: 0 as written by sa_fused.hpp / sa_stream.hpp, 1 by sa_stream32.hpp
+  int32_t layout;     // slot layout: 0 as written by sa_fused.hpp / sa_stream.hpp, 1 by sa_stream32.hpp / sa_wide.hpp
   int64_t offsets[kMaxUsersPerLaunch + 1];
 };
 

@@ -301,7 +301,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t sta
 
 // ------------------------------------------------------------ dispatch
 static DispatchFn plan_group(const Plan& p) {
-  if (p.kind == 2) return p.dtype == 1 && p.d == 128 ? dispatch_stream_d128 : nullptr;
+  if (p.kind == 2 || p.kind == 3) return p.dtype == 1 && p.d == 128 ? dispatch_stream_d128 : nullptr;
   if (p.kind == 1) {
     if (p.dtype != 1) return nullptr;
     if (p.d == 64) return dispatch_stream_d64;

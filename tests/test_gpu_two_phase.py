@@ -85,13 +85,53 @@ def test_two_phase_is_bitwise_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("k,lengths", [(256, [1, 63, 64, 65, 3000, 0]), (200, [700, 129, 5])])
-def test_wide_products_one_pass(k, lengths, monkeypatch):
-    """The 32x32x16 pass (the one both phases above run on) as a one-pass
-    kernel for d = 128, k <= 256, selected by the plan override: parity with
-    the oracle, padded and full prototype counts, ragged users."""
-    monkeypatch.setenv("SA_PLAN", "32,8,1,0,2,1,4,2")
+# plan overrides of the two 32x32x16 passes: prototypes along the registers
+# with the weights through LDS (sa_stream32.hpp), and along the lanes with the
+# weights in registers (sa_wide.hpp)
+WIDE_PLANS = {"stream32": "32,8,1,0,2,1,4,2", "lanes": "32,8,1,0,3,1,4,2"}
+
+
+@pytest.mark.parametrize("plan", sorted(WIDE_PLANS))
+@pytest.mark.parametrize("k,lengths", [(256, [1, 63, 64, 65, 3000, 0]), (200, [700, 129, 5]), (129, [2, 5000])])
+def test_wide_products_one_pass(k, lengths, plan, monkeypatch):
+    """The 32x32x16 passes as one-pass kernels for d = 128, k <= 256,
+    selected by the plan override: parity with the oracle, padded and full
+    prototype counts, ragged users."""
+    monkeypatch.setenv("SA_PLAN", WIDE_PLANS[plan])
     wl = W.make_workload(lengths=lengths, d=128, k=k, dtype="bf16", seed=5 * k, name=f"wide-one-pass-{k}")
     got = run_gpu(wl)
     _assert_parity(wl, got)
     _assert_mass_identity(wl, got)
+
+
+@pytest.mark.parametrize("plan", sorted(WIDE_PLANS))
+def test_wide_products_exact_path(plan, monkeypatch):
+    """Every tile of the 32x32x16 one-pass kernels overflows the unshifted
+    softmax (hard assignment at tau = 4) and takes the exact pass; then only a
+    few rows do, so exact and fast tiles alternate."""
+    from test_gpu_parity import _hard_bf16_workload
+    monkeypatch.setenv("SA_PLAN", WIDE_PLANS[plan])
+    wl = _hard_bf16_workload([3000, 77, 1], d=128, k=256, tau=4.0, seed=23)
+    got = run_gpu(wl)
+    assert np.isfinite(got).all()
+    _assert_parity(wl, got)
+    rng = np.random.default_rng(24)
+    spikes = np.sort(rng.choice(5000, size=7, replace=False))
+    wl = _hard_bf16_workload([5000], d=128, k=200, tau=4.0, seed=25, spike_rows=spikes)
+    wl.X = W.round_to_bf16(wl.X * np.float32(0.05))
+    wl.X[spikes] = W.round_to_bf16(wl.X[spikes] * np.float32(20.0))
+    got = run_gpu(wl)
+    assert np.isfinite(got).all()
+    _assert_parity(wl, got)
+
+
+@pytest.mark.parametrize("plan", sorted(WIDE_PLANS))
+def test_wide_products_per_user_matrices(plan, monkeypatch):
+    """Two refinement layers on the 32x32x16 one-pass kernels: the second
+    layer's folded matrix is per user (reloaded when a group's tile list
+    crosses a user boundary)."""
+    from test_gpu_stack import _check
+    monkeypatch.setenv("SA_PLAN", WIDE_PLANS[plan])
+    wl = W.make_workload(lengths=[1500, 10, 0, 4097, 64], d=128, k=256, dtype="bf16", seed=26, name="wide-stack")
+    layers = W.make_stack_layers(d=128, d_ff=256, layers=2, dtype="bf16", seed=27)
+    _check(wl, layers)
