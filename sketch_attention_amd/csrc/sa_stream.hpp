@@ -132,6 +132,49 @@ __device__ __forceinline__ constexpr int chunk_sw(int r) {
   return D == 128 ? 8 * ((r ^ (r >> 3)) & 1) + 2 * ((r >> 1) & 3) : 4 * ((r >> 2) & 1) + 2 * (((r >> 1) ^ (r >> 3)) & 1);
 }
 
+// The tile list of one work group: pieces (user segments) of [r_begin,
+// r_end), each cut into tiles of nt rows.  Every lane examines up to four
+// users at once (no chain of dependent loads): u_first is the last user
+// starting at or before r_begin (a prefix, offsets being non-decreasing; it is
+// the user holding row r_begin, so first_end = offsets[u_first + 1] >
+// r_begin, read from the lane that loaded it), ntot the sum of the pieces'
+// tile counts.
+struct TileList {
+  int u_first, ntot;
+  int64_t first_end;
+};
+__device__ __forceinline__ TileList tile_list(const FusedArgs& args, int64_t r_begin, int64_t r_end, int nt, int lane) {
+  int cnt = 0, tiles = 0;
+  int64_t first_end = r_end;
+  const int nq = (args.users + 63) / 64;
+  for (int q = 0; q < nq; ++q) {
+    const int uu = lane + 64 * q;
+    int64_t a = 0, b = 0;
+    if (uu < args.users) {
+      a = args.offsets[uu];
+      b = args.offsets[uu + 1];
+      cnt += a <= r_begin ? 1 : 0;
+      const int64_t lo = a > r_begin ? a : r_begin, hi = b < r_end ? b : r_end;
+      if (hi > lo) tiles += (int)((hi - lo + nt - 1) / nt);
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(uu < args.users && a <= r_begin && b > r_begin);
+    if (hit != 0) {
+      const int src = __builtin_ctzll(hit);
+      first_end = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(b >> 32), src) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)b, src));
+    }
+  }
+  cnt = row16_sum_i(cnt);
+  tiles = row16_sum_i(tiles);
+  TileList t;
+  t.u_first = __builtin_amdgcn_readlane(cnt, 0) + __builtin_amdgcn_readlane(cnt, 16) +
+              __builtin_amdgcn_readlane(cnt, 32) + __builtin_amdgcn_readlane(cnt, 48) - 1;
+  t.ntot = __builtin_amdgcn_readlane(tiles, 0) + __builtin_amdgcn_readlane(tiles, 16) +
+           __builtin_amdgcn_readlane(tiles, 32) + __builtin_amdgcn_readlane(tiles, 48);
+  t.first_end = first_end;
+  return t;
+}
+
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, int LM = 0>
 struct StreamGeom {
   static_assert(KW % 16 == 0 && (D == 64 || D == 128) && PF >= 1 && PF <= 3 && (RB == 2 || RB == 4) &&
@@ -243,20 +286,30 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   if (r_begin >= r_end) return;
 
   int u_first = 0, ntot = 0;
-  // A cursor walks the tile list: first row of the tile, end of its piece, user.
+  int64_t first_end = 0;  // end of the piece holding r_begin
+  // A cursor walks the tile list: first row of the tile, end of its piece
+  // (both relative to r_begin: a group's range fits in 32 bits, so the
+  // per-step bookkeeping stays in 32-bit scalar arithmetic), user.
+  const int nrel = (int)(r_end - r_begin);
   struct Cursor {
-    int64_t row, end;
-    int u;
+    int row, end, u;
   };
-  auto cursor_begin = [&]() { return Cursor{r_begin, min(r_end, args.offsets[u_first + 1]), u_first}; };
+  auto user_end = [&](int u) {
+    const int64_t e = args.offsets[u + 1] - r_begin;
+    return e < (int64_t)nrel ? (int)e : nrel;
+  };
+  auto cursor_begin = [&]() {
+    const int64_t e = first_end - r_begin;
+    return Cursor{0, e < (int64_t)nrel ? (int)e : nrel, u_first};
+  };
   auto cursor_next = [&](Cursor& c) {
     c.row += NT;
     if (c.row >= c.end) {
       c.row = c.end;
-      if (c.row < r_end) {
+      if (c.row < nrel) {
         ++c.u;
-        while (c.u < args.users && args.offsets[c.u + 1] <= c.row) ++c.u;
-        c.end = min(r_end, args.offsets[c.u + 1]);
+        while (c.u < args.users && args.offsets[c.u + 1] - r_begin <= (int64_t)c.row) ++c.u;
+        c.end = user_end(c.u);
       }
     }
   };
@@ -307,10 +360,10 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     dma_row[s] = j * G::RPI + lane / G::CH;
     dma_col[s] = 8 * ((lane % G::CH) ^ chunk_sw<D>(dma_row[s]));
   }
-  auto issue_tile = [&](const auto& c, int q) {
-    const int64_t last = c.end - 1 - c.row;  // -1 past the list
-    const int64_t b0 = last < 0 ? c.end - 1 : c.row;
-    const int lim = last < 0 ? 0 : (int)(last < G::NT ? last : G::NT - 1);
+  auto issue_tile = [&](const Cursor& c, int q) {
+    const int last = c.end - 1 - c.row;  // -1 past the list
+    const int64_t b0 = r_begin + (last < 0 ? c.end - 1 : c.row);
+    const int lim = last < 0 ? 0 : (last < G::NT ? last : G::NT - 1);
     const bf16* const base = X + b0 * D;
     const uint32_t slot = slot_of(q);
 #pragma unroll
@@ -343,37 +396,14 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // tile 0 starts at r_begin whatever the users: its DMA goes out before the
   // tile list is known (rows clamped to the group's range; rows of the next
   // user get factor 0)
-  {
-    struct {
-      int64_t row, end;
-    } c0{r_begin, r_end};
-    issue_tile(c0, 0);
-  }
+  issue_tile(Cursor{0, nrel, 0}, 0);
 
-  // ---- the group's tile list: pieces (user segments) of [r_begin, r_end),
-  // each cut into tiles of NT rows.  Every lane examines up to four users at
-  // once (no chain of dependent loads): u_first is the last user starting at
-  // or before r_begin (a prefix, offsets being non-decreasing; it is
-  // non-empty because offsets[u_first + 1] > r_begin), ntot the sum of the
-  // pieces' tile counts.
+  // ---- the group's tile list
   {
-    int cnt = 0, tiles = 0;
-    const int nq = (args.users + 63) / 64;
-    for (int q = 0; q < nq; ++q) {
-      const int uu = lane + 64 * q;
-      if (uu < args.users) {
-        const int64_t a = args.offsets[uu], b = args.offsets[uu + 1];
-        cnt += a <= r_begin ? 1 : 0;
-        const int64_t lo = a > r_begin ? a : r_begin, hi = b < r_end ? b : r_end;
-        if (hi > lo) tiles += (int)((hi - lo + NT - 1) / NT);
-      }
-    }
-    cnt = row16_sum_i(cnt);
-    tiles = row16_sum_i(tiles);
-    u_first = __builtin_amdgcn_readlane(cnt, 0) + __builtin_amdgcn_readlane(cnt, 16) +
-              __builtin_amdgcn_readlane(cnt, 32) + __builtin_amdgcn_readlane(cnt, 48) - 1;
-    ntot = __builtin_amdgcn_readlane(tiles, 0) + __builtin_amdgcn_readlane(tiles, 16) +
-           __builtin_amdgcn_readlane(tiles, 32) + __builtin_amdgcn_readlane(tiles, 48);
+    const TileList tl = tile_list(args, r_begin, r_end, NT, lane);
+    u_first = tl.u_first;
+    ntot = tl.ntot;
+    first_end = tl.first_end;
   }
   // ---- affinity of rows 16 ib + .. with prototypes 16 jb + .. of block `mf`:
   // s[ib][jb][r] = S'^T[rw + 16 ib + 4 g + r][16 jb + l16]
@@ -644,7 +674,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     cursor_next(cl);
   }
   // factor of this lane's row of the tile at cursor c (0 for rows past its piece)
-  auto row_ok = [&](const Cursor& c) { return (int64_t)my_row < c.end - c.row; };
+  auto row_ok = [&](const Cursor& c) { return my_row < c.end - c.row; };
   // per-user matrices: the matrix of user u before an affinity of its tile.
   // With the LDS copy, the caller's last barrier ended the reads of the old
   // matrix (the affinity runs once per step) and the copy is published by
@@ -686,13 +716,13 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     bf16x8 a[RB / 2][JB];
     // weights of the tile at cursor c from its scores in S (rows past the piece excluded)
     auto hs_weights = [&](const Cursor& c) {
-      const int64_t nv = c.end - c.row;
+      const int nv = c.end - c.row;
       if (nv < NT) {
 #pragma unroll
         for (int ib = 0; ib < RB; ++ib)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const bool ok = (int64_t)(rw + 16 * ib + 4 * g + r) < nv;
+            const bool ok = rw + 16 * ib + 4 * g + r < nv;
 #pragma unroll
             for (int jb = 0; jb < JB; ++jb) S[ib][jb][r] = ok ? S[ib][jb][r] : -INFINITY;
           }
@@ -804,13 +834,13 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     auto softmax_next = [&](f32x4 (&sc)[RB][JB], int par, int q) {
       if constexpr (LM == 2) {
         const float* Lq = reinterpret_cast<const float*>(lds + G::OFF_L) + q * NT;
-        const int64_t nv = cx.end - cx.row;
+        const int nv = cx.end - cx.row;
 #pragma unroll
         for (int ib = 0; ib < RB; ++ib) {
           f32x4 Lv = *reinterpret_cast<const f32x4*>(Lq + rw + 16 * ib + 4 * g);
           if (nv < NT) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Lv[r] = (int64_t)(rw + 16 * ib + 4 * g + r) < nv ? Lv[r] : INFINITY;
+            for (int r = 0; r < 4; ++r) Lv[r] = rw + 16 * ib + 4 * g + r < nv ? Lv[r] : INFINITY;
           }
 #pragma unroll
           for (int jb = 0; jb < JB; ++jb)
@@ -862,7 +892,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
         combine_fast(f, l, bad, t & 1);
         lse = __log2f(l);
         if (bad) exact_wave(Sa, f, lse, slot_of(q0), cc.u);
-        if (wj == 0 && (l16 >> 2) < RB && row_ok(cc)) args.stats[(int64_t)blk * rows + cc.row + my_row] = lse;
+        if (wj == 0 && (l16 >> 2) < RB && row_ok(cc)) args.stats[(int64_t)blk * rows + r_begin + cc.row + my_row] = lse;
       } else {
         bf16x8 a[RB / 2][JB];
         if constexpr (LM == 2) {

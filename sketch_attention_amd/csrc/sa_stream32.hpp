@@ -155,20 +155,26 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
 
-  // ---- tile list: pieces (user segments) of [r_begin, r_end) cut into tiles of NT rows
+  // ---- tile list: pieces (user segments) of [r_begin, r_end) cut into tiles
+  // of NT rows.  Cursor rows are relative to r_begin (a group's range fits in
+  // 32 bits), so the per-step bookkeeping stays in 32-bit scalar arithmetic.
+  const int nrel = (int)(r_end - r_begin);
   struct Cursor {
-    int64_t row, end;
-    int u;
+    int row, end, u;
   };
   int u_first = 0, ntot = 0;
+  auto user_end = [&](int u) {
+    const int64_t e = args.offsets[u + 1] - r_begin;
+    return e < (int64_t)nrel ? (int)e : nrel;
+  };
   auto cursor_next = [&](Cursor& c) {
     c.row += NT;
     if (c.row >= c.end) {
       c.row = c.end;
-      if (c.row < r_end) {
+      if (c.row < nrel) {
         ++c.u;
-        while (c.u < args.users && args.offsets[c.u + 1] <= c.row) ++c.u;
-        c.end = min(r_end, args.offsets[c.u + 1]);
+        while (c.u < args.users && args.offsets[c.u + 1] - r_begin <= (int64_t)c.row) ++c.u;
+        c.end = user_end(c.u);
       }
     }
   };
@@ -197,10 +203,10 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
     dma_row[s] = j * RPI + lane / CH;
     dma_col[s] = 8 * ((lane % CH) ^ chunk_sw32(dma_row[s]));
   }
-  auto issue_tile = [&](const auto& c, int q) {
-    const int64_t last = c.end - 1 - c.row;  // -1 past the list
-    const int64_t b0 = last < 0 ? c.end - 1 : c.row;
-    const int lim = last < 0 ? 0 : (int)(last < NT ? last : NT - 1);
+  auto issue_tile = [&](const Cursor& c, int q) {
+    const int last = c.end - 1 - c.row;  // -1 past the list
+    const int64_t b0 = r_begin + (last < 0 ? c.end - 1 : c.row);
+    const int lim = last < 0 ? 0 : (last < NT ? last : NT - 1);
     const bf16* const base = X + b0 * D;
     const uint32_t slot = slot_of(q);
 #pragma unroll
@@ -219,30 +225,13 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
     wait_vm<DMA_PER_TILE * n>();
   };
 
+  issue_tile(Cursor{0, nrel, 0}, 0);
+  int64_t first_end;  // end of the piece holding r_begin
   {
-    struct {
-      int64_t row, end;
-    } c0{r_begin, r_end};
-    issue_tile(c0, 0);
-  }
-  {
-    int cnt = 0, tiles = 0;
-    const int nq = (args.users + 63) / 64;
-    for (int q = 0; q < nq; ++q) {
-      const int uu = lane + 64 * q;
-      if (uu < args.users) {
-        const int64_t a = args.offsets[uu], b = args.offsets[uu + 1];
-        cnt += a <= r_begin ? 1 : 0;
-        const int64_t lo = a > r_begin ? a : r_begin, hi = b < r_end ? b : r_end;
-        if (hi > lo) tiles += (int)((hi - lo + NT - 1) / NT);
-      }
-    }
-    cnt = row16_sum_i(cnt);
-    tiles = row16_sum_i(tiles);
-    u_first = __builtin_amdgcn_readlane(cnt, 0) + __builtin_amdgcn_readlane(cnt, 16) +
-              __builtin_amdgcn_readlane(cnt, 32) + __builtin_amdgcn_readlane(cnt, 48) - 1;
-    ntot = __builtin_amdgcn_readlane(tiles, 0) + __builtin_amdgcn_readlane(tiles, 16) +
-           __builtin_amdgcn_readlane(tiles, 32) + __builtin_amdgcn_readlane(tiles, 48);
+    const TileList tl = tile_list(args, r_begin, r_end, NT, lane);
+    u_first = tl.u_first;
+    ntot = tl.ntot;
+    first_end = tl.first_end;
   }
 
   // ---- affinity: s[rb][v] = S'[jbase + 8 (v / 4) + 4 h + v % 4][row 32 rb + l32 of the tile]
@@ -291,11 +280,11 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
   auto softmax_next = [&](f32x16 (&s)[2], int par, int q) {
     if constexpr (LM == 2) {
       const float* Lq = reinterpret_cast<const float*>(lds + OFF_L) + q * NT;
-      const int64_t nv = cx.end - cx.row;
+      const int nv = cx.end - cx.row;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         float L = Lq[32 * rb + l32];
-        L = (int64_t)(32 * rb + l32) < nv ? L : INFINITY;  // rows past the piece: weight 0
+        L = 32 * rb + l32 < nv ? L : INFINITY;  // rows past the piece: weight 0
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[rb][v] = fast_exp2(s[rb][v] - L);
       }
@@ -332,7 +321,7 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
       if ((i & 3) == 0) {
         const float* Lq = reinterpret_cast<const float*>(lds + OFF_L) + q * NT;
         const float L = Lq[32 * rb + l32];
-        sm_L = (int64_t)(32 * rb + l32) < cx.end - cx.row ? L : INFINITY;
+        sm_L = 32 * rb + l32 < cx.end - cx.row ? L : INFINITY;
       }
 #pragma unroll
       for (int v = v0; v < v0 + 4; ++v) s[rb][v] = fast_exp2(s[rb][v] - sm_L);
@@ -513,9 +502,10 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
 #pragma unroll
   for (int cb = 0; cb < CBK; ++cb) acc[cb] = f32x16{};
 
-  Cursor cc{r_begin, min(r_end, args.offsets[u_first + 1]), u_first};  // tile t
-  Cursor cl = cc;                                                        // next tile to load
-  Cursor ca = cc;                                                        // tile whose affinity comes next
+  const int64_t e0 = first_end - r_begin;
+  Cursor cc{0, e0 < (int64_t)nrel ? (int)e0 : nrel, u_first};  // tile t
+  Cursor cl = cc;  // next tile to load
+  Cursor ca = cc;  // tile whose affinity comes next
   cx = cc;
   cursor_next(cl);
 #pragma unroll
@@ -523,7 +513,7 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
     issue_tile(cl, p);
     cursor_next(cl);
   }
-  auto row_ok = [&](const Cursor& c, int row) { return (int64_t)row < c.end - c.row; };
+  auto row_ok = [&](const Cursor& c, int row) { return row < c.end - c.row; };
   auto ensure_m = [&]() {
     if constexpr (PU) {
       if (ca.u != m_user) {
@@ -600,7 +590,7 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
     }
     if constexpr (LM == 1) {
       const int row = 32 * h + l32;
-      if (wj == 0 && row_ok(cc, row)) args.stats[(int64_t)blk * rows + cc.row + row] = h ? lse[1] : lse[0];
+      if (wj == 0 && row_ok(cc, row)) args.stats[(int64_t)blk * rows + r_begin + cc.row + row] = h ? lse[1] : lse[0];
       if (nxt) softmax_next(Sb, (t + 1) & 1, q1);
     } else {
       auto shadow_g = [&](int q) {

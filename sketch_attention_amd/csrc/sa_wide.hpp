@@ -227,24 +227,12 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
   };
 
   issue_tile(Cursor{0, nrel, 0}, 0);
+  int64_t first_end;  // end of the piece holding r_begin
   {
-    int cnt = 0, tiles = 0;
-    const int nq = (args.users + 63) / 64;
-    for (int q = 0; q < nq; ++q) {
-      const int uu = lane + 64 * q;
-      if (uu < args.users) {
-        const int64_t a = args.offsets[uu], b = args.offsets[uu + 1];
-        cnt += a <= r_begin ? 1 : 0;
-        const int64_t lo = a > r_begin ? a : r_begin, hi = b < r_end ? b : r_end;
-        if (hi > lo) tiles += (int)((hi - lo + NT - 1) / NT);
-      }
-    }
-    cnt = row16_sum_i(cnt);
-    tiles = row16_sum_i(tiles);
-    u_first = __builtin_amdgcn_readlane(cnt, 0) + __builtin_amdgcn_readlane(cnt, 16) +
-              __builtin_amdgcn_readlane(cnt, 32) + __builtin_amdgcn_readlane(cnt, 48) - 1;
-    ntot = __builtin_amdgcn_readlane(tiles, 0) + __builtin_amdgcn_readlane(tiles, 16) +
-           __builtin_amdgcn_readlane(tiles, 32) + __builtin_amdgcn_readlane(tiles, 48);
+    const TileList tl = tile_list(args, r_begin, r_end, NT, lane);
+    u_first = tl.u_first;
+    ntot = tl.ntot;
+    first_end = tl.first_end;
   }
 
   // ---- affinity: s[f][v] = S'[jbase + l32][row 32 f + 8 (v / 4) + 4 h + v % 4 of the tile]
@@ -472,9 +460,10 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
 #pragma unroll
   for (int cb = 0; cb < CBK; ++cb) acc[cb] = f32x16{};
 
-  Cursor cc{0, user_end(u_first), u_first};  // tile t
-  Cursor cl = cc;                                                        // next tile to load
-  Cursor ca = cc;                                                        // tile whose affinity comes next
+  const int64_t e0 = first_end - r_begin;
+  Cursor cc{0, e0 < (int64_t)nrel ? (int)e0 : nrel, u_first};  // tile t
+  Cursor cl = cc;  // next tile to load
+  Cursor ca = cc;  // tile whose affinity comes next
   cursor_next(cl);
 #pragma unroll
   for (int p = 1; p < NS - 1; ++p) {
