@@ -175,7 +175,7 @@ __device__ __forceinline__ TileList tile_list(const FusedArgs& args, int64_t r_b
   return t;
 }
 
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, int LM = 0>
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
 struct StreamGeom {
   static_assert(KW % 16 == 0 && (D == 64 || D == 128) && PF >= 1 && PF <= 3 && (RB == 2 || RB == 4) &&
                     (SB == 1 || SB == 2),
@@ -218,14 +218,9 @@ struct StreamGeom {
   // P rows per 256 bytes), so fragment reads are conflict-free without padding
   static constexpr int M_BYTES = SB == 1 ? KPAD * D * 2 : 0;
   static constexpr int OFF_M = OFF_STAGE + STAGE_BYTES;
-  // two-phase pass, second phase: the rows' log-sum-exp arrive with each tile
-  // (one dword per row, by LDS DMA) into a ring of NS slots of NT floats
-  static constexpr int L_BYTES = LM == 2 ? NS * NT * 4 : 0;
-  static constexpr int OFF_L = OFF_M + M_BYTES;
-  static constexpr int LDS_BYTES = OFF_L + L_BYTES;
-  // vector-memory operations of one wave per tile (the X blocks, plus the
-  // log-sum-exp dwords in the second phase)
-  static constexpr int DMA_LO = NI / NW + (LM == 2 ? 1 : 0);
+  static constexpr int LDS_BYTES = OFF_M + M_BYTES;
+  // vector-memory operations (X blocks) of one wave per tile
+  static constexpr int DMA_LO = NI / NW;
   static constexpr int DMA_HI = DMA_LO + 1;  // waves w < NI % NW issue one block more
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 compute unit");
 };
@@ -233,17 +228,12 @@ struct StreamGeom {
 // PU: one folded matrix per user (args.m_stride apart) instead of one shared
 // matrix; a separate instantiation so the shared case carries none of its
 // bookkeeping.  HS: the comparator of section 3.1, the softmax taken over the
-// history axis instead of the prototype axis (see the main loop below).
-// LM: 0 the one-pass kernel; 1 and 2 the two phases of the pass for more
-// prototypes than one work group holds (FusedArgs::lse_mode): phase 1 writes
-// every row's log-sum-exp over one block of prototypes, phase 2 takes the
-// row's log-sum-exp over all prototypes as given, so its weights are
-// 2^(s' - L) with no exchange between waves, and aggregates one block.
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU, bool HS = false, int LM = 0>
+// history axis instead of the prototype axis (see the main loop below).  The
+// two phases of the pass for more prototypes than one work group holds run on
+// sa_stream32.hpp.
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU, bool HS = false>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args) {
-  using G = StreamGeom<D, KW, WJ, WI, RB, PF, SB, LM>;
-  static_assert(LM == 0 || (SB == 2 && WI == 1 && !HS && G::NT == 64), "two-phase plans: one tile of 64 rows, "
-                "two score buffers, waves over the prototypes only");
+  using G = StreamGeom<D, KW, WJ, WI, RB, PF, SB>;
   using MF = Mfma<bf16>;
   constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, RW = G::RW, THREADS = G::THREADS;
 
@@ -268,12 +258,12 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int wi = wave / WJ;
   const int rw = wi * RW;     // first tile row of this wave
   const int jbase = wj * KW;  // first prototype of this wave
-  // two-phase pass, and the comparator beyond one block of prototypes (its
-  // softmax is per prototype, so blocks need no merge): work group g handles
-  // prototype block g % blocks (consecutive groups read the same rows at about
-  // the same time) for row range g / blocks
-  const int nblk = (LM || HS) ? args.blocks : 1;
-  const int blk = (LM || HS) ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  // the comparator beyond one block of prototypes (its softmax is per
+  // prototype, so blocks need no merge): work group g handles prototype block
+  // g % blocks (consecutive groups read the same rows at about the same time)
+  // for row range g / blocks
+  const int nblk = HS ? args.blocks : 1;
+  const int blk = HS ? (int)(blockIdx.x % (unsigned)nblk) : 0;
   const bf16* const X = static_cast<const bf16*>(args.X);
   const bf16* const Mg = static_cast<const bf16*>(args.M) + (int64_t)blk * G::KPAD * D;
   const int k = args.k - blk * G::KPAD;  // real prototypes of this block (may exceed KPAD)
@@ -373,12 +363,6 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
         const int rr = dma_row[s] < lim ? dma_row[s] : lim;
         dma16(base, (uint32_t)(rr * D + dma_col[s]) * 2u, slot + 1024u * (uint32_t)j);
       }
-    }
-    if constexpr (LM == 2) {
-      // every wave brings the tile's 64 log-sum-exps (the same values into the
-      // same slot, so the waves' vector-memory counts stay equal)
-      const int rr = lane < lim ? lane : lim;
-      dma4(args.stats + b0, (uint32_t)rr * 4u, xr0 + (uint32_t)(G::OFF_L + q * G::NT * 4));
     }
   };
   // wait until every DMA block of this wave is done but those of the n most
@@ -523,7 +507,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   // ---- exact path of one wave (rare): for each of its row blocks, an online
   // max / shifted-sum pass over all prototypes (M fragments from global
   // memory), then its own prototypes' weights 2^(s' - m) with factor 1 / l.
-  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, float& lse, uint32_t xs, int u) {
+  auto exact_wave = [&](f32x4 (&s)[RB][JB], float& f, uint32_t xs, int u) {
     const bf16* const Mu = PU ? Mg + (int64_t)u * args.m_stride : Mg;
 #pragma unroll  // s[ib] must be indexed by constants to stay in registers
     for (int ib = 0; ib < RB; ++ib) {
@@ -561,10 +545,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       for (int r = 0; r < 4; ++r) {
 #pragma unroll
         for (int jb = 0; jb < JB; ++jb) s[ib][jb][r] = fast_exp2(s[ib][jb][r] - m[r]);
-        if (ib == my_ib && r == my_r) {
-          f = 1.f / l[r];
-          lse = m[r] + __log2f(l[r]);  // log2 sum over the prototypes of this block
-        }
+        if (ib == my_ib && r == my_r) f = 1.f / l[r];
       }
     }
   };
@@ -589,15 +570,6 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   auto weights = [&](bf16x8 (&a)[RB / 2][JB], const f32x4 (&s)[RB][JB], float f) {
 #pragma unroll
     for (int h = 0; h < RB / 2; ++h) weights_h(a, s, f, h);
-  };
-  // second phase of the two-phase pass: the scores already are the weights
-  auto weights_plain = [&](bf16x8 (&a)[RB / 2][JB], const f32x4 (&s)[RB][JB]) {
-#pragma unroll
-    for (int h = 0; h < RB / 2; ++h)
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[h][jb][e] = (bf16)s[2 * h + (e >> 2)][jb][e & 3];
   };
   auto aggregate_h = [&](f32x4 (&acc)[JB][CB], const bf16x8 (&a)[RB / 2][JB], uint32_t xs, int h) {
     const uint32_t xp = xs + (uint32_t)(2 * rw * D) + trb;
@@ -826,32 +798,6 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     }
   } else if constexpr (SB == 2) {
     f32x4 S0[RB][JB], S1[RB][JB];
-    // exponentials of the next tile's scores.  One-pass kernel and first
-    // phase: 2^s' and this wave's row sums to LDS.  Second phase: 2^(s' - L)
-    // with L the row's log-sum-exp over all prototypes, from the tile's LDS
-    // slot; rows past the piece get L = +inf, hence weight 0.
-    Cursor cx = cc;  // tile whose exponentials come next (second phase)
-    auto softmax_next = [&](f32x4 (&sc)[RB][JB], int par, int q) {
-      if constexpr (LM == 2) {
-        const float* Lq = reinterpret_cast<const float*>(lds + G::OFF_L) + q * NT;
-        const int nv = cx.end - cx.row;
-#pragma unroll
-        for (int ib = 0; ib < RB; ++ib) {
-          f32x4 Lv = *reinterpret_cast<const f32x4*>(Lq + rw + 16 * ib + 4 * g);
-          if (nv < NT) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Lv[r] = rw + 16 * ib + 4 * g + r < nv ? Lv[r] : INFINITY;
-          }
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[ib][jb][r] = fast_exp2(sc[ib][jb][r] - Lv[r]);
-        }
-        cursor_next(cx);
-      } else {
-        softmax_fast(sc, par);
-      }
-    };
     ensure_m(false);
     wait_tiles(std::integral_constant<int, NS - 2>{});
     __syncthreads();
@@ -862,7 +808,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     __syncthreads();
     affinity(S1, slot_of(1));
     next_affinity_tile();
-    softmax_next(S0, 0, 0);
+    softmax_fast(S0, 0);
     wait_tiles(std::integral_constant<int, NS - 4>{});
     __syncthreads();
 
@@ -879,41 +825,25 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
     // branch but the exact one; the last two steps of a list skip the
     // affinity and exponentials of tiles past its end.
     int q0 = 0;  // ring slot of tile t
-    // First phase of the two-phase pass: no aggregation; each row's
-    // log2 sum over this block's prototypes goes to stats[block][row].
     auto step = [&](int t, f32x4 (&Sa)[RB][JB], f32x4 (&Sb)[RB][JB], auto full) {
-      const int q1 = q0 + 1 < NS ? q0 + 1 : q0 + 1 - NS;
       const int q2 = q0 + 2 < NS ? q0 + 2 : q0 + 2 - NS;
       const int qn = q0 == 0 ? NS - 1 : q0 - 1;
       issue_tile(cl, qn);
-      if constexpr (LM == 1) {
-        float f, l, lse;
+      {
+        bf16x8 a[RB / 2][JB];
+        float f, l;
         bool bad;
         combine_fast(f, l, bad, t & 1);
-        lse = __log2f(l);
-        if (bad) exact_wave(Sa, f, lse, slot_of(q0), cc.u);
-        if (wj == 0 && (l16 >> 2) < RB && row_ok(cc)) args.stats[(int64_t)blk * rows + r_begin + cc.row + my_row] = lse;
-      } else {
-        bf16x8 a[RB / 2][JB];
-        if constexpr (LM == 2) {
-          weights_plain(a, Sa);
-        } else {
-          float f, l, lse;
-          bool bad;
-          combine_fast(f, l, bad, t & 1);
-          if (bad) exact_wave(Sa, f, lse, slot_of(q0), cc.u);
-          f = row_ok(cc) ? f : 0.f;
-          weights(a, Sa, f);
-        }
+        if (bad) exact_wave(Sa, f, slot_of(q0), cc.u);
+        f = row_ok(cc) ? f : 0.f;
+        weights(a, Sa, f);
         aggregate(acc, a, slot_of(q0));
       }
       ensure_m(false);
       if (decltype(full)::value || t + 2 < ntot) affinity(Sa, slot_of(q2));
       next_affinity_tile();
-      if (decltype(full)::value || t + 1 < ntot) softmax_next(Sb, (t + 1) & 1, q1);
-      if constexpr (LM != 1) {
-        if (cc.row + NT >= cc.end) flush(acc, cc.u, q0);  // its first barrier ends every read of slot q0
-      }
+      if (decltype(full)::value || t + 1 < ntot) softmax_fast(Sb, (t + 1) & 1);
+      if (cc.row + NT >= cc.end) flush(acc, cc.u, q0);  // its first barrier ends every read of slot q0
       cursor_next(cc);
       cursor_next(cl);
       q0 = q0 + 1 < NS ? q0 + 1 : 0;
@@ -952,10 +882,10 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
       const int qn = q0 == 0 ? NS - 1 : q0 - 1;
       issue_tile(cl, qn);
       ensure_m(true);  // matrix of tile t+1's user
-      float f, l, lse;
+      float f, l;
       bool bad;
       combine_fast(f, l, bad, t & 1);
-      if (bad) exact_wave(S, f, lse, slot_of(q0), cc.u);
+      if (bad) exact_wave(S, f, slot_of(q0), cc.u);
       f = row_ok(cc) ? f : 0.f;
       bf16x8 a[RB / 2][JB];
       weights(a, S, f);
@@ -975,35 +905,22 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   wait_vm<0>();  // no DMA outlives the work group
 }
 
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU, bool HS, int LM = 0>
+template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD, bool PU, bool HS>
 hipError_t launch_stream_pu(const FusedArgs& a, const Launch& l) {
   constexpr int threads = 64 * WJ * WI;
   if (l.start || l.stop) {
-    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU, HS, LM>), dim3(l.groups),
-                          dim3(threads), 0, l.stream, l.start, l.stop, 0, a);
+    hipExtLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU, HS>), dim3(l.groups), dim3(threads), 0,
+                          l.stream, l.start, l.stop, 0, a);
   } else {
-    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU, HS, LM>), dim3(l.groups), dim3(threads), 0,
+    hipLaunchKernelGGL((sa_stream_kernel<D, KW, WJ, WI, RB, PF, SB, PAD, PU, HS>), dim3(l.groups), dim3(threads), 0,
                        l.stream, a);
   }
   return hipGetLastError();
 }
-// plans that also run the two phases of the pass for more prototypes than
-// one work group holds (d = 128 above k = 512): blocks of 8 x 32 prototypes
-template <int D, int KW, int WJ, int WI, int RB, int PF, int SB>
-constexpr bool kTwoPhasePlan = D == 128 && KW == 32 && WJ == 8 && WI == 1 && RB == 4 && PF == 1 && SB == 2;
 
 template <int D, int KW, int WJ, int WI, int RB, int PF, int SB, bool PAD>
 hipError_t launch_stream_t(const FusedArgs& a, const Launch& l) {
-  if constexpr (kTwoPhasePlan<D, KW, WJ, WI, RB, PF, SB>) {
-    if (a.lse_mode == 1)
-      return a.m_stride != 0 ? launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, true, false, 1>(a, l)
-                             : launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false, false, 1>(a, l);
-    if (a.lse_mode == 2)
-      return a.m_stride != 0 ? launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, true, false, 2>(a, l)
-                             : launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false, false, 2>(a, l);
-  } else {
-    if (a.lse_mode != 0) return hipErrorInvalidValue;
-  }
+  if (a.lse_mode != 0) return hipErrorInvalidValue;  // the two phases run on sa_stream32.hpp
   if constexpr (WI == 1) {
     if (a.history_softmax) return launch_stream_pu<D, KW, WJ, WI, RB, PF, SB, PAD, false, true>(a, l);
   } else {
