@@ -76,20 +76,26 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   if (r_begin >= r_end) return;  // the host launches at most one group per row
 
   // ---- tiles: pieces of [r_begin, r_end) per user, NT rows each
+  // cursor rows relative to r_begin (a group's range fits in 32 bits: the
+  // per-tile bookkeeping stays in 32-bit scalar arithmetic)
+  const int nrel = (int)(r_end - r_begin);
   struct Cursor {
-    int64_t row, end;
-    int u;
+    int row, end, u;
   };
   int u0 = 0;
   while (args.offsets[u0 + 1] <= r_begin) ++u0;
+  auto user_end = [&](int u) {
+    const int64_t e = args.offsets[u + 1] - r_begin;
+    return e < (int64_t)nrel ? (int)e : nrel;
+  };
   auto cursor_next = [&](Cursor& c) {
     c.row += NT;
     if (c.row >= c.end) {
       c.row = c.end;
-      if (c.row < r_end) {
+      if (c.row < nrel) {
         ++c.u;
-        while (args.offsets[c.u + 1] <= c.row) ++c.u;
-        c.end = min(r_end, args.offsets[c.u + 1]);
+        while (args.offsets[c.u + 1] - r_begin <= (int64_t)c.row) ++c.u;
+        c.end = user_end(c.u);
       }
     }
   };
@@ -99,9 +105,9 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   // chunk i % CH = global chunk (i % CH) ^ sw(row).  Rows past the piece read
   // its last row; past the list every lane reads row c.end - 1 (in bounds).
   auto issue_tile = [&](const Cursor& c, int q) {
-    const int64_t last = c.end - 1 - c.row;
-    const int64_t b0 = last < 0 ? c.end - 1 : c.row;
-    const int lim = last < 0 ? 0 : (int)(last < NT ? last : NT - 1);
+    const int last = c.end - 1 - c.row;
+    const int64_t b0 = r_begin + (last < 0 ? c.end - 1 : c.row);
+    const int lim = last < 0 ? 0 : (last < NT ? last : NT - 1);
 #pragma unroll
     for (int s = 0; s < NIW; ++s) {
       const int j = wj + s * WJ;
@@ -261,9 +267,9 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Cursor cc{r_begin, min(r_end, args.offsets[u0 + 1]), u0};  // tile t (merge, aggregation)
-  Cursor ca = cc;                                             // tile t + 1 (affinity)
-  Cursor cl = cc;                                             // next tile to load
+  Cursor cc{0, user_end(u0), u0};  // tile t (merge, aggregation)
+  Cursor ca = cc;                  // tile t + 1 (affinity)
+  Cursor cl = cc;                  // next tile to load
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) {
     issue_tile(cl, p);
@@ -279,15 +285,16 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   __syncthreads();
 
   int t = 0;
-  while (cc.row < r_end) {
+  while (cc.row < nrel) {
     issue_tile(cl, (t + NS - 1) % NS);  // the slot of tile t - 1
     cursor_next(cl);
     const int par = t & 1;
-    const bool valid = (int64_t)my_row < cc.end - cc.row;
+    const bool valid = my_row < cc.end - cc.row;
+    const int64_t grow = r_begin + cc.row + my_row;  // global row of my_row
     float lse, c;
     if (phase == 2) {
       // the merged statistics of all blocks (the lanes of a row read the same 8 bytes)
-      const float* st = args.stats + (valid ? (cc.row + my_row) * 4 : 0);
+      const float* st = args.stats + (valid ? grow * 4 : 0);
       lse = st[0];
       c = st[1];
     } else {
@@ -306,13 +313,13 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
       if (phase == 1) {
         // this block's share: (m, l, sum over its prototypes of 2^(s' - m) dA)
         if (valid && wj == 0 && l16 < 8)
-          *reinterpret_cast<f32x4*>(args.stats + ((int64_t)blk * rows + cc.row + my_row) * 4) = f32x4{m, l, c, 0.f};
+          *reinterpret_cast<f32x4*>(args.stats + ((int64_t)blk * rows + grow) * 4) = f32x4{m, l, c, 0.f};
       } else {
         c *= 1.f / l;
         // log-sum-exp of the row in log2 units: A = 2^(s' - lse)
         lse = m + __builtin_amdgcn_logf(l);
         if (valid && wj == 0 && l16 < 8)
-          *reinterpret_cast<f32x4*>(args.stats + (cc.row + my_row) * 4) = f32x4{lse, c, 0.f, 0.f};
+          *reinterpret_cast<f32x4*>(args.stats + grow * 4) = f32x4{lse, c, 0.f, 0.f};
       }
     }
     if (phase != 1) {
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
     }
     }  // phase != 1
     // products and row statistics of tile t + 1
-    if (ca.row < r_end) {
+    if (ca.row < nrel) {
       ensure_g(ca.u);
       affinity((t + 1) % NS);
       if (phase != 2) row_stats(par ^ 1);
