@@ -138,21 +138,40 @@ __device__ __forceinline__ constexpr int chunk_sw(int r) {
 // starting at or before r_begin (a prefix, offsets being non-decreasing; it is
 // the user holding row r_begin, so first_end = offsets[u_first + 1] >
 // r_begin, read from the lane that loaded it), ntot the sum of the pieces'
-// tile counts.
+// tile counts.  The kernels issue the loads (tile_list_loads) before their
+// folded-matrix loads and first tile DMA and finish the scan after those:
+// vector-memory loads complete in order, so waiting for the offsets then does
+// not wait for the larger transfers issued after them.
 struct TileList {
   int u_first, ntot;
   int64_t first_end;
 };
-__device__ __forceinline__ TileList tile_list(const FusedArgs& args, int64_t r_begin, int64_t r_end, int nt, int lane) {
+struct OffsetLoads {
+  int64_t a[4], b[4];  // offsets[lane + 64 q] and offsets[lane + 64 q + 1] (0 past the users)
+};
+__device__ __forceinline__ OffsetLoads tile_list_loads(const FusedArgs& args, int lane) {
+  OffsetLoads o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int uu = lane + 64 * q;
+    o.a[q] = 0;
+    o.b[q] = 0;
+    if (uu < args.users) {
+      o.a[q] = args.offsets[uu];
+      o.b[q] = args.offsets[uu + 1];
+    }
+  }
+  return o;
+}
+__device__ __forceinline__ TileList tile_list(const FusedArgs& args, const OffsetLoads& o, int64_t r_begin,
+                                              int64_t r_end, int nt, int lane) {
   int cnt = 0, tiles = 0;
   int64_t first_end = r_end;
-  const int nq = (args.users + 63) / 64;
-  for (int q = 0; q < nq; ++q) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
     const int uu = lane + 64 * q;
-    int64_t a = 0, b = 0;
+    const int64_t a = o.a[q], b = o.b[q];
     if (uu < args.users) {
-      a = args.offsets[uu];
-      b = args.offsets[uu + 1];
       cnt += a <= r_begin ? 1 : 0;
       const int64_t lo = a > r_begin ? a : r_begin, hi = b < r_end ? b : r_end;
       if (hi > lo) tiles += (int)((hi - lo + nt - 1) / nt);
@@ -274,6 +293,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int64_t r_begin = grp * rows / ngroups;
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
+  const OffsetLoads offs = tile_list_loads(args, lane);  // first: see tile_list
 
   int u_first = 0, ntot = 0;
   int64_t first_end = 0;  // end of the piece holding r_begin
@@ -384,7 +404,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
 
   // ---- the group's tile list
   {
-    const TileList tl = tile_list(args, r_begin, r_end, NT, lane);
+    const TileList tl = tile_list(args, offs, r_begin, r_end, NT, lane);
     u_first = tl.u_first;
     ntot = tl.ntot;
     first_end = tl.first_end;

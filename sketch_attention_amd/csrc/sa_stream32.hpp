@@ -154,6 +154,7 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
   const int64_t r_begin = grp * rows / ngroups;
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
+  const OffsetLoads offs = tile_list_loads(args, lane);  // first: see tile_list
 
   // ---- tile list: pieces (user segments) of [r_begin, r_end) cut into tiles
   // of NT rows.  Cursor rows are relative to r_begin (a group's range fits in
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
   issue_tile(Cursor{0, nrel, 0}, 0);
   int64_t first_end;  // end of the piece holding r_begin
   {
-    const TileList tl = tile_list(args, r_begin, r_end, NT, lane);
+    const TileList tl = tile_list(args, offs, r_begin, r_end, NT, lane);
     u_first = tl.u_first;
     ntot = tl.ntot;
     first_end = tl.first_end;
