@@ -289,7 +289,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream, hipEvent_t sta
   }
   const int slot_f4 = a.k_pad * a.d / 4;
   int shares = 1;
-  while (shares < kReduceShares && 8 * 2 * shares <= per_user) shares *= 2;
+  while (shares < kReduceShares && 8 * shares <= per_user) shares *= 2;
   const dim3 grid((slot_f4 + kReduceLanes - 1) / kReduceLanes, a.users, a.blocks > 1 ? a.blocks : 1),
       block(kReduceLanes * shares);
   if (start || stop)
