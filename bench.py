@@ -135,6 +135,20 @@ def cpu_baseline(wl, budget_s: float, layers=None, norm: str = "prototypes"):
     }
 
 
+def fused_kernel_name(dtype: str, d: int, k: int, norm: str = "prototypes") -> str:
+    """Name of the fused kernel the library's planner picks for a shape (labels only; the rule of make_plan):
+    bf16 d = 128 beyond 512 prototypes runs the two phases on sa_stream32_kernel, bf16 d = 128 with 128 < k <= 256
+    the 32x32x16 lanes pass sa_wide_kernel (the comparator keeps sa_stream_kernel), other bf16 with k > 32 the
+    streamed sa_stream_kernel, and the rest the lockstep sa_fused_kernel."""
+    if dtype != "bf16" or k <= 32:
+        return "sa_fused_kernel"
+    if norm == "prototypes" and d == 128 and k > 512:
+        return "sa_stream32_kernel"
+    if norm == "prototypes" and d == 128 and 128 < k <= 256:
+        return "sa_wide_kernel"
+    return "sa_stream_kernel"
+
+
 def kernel_source_hash(dtype: str = "bf16", d: int = 128) -> str:
     """sha256 over the sources and compiler options that decide the fused kernel
     a launch runs (include paths left out: they differ between checkouts)."""
@@ -520,8 +534,7 @@ def main() -> int:
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
     roof["traffic"] = measured_traffic(wl.name, wl.dtype, wl.d) if (args.users is None and not args.layers and
                                                                      args.norm == "prototypes") else None
-    # the library runs the streamed pass for bf16 with k > 32, the lockstep pass otherwise
-    roof["kernel"] = "sa_stream_kernel" if wl.dtype == "bf16" and wl.k > 32 else "sa_fused_kernel"
+    roof["kernel"] = fused_kernel_name(wl.dtype, wl.d, wl.k, args.norm)
     roof["kernel_avg_us"] = round(fused_avg_ms * 1e3, 2)
     roof["kernel_launches_timed"] = int(launches)
     log(f"[bench] fused kernel avg {fused_avg_ms * 1e3:.2f} us ({tflops:.1f} TFLOP/s, {gbs:.0f} GB/s), "

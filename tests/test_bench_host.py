@@ -69,3 +69,15 @@ def test_kernel_timing_pass_is_long_enough():
 
 def test_cpu_model_is_named():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model() != ""
+
+
+def test_roofline_kernel_label_follows_the_planner():
+    # the kernel the bench line names for each workload shape (make_plan's rule)
+    assert bench.fused_kernel_name("bf16", 128, 256) == "sa_wide_kernel"
+    assert bench.fused_kernel_name("bf16", 128, 256, "history") == "sa_stream_kernel"
+    assert bench.fused_kernel_name("bf16", 128, 1024) == "sa_stream32_kernel"
+    assert bench.fused_kernel_name("bf16", 128, 64) == "sa_stream_kernel"
+    assert bench.fused_kernel_name("bf16", 128, 128) == "sa_stream_kernel"
+    assert bench.fused_kernel_name("bf16", 64, 1024) == "sa_stream_kernel"
+    assert bench.fused_kernel_name("f32", 64, 16) == "sa_fused_kernel"
+    assert bench.fused_kernel_name("bf16", 128, 32) == "sa_fused_kernel"
