@@ -118,7 +118,8 @@ sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype
  *   X          device, [offsets[num_users]][d] packed history rows in the
  *              handle's dtype, 16-byte aligned; user u owns rows
  *              offsets[u] .. offsets[u+1]-1 (section 2.1: X in R^{n x d})
- *   offsets    host, int64 [num_users + 1], offsets[0] == 0, non-decreasing
+ *   offsets    host, int64 [num_users + 1], offsets[0] == 0, non-decreasing,
+ *              offsets[num_users] <= 2^31 - 1 (else SA_ERR_INVALID_ARG)
  *   num_users  U >= 0; U == 0 is a no-op returning SA_OK
  *   out        device, float32 [num_users][k][d], 16-byte aligned, fully
  *              overwritten; a user with no rows gets a zero sketch (empty sum)

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -206,7 +207,8 @@ sa_status check_batch(const int64_t* offsets, int32_t num_users) {
   if (offsets[0] != 0) return SA_ERR_INVALID_ARG;
   for (int32_t u = 0; u < num_users; ++u)
     if (offsets[u + 1] < offsets[u]) return SA_ERR_INVALID_ARG;
-  if (offsets[num_users] > (int64_t(1) << 40)) return SA_ERR_INVALID_ARG;
+  // the streamed kernels keep a work group's rows in 32-bit offsets from its first row
+  if (offsets[num_users] > INT32_MAX) return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
 

@@ -83,6 +83,8 @@ def test_check_config(d, k, tau, dtype, want):
     ([0, 5, 4], B.SA_ERR_INVALID_ARG),
     ([0, -1], B.SA_ERR_INVALID_ARG),
     ([0, 2 ** 41], B.SA_ERR_INVALID_ARG),
+    ([0, 2 ** 31 - 1], B.SA_OK),                 # the largest batch (a work group's rows in 32-bit offsets)
+    ([0, 2 ** 30, 2 ** 31], B.SA_ERR_INVALID_ARG),
 ])
 def test_check_batch(offsets, want):
     assert B.sa_check_batch(16, np.array(offsets, dtype=np.int64)) == want
