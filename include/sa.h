@@ -38,7 +38,8 @@
  *     by stream capture into a HIP graph and replayed -- but a graph captured
  *     before a later growth still points at the freed buffers and must not be
  *     replayed after it: make the call with the largest workspace need first,
- *     or capture sa_compress_batch_noalloc, whose workspace never moves.
+ *     freeze the workspace with sa_reserve, or capture
+ *     sa_compress_batch_noalloc, whose workspace never moves.
  *     Kernel timing (the *_set_kernel_timing calls) records events and is for
  *     eager use.
  */
@@ -156,6 +157,30 @@ sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, 
  */
 sa_status sa_compress_batch_noalloc(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users,
                                     float* out, void* stream);
+
+/*
+ * sa_reserve -- sizes, and optionally freezes, a handle's workspace for
+ * callers that record sa_compress_batch into HIP graphs (a graph keeps the
+ * workspace's address, which a later growing call would otherwise free).
+ *
+ *   h          handle from sa_create
+ *   max_rows   0 .. 2^31 - 1: the most rows (offsets[num_users]) of a later call
+ *   max_users  >= 0: the most users of a later call
+ *   freeze     1: later sa_compress_batch calls never free or allocate the
+ *              workspace -- a call within the bounds runs exactly as it
+ *              would unfrozen, a larger one in more launches sized to the
+ *              workspace (as sa_compress_batch_noalloc does), or returns
+ *              SA_ERR_UNSUPPORTED if one user alone does not fit; with both
+ *              bounds 0 and no workspace yet the handle stays unfrozen.
+ *              0: the workspace grows on demand again.
+ *   stream     synchronised before an old, smaller workspace is freed
+ *
+ * Grows the workspace (it never shrinks) to what any call within the bounds
+ * needs; call it outside capture.  Errors: SA_ERR_INVALID_ARG (null handle,
+ * bounds out of range), SA_ERR_OUT_OF_MEMORY (the handle is then unfrozen),
+ * SA_ERR_DEVICE.
+ */
+sa_status sa_reserve(sa_handle h, int64_t max_rows, int32_t max_users, int32_t freeze, void* stream);
 
 /*
  * sa_destroy -- free the handle and its device memory.  NULL is allowed.

@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     sa_grad_destroy,
     sa_measure_ceilings,
     sa_read_kernel_timing,
+    sa_reserve,
     sa_set_kernel_timing,
     sa_stack_compress_batch,
     sa_stack_compress_batch_bound,

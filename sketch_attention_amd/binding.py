@@ -34,7 +34,8 @@ _DTYPES = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}
 _DTYPE_NAMES = {"f32": SA_F32, "bf16": SA_BF16}
 
 EXPORTED = (
-    "sa_create", "sa_create_ex", "sa_compress_batch", "sa_compress_batch_noalloc", "sa_destroy", "sa_status_string", "sa_check_config", "sa_check_batch",
+    "sa_create", "sa_create_ex", "sa_compress_batch", "sa_compress_batch_noalloc", "sa_reserve", "sa_destroy",
+    "sa_status_string", "sa_check_config", "sa_check_batch",
     "sa_get_folded", "sa_set_kernel_timing", "sa_read_kernel_timing", "sa_describe_plan",
     "sa_stack_create", "sa_stack_compress_batch", "sa_stack_destroy", "sa_stack_set_kernel_timing",
     "sa_stack_read_kernel_timing",
@@ -101,6 +102,7 @@ def library() -> ctypes.CDLL:
         "sa_create_ex": (i32, [ctypes.POINTER(vp), i32, i32, f32, i32, vp, vp, vp, i32, vp]),
         "sa_compress_batch": (i32, [vp, vp, vp, i32, vp, vp]),
         "sa_compress_batch_noalloc": (i32, [vp, vp, vp, i32, vp, vp]),
+        "sa_reserve": (i32, [vp, i64, i32, i32, vp]),
         "sa_destroy": (None, [vp]),
         "sa_status_string": (ctypes.c_char_p, [i32]),
         "sa_check_config": (i32, [i32, i32, f32, i32]),
@@ -209,7 +211,7 @@ def sa_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
                                         ctypes.c_void_p(P.data_ptr()), ctypes.c_void_p(W_Q.data_ptr()),
                                         ctypes.c_void_p(W_K.data_ptr()), _NORMS[norm], _stream_ptr(stream, P.device))
     _check(st, "sa_create")
-    _remember(h, "sa", k=int(k), d=int(d), dtype=P.dtype)
+    _remember(h, "sa", k=int(k), d=int(d), dtype=P.dtype, device=P.device)
     return h
 
 
@@ -275,6 +277,17 @@ def sa_compress_batch_noalloc(handle: ctypes.c_void_p, X: torch.Tensor, offsets,
     st = library().sa_compress_batch_noalloc(handle, X.data_ptr(), offs.ctypes.data, offs.size - 1, out.data_ptr(),
                                              stream.cuda_stream)
     _check(st, "sa_compress_batch_noalloc")
+
+
+def sa_reserve(handle: ctypes.c_void_p, max_rows: int, max_users: int, freeze: bool = True,
+               stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Size (and with freeze, fix) the handle's workspace for calls of up to max_rows rows and max_users users
+    (see include/sa.h)."""
+    info = _info(handle, "sa")
+    if stream is None:
+        stream = torch.cuda.current_stream(info["device"])
+    _check(library().sa_reserve(handle, int(max_rows), int(max_users), 1 if freeze else 0, stream.cuda_stream),
+           "sa_reserve")
 
 
 def _check_batch_tensors(info: dict, X: torch.Tensor, offs: np.ndarray, out: torch.Tensor) -> None:
@@ -349,6 +362,12 @@ class SketchAttention:
             out = torch.empty((offs.size - 1, self.k, self.d), dtype=torch.float32, device=X.device)
         sa_compress_batch(self.handle, X, offs, out, stream)
         return out
+
+    def reserve(self, max_rows: int, max_users: int, freeze: bool = True,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Workspace for calls of up to max_rows rows and max_users users; with freeze it never moves again
+        (for HIP graph capture of compress)."""
+        sa_reserve(self.handle, max_rows, max_users, freeze, stream)
 
     def folded(self) -> torch.Tensor:
         dst = torch.empty((self.k, self.d), dtype=torch.float32, device=self.device)

@@ -42,6 +42,7 @@ struct sa_handle_s {
   void* M = nullptr;           // folded matrix [k_pad][d], dtype
   float* workspace = nullptr;  // partial sketches
   size_t workspace_bytes = 0;
+  bool frozen = false;         // sa_reserve: the workspace never moves; launches are sized to fit it
   bool timing = false;
   std::vector<TimingSlot> slots;  // recorded since the last read
   std::vector<TimingSlot> spare;  // event triples ready for reuse
@@ -359,8 +360,38 @@ namespace {
 // then formed greedily so that each fits (at least one work group per
 // prototype block and launch); if one user alone does not fit, nothing is
 // enqueued and SA_ERR_UNSUPPORTED is returned.  No event is recorded.
+// Workspace sizing of one launch of `rows` rows and `nu` users: a partial
+// slot is the block's k x d accumulator (plus per-prototype maxima and sums
+// for the comparator) per work group and user piece and prototype block; the
+// two-phase pass adds per-block and merged log-sum-exps of every row.
+struct Sizing {
+  int nb;             // prototype blocks
+  size_t slot_bytes;  // one partial slot
+  bool two_phase;
+};
+Sizing sizing_of(const sa_handle_s* h) {
+  const Plan& plan = h->plan;
+  const bool hist = h->norm == SA_NORM_HISTORY;
+  Sizing z;
+  z.nb = plan.blocks > 1 ? plan.blocks : 1;
+  z.slot_bytes = (size_t)(plan.kw * plan.waves_k) * (plan.d + (hist ? 2 : 0)) * sizeof(float);
+  z.two_phase = z.nb > 1 && !hist;
+  return z;
+}
+// work groups per prototype block for a launch of `rows` rows (the grid is nb times that)
+int launch_groups(const sa_handle_s* h, const Sizing& z, int64_t rows) {
+  if (rows <= 0) return 0;
+  const int g = groups_for(h, rows);
+  return z.nb > 1 ? (g + z.nb - 1) / z.nb : g;
+}
+size_t stats_bytes(const Sizing& z, int64_t rows) { return z.two_phase ? (size_t)(z.nb + 1) * (size_t)rows * sizeof(float) : 0; }
+size_t launch_bytes(const Sizing& z, int groups, int32_t nu, int64_t rows) {
+  return (size_t)z.nb * (groups + nu) * z.slot_bytes + stats_bytes(z, rows);
+}
+
 sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_t num_users, float* out, void* stream,
-                   const void* M, int64_t m_stride, float* fixed_ws = nullptr, size_t fixed_bytes = 0) {
+                   const void* M, int64_t m_stride, float* fixed_ws = nullptr, size_t fixed_bytes = 0,
+                   bool allow_timing = false) {
   if (h == nullptr) return SA_ERR_INVALID_ARG;
   sa_status st = check_batch(offsets, num_users);
   if (st != SA_OK) return st;
@@ -372,20 +403,18 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
   const Plan& plan = h->plan;
   const size_t elem = plan.dtype == SA_BF16 ? 2 : 4;
   const bool hist = h->norm == SA_NORM_HISTORY;
-  const int nb = plan.blocks > 1 ? plan.blocks : 1;
+  const Sizing z = sizing_of(h);
+  const int nb = z.nb;
   const int block_k = plan.kw * plan.waves_k;  // prototypes per block (one partial slot)
-  // a partial slot: the block_k x d accumulator, plus per-prototype maxima and sums for the comparator
-  const size_t slot_bytes = (size_t)block_k * (plan.d + (hist ? 2 : 0)) * sizeof(float);
-  // two-phase statistics: per-block and merged log-sum-exp of every row
-  auto stats_bytes = [&](int64_t rows) {
-    return nb > 1 && !hist ? (size_t)(nb + 1) * (size_t)rows * sizeof(float) : 0;
-  };
-  // work groups per prototype block for a launch of `rows` rows (the grid is nb times that)
-  auto launch_groups = [&](int64_t rows) {
-    if (rows <= 0) return 0;
-    const int g = groups_for(h, rows);
-    return nb > 1 ? (g + nb - 1) / nb : g;
-  };
+  const size_t slot_bytes = z.slot_bytes;
+  // a frozen handle's workspace is fixed: launches are sized to fit it
+  if (fixed_ws == nullptr && h->frozen) {
+    fixed_ws = h->workspace;
+    fixed_bytes = h->workspace_bytes;
+    allow_timing = true;
+  } else if (fixed_ws == nullptr) {
+    allow_timing = true;
+  }
 
   struct LaunchPlan {
     int32_t u0, nu;
@@ -396,8 +425,8 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
   for (int32_t u0 = 0; u0 < num_users;) {
     int32_t nu = num_users - u0 < sa::kMaxUsersPerLaunch ? num_users - u0 : sa::kMaxUsersPerLaunch;
     int64_t rows = offsets[u0 + nu] - offsets[u0];
-    int g = launch_groups(rows);
-    auto bytes_of = [&](int gg, int32_t n, int64_t r) { return (size_t)nb * (gg + n) * slot_bytes + stats_bytes(r); };
+    int g = launch_groups(h, z, rows);
+    auto bytes_of = [&](int gg, int32_t n, int64_t r) { return launch_bytes(z, gg, n, r); };
     if (fixed_ws != nullptr) {
       // the most users (up to the launch limit) that fit with at least one group each
       while (nu > 1 && bytes_of(1, nu, rows) > fixed_bytes) {
@@ -405,8 +434,8 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
         rows = offsets[u0 + nu] - offsets[u0];
       }
       if (bytes_of(rows > 0 ? 1 : 0, nu, rows) > fixed_bytes) return SA_ERR_UNSUPPORTED;
-      g = launch_groups(rows);
-      const int64_t room = (int64_t)((fixed_bytes - stats_bytes(rows)) / slot_bytes) / nb - nu;
+      g = launch_groups(h, z, rows);
+      const int64_t room = (int64_t)((fixed_bytes - stats_bytes(z, rows)) / slot_bytes) / nb - nu;
       if (g > room) g = (int)room;
     }
     launches.push_back({u0, nu, g, bytes_of(g, nu, rows)});
@@ -474,7 +503,7 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
     }
 
     TimingSlot ts{};
-    const bool timed = h->timing && fixed_ws == nullptr;
+    const bool timed = h->timing && allow_timing;
     if (timed) {
       ts = take_slot(h);
       ts.fused = rows > 0;
@@ -516,6 +545,33 @@ SA_API sa_status sa_compress_batch_noalloc(sa_handle h, const void* X, const int
   float* ws = nullptr;
   if (sa::noalloc_scratch(h->device, &ws) != hipSuccess) return SA_ERR_DEVICE;
   return compress(h, X, offsets, num_users, out, stream, h->M, 0, ws, sa::kNoAllocScratchBytes);
+}
+
+SA_API sa_status sa_reserve(sa_handle h, int64_t max_rows, int32_t max_users, int32_t freeze, void* stream) {
+  if (h == nullptr || max_rows < 0 || max_rows > INT32_MAX || max_users < 0) return SA_ERR_INVALID_ARG;
+  DeviceGuard guard(h->device);
+  // the largest launch a call within the bounds forms: all its rows (groups grow with rows) and up to the
+  // launch limit of users
+  const Sizing z = sizing_of(h);
+  const int32_t nu = max_users < sa::kMaxUsersPerLaunch ? max_users : sa::kMaxUsersPerLaunch;
+  const size_t need = launch_bytes(z, launch_groups(h, z, max_rows), nu, max_rows);
+  if (need > h->workspace_bytes) {
+    if (h->workspace) {
+      if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SA_ERR_DEVICE;
+      (void)hipFree(h->workspace);
+      h->workspace = nullptr;
+      h->workspace_bytes = 0;
+    }
+    if (hipMalloc(&h->workspace, need) != hipSuccess) {
+      h->workspace = nullptr;
+      h->frozen = false;
+      return SA_ERR_OUT_OF_MEMORY;
+    }
+    h->workspace_bytes = need;
+  }
+  // a frozen handle with no workspace yet (both bounds 0) keeps growing on demand
+  h->frozen = freeze != 0 && h->workspace != nullptr;
+  return SA_OK;
 }
 
 SA_API sa_status sa_get_folded(sa_handle h, float* dst, void* stream) {

@@ -211,3 +211,8 @@ def test_action_entry_points_validate_before_device_work():
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.sa_action_read_kernel_timing(None, ctypes.byref(ms), ctypes.byref(n)) == B.SA_ERR_INVALID_ARG
     lib.sa_action_destroy(None)
+
+
+def test_reserve_rejects_a_null_handle_and_bad_bounds():
+    lib = B.library()
+    assert lib.sa_reserve(None, 100, 2, 1, None) == B.SA_ERR_INVALID_ARG
