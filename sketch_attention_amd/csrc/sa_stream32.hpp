@@ -43,8 +43,12 @@
 // The operands of each product are read ahead of it (one d-chunk for the
 // affinity, one row step for the aggregation).  A row whose sum leaves
 // [2^-100, 2^100] sends the wave through an exact pass (a running maximum
-// over all prototypes, M from global memory).  The two-phase modes
-// (FusedArgs::lse_mode) are those of sa_stream.hpp.
+// over all prototypes, M from global memory).  Modes (FusedArgs::lse_mode):
+// 0 one pass; 1 and 2 the two phases of the pass for more prototypes than
+// one work group holds -- phase 1 writes every row's log-sum-exp over one
+// block of prototypes, phase 2 takes the row's log-sum-exp over all
+// prototypes (merged between the phases) as given, so its weights are
+// 2^(s' - L) with no exchange between waves, and aggregates one block.
 #pragma once
 
 #include "sa_stream.hpp"

@@ -278,41 +278,39 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
   float part[2][4];
   auto softmax_piece = [&](f32x16 (&s)[2], int i, int par) {
     const int sl = i >> 1;
-    {
-      if ((i & 1) == 0) {
+    if ((i & 1) == 0) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            s[f][4 * sl + p] = fast_exp2(s[f][4 * sl + p]);
-            s[f][8 + 4 * sl + p] = fast_exp2(s[f][8 + 4 * sl + p]);
-          }
-      } else {
-        float x0[4], x1[4], y0[4], y1[4], o0[4], o1[4];
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          x0[p] = s[0][4 * sl + p];
-          y0[p] = s[1][4 * sl + p];
-          x1[p] = s[0][8 + 4 * sl + p];
-          y1[p] = s[1][8 + 4 * sl + p];
+          s[f][4 * sl + p] = fast_exp2(s[f][4 * sl + p]);
+          s[f][8 + 4 * sl + p] = fast_exp2(s[f][8 + 4 * sl + p]);
         }
-        fold_bit3(o0, x0, y0);  // q = sl: rows of block b3
-        fold_bit3(o1, x1, y1);  // q = 2 + sl
-        fold_bit2(part[sl], o0, o1);
-        if (i == 3) {
-          float r3[4];
+    } else {
+      float x0[4], x1[4], y0[4], y1[4], o0[4], o1[4];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) r3[p] = fold_bit4(part[0][p], part[1][p]);
-          const bool c1 = (lane & 2) != 0, c0 = (lane & 1) != 0;
-          float r4[2];
+      for (int p = 0; p < 4; ++p) {
+        x0[p] = s[0][4 * sl + p];
+        y0[p] = s[1][4 * sl + p];
+        x1[p] = s[0][8 + 4 * sl + p];
+        y1[p] = s[1][8 + 4 * sl + p];
+      }
+      fold_bit3(o0, x0, y0);  // q = sl: rows of block b3
+      fold_bit3(o1, x1, y1);  // q = 2 + sl
+      fold_bit2(part[sl], o0, o1);
+      if (i == 3) {
+        float r3[4];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float keep = c1 ? r3[2 + e] : r3[e], send = c1 ? r3[e] : r3[2 + e];
-            r4[e] = keep + dpp_f32<0x4E>(send);  // quad_perm [2,3,0,1]: lane ^ 2
-          }
-          const float keep = c0 ? r4[1] : r4[0], send = c0 ? r4[0] : r4[1];
-          xl[xl_at(par, my_row, wj)] = keep + dpp_f32<0xB1>(send);  // quad_perm [1,0,3,2]: lane ^ 1
+        for (int p = 0; p < 4; ++p) r3[p] = fold_bit4(part[0][p], part[1][p]);
+        const bool c1 = (lane & 2) != 0, c0 = (lane & 1) != 0;
+        float r4[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float keep = c1 ? r3[2 + e] : r3[e], send = c1 ? r3[e] : r3[2 + e];
+          r4[e] = keep + dpp_f32<0x4E>(send);  // quad_perm [2,3,0,1]: lane ^ 2
         }
+        const float keep = c0 ? r4[1] : r4[0], send = c0 ? r4[0] : r4[1];
+        xl[xl_at(par, my_row, wj)] = keep + dpp_f32<0xB1>(send);  // quad_perm [1,0,3,2]: lane ^ 1
       }
     }
   };
