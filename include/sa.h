@@ -413,6 +413,23 @@ sa_status sa_action_create(sa_action* out, int32_t d, int32_t d_a, int32_t d_ff,
  */
 sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actions, int64_t rows, void* X, void* stream);
 
+/*
+ * sa_action_compress_batch -- out[u] = the sketch (as sa_compress_batch on h)
+ * of the rows x_i of user u, formed from E and actions inside the sketch
+ * kernel: X is never written to memory (section 2.2 builds the rows the
+ * compression of section 2.1 reads; section 2.4 fuses the pass).  E and
+ * actions are as for sa_action_fuse, with offsets[num_users] rows, packed as
+ * the rows of sa_compress_batch; offsets, out, num_users and the workspace,
+ * timing and stream rules are those of sa_compress_batch on h, whose kernel
+ * timing covers the fused kernel.  The result equals sa_action_fuse followed
+ * by sa_compress_batch bit for bit.
+ * SA_ERR_UNSUPPORTED (nothing enqueued) unless d = 128, h and a are on the
+ * same device and h uses the one-pass plan of eight waves of 32 prototypes:
+ * SA_BF16, d = 128, 128 < k <= 256, softmax over the prototypes.
+ */
+sa_status sa_action_compress_batch(sa_action a, sa_handle h, const void* E, const int32_t* actions,
+                                   const int64_t* offsets, int32_t num_users, float* out, void* stream);
+
 /* HIP events on the pass's dispatch (as for sa_set_kernel_timing): total
  * milliseconds and launches since the last read. */
 sa_status sa_action_set_kernel_timing(sa_action h, int32_t enable);

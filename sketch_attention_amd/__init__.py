@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     SketchAttentionGrad,
     SketchStack,
     sa_action_check_config,
+    sa_action_compress_batch,
     sa_action_create,
     sa_action_destroy,
     sa_action_fuse,

@@ -41,7 +41,7 @@ EXPORTED = (
     "sa_stack_read_kernel_timing",
     "sa_grad_check_config", "sa_grad_create", "sa_grad_compute", "sa_grad_destroy", "sa_grad_set_kernel_timing",
     "sa_grad_read_kernel_timing",
-    "sa_action_check_config", "sa_action_create", "sa_action_fuse", "sa_action_destroy",
+    "sa_action_check_config", "sa_action_create", "sa_action_fuse", "sa_action_compress_batch", "sa_action_destroy",
     "sa_action_set_kernel_timing", "sa_action_read_kernel_timing",
     "sa_measure_ceilings",
 )
@@ -126,6 +126,7 @@ def library() -> ctypes.CDLL:
         "sa_action_check_config": (i32, [i32, i32, i32, i32, i32]),
         "sa_action_create": (i32, [ctypes.POINTER(vp), i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "sa_action_fuse": (i32, [vp, vp, vp, i64, vp, vp]),
+        "sa_action_compress_batch": (i32, [vp, vp, vp, vp, vp, i32, vp, vp]),
         "sa_action_destroy": (None, [vp]),
         "sa_action_set_kernel_timing": (i32, [vp, i32]),
         "sa_action_read_kernel_timing": (i32, [vp, p_f64, p_i64]),
@@ -684,6 +685,28 @@ def sa_action_fuse(handle: ctypes.c_void_p, E: torch.Tensor, actions: torch.Tens
                                     stream.cuda_stream), "sa_action_fuse")
 
 
+def sa_action_compress_batch(action: ctypes.c_void_p, handle: ctypes.c_void_p, E: torch.Tensor,
+                             actions: torch.Tensor, offsets, out: torch.Tensor,
+                             stream: Optional[torch.cuda.Stream] = None) -> None:
+    """out[u] = the sketch of user u's rows x_i = e_i + FFN([e_i; a_i]), formed inside the sketch kernel
+    (X never written; see include/sa.h)."""
+    ainfo = _info(action, "action")
+    offs = _offsets_array(offsets)
+    if offs.ndim != 1 or offs.size < 1:
+        raise ValueError("offsets must be a 1-D array of length num_users + 1")
+    if E.dim() != 2 or E.shape[1] != ainfo["d"] or E.dtype != ainfo["dtype"]:
+        raise ValueError(f"E must be [rows, {ainfo['d']}] {ainfo['dtype']}")
+    if actions.dtype != torch.int32 or actions.dim() != 1 or actions.shape[0] != E.shape[0]:
+        raise ValueError("actions must be int32 [rows]")
+    _check_batch_tensors(_info(handle, "sa"), E, offs, out)
+    _device_tensor(actions, "actions")
+    if stream is None:
+        stream = torch.cuda.current_stream(E.device)
+    _check(library().sa_action_compress_batch(action, handle, E.data_ptr(), actions.data_ptr(), offs.ctypes.data,
+                                              offs.size - 1, out.data_ptr(), stream.cuda_stream),
+           "sa_action_compress_batch")
+
+
 def sa_action_destroy(handle: Optional[ctypes.c_void_p]) -> None:
     if handle is not None and handle.value:
         _forget(handle)
@@ -715,6 +738,15 @@ class ActionFusion:
         if out is None:
             out = torch.empty_like(E)
         sa_action_fuse(self.handle, E, actions, out, stream)
+        return out
+
+    def compress(self, sa: "SketchAttention", E: torch.Tensor, actions: torch.Tensor, offsets,
+                 out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """The sketches ([U, k, d] float32) of the fused rows, without writing X."""
+        offs = _offsets_array(offsets)
+        if out is None:
+            out = torch.empty((offs.size - 1, sa.k, sa.d), dtype=torch.float32, device=E.device)
+        sa_action_compress_batch(self.handle, sa.handle, E, actions, offs, out, stream)
         return out
 
     def close(self) -> None:

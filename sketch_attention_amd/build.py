@@ -34,6 +34,7 @@ SOURCES = [
     "sa_grad.hip",
     "sa_grad_api.cpp",
     "sa_action.hip",
+    "sa_action_sa.hip",
     "sa_action_api.cpp",
     "sa_ceilings.hip",
 ]

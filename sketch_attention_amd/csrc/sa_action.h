@@ -1,10 +1,13 @@
-// Internal interface of the action-fusion pass (sa_action.hip,
-// sa_action_api.cpp).  Not part of the public ABI.
+// Internal interface of the action-fusion passes (sa_action.hip,
+// sa_action_sa.hip, sa_action_api.cpp).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include "sa.h"
+#include "sa_internal.h"
 
 namespace sa {
 
@@ -31,5 +34,40 @@ hipError_t launch_action_pack(int d, int kp, const void* Wg, const void* Wu, con
 hipError_t launch_action_fuse(int d, int kp, const ActionArgs& a, int groups, hipStream_t stream,
                               hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t action_occupancy(int d, int kp, int* groups_per_cu);
+
+// The action fusion as the prologue of the one-pass sketch kernel of eight
+// waves of 32 prototypes (sa_action_sa.hip): sa as for that kernel with
+// sa.X unused; E and actions start at the launch's first row.
+struct ActSaArgs {
+  FusedArgs sa;
+  const void* E;           // bf16 [rows][128]
+  const int32_t* actions;  // [rows]
+  const void* table;       // bf16 [n_actions][d_a]
+  const void* packed;      // packed weight chunks (launch_action_pack)
+  int32_t n_actions;
+  int32_t d_a;
+  int32_t chunks;          // d_ff / 32
+};
+// kp: 128, 192 or 256 (action_kpad(128, d_a)).  occ != nullptr: report the work
+// groups that fit on a compute unit instead of launching.
+hipError_t launch_action_sa(int kp, const ActSaArgs& a, const Launch& l, int* occ = nullptr);
+
+// Where the fused variant takes its rows from, for the sketch handle's batch
+// loop (sa_api.cpp).
+struct ActionSource {
+  const void* E;
+  const int32_t* actions;
+  const void* table;
+  const void* packed;
+  int32_t n_actions, d_a, d_ff, kp;
+  int device;  // of the action handle
+};
+// The sketch of the fused rows of a packed batch into out [U][k][d]: the
+// batch loop of sa_compress_batch with the fused kernel in place of the
+// sketch kernel.  SA_ERR_UNSUPPORTED unless the handle's plan is the one-pass
+// plan of eight waves of 32 prototypes (bf16, d = 128, 128 < k <= 256,
+// softmax over the prototypes) on src.device.
+sa_status compress_actions(sa_handle h, const ActionSource& src, const int64_t* offsets, int32_t num_users,
+                           float* out, void* stream);
 
 }  // namespace sa

@@ -4,29 +4,18 @@
 //   x_i = e_i + (silu(z_i W_gate) * (z_i W_up)) W_down,   z_i = [e_i ; a_i],
 //
 // e_i the item embedding, a_i = table[action_i] the action-type embedding.
-// One pass over the rows; waves own rows, the weights stream through LDS:
-//
-//   8 waves x 32 rows per 256-row tile.  z for the wave's rows is built in
-//   registers as matrix-core B operands (rows along the lanes, 8 consecutive
-//   features per lane group): fragments of e_i from HBM, of a_i from the
-//   (cache-resident) table, zero past d + d_a (K padded to a multiple of 64).
-//   The FFN width is walked in chunks of 32 whose weights (W_gate and W_up
-//   transposed, W_down transposed with its rows permuted) are packed once
-//   and arrive by LDS DMA, double-buffered.  Per chunk:
-//     gate^T, up^T  = W^T z^T        (A = weight rows, B = z: rows on lanes)
-//     H = silu(gate) * up            in registers, already in the B-operand
-//                                    layout of the next product: the 16x16
-//                                    output puts chunk column 16 (e/4) + 4 g
-//                                    + e%4 in slot (g, e) of row l16
-//     x^T          += W_down^T H^T   (A = W_down^T rows permuted to match)
-//   and x = e + (x^T)^T is stored in bf16, eight columns per lane, e_i taken
-//   from the z fragments (the W_down^T row order lines the output columns up
-//   with them).  A tile's action ids and, where the registers allow, its E
-//   fragments are loaded while the previous tile runs.
+// One pass over the rows, writing X; waves own rows, the weights stream
+// through LDS.  8 waves x 32 rows per 256-row tile; z for the wave's rows is
+// built in registers (fragments of e_i from HBM, of a_i from the
+// cache-resident table, zero past d + d_a, K padded to a multiple of 64) and
+// the FFN runs chunk by chunk as sa_action_ffn.hpp describes, the chunks
+// arriving by LDS DMA, double-buffered.  x = e + (x^T)^T is stored in bf16,
+// eight columns per lane.  A tile's action ids and, where the registers
+// allow, its E fragments are loaded while the previous tile runs.
 #include <hip/hip_runtime.h>
 
 #include "sa_action.h"
-#include "sa_stream.hpp"
+#include "sa_action_ffn.hpp"
 
 namespace sa {
 
@@ -34,20 +23,11 @@ namespace {
 
 constexpr int kActWaves = 8;
 
-// Byte layout of one packed chunk (32 FFN columns): W_gate^T block [32][KP],
-// W_up^T block [32][KP] (16-byte chunk h of row f at h ^ (f % 8)), then the
-// W_down^T block [D][32]: row 16 cb + i holds output column
-// oc = 32 (cb / 2) + 4 (cb % 2) + 8 (i / 4) + i % 4, W_down[32 c0 + perm(pos)][oc]
-// at position pos = 8 g + e, perm = 16 (e / 4) + 4 g + e % 4; chunk g stored
-// at g ^ 2 ((row / 8) % 2).  The row order puts output column 32 ks + 8 g + e
-// in accumulator (cb = 2 ks + e / 4, register e % 4) of lane group g: the
-// lane's z fragment for K slots 32 ks + 8 g .. + 7, so the residual e_i is
-// added from registers and stored as 16-byte pieces.
+// The packed chunk layout is that of ActChunk (sa_action_ffn.hpp); two steps'
+// buffers of CPS chunks each fit in LDS.
 template <int D, int KP>
-struct ActGeom {
-  static constexpr int W_BYTES = 32 * KP * 2;
-  static constexpr int D_BYTES = D * 32 * 2;
-  static constexpr int CHUNK = 2 * W_BYTES + D_BYTES;
+struct ActGeom : ActChunk<D, KP> {
+  using ActChunk<D, KP>::CHUNK;
   static constexpr int CPS = 4 * CHUNK <= 144 * 1024 ? 2 : 1;  // chunks per step (two steps' buffers in LDS)
   static constexpr int STEP = CPS * CHUNK;
   static_assert(STEP % 1024 == 0, "whole DMA blocks");
@@ -86,7 +66,6 @@ __global__ __launch_bounds__(256) void action_pack_kernel(const bf16* Wg, const 
 template <int D, int KP>
 __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs args) {
   using G = ActGeom<D, KP>;
-  using MF = Mfma<bf16>;
   constexpr int NT = 32 * kActWaves, KS = KP / 32, CB = D / 16, CPS = G::CPS;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * G::STEP];
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
@@ -113,12 +92,7 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
         dma16(src, (uint32_t)(1024 * j + 16 * lane), lds0 + (uint32_t)(b * G::STEP + 1024 * j));
     }
   };
-  // fragment offsets: weight row 16 fb + l16, chunk 4 ks + g (swizzled by the row's low bits);
-  // W_down^T row 16 cb + l16, chunk g
-  uint32_t woff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) woff[ks] = (uint32_t)(2 * (l16 * KP + 8 * ((4 * ks + g) ^ (l16 & 7))));
-  const uint32_t doff = (uint32_t)(2 * 2 * 32 * KP + 2 * (l16 * 32 + 8 * (g ^ (2 * ((l16 >> 3) & 1)))));
+  const FfnOffsets<D, KP> fo = ffn_offsets<D, KP>(l16, g);
 
   // action ids of a tile's rows (this lane's rows 16 ib + l16 of the wave), loaded a tile ahead so that the
   // table rows they select do not wait for them
@@ -195,76 +169,20 @@ __global__ __launch_bounds__(64 * kActWaves) void action_fuse_kernel(ActionArgs 
       else if (!last_tile) issue_step(0, q ^ 1);
       if (busy) {
 #pragma unroll
-        for (int h = 0; h < CPS; ++h) {
-          const uint32_t buf = lds0 + (uint32_t)(q * G::STEP + h * G::CHUNK);
-          // gate^T and up^T: [fb][ib] holds column 16 fb + 4 g + r of the chunk for row 16 ib + l16.
-          // Unit p = 2 ks + fb (its W_gate^T and W_up^T fragments, four MFMAs),
-          // fragments loaded PD units ahead behind scheduling fences, so the
-          // LDS latency hides under the MFMAs of the units in between.
-          constexpr int NU = 2 * KS, PD = 3;
-          f32x4 ga[2][2], ua[2][2];
-          bf16x8 wg[NU], wu[NU];
-          auto load = [&](int p) {
-            const uint32_t o = woff[p >> 1] + (uint32_t)(2 * 16 * (p & 1) * KP);
-            wg[p] = lds_b128(buf + o);
-            wu[p] = lds_b128(buf + (uint32_t)G::W_BYTES + o);
-          };
-#pragma unroll
-          for (int p = 0; p < PD; ++p) load(p);
-#pragma unroll
-          for (int p = 0; p < NU; ++p) {
-            if (p + PD < NU) load(p + PD);
-            __builtin_amdgcn_sched_barrier(0);
-            const int ks = p >> 1, fb = p & 1;
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-              const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-              ga[fb][ib] = MF::run(wg[p], zf[ib][ks], ks == 0 ? z : ga[fb][ib]);
-              ua[fb][ib] = MF::run(wu[p], zf[ib][ks], ks == 0 ? z : ua[fb][ib]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          // the W_down^T fragments of this chunk, issued before the H arithmetic
-          bf16x8 wd[CB];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) wd[cb] = lds_b128(buf + doff + (uint32_t)(2 * 16 * cb * 32));
-          // H = silu(gate) * up, slot (g, e) <-> column 16 (e / 4) + 4 g + e % 4
-          bf16x8 hf[2];
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib) {
-            float hv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float gv = ga[e >> 2][ib][e & 3];
-              hv[e] = gv * __builtin_amdgcn_rcpf(1.f + fast_exp2(-1.4426950408889634f * gv)) * ua[e >> 2][ib][e & 3];
-            }
-            typedef float f32x8 __attribute__((ext_vector_type(8)));
-            hf[ib] = __builtin_convertvector((f32x8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]}), bf16x8);
-          }
-          // x^T[16 cb + 4 g + r][row 16 ib + l16] += W_down^T H^T over the chunk
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) acc[ib][cb] = MF::run(wd[cb], hf[ib], acc[ib][cb]);
-        }
+        for (int h = 0; h < CPS; ++h) ffn_chunk<D, KP, 2>(lds0 + (uint32_t)(q * G::STEP + h * G::CHUNK), fo, zf, acc);
       }
       wait_vm<0>();
       __syncthreads();
       q ^= 1;
     }
-    // x = e + FFN: this lane holds columns 32 ks + 8 g .. + 7 of row 16 ib + l16, the FFN part in
-    // accumulators 2 ks and 2 ks + 1, e_i in z fragment ks
+    // x = e + FFN: this lane holds columns 32 ks + 8 g .. + 7 of row 16 ib + l16
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       if (!valid[ib]) continue;
       const int64_t row = t0 + rw + 16 * ib + l16;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)zf[ib][ks][e] + acc[ib][2 * ks + (e >> 2)][e & 3]);
-        *reinterpret_cast<bf16x8*>(X + row * D + 32 * ks + 8 * g) = v;
-      }
+      for (int ks = 0; ks < D / 32; ++ks)
+        *reinterpret_cast<bf16x8*>(X + row * D + 32 * ks + 8 * g) = ffn_residual<D, KP, 2>(zf, acc, ib, ks);
     }
   }
   wait_vm<0>();

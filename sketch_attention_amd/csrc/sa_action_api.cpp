@@ -156,6 +156,15 @@ SA_API sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actio
   return e == hipSuccess ? SA_OK : SA_ERR_DEVICE;
 }
 
+SA_API sa_status sa_action_compress_batch(sa_action a, sa_handle h, const void* E, const int32_t* actions,
+                                          const int64_t* offsets, int32_t num_users, float* out, void* stream) {
+  if (a == nullptr || h == nullptr) return SA_ERR_INVALID_ARG;
+  if (a->d != 128) return SA_ERR_UNSUPPORTED;
+  DeviceGuard guard(a->device);
+  sa::ActionSource src{E, actions, a->table, a->packed, a->n_actions, a->d_a, a->d_ff, a->kp, a->device};
+  return sa::compress_actions(h, src, offsets, num_users, out, stream);
+}
+
 SA_API sa_status sa_action_set_kernel_timing(sa_action h, int32_t enable) {
   if (h == nullptr) return SA_ERR_INVALID_ARG;
   h->timing = enable != 0;

@@ -14,6 +14,7 @@
 #include <new>
 #include <vector>
 
+#include "sa_action.h"
 #include "sa_internal.h"
 
 #define SA_API extern "C" __attribute__((visibility("default")))
@@ -389,15 +390,23 @@ size_t launch_bytes(const Sizing& z, int groups, int32_t nu, int64_t rows) {
   return (size_t)z.nb * (groups + nu) * z.slot_bytes + stats_bytes(z, rows);
 }
 
+// act: the rows are formed by the action fusion from act->E and act->actions
+// inside the sketch kernel (X unused); the handle's plan must be the one-pass
+// plan of eight waves of 32 prototypes.
 sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_t num_users, float* out, void* stream,
                    const void* M, int64_t m_stride, float* fixed_ws = nullptr, size_t fixed_bytes = 0,
-                   bool allow_timing = false) {
+                   bool allow_timing = false, const sa::ActionSource* act = nullptr) {
   if (h == nullptr) return SA_ERR_INVALID_ARG;
   sa_status st = check_batch(offsets, num_users);
   if (st != SA_OK) return st;
   if (num_users == 0) return SA_OK;
   const int64_t total = offsets[num_users];
   if (out == nullptr || !aligned16(out)) return SA_ERR_INVALID_ARG;
+  if (act != nullptr) {
+    X = act->E;
+    if (total > 0 && (act->actions == nullptr || (reinterpret_cast<uintptr_t>(act->actions) & 3u) != 0))
+      return SA_ERR_INVALID_ARG;
+  }
   if (total > 0 && (X == nullptr || !aligned16(X))) return SA_ERR_INVALID_ARG;
 
   const Plan& plan = h->plan;
@@ -519,7 +528,22 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
         fa.lse_mode = 2;
         fa.stats = stats_m;
       }
-      if (sa::launch_fused(plan, fa, nb * groups, s, ts.ev[0], ts.ev[1]) != hipSuccess) return SA_ERR_DEVICE;
+      if (act != nullptr) {
+        sa::ActSaArgs aa;
+        aa.sa = fa;
+        aa.sa.X = nullptr;
+        aa.E = fa.X;
+        aa.actions = act->actions + base;
+        aa.table = act->table;
+        aa.packed = act->packed;
+        aa.n_actions = act->n_actions;
+        aa.d_a = act->d_a;
+        aa.chunks = act->d_ff / 32;
+        if (sa::launch_action_sa(act->kp, aa, sa::Launch{groups, s, ts.ev[0], ts.ev[1]}) != hipSuccess)
+          return SA_ERR_DEVICE;
+      } else if (sa::launch_fused(plan, fa, nb * groups, s, ts.ev[0], ts.ev[1]) != hipSuccess) {
+        return SA_ERR_DEVICE;
+      }
     }
     if (sa::launch_reduce(ra, s, ts.ev[2], ts.ev[3]) != hipSuccess) return SA_ERR_DEVICE;
     if (timed) h->slots.push_back(ts);
@@ -528,6 +552,20 @@ sa_status compress(sa_handle_s* h, const void* X, const int64_t* offsets, int32_
 }
 
 }  // namespace
+
+namespace sa {
+
+sa_status compress_actions(sa_handle h, const ActionSource& src, const int64_t* offsets, int32_t num_users,
+                           float* out, void* stream) {
+  if (h == nullptr) return SA_ERR_INVALID_ARG;
+  const Plan& p = h->plan;
+  if (p.kind != 3 || p.blocks != 1 || h->norm != SA_NORM_PROTOTYPES || p.d != 128 || p.dtype != SA_BF16 ||
+      (src.kp != 128 && src.kp != 192 && src.kp != 256) || src.d_ff % 32 != 0 || src.device != h->device)
+    return SA_ERR_UNSUPPORTED;
+  return compress(h, nullptr, offsets, num_users, out, stream, h->M, 0, nullptr, 0, false, &src);
+}
+
+}  // namespace sa
 
 SA_API sa_status sa_compress_batch(sa_handle h, const void* X, const int64_t* offsets, int32_t num_users, float* out,
                                    void* stream) {

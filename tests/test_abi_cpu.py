@@ -216,3 +216,9 @@ def test_action_entry_points_validate_before_device_work():
 def test_reserve_rejects_a_null_handle_and_bad_bounds():
     lib = B.library()
     assert lib.sa_reserve(None, 100, 2, 1, None) == B.SA_ERR_INVALID_ARG
+
+
+def test_action_compress_rejects_null_handles():
+    lib = B.library()
+    offs = (ctypes.c_int64 * 2)(0, 0)
+    assert lib.sa_action_compress_batch(None, None, None, None, offs, 1, None, None) == B.SA_ERR_INVALID_ARG
