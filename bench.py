@@ -312,10 +312,12 @@ def action_cpu_baseline(inp, wl, budget_s: float):
 
 
 def run_actions(args, wl, dev) -> int:
-    """One step = the action fusion over every row (E, action ids -> X in HBM)
-    followed by one compression of X.  The roofline is the fusion pass's, on
-    2 (2 (d + d_a) d_ff + d_ff d) FLOP per row; the two passes are separate
-    launches (X is written once and read once)."""
+    """One step = the action fusion over every row followed by one compression
+    of the rows.  --action-path two-pass: the fusion pass writes X to HBM and
+    the sketch pass reads it (two launches); the roofline is the fusion
+    pass's, on 2 (2 (d + d_a) d_ff + d_ff d) FLOP per row.  fused: one kernel
+    forms the rows in LDS and sketches them (X never written); its roofline
+    is on those FLOP plus the sketch's 4 k d per row."""
     from sketch_attention_amd import ActionFusion, SketchAttention, binding, workloads
 
     d, d_a, d_ff, n_act = wl.d, args.d_a, args.d_ff or 2 * wl.d, args.n_actions
@@ -333,9 +335,14 @@ def run_actions(args, wl, dev) -> int:
     offs = np.ascontiguousarray(wl.offsets, dtype=np.int64)
     stream = torch.cuda.current_stream(dev)
 
+    fused = args.action_path == "fused"
+
     def step(i):
-        binding.sa_action_fuse(af.handle, Es[i % copies], acts, X, stream)
-        binding.sa_compress_batch(sa.handle, X, offs, out, stream)
+        if fused:
+            binding.sa_action_compress_batch(af.handle, sa.handle, Es[i % copies], acts, offs, out, stream)
+        else:
+            binding.sa_action_fuse(af.handle, Es[i % copies], acts, X, stream)
+            binding.sa_compress_batch(sa.handle, X, offs, out, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -362,13 +369,21 @@ def run_actions(args, wl, dev) -> int:
     n = wl.total_rows
     a_us, f_us = a_ms * 1e3 / max(a_n, 1), f_ms * 1e3 / max(f_n, 1)
     a_flop = 2.0 * (2.0 * (d + d_a) * d_ff + d_ff * d) * n
-    a_tf = a_flop / (a_us * 1e-6) / 1e12 if a_us > 0 else 0.0
     ms_per_step = elapsed * 1e3 / args.steps
-    log(f"[bench] actions: fusion pass {a_us:.2f} us ({a_tf:.1f} TFLOP/s), fused SA pass {f_us:.2f} us; whole step "
-        f"{ms_per_step * 1e3:.2f} us (d_a={d_a}, d_ff={d_ff}, {n_act} action types)")
-    roof = {"bound": "mfma", "achieved": round(a_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "action_fuse_kernel",
-            "kernel_avg_us": round(a_us, 2)}
+    if fused:
+        flop = a_flop + 4.0 * wl.k * d * n
+        tf = flop / (f_us * 1e-6) / 1e12 if f_us > 0 else 0.0
+        log(f"[bench] actions (fused prologue): action + sketch kernel {f_us:.2f} us ({tf:.1f} TFLOP/s on the FFN and "
+            f"sketch FLOP); whole step {ms_per_step * 1e3:.2f} us (d_a={d_a}, d_ff={d_ff}, {n_act} action types)")
+        kern, k_us = "action_sa_kernel", f_us
+    else:
+        tf = a_flop / (a_us * 1e-6) / 1e12 if a_us > 0 else 0.0
+        log(f"[bench] actions: fusion pass {a_us:.2f} us ({tf:.1f} TFLOP/s), fused SA pass {f_us:.2f} us; whole step "
+            f"{ms_per_step * 1e3:.2f} us (d_a={d_a}, d_ff={d_ff}, {n_act} action types)")
+        kern, k_us = "action_fuse_kernel", a_us
+    roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": kern,
+            "kernel_avg_us": round(k_us, 2)}
     cpu = None if args.no_cpu_baseline else action_cpu_baseline(inp, wl, args.cpu_budget)
     if cpu:
         log(f"[bench] cpu baseline: {cpu}")
@@ -378,7 +393,8 @@ def run_actions(args, wl, dev) -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.num_users} users x n={n // max(wl.num_users, 1)}, d={d}, k={wl.k}, "
-                               f"{wl.dtype}, action fusion d_a={d_a} d_ff={d_ff}", "users": wl.num_users, "rows": n,
+                               f"{wl.dtype}, action fusion d_a={d_a} d_ff={d_ff} ({args.action_path})",
+                   "users": wl.num_users, "rows": n, "action_path": args.action_path,
                    "d": d, "k": wl.k, "d_a": d_a, "d_ff": d_ff, "n_actions": n_act, "parallelism": "single-gpu"},
         "roofline": roof, "cpu_baseline": cpu,
     }
@@ -404,6 +420,8 @@ def main() -> int:
     ap.add_argument("--actions", action="store_true",
                     help="build the rows by the action fusion (x = e + SwiGLU-FFN([e; a])) before each compression")
     ap.add_argument("--d-a", type=int, default=64, help="action embedding width for --actions")
+    ap.add_argument("--action-path", choices=["two-pass", "fused"], default="two-pass",
+                    help="--actions: X through HBM between two passes, or formed inside the sketch kernel")
     ap.add_argument("--n-actions", type=int, default=8, help="action types for --actions")
     ap.add_argument("--grad", action="store_true",
                     help="time the backward pass (gradients w.r.t. X, P, W_Q, W_K) instead of the compression")
