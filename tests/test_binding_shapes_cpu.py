@@ -104,3 +104,16 @@ def test_action_rejects_mismatched_tensors(handles, E, acts, X, what):
 def test_folded_buffer_shape(handles):
     with pytest.raises(ValueError, match="dst must be"):
         B.sa_get_folded(handles["sa"], torch.zeros((K, D - 1)))
+
+
+@pytest.mark.parametrize("E,acts,out,what", [
+    (_x(10, 32), torch.zeros(10, dtype=torch.int32), torch.zeros((2, K, D)), "E must be"),         # narrow rows
+    (_x(10, dt=torch.float32), torch.zeros(10, dtype=torch.int32), torch.zeros((2, K, D)), "E must be"),
+    (_x(10), torch.zeros(10, dtype=torch.int64), torch.zeros((2, K, D)), "actions must be"),       # id dtype
+    (_x(10), torch.zeros(9, dtype=torch.int32), torch.zeros((2, K, D)), "actions must be"),        # id count
+    (_x(9), torch.zeros(9, dtype=torch.int32), torch.zeros((2, K, D)), "X must be"),               # rows vs offsets
+    (_x(10), torch.zeros(10, dtype=torch.int32), torch.zeros((2, K - 1, D)), "out must be"),       # sketch buffer
+])
+def test_action_compress_rejects_mismatched_tensors(handles, E, acts, out, what):
+    with pytest.raises(ValueError, match=what):
+        B.sa_action_compress_batch(handles["action"], handles["sa"], E, acts, OFFS, out)
