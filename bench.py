@@ -610,14 +610,15 @@ def measured_ceilings() -> dict:
     `roofline` stay against the published ones)."""
     from sketch_attention_amd import binding
     c = binding.sa_measure_ceilings()
+    read_gbs = binding.sa_measure_hbm_read()
     return {
         "mfma_bf16_16x16x32_tflops": round(c["mfma_bf16_tflops"], 1),
         "mfma_bf16_32x32x16_tflops": round(c["mfma_bf16_32x32_tflops"], 1), "mfma_bf16_spec_tflops": PEAK_BF16_TFLOPS,
-        "hbm_copy_gbs": round(c["copy_gbs"], 1), "hbm_spec_gbs": PEAK_HBM_GBS,
+        "hbm_copy_gbs": round(c["copy_gbs"], 1), "hbm_read_gbs": round(read_gbs, 1), "hbm_spec_gbs": PEAK_HBM_GBS,
         "valu_fp32_fma_tflops": round(c["valu_fma_tflops"], 1), "valu_fp32_spec_tflops": 157.3,
         "exp2_per_sec": float(f"{c['exp2_per_sec']:.4g}"),
         "how": "bf16 matrix-core loops of 16x16x32 and of 32x32x16 products; fp32 FMA and hardware exp2 loops of independent chains; "
-               "streaming copy of 1 GiB (read + write counted)",
+               "streaming copy of 1 GiB (read + write counted); read-only stream of 1 GiB",
     }
 
 

@@ -247,6 +247,16 @@ sa_status sa_measure_ceilings(double* mfma_bf16_tflops, double* mfma_bf16_32x32_
                               double* exp2_per_sec, double* copy_gbs, void* stream);
 
 /*
+ * sa_measure_hbm_read -- GB/s of a read-only stream over 1 GiB (four times
+ * the Infinity Cache): 16-byte loads, four or eight in flight per thread,
+ * the best over 4 to 32 work groups of 256 threads per compute unit.  The ceiling for kernels that read far more than they
+ * write, such as the compression at small k.  Allocates 1 GiB and a few
+ * bytes, runs on stream and synchronises it; read_gbs may be NULL.  Returns
+ * SA_ERR_OUT_OF_MEMORY or SA_ERR_DEVICE on failure.
+ */
+sa_status sa_measure_hbm_read(double* read_gbs, void* stream);
+
+/*
  * Stacked refinement (SequenceO1 close-reading page, section 2.2 "Stacked
  * Refinement and action-side fusion").  After one assignment and aggregation
  * the k x d state carries the user's information, so it queries the same raw

@@ -43,7 +43,7 @@ EXPORTED = (
     "sa_grad_read_kernel_timing",
     "sa_action_check_config", "sa_action_create", "sa_action_fuse", "sa_action_compress_batch", "sa_action_destroy",
     "sa_action_set_kernel_timing", "sa_action_read_kernel_timing",
-    "sa_measure_ceilings",
+    "sa_measure_ceilings", "sa_measure_hbm_read",
 )
 
 
@@ -131,6 +131,7 @@ def library() -> ctypes.CDLL:
         "sa_action_set_kernel_timing": (i32, [vp, i32]),
         "sa_action_read_kernel_timing": (i32, [vp, p_f64, p_i64]),
         "sa_measure_ceilings": (i32, [p_f64, p_f64, p_f64, p_f64, p_f64, vp]),
+        "sa_measure_hbm_read": (i32, [p_f64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -778,3 +779,11 @@ def sa_measure_ceilings(stream: Optional[torch.cuda.Stream] = None) -> dict:
            "sa_measure_ceilings")
     keys = ("mfma_bf16_tflops", "mfma_bf16_32x32_tflops", "valu_fma_tflops", "exp2_per_sec", "copy_gbs")
     return {k: v.value for k, v in zip(keys, vals)}
+
+
+def sa_measure_hbm_read(stream: Optional[torch.cuda.Stream] = None) -> float:
+    """GB/s of a read-only stream over 1 GiB on the current GPU (see include/sa.h)."""
+    v = ctypes.c_double()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    _check(library().sa_measure_hbm_read(ctypes.byref(v), _stream_ptr(stream, dev)), "sa_measure_hbm_read")
+    return v.value

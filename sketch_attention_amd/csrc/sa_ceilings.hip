@@ -81,7 +81,93 @@ __global__ __launch_bounds__(256) void copy_kernel(const f32x4* __restrict__ src
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
 }
 
+// Read-only stream: each thread XORs the bits of U independent 16-byte
+// loads per iteration (grid-stride), so the loads stay in flight together;
+// one lane stores only if the result hits a value the zeroed buffer never
+// gives.
+template <int U>
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, int64_t n, unsigned* sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint4 acc = {0u, 0u, 0u, 0u};
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc.x ^= v[u].x;
+      acc.y ^= v[u].y;
+      acc.z ^= v[u].z;
+      acc.w ^= v[u].w;
+    }
+  }
+  for (; i < n; i += stride) {
+    const uint4 a = src[i];
+    acc.x ^= a.x;
+    acc.y ^= a.y;
+    acc.z ^= a.z;
+    acc.w ^= a.w;
+  }
+  if ((acc.x | acc.y | acc.z | acc.w) == 0x5a5a5a5au) sink[blockIdx.x] = acc.x;
+}
+
 }  // namespace
+
+SA_API sa_status sa_measure_hbm_read(double* read_gbs, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return SA_ERR_DEVICE;
+  const int cus = prop.multiProcessorCount;
+  const int64_t bytes = int64_t(1) << 30;  // four times the Infinity Cache
+  const int64_t n = bytes / 16;
+  void* buf = nullptr;
+  unsigned* sink = nullptr;
+  if (hipMalloc(&buf, bytes) != hipSuccess) return SA_ERR_OUT_OF_MEMORY;
+  if (hipMalloc(&sink, (size_t)cus * 32 * sizeof(unsigned)) != hipSuccess) {
+    (void)hipFree(buf);
+    return SA_ERR_OUT_OF_MEMORY;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  sa_status st = SA_OK;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) st = SA_ERR_DEVICE;
+  if (st == SA_OK && hipMemsetAsync(buf, 0, bytes, s) != hipSuccess) st = SA_ERR_DEVICE;
+  double best = 0.0;
+  // the best over four or eight loads in flight per thread and 4 to 32 work
+  // groups of four waves per compute unit
+  for (int cfg = 0; st == SA_OK && cfg < 8; ++cfg) {
+    const dim3 grid(cus * (4 << (cfg % 4)));
+    const bool eight = cfg >= 4;
+    const uint4* src = static_cast<const uint4*>(buf);
+    auto launch = [&] {
+      if (eight)
+        hipLaunchKernelGGL(read_kernel<8>, grid, dim3(256), 0, s, src, n, sink);
+      else
+        hipLaunchKernelGGL(read_kernel<4>, grid, dim3(256), 0, s, src, n, sink);
+    };
+    launch();  // warm-up
+    const int reps = 10;
+    if (hipEventRecord(e0, s) != hipSuccess) { st = SA_ERR_DEVICE; break; }
+    for (int r = 0; r < reps; ++r) launch();
+    float ms = 0.f;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.f) {
+      st = SA_ERR_DEVICE;
+      break;
+    }
+    const double gbs = (double)bytes * reps / (ms * 1e-3) / 1e9;
+    if (gbs > best) best = gbs;
+  }
+  if (hipGetLastError() != hipSuccess) st = SA_ERR_DEVICE;
+  if (st == SA_OK && read_gbs) *read_gbs = best;
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(sink);
+  (void)hipFree(buf);
+  return st;
+}
 
 SA_API sa_status sa_measure_ceilings(double* mfma_bf16_tflops, double* mfma_bf16_32x32_tflops, double* valu_fma_tflops,
                                      double* exp2_per_sec, double* copy_gbs, void* stream) {
