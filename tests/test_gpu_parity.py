@@ -84,18 +84,19 @@ def test_long_full():
 
 
 def test_many_proto_full_sampled():
+    # a quarter of the users element by element (the fp64 oracle takes ~2 s per
+    # 100 000-row user at k = 1024), every user through the mass identity
     wl = W.named_workload("many_proto")
     got = run_gpu(wl)
-    _assert_parity(wl, got, users=[0, 13, 31])
+    _assert_parity(wl, got, users=[0, 4, 9, 13, 18, 22, 27, 31])
     _assert_mass_identity(wl, got)
 
 
-def test_ragged_full_sampled():
+def test_ragged_full():
+    # every one of the 64 users element by element, shortest and longest included
     wl = W.named_workload("ragged")
     got = run_gpu(wl)
-    lens = np.diff(wl.offsets)
-    users = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 33, 63})
-    _assert_parity(wl, got, users=users)
+    _assert_parity(wl, got)
     _assert_mass_identity(wl, got)
 
 
