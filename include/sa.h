@@ -105,9 +105,9 @@ sa_status sa_create(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dt
  * sa_create_ex -- sa_create with a choice of softmax axis.  SA_NORM_HISTORY
  * (the comparator) computes, per user, X~_j = sum_i a_ji x_i with
  * a_ji = exp(S_ji) / sum_i' exp(S_ji') over the user's rows (an empty history
- * gives zeros); it is implemented for SA_BF16 only (SA_ERR_UNSUPPORTED for
- * SA_F32) over the same d and k range.  sa_compress_batch then computes that
- * summary for the handle; all other behaviour is as for sa_create.
+ * gives zeros), for both dtypes over the same d and k range.
+ * sa_compress_batch then computes that summary for the handle; all other
+ * behaviour is as for sa_create.
  */
 sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, sa_dtype dtype,
                        const void* P, const void* W_Q, const void* W_K, sa_norm norm, void* stream);

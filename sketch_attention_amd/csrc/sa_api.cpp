@@ -67,12 +67,33 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // folded matrix in registers.
 // SA_PLAN="kw,waves_k,waves_rows,m_in_lds[,kind[,prefetch[,row_blocks[,score_buffers]]]]"
 // in the environment overrides the choice when that plan is compiled.
-// The comparator (softmax over the history axis) runs the streamed pass with
-// waves that never split a tile's rows: four waves of 32 prototypes for
-// k <= 128, else eight waves of 32 (k <= 256), 64 (k <= 512) or 128 (d = 64,
-// k <= 1024) prototypes each.
-Plan make_history_plan(int d, int k) {
+// The comparator (softmax over the history axis) runs, for bf16, the
+// streamed pass with waves that never split a tile's rows: four waves of 32
+// prototypes for k <= 128, else eight waves of 32 (k <= 256), 64 (k <= 512)
+// or 128 (d = 64, k <= 1024) prototypes each; for float32 the lockstep pass
+// (below).
+Plan make_history_plan(int dtype, int d, int k) {
   Plan p{};
+  if (dtype == SA_F32) {
+    // float32: the lockstep pass, four waves over 16, 32 or (d = 64) 64
+    // prototypes each and none over the rows, in independent blocks of 128
+    // (d = 128) or 256 (d = 64) prototypes beyond that
+    p.dtype = SA_F32;
+    p.d = d;
+    p.k = k;
+    p.kind = 0;
+    p.prefetch = 1;
+    p.row_blocks = 2;
+    p.score_buffers = 2;
+    p.waves_k = 4;
+    p.waves_rows = 1;
+    p.kw = k <= 64 ? 16 : (k <= 128 || d == 128 ? 32 : 64);
+    p.m_in_lds = 0;
+    p.blocks = (k + 4 * p.kw - 1) / (4 * p.kw);
+    p.k_pad = 4 * p.kw * p.blocks;
+    p.tile_rows = sa::kRowsPerWave;
+    return p;
+  }
   p.dtype = SA_BF16;
   p.d = d;
   p.k = k;
@@ -286,7 +307,6 @@ SA_API sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, s
   sa_status st = check_config(d, k, tau, dtype);
   if (st != SA_OK) return st;
   if (norm != SA_NORM_PROTOTYPES && norm != SA_NORM_HISTORY) return SA_ERR_INVALID_ARG;
-  if (norm == SA_NORM_HISTORY && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   if (P == nullptr || W_Q == nullptr || W_K == nullptr) return SA_ERR_INVALID_ARG;
   if (!aligned16(P) || !aligned16(W_Q) || !aligned16(W_K)) return SA_ERR_INVALID_ARG;
 
@@ -295,7 +315,7 @@ SA_API sa_status sa_create_ex(sa_handle* out, int32_t d, int32_t k, float tau, s
   hipStream_t s = static_cast<hipStream_t>(stream);
   h->tau = tau;
   h->norm = norm;
-  h->plan = norm == SA_NORM_HISTORY ? make_history_plan(d, k) : make_plan((int)dtype, d, k);
+  h->plan = norm == SA_NORM_HISTORY ? make_history_plan((int)dtype, d, k) : make_plan((int)dtype, d, k);
   const size_t elem = dtype == SA_BF16 ? 2 : 4;
   float* tmp = nullptr;
   hipDeviceProp_t prop;

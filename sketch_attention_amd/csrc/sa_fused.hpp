@@ -270,7 +270,15 @@ __device__ __forceinline__ float frag_c_t(const float* xt, int xts, int row, int
 // sum over this block's prototypes into stats[block][row], no aggregation;
 // 2 weights 2^(s' - L) with L the row's log2 sum over every block from
 // stats[row] (no row sums, no exact path).  Work group g takes prototype
-// block g % blocks in modes 1 and 2.
+// block g % blocks in modes 1, 2 and 3.
+// LM 3 is the comparator (FusedArgs::history_softmax; the SequenceO1 page's
+// section 3.1 baseline): the softmax runs over the user's rows, per
+// prototype, so no row statistics are exchanged between waves.  Per piece
+// each prototype keeps a running maximum m (raised only when a tile exceeds
+// it by more than 8 in log2 units, so every weight stays below 2^8), the sum
+// l of 2^(s' - m) over its rows and the accumulator in the scale of m; the
+// piece's partial is (acc, m, l) and reduce_history_kernel merges a user's
+// pieces and divides.  Waves never split a tile's rows in this mode.
 template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD, int LM = 0>
 __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) {
   using G = FusedGeom<T, D, KW, WJ, WI, MLDS>;
@@ -278,6 +286,8 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   using Frag = typename MF::Frag;
   constexpr int JB = G::JB, CB = G::CB, CS = G::CS, NT = G::NT, NW = G::NW, THREADS = G::THREADS;
   static_assert(!MLDS || sizeof(T) == 2, "LDS-resident M is bf16 only");
+  static_assert(LM != 3 || WI == 1, "the comparator keeps whole tile columns per wave");
+  constexpr int SLOT = LM == 3 ? G::KPAD * (D + 2) : G::KPAD * D;  // floats per partial slot
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
   T* const Xr = reinterpret_cast<T*>(lds);
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   // the exact shifted path recomputes the tile).
   auto softmax_fast = [&](f32x4 (&s)[2][JB]) {
     bool bad = false;
-    if constexpr (LM == 2) return;  // exponentials are taken against the stored log-sum-exp in finish_tile
+    if constexpr (LM >= 2) return;  // exponentials are taken against the stored log-sum-exp (2) or the prototype's maximum (3) in finish_tile
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       float p[4];
@@ -429,7 +439,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   };
 
   auto any_flag = [&]() {
-    if constexpr (LM == 2) return false;
+    if constexpr (LM >= 2) return false;
     int f = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) f |= flags[w];
@@ -543,8 +553,70 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
 
   // ---- after the exchange barrier: factors for the tile's rows, then the
   // aggregation (exact path in the rare tiles that need it).
-  auto finish_tile = [&](f32x4 (&acc)[JB][CB], f32x4 (&sc)[2][JB], const T* xt, int64_t t0, int rows_left) {
+  auto finish_tile = [&](f32x4 (&acc)[JB][CB], f32x4 (&sc)[2][JB], const T* xt, int64_t t0, int rows_left,
+                         float (&hm)[JB], float (&hl)[JB]) {
     float fac[2][4];
+    if constexpr (LM == 3) {
+      // rows past the piece take no weight
+      if (rows_left < NT) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = rw + 16 * ib + 4 * g + r < rows_left;
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) sc[ib][jb][r] = ok ? sc[ib][jb][r] : -INFINITY;
+          }
+      }
+      // the tile's maximum per prototype: lanes l16, l16 + 16, l16 + 32 and l16 + 48 share one
+      float mnew[JB];
+      bool grow = false;
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        float tm = sc[0][jb][0];
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tm = fmaxf(tm, sc[ib][jb][r]);
+        tm = fmaxf(tm, __shfl_xor(tm, 16));
+        tm = fmaxf(tm, __shfl_xor(tm, 32));
+        mnew[jb] = fmaxf(hm[jb], tm);
+        grow |= mnew[jb] > hm[jb] + 8.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // a piece's first tile, or a jump of a maximum
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          const float alpha = hm[jb] == -INFINITY ? 0.f : fast_exp2(hm[jb] - mnew[jb]);
+          hl[jb] *= alpha;
+          // accumulator register r of this lane holds prototype 16 jb + 4 g + r, whose factor lane 4 g + r has
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) acc[jb][cb][r] *= ar;
+          }
+          hm[jb] = mnew[jb];
+        }
+      }
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        const float mu = hm[jb] == -INFINITY ? 0.f : hm[jb];  // a prototype that saw no row (padding): weights 0
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w = fast_exp2(sc[ib][jb][r] - mu);
+            hl[jb] += w;
+            sc[ib][jb][r] = w;
+          }
+      }
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fac[ib][r] = 1.f;
+      aggregate(acc, sc, fac, xt);
+      return;
+    }
     if constexpr (LM == 2) {
       // 2^(s' - L) with the row's log-sum-exp over all blocks; rows past the piece weigh 0
 #pragma unroll
@@ -617,6 +689,12 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
     for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) acc[jb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float hm[JB], hl[JB];  // comparator: the piece's maximum and sum per prototype (this lane's rows)
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      hm[jb] = -INFINITY;
+      hl[jb] = 0.f;
+    }
 
     Quad<T> pre[G::BPT];
     auto prefetch = [&](int it) {
@@ -677,9 +755,9 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
       if constexpr (G::NXT == 2) {
         store_t((it & 1) ? Xt0 : Xt1);
         prefetch(it + 2);
-        finish_tile(acc, S, xt_cur, t0, rows_left);
+        finish_tile(acc, S, xt_cur, t0, rows_left, hm, hl);
       } else {
-        finish_tile(acc, S, Xt0, t0, rows_left);
+        finish_tile(acc, S, Xt0, t0, rows_left, hm, hl);
         __syncthreads();  // every wave is done reading Xt
         store_t(Xt0);
         prefetch(it + 2);
@@ -713,12 +791,24 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
       }
     }
     if (LM != 1 && wi == 0) {
-      float* dst = args.partial + ((int64_t)blk * (ngroups + args.users) + grp + u) * (int64_t)(G::KPAD * D);
+      float* dst = args.partial + ((int64_t)blk * (ngroups + args.users) + grp + u) * (int64_t)SLOT;
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           *reinterpret_cast<f32x4*>(dst + (((wj * JB + jb) * CB + cb) * 64 + lane) * 4) = acc[jb][cb];
+      if constexpr (LM == 3) {
+        // after the accumulators: the maxima [KPAD], then the sums over the piece's rows [KPAD]
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+          float lt = hl[jb] + __shfl_xor(hl[jb], 16);
+          lt += __shfl_xor(lt, 32);
+          if (g == 0) {
+            dst[G::KPAD * D + jbase + 16 * jb + l16] = hm[jb];
+            dst[G::KPAD * D + G::KPAD + jbase + 16 * jb + l16] = lt;
+          }
+        }
+      }
     }
 
     row = seg_end;
@@ -740,8 +830,18 @@ hipError_t launch_fused_lm(const FusedArgs& args, const Launch& l) {
 }
 // The two-phase modes are compiled for the float32 plan of 4 x 64 prototypes
 // per block only (float32 beyond 256 prototypes).
+// The comparator (history_softmax) is compiled for the float32 plans of four
+// waves over the prototypes and none over the rows (at d = 128 with at most
+// 32 prototypes per wave: 64 spill registers there).
 template <typename T, int D, int KW, int WJ, int WI, bool MLDS, bool PAD>
 hipError_t launch_fused_t(const FusedArgs& args, const Launch& l) {
+  if constexpr (sizeof(T) == 4 && WJ == 4 && WI == 1 && !MLDS && (D == 64 || KW <= 32)) {
+    if (args.history_softmax) {
+      if (args.lse_mode != 0) return hipErrorInvalidValue;
+      return launch_fused_lm<T, D, KW, WJ, WI, MLDS, PAD, 3>(args, l);
+    }
+  }
+  if (args.history_softmax) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 4 && KW == 64 && WJ == 4 && WI == 1 && !MLDS) {
     if (args.lse_mode == 1) return launch_fused_lm<T, D, KW, WJ, WI, MLDS, PAD, 1>(args, l);
     if (args.lse_mode == 2) return launch_fused_lm<T, D, KW, WJ, WI, MLDS, PAD, 2>(args, l);

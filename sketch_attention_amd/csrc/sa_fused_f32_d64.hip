@@ -1,4 +1,5 @@
-// Fused compression plans, d = 64: float32 inputs; four waves per group, folded matrix in registers.
+// Fused compression plans, d = 64: float32 inputs; four waves per group, folded matrix in registers
+// (four waves over 16, 32 or 64 prototypes each also run the comparator).
 // Each plan group is its own translation unit so groups compile in parallel
 // and can take their own code-generation options.
 #include "sa_fused.hpp"
@@ -11,6 +12,8 @@ hipError_t dispatch_f32_d64(const Plan& p, const FusedArgs& a, const Launch& l, 
   SA_PLAN(float, 64, 64, 1, 4, false)
   SA_PLAN(float, 64, 64, 2, 2, false)
   SA_PLAN(float, 64, 64, 4, 1, false)
+  SA_PLAN(float, 64, 16, 4, 1, false)  // comparator plans (with 4 x 64 above)
+  SA_PLAN(float, 64, 32, 4, 1, false)
   return hipErrorInvalidValue;
 }
 

@@ -120,8 +120,8 @@ def test_create_ex_validates_before_device_work():
     assert lib.sa_create_ex(None, 128, 16, f, 1, None, None, None, 1, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_create_ex(ctypes.byref(h), 128, 16, f, 1, None, None, None, 7, None) == B.SA_ERR_INVALID_ARG
     assert h.value is None
-    # the comparator is implemented for bf16 only
-    assert lib.sa_create_ex(ctypes.byref(h), 128, 16, f, 0, None, None, None, 1, None) == B.SA_ERR_UNSUPPORTED
+    # the comparator takes both dtypes: with null weights, float32 fails on the arguments, not the dtype
+    assert lib.sa_create_ex(ctypes.byref(h), 128, 16, f, 0, None, None, None, 1, None) == B.SA_ERR_INVALID_ARG
     assert lib.sa_create_ex(ctypes.byref(h), 96, 16, f, 1, None, None, None, 1, None) == B.SA_ERR_UNSUPPORTED
 
 

@@ -6,7 +6,9 @@ registers and in LDS, padded prototypes, and at d = 128 beyond 512 prototypes
 independent blocks of 512, each its own work groups), several users per work group,
 tiles cut by piece ends, maxima that jump between tiles, and the invariance
 the comparator has and Sketch Attention has not: duplicating every row of a
-history changes nothing."""
+history changes nothing.  The float32 comparator (lockstep pass, four waves
+of 16, 32 or 64 prototypes, independent blocks beyond that) is held to 1e-4
+on the same kinds of cases."""
 import numpy as np
 import pytest
 import torch
@@ -33,7 +35,7 @@ def _check(wl, got, users=None):
     err = max(normwise_err(g, w) for g, w in zip(sel, want))
     print(f"[history] {wl.name} err={err:.3e}", flush=True)
     assert np.isfinite(got).all()
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[wl.dtype], err
 
 
 CASES = [
@@ -93,3 +95,39 @@ def test_history_softmax_long_workload_sampled_user():
     wl = W.named_workload("long")
     got = _run(wl)
     _check(wl, got, users=[1])
+
+
+F32_CASES = [
+    (64, 16, [40, 3, 0, 1]),                    # 16 prototypes per wave
+    (64, 33, [1, 95, 33]),                      # padded to 64
+    (128, 100, [7, 500, 2]),                    # 32 per wave, padded to 128
+    (128, 128, [1, 64, 65, 1500, 0, 129]),
+    (64, 256, [300, 64, 31]),                   # d = 64, 64 per wave
+    (64, 700, [1, 900]),                        # d = 64, blocks of 256 (the last one padded)
+    (128, 300, [33, 1200]),                     # d = 128, blocks of 128
+    (128, 1024, [700, 31, 0]),
+]
+
+
+@pytest.mark.parametrize("d,k,lengths", F32_CASES, ids=lambda v: str(v))
+def test_history_softmax_f32_parity(d, k, lengths):
+    wl = W.make_workload(lengths=lengths, d=d, k=k, dtype="f32", seed=7 * k + d, name=f"hist-f32-{d}-{k}")
+    got = _run(wl)
+    for u, n in enumerate(lengths):
+        if n == 0:
+            assert not got[u].any()
+    _check(wl, got)
+
+
+def test_history_softmax_f32_jumping_maxima():
+    # rows scaled by 8 deep into the histories: maxima jump past the lazy threshold in later tiles
+    wl = W.make_workload(lengths=[3000, 500], d=128, k=128, dtype="f32", seed=9, name="hist-f32-jump")
+    for r in (1700, 1701, 2999, 3000 + 450):
+        wl.X[r] *= 8.0
+    _check(wl, _run(wl))
+
+
+def test_history_softmax_f32_many_users():
+    lengths = list(np.random.default_rng(4).integers(0, 90, size=280))  # two launches of users
+    wl = W.make_workload(lengths=lengths, d=64, k=64, dtype="f32", seed=22, name="hist-f32-many")
+    _check(wl, _run(wl))
