@@ -69,8 +69,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // in the environment overrides the choice when that plan is compiled.
 // The comparator (softmax over the history axis) runs, for bf16, the
 // streamed pass with waves that never split a tile's rows: four waves of 32
-// prototypes for k <= 128, else eight waves of 32 (k <= 256), 64 (k <= 512)
-// or 128 (d = 64, k <= 1024) prototypes each; for float32 the lockstep pass
+// prototypes for k <= 128, else eight waves of 32 (k <= 256; at d = 128 on
+// the 32x32x16 pass with the prototypes along the lanes), 64 (k <= 512) or
+// 128 (d = 64, k <= 1024) prototypes each; for float32 the lockstep pass
 // (below).
 Plan make_history_plan(int dtype, int d, int k) {
   Plan p{};
@@ -105,6 +106,7 @@ Plan make_history_plan(int dtype, int d, int k) {
     p.kw = 32; p.waves_k = 4; p.row_blocks = 4; p.score_buffers = 2;  // four-wave groups, two per CU
   } else if (k <= 256) {
     p.kw = 32; p.row_blocks = 4; p.score_buffers = 2;
+    if (d == 128) p.kind = 3;  // the 32x32x16 pass with the prototypes along the lanes (sa_wide.hpp)
   } else if (k <= 512 || d == 128) {
     p.kw = 64; p.row_blocks = 2; p.score_buffers = d == 128 ? 1 : 2;
   } else {

@@ -231,15 +231,29 @@ __global__ __launch_bounds__(kReduceLanes * kReduceShares) void reduce_history_k
   const int lane = threadIdx.x % kReduceLanes;
   const int q = threadIdx.x / kReduceLanes;
   const int p = blockIdx.x * kReduceLanes + lane;
-  int t = p >> 6;
-  const int cbs = a.d / 16, jbs = a.kw / 16;
-  const int cb = t % cbs;
-  t /= cbs;
-  const int jb = t % jbs;
-  const int wj = t / jbs;
   const int l = p & 63;
-  const int j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);  // within the block
-  const int c = 16 * cb + (l & 15);
+  int j0, c;  // first of the float4's four prototypes (within the block), its column
+  if (a.layout == 1) {
+    // 32x32 products: float4 ((jb CB + cb) 4 + vq) 64 + lane holds prototypes
+    // 32 jb + 8 vq + 4 (lane / 32) + 0..3 at column 32 cb + lane % 32
+    int t = p >> 6;
+    const int cbs = a.d / 32;
+    const int vq = t & 3;
+    t >>= 2;
+    const int cb = t % cbs;
+    const int jb = t / cbs;
+    j0 = 32 * jb + 8 * vq + 4 * (l >> 5);
+    c = 32 * cb + (l & 31);
+  } else {
+    int t = p >> 6;
+    const int cbs = a.d / 16, jbs = a.kw / 16;
+    const int cb = t % cbs;
+    t /= cbs;
+    const int jb = t % jbs;
+    const int wj = t / jbs;
+    j0 = wj * a.kw + 16 * jb + 4 * (l >> 4);
+    c = 16 * cb + (l & 15);
+  }
   HistPart x[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) x[r] = HistPart{-INFINITY, 0.f, 0.f};

@@ -40,6 +40,16 @@
 // leaves [2^-100, 2^100] sends its wave through an exact pass (a running
 // maximum over all prototypes, M from global memory).  One pass only: the
 // two phases of the pass for more prototypes run on sa_stream32.hpp.
+//
+// HS: the comparator (the page's section 3.1 baseline), softmax over the
+// user's rows per prototype.  This layout suits it: a prototype's 64 scores
+// of a tile sit in one lane and its half-wave partner, so the tile maximum
+// and the sum over rows are in-lane work plus one half-wave exchange, with no
+// exchange between waves.  Per piece each prototype keeps a running maximum m
+// (raised only when a tile exceeds it by more than 8 in log2 units, so every
+// weight stays below 2^8), the sum l of 2^(s' - m) and the accumulator in the
+// scale of m; the weights 2^(s' - m) go to the products as they are.  The
+// piece's partial is (acc, m, l), merged by reduce_history_kernel.
 #pragma once
 
 #include "sa_stream32.hpp"
@@ -109,8 +119,9 @@ __device__ __forceinline__ float bcast16(float x, int n) {
   }
 }
 
-template <bool PAD, bool PU>
+template <bool PAD, bool PU, bool HS = false>
 __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
+  static_assert(!(HS && PU), "the comparator shares one folded matrix");
   constexpr int D = 128, KW = 32, WJ = 8, NW = 8, NT = 64, KC = D / 16, CBK = D / 32, NS = 4;
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int SLOT_BYTES = NT * D * 2;          // one X tile
@@ -442,8 +453,19 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
   };
 
   // ---- partial of one (group, user) piece: float4 number ((wj CBK + cb) 4 + v / 4) 64 + lane of the slot
+  float hm = -INFINITY, hl = 0.f;  // comparator: the piece's maximum and this lane's sum for prototype jbase + l32
   auto flush = [&](f32x16 (&acc)[CBK], int u) {
-    float* dst = args.partial + (grp + u) * (int64_t)(KPAD * D);
+    float* dst = args.partial + (grp + u) * (int64_t)(HS ? KPAD * (D + 2) : KPAD * D);
+    if constexpr (HS) {
+      // after the accumulators: the maxima [KPAD], then the sums over the piece's rows [KPAD]
+      const float lt = pair32_sum(hl);
+      if (h == 0) {
+        dst[KPAD * D + jbase + l32] = hm;
+        dst[KPAD * D + KPAD + jbase + l32] = lt;
+      }
+      hm = -INFINITY;
+      hl = 0.f;
+    }
 #pragma unroll
     for (int cb = 0; cb < CBK; ++cb)
 #pragma unroll
@@ -458,6 +480,48 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
   f32x16 acc[CBK];
 #pragma unroll
   for (int cb = 0; cb < CBK; ++cb) acc[cb] = f32x16{};
+
+  // ---- comparator: rows past the piece out, the tile maximum of the lane's
+  // prototype (in-lane, then the half-wave partner), and when a maximum grows
+  // by more than 8 the rescale of its sum and accumulator rows (register v of
+  // acc holds prototype 8 (v / 4) + 4 h + v % 4, whose factor lane that is)
+  auto hs_max = [&](f32x16 (&sv)[2], int nv) {
+    if (nv < NT) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          sv[f][v] = 32 * f + 8 * (v >> 2) + 4 * h + (v & 3) < nv ? sv[f][v] : -INFINITY;
+    }
+    float tm = sv[0][0];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tm = fmaxf(tm, sv[f][v]);
+    const float mnew = fmaxf(hm, pair32_max(tm));
+    if (__builtin_amdgcn_ballot_w64(mnew > hm + 8.f) != 0) {  // a piece's first tile, or a jump of a maximum
+      const float alpha = hm == -INFINITY ? 0.f : fast_exp2(hm - mnew);
+      hl *= alpha;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float av = __shfl(alpha, 8 * (v >> 2) + 4 * h + (v & 3));
+#pragma unroll
+        for (int cb = 0; cb < CBK; ++cb) acc[cb][v] *= av;
+      }
+      hm = mnew;
+    }
+  };
+  // weights of row step rs, 2^(s' - m) (a prototype that saw no row, i.e. padding: 0)
+  auto hs_weights_rs = [&](bf16x8 (&a)[4], const f32x16 (&sv)[2], int rs) {
+    const int f = rs >> 1, o = 8 * (rs & 1);
+    const float mu = hm == -INFINITY ? 0.f : hm;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float w = fast_exp2(sv[f][o + e] - mu);
+      hl += w;
+      a[rs][e] = (bf16)w;
+    }
+  };
 
   const int64_t e0 = first_end - r_begin;
   Cursor cc{0, e0 < (int64_t)nrel ? (int)e0 : nrel, u_first};  // tile t
@@ -486,7 +550,7 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
   __syncthreads();
   affinity(S0, slot_of(0), no_hook);
   cursor_next(ca);
-  softmax_all(S0, 0);
+  if constexpr (!HS) softmax_all(S0, 0);
   wait_tiles(std::integral_constant<int, NS - 3>{});  // tile 1
   __syncthreads();
 
@@ -502,6 +566,31 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
     constexpr bool F = decltype(full)::value;
     issue_tile(cl, qn);
     const bool nxt = F || t + 1 < ntot;
+    if constexpr (HS) {
+      // the comparator: tile t's maximum and rescale, its weights in the shadow
+      // of tile t+1's affinity, then tile t's aggregation (no row statistics)
+      bf16x8 a[4];
+      bf16x8 B[2][CBK];
+      hs_max(Sa, cc.end - cc.row);
+      auto shadow_h = [&](int kc) {
+        if (kc < 4) hs_weights_rs(a, Sa, kc);
+        if (kc == KC - 1) agg_load(0, B[0], slot_of(q0));
+      };
+      if (nxt) {
+        affinity(Sb, slot_of(q1), shadow_h);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) shadow_h(kc);
+      }
+      cursor_next(ca);
+      aggregate(acc, a, B, slot_of(q0), no_hook);
+      if (cc.row + NT >= cc.end) flush(acc, cc.u);
+      cursor_next(cc);
+      cursor_next(cl);
+      wait_tiles(std::integral_constant<int, NS - 3>{});  // tile t+2
+      __syncthreads();
+      return;
+    }
     f32x4 pv[2][WJ / 4];
     combine_issue(pv, t & 1);
     float fr[2] = {1.f, 1.f}, lr[2] = {1.f, 1.f};
@@ -572,19 +661,23 @@ __global__ __launch_bounds__(512) void sa_wide_kernel(FusedArgs args) {
   wait_vm<0>();  // no DMA outlives the work group
 }
 
-template <bool PAD, bool PU>
+template <bool PAD, bool PU, bool HS>
 hipError_t launch_wide_t(const FusedArgs& a, const Launch& l) {
   if (l.start || l.stop)
-    hipExtLaunchKernelGGL((sa_wide_kernel<PAD, PU>), dim3(l.groups), dim3(512), 0, l.stream, l.start, l.stop, 0, a);
+    hipExtLaunchKernelGGL((sa_wide_kernel<PAD, PU, HS>), dim3(l.groups), dim3(512), 0, l.stream, l.start, l.stop, 0, a);
   else
-    hipLaunchKernelGGL((sa_wide_kernel<PAD, PU>), dim3(l.groups), dim3(512), 0, l.stream, a);
+    hipLaunchKernelGGL((sa_wide_kernel<PAD, PU, HS>), dim3(l.groups), dim3(512), 0, l.stream, a);
   return hipGetLastError();
 }
 
 template <bool PAD>
 hipError_t launch_wide_pad(const FusedArgs& a, const Launch& l) {
-  if (a.lse_mode != 0 || a.history_softmax) return hipErrorInvalidValue;  // one pass over the prototype axis only
-  return a.m_stride != 0 ? launch_wide_t<PAD, true>(a, l) : launch_wide_t<PAD, false>(a, l);
+  if (a.lse_mode != 0) return hipErrorInvalidValue;  // one pass
+  if (a.history_softmax) {
+    if (a.m_stride != 0 || a.blocks != 1) return hipErrorInvalidValue;  // one shared matrix, one block
+    return launch_wide_t<PAD, false, true>(a, l);
+  }
+  return a.m_stride != 0 ? launch_wide_t<PAD, true, false>(a, l) : launch_wide_t<PAD, false, false>(a, l);
 }
 
 }  // namespace sa
