@@ -143,8 +143,10 @@ SA_API sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actio
       h->spare.pop_back();
       e0 = h->spare.back();
       h->spare.pop_back();
-    } else if (hipEventCreateWithFlags(&e0, hipEventDisableSystemFence) != hipSuccess ||
-               hipEventCreateWithFlags(&e1, hipEventDisableSystemFence) != hipSuccess) {
+    } else if (hipEventCreateWithFlags(&e0, hipEventDisableSystemFence) != hipSuccess) {
+      return SA_ERR_DEVICE;
+    } else if (hipEventCreateWithFlags(&e1, hipEventDisableSystemFence) != hipSuccess) {
+      h->spare.push_back(e0);  // kept for the next timed call rather than leaked
       return SA_ERR_DEVICE;
     }
   }
