@@ -396,10 +396,14 @@ void sa_grad_destroy(sa_grad h);
  * embedding width nor the FFN width: here a_i = action_table[action_i] with
  * d_a columns and the gated layer has d_ff columns (parameters).
  *
- * sa_action_check_config -- SA_BF16 only, d in {64, 128}, d_a a multiple of 8
- * with d + d_a <= 256, d_ff a multiple of 64 (of 32 when d + d_a > 192 for
- * d = 128) and at most 4096, 1 <= n_actions <= 2^20; else SA_ERR_UNSUPPORTED
- * or SA_ERR_INVALID_ARG.
+ * sa_action_check_config -- d in {64, 128}, d_a a multiple of 8 with
+ * d + d_a <= 256, d_ff at most 4096 and, for SA_BF16, a multiple of 64 (of 32
+ * when d + d_a > 192 for d = 128), for SA_F32 a multiple of 32;
+ * 1 <= n_actions <= 2^20; else SA_ERR_UNSUPPORTED or SA_ERR_INVALID_ARG.
+ * SA_BF16 runs one fused pass (bf16 matrix-core products, float32
+ * accumulation, x rounded to bf16 once); SA_F32 gathers z into a staging
+ * buffer of the handle and runs the FFN as float32 matrix-core products, in
+ * passes of 32768 rows.
  *
  * sa_action_create -- device pointers in the dtype, row-major, 16-byte
  * aligned: action_table [n_actions][d_a] (may be NULL when d_a == 0),
@@ -414,12 +418,14 @@ sa_status sa_action_create(sa_action* out, int32_t d, int32_t d_a, int32_t d_ff,
 
 /*
  * sa_action_fuse -- X[i] = x_i for rows i < rows (enqueued on stream).
- *   E        device, bf16 [rows][d], 16-byte aligned
+ *   E        device, [rows][d] in the handle's dtype, 16-byte aligned
  *   actions  device, int32 [rows], 4-byte aligned; ids outside
  *            [0, n_actions) are clamped into it (the device cannot report them)
- *   X        device, bf16 [rows][d], 16-byte aligned, fully overwritten; it is
- *            the history input of sa_compress_batch
- * rows == 0 is a no-op.  Calls on one handle may overlap (no workspace).
+ *   X        device, [rows][d] in the dtype, 16-byte aligned, fully
+ *            overwritten; it is the history input of sa_compress_batch
+ * rows == 0 is a no-op.  SA_BF16: calls on one handle may overlap (no
+ * workspace).  SA_F32: the handle's staging buffers are reused, so calls on
+ * one handle must be ordered (one stream, or synchronised streams).
  */
 sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actions, int64_t rows, void* X, void* stream);
 
@@ -433,7 +439,7 @@ sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actions, int
  * timing and stream rules are those of sa_compress_batch on h, whose kernel
  * timing covers the fused kernel.  The result equals sa_action_fuse followed
  * by sa_compress_batch bit for bit.
- * SA_ERR_UNSUPPORTED (nothing enqueued) unless d = 128, h and a are on the
+ * SA_ERR_UNSUPPORTED (nothing enqueued) unless a is SA_BF16 with d = 128, h and a are on the
  * same device and h uses the one-pass plan of eight waves of 32 prototypes:
  * SA_BF16, d = 128, 128 < k <= 256, softmax over the prototypes.
  */

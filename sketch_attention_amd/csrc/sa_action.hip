@@ -255,6 +255,58 @@ hipError_t action_occupancy(int d, int kp, int* groups_per_cu) {
   return hipErrorInvalidValue;
 }
 
+// ---- float32 path: the rows z = [e; a; 0] gathered into a staging buffer,
+// then the FFN as float32 matrix-core products (launch_plain_ffn) with the
+// residual e added on output.
+namespace {
+
+// dst[c][r] = r < rows_in ? src[r][c] : 0 for c < cols, r < rows_pad
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const float* __restrict__ src, int rows_in, int cols,
+                                                            int rows_pad, float* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)cols * rows_pad) return;
+  const int c = (int)(i / rows_pad), r = (int)(i % rows_pad);
+  dst[i] = r < rows_in ? src[(int64_t)r * cols + c] : 0.f;
+}
+
+// Z[r] = [E[r]; table[clamp(actions[r])]; 0 ...] (k_pad floats), one float4 per thread
+__global__ __launch_bounds__(256) void gather_f32_kernel(const float* __restrict__ E, const int32_t* __restrict__ actions,
+                                                         const float* __restrict__ table, int64_t rows, int d, int d_a,
+                                                         int k_pad, int n_actions, float* __restrict__ Z) {
+  const int q = k_pad / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * q) return;
+  const int64_t r = i / q;
+  const int c = 4 * (int)(i % q);
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  if (c < d) {
+    v = *reinterpret_cast<const float4*>(E + r * d + c);
+  } else if (c < d + d_a) {
+    int a = actions[r];
+    a = a < 0 ? 0 : (a >= n_actions ? n_actions - 1 : a);
+    v = *reinterpret_cast<const float4*>(table + (int64_t)a * d_a + (c - d));
+  }
+  *reinterpret_cast<float4*>(Z + r * k_pad + c) = v;
+}
+
+}  // namespace
+
+hipError_t launch_transpose_pad(const float* src, int rows_in, int cols, int rows_pad, float* dst, hipStream_t s) {
+  const int64_t n = (int64_t)cols * rows_pad;
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows_in, cols,
+                     rows_pad, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_gather_f32(const float* E, const int32_t* actions, const float* table, int64_t rows, int d,
+                                    int d_a, int k_pad, int n_actions, float* Z, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = rows * (k_pad / 4);
+  hipLaunchKernelGGL(gather_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, E, actions, table, rows,
+                     d, d_a, k_pad, n_actions, Z);
+  return hipGetLastError();
+}
+
 int action_chunks_per_step(int d, int kp) {
   const int chunk = 2 * 32 * kp * 2 + d * 32 * 2;
   return 4 * chunk <= 144 * 1024 ? 2 : 1;

@@ -28,6 +28,7 @@ struct DeviceGuard {
 };
 
 constexpr int kMaxActionTypes = 1 << 20;
+constexpr int64_t kF32ChunkRows = 32768;  // float32 path: rows per staging pass
 
 }  // namespace
 
@@ -36,8 +37,18 @@ struct sa_action_s {
   int cu_count = 0;
   int groups_per_cu = 1;
   int d = 0, d_a = 0, d_ff = 0, n_actions = 0, kp = 0;
-  void* table = nullptr;   // bf16 [n_actions][d_a], a copy
-  void* packed = nullptr;  // packed weight chunks
+  sa_dtype dtype = SA_BF16;
+  void* table = nullptr;   // [n_actions][d_a] in the dtype, a copy
+  void* packed = nullptr;  // bf16: packed weight chunks
+  // float32: transposed weights (gate_t, up_t [d_ff][k_pad] with zero columns past d + d_a;
+  // down_t [d][d_ff]) and the staging buffers of one pass of kF32ChunkRows rows (Z [rows][k_pad],
+  // H [rows][d_ff]), owned by the handle
+  int k_pad = 0;
+  float* gate_t = nullptr;
+  float* up_t = nullptr;
+  float* down_t = nullptr;
+  float* stage_z = nullptr;
+  float* stage_h = nullptr;
   bool timing = false;
   std::vector<hipEvent_t> pending, spare;  // start/stop pairs
 };
@@ -47,6 +58,8 @@ namespace {
 void free_action(sa_action_s* h) {
   if (h->table) (void)hipFree(h->table);
   if (h->packed) (void)hipFree(h->packed);
+  for (float* p : {h->gate_t, h->up_t, h->down_t, h->stage_z, h->stage_h})
+    if (p) (void)hipFree(p);
   for (auto* v : {&h->pending, &h->spare})
     for (hipEvent_t e : *v)
       if (e) (void)hipEventDestroy(e);
@@ -58,7 +71,8 @@ void free_action(sa_action_s* h) {
 SA_API sa_status sa_action_check_config(int32_t d, int32_t d_a, int32_t d_ff, int32_t n_actions, sa_dtype dtype) {
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_INVALID_ARG;
   if (d < 1 || d_a < 0 || d_ff < 1 || n_actions < 1 || n_actions > kMaxActionTypes) return SA_ERR_INVALID_ARG;
-  if (dtype != SA_BF16 || (d != 64 && d != 128) || d_a % 8 != 0 || d + d_a > 256) return SA_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || d_a % 8 != 0 || d + d_a > 256) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_F32) return d_ff % 32 == 0 && d_ff <= 4096 ? SA_OK : SA_ERR_UNSUPPORTED;
   const int kp = sa::action_kpad(d, d_a);
   if (d_ff % (32 * sa::action_chunks_per_step(d, kp)) != 0 || d_ff > 4096) return SA_ERR_UNSUPPORTED;
   return SA_OK;
@@ -90,6 +104,37 @@ SA_API sa_status sa_action_create(sa_action* out, int32_t d, int32_t d_a, int32_
     return SA_ERR_DEVICE;
   }
   h->cu_count = prop.multiProcessorCount;
+  h->dtype = dtype;
+  if (dtype == SA_F32) {
+    const int kin = d + d_a;
+    h->k_pad = 16 * ((kin + 15) / 16);
+    const size_t fb = sizeof(float);
+    if (hipMalloc(&h->table, (size_t)n_actions * (d_a > 0 ? d_a : 4) * fb) != hipSuccess ||
+        hipMalloc(&h->gate_t, (size_t)d_ff * h->k_pad * fb) != hipSuccess ||
+        hipMalloc(&h->up_t, (size_t)d_ff * h->k_pad * fb) != hipSuccess ||
+        hipMalloc(&h->down_t, (size_t)d * d_ff * fb) != hipSuccess ||
+        hipMalloc(&h->stage_z, (size_t)kF32ChunkRows * h->k_pad * fb) != hipSuccess ||
+        hipMalloc(&h->stage_h, (size_t)kF32ChunkRows * d_ff * fb) != hipSuccess) {
+      free_action(h);
+      return SA_ERR_OUT_OF_MEMORY;
+    }
+    hipError_t e = hipSuccess;
+    if (d_a > 0)
+      e = hipMemcpyAsync(h->table, action_table, (size_t)n_actions * d_a * fb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = sa::launch_transpose_pad(static_cast<const float*>(W_gate), kin, d_ff, h->k_pad, h->gate_t, s);
+    if (e == hipSuccess)
+      e = sa::launch_transpose_pad(static_cast<const float*>(W_up), kin, d_ff, h->k_pad, h->up_t, s);
+    if (e == hipSuccess)
+      e = sa::launch_transpose_pad(static_cast<const float*>(W_down), d_ff, d, d_ff, h->down_t, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      free_action(h);
+      return SA_ERR_DEVICE;
+    }
+    *out = h;
+    return SA_OK;
+  }
   const size_t table_bytes = (size_t)n_actions * (d_a > 0 ? d_a : 8) * 2;
   if (hipMalloc(&h->table, table_bytes) != hipSuccess ||
       hipMalloc(&h->packed, sa::action_packed_bytes(d, h->kp, d_ff)) != hipSuccess) {
@@ -123,6 +168,21 @@ SA_API sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actio
     return SA_ERR_INVALID_ARG;
   DeviceGuard guard(h->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h->dtype == SA_F32) {
+    // passes of kF32ChunkRows rows through the handle's staging buffers, in stream order
+    const float* Ef = static_cast<const float*>(E);
+    float* Xf = static_cast<float*>(X);
+    for (int64_t r0 = 0; r0 < rows; r0 += kF32ChunkRows) {
+      const int64_t n = rows - r0 < kF32ChunkRows ? rows - r0 : kF32ChunkRows;
+      hipError_t e = sa::launch_action_gather_f32(Ef + r0 * h->d, actions + r0, static_cast<const float*>(h->table),
+                                                  n, h->d, h->d_a, h->k_pad, h->n_actions, h->stage_z, s);
+      if (e == hipSuccess)
+        e = sa::launch_plain_ffn(h->stage_z, n, h->k_pad, h->d, h->d_ff, h->gate_t, h->up_t, h->down_t, h->stage_h,
+                                 Ef + r0 * h->d, Xf + r0 * h->d, s);
+      if (e != hipSuccess) return SA_ERR_DEVICE;
+    }
+    return SA_OK;
+  }
   sa::ActionArgs a{};
   a.E = E;
   a.actions = actions;
@@ -161,7 +221,7 @@ SA_API sa_status sa_action_fuse(sa_action h, const void* E, const int32_t* actio
 SA_API sa_status sa_action_compress_batch(sa_action a, sa_handle h, const void* E, const int32_t* actions,
                                           const int64_t* offsets, int32_t num_users, float* out, void* stream) {
   if (a == nullptr || h == nullptr) return SA_ERR_INVALID_ARG;
-  if (a->d != 128) return SA_ERR_UNSUPPORTED;
+  if (a->d != 128 || a->dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
   DeviceGuard guard(a->device);
   sa::ActionSource src{E, actions, a->table, a->packed, a->n_actions, a->d_a, a->d_ff, a->kp, a->device};
   return sa::compress_actions(h, src, offsets, num_users, out, stream);

@@ -124,6 +124,12 @@ hipError_t launch_add_ln(const float* a, int64_t a_period, const float* b, const
 // and its rows are formed (and stored to ln->out) by the layer norm first.
 hipError_t launch_ffn(const LnPrologue* ln, const float* Z, int64_t rows, int d, int d_ff, const float* gate_t,
                       const float* up_t, const float* down_t, float* H, float* F, hipStream_t stream);
+// H = silu(Z W_gate) * (Z W_up) [rows][d_ff], X = resid + H W_down [rows][d_out] (float32), with the
+// weights given transposed (gate_t, up_t: [d_ff][k_in]; down_t: [d_out][d_ff]); k_in a multiple of 16,
+// d_out and d_ff multiples of 32.
+hipError_t launch_plain_ffn(const float* Z, int64_t rows, int k_in, int d_out, int d_ff, const float* gate_t,
+                            const float* up_t, const float* down_t, float* H, const float* resid, float* X,
+                            hipStream_t stream);
 
 // Plan groups, one translation unit each (see sa_fused_*.hip).  With
 // occ != nullptr they report occupancy instead of launching.

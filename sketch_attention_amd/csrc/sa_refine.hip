@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const float* a, int64_t a_p
 // are not stored.  Epilogues:
 //   EPI_STORE  C[r][c] = acc
 //   EPI_GATED  C[r][c] = silu(A Bt0^T) * (A Bt1^T)      (SwiGLU hidden layer)
+//   EPI_RESID  C[r][c] = A Bt0^T + A2[r][c]  (a residual added on output)
 //   EPI_FOLD   row r = u k + j of the per-user states -> M[u][j][c] =
 //              scale * acc rounded to T (rows k..k_pad-1 of each user are
 //              left as they are: zero from allocation)
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256) void add_ln_kernel(const float* a, int64_t a_p
 // by all waves of the group into LDS; the work groups of the first column
 // block also store them to ln_out (the block's output, needed again later).
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-enum { EPI_STORE = 0, EPI_GATED = 1, EPI_FOLD = 2 };
+enum { EPI_STORE = 0, EPI_GATED = 1, EPI_FOLD = 2, EPI_RESID = 3 };
 
 struct GemmArgs {
   const float* A;
@@ -277,6 +278,8 @@ __global__ __launch_bounds__(64 * KS) void small_gemm_kernel(const GemmArgs args
         // silu(gate) * up, with the hardware exp2 and reciprocal (about 1 ulp each)
         v = v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v)) * sum1[j][r];
         C[row * N + col] = (T)v;
+      } else if constexpr (EPI == EPI_RESID) {
+        C[row * N + col] = (T)(v + args.A2[row * N + col]);
       } else if constexpr (EPI == EPI_FOLD) {
         const int64_t u = row / args.k, jj = row % args.k;
         C[(u * args.k_pad + jj) * N + col] = (T)(args.scale * v);
@@ -390,6 +393,32 @@ hipError_t launch_ffn(const LnPrologue* ln, const float* Z, int64_t rows, int d,
   dn.N = d;
   dn.C = F;
   return launch_gemm<EPI_STORE, float, 2, 8, false>(dn, 0, s);
+}
+
+hipError_t launch_plain_ffn(const float* Z, int64_t rows, int k_in, int d_out, int d_ff, const float* gate_t,
+                            const float* up_t, const float* down_t, float* H, const float* resid, float* X,
+                            hipStream_t s) {
+  if (k_in % 16 != 0 || d_out % 32 != 0 || d_ff % 32 != 0 || rows < 0) return hipErrorInvalidValue;
+  if (rows == 0) return hipSuccess;
+  GemmArgs g{};
+  g.A = Z;
+  g.M = rows;
+  g.K = k_in;
+  g.Bt0 = gate_t;
+  g.Bt1 = up_t;
+  g.N = d_ff;
+  g.C = H;
+  hipError_t e = launch_gemm<EPI_GATED, float, 2, 2, false>(g, 0, s);
+  if (e != hipSuccess) return e;
+  GemmArgs dn{};
+  dn.A = H;
+  dn.M = rows;
+  dn.K = d_ff;
+  dn.Bt0 = down_t;
+  dn.N = d_out;
+  dn.C = X;
+  dn.A2 = resid;
+  return launch_gemm<EPI_RESID, float, 2, 8, false>(dn, 0, s);
 }
 
 }  // namespace sa

@@ -201,7 +201,12 @@ def test_action_entry_points_validate_before_device_work():
     assert lib.sa_action_check_config(128, 136, 64, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED  # d + d_a > 256
     assert lib.sa_action_check_config(128, 12, 64, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED   # d_a % 8
     assert lib.sa_action_check_config(96, 32, 64, 4, B.SA_BF16) == B.SA_ERR_UNSUPPORTED
-    assert lib.sa_action_check_config(128, 32, 64, 4, B.SA_F32) == B.SA_ERR_UNSUPPORTED
+    # float32: d_ff a multiple of 32, the same d, d_a and K limits
+    assert lib.sa_action_check_config(128, 32, 64, 4, B.SA_F32) == ok
+    assert lib.sa_action_check_config(64, 8, 96, 4, B.SA_F32) == ok
+    assert lib.sa_action_check_config(128, 32, 48, 4, B.SA_F32) == B.SA_ERR_UNSUPPORTED   # d_ff % 32
+    assert lib.sa_action_check_config(128, 136, 64, 4, B.SA_F32) == B.SA_ERR_UNSUPPORTED  # d + d_a > 256
+    assert lib.sa_action_check_config(96, 32, 64, 4, B.SA_F32) == B.SA_ERR_UNSUPPORTED
     assert lib.sa_action_check_config(128, 32, 64, 0, B.SA_BF16) == B.SA_ERR_INVALID_ARG
     assert lib.sa_action_check_config(128, -8, 64, 4, B.SA_BF16) == B.SA_ERR_INVALID_ARG
     h = ctypes.c_void_p()

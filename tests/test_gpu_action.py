@@ -137,3 +137,35 @@ def test_action_full_size(case):
     bound = TOL["bf16"] * f_max + 2.0 ** -8 * x_max
     print(f"[action] {name} rows={rows} err={err:.3e} bound={bound:.3e}", flush=True)
     assert err <= bound, (err, bound)
+
+
+F32_CASES = [
+    # name, rows, d, d_a, d_ff, n_actions: K = d + d_a padded to 16 (72 -> 80, 136 -> 144), both widths,
+    # d_ff multiples of 32, row counts around the 16-row product tiles and past one 32768-row pass
+    ("f32_d128_da64_ff256", 3000, 128, 64, 256, 8),
+    ("f32_d64_da8_ff96", 513, 64, 8, 96, 5),
+    ("f32_d128_da8_ff32", 17, 128, 8, 32, 3),
+    ("f32_d64_da0_ff64", 1, 64, 0, 64, 1),
+    ("f32_d128_da128_ff512", 40000, 128, 128, 512, 1000),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_action_f32_parity(case):
+    """float32 rows, gathered z and float32 matrix-core products: the whole of x within 1e-4 normwise
+    (max |X - x| <= 1e-4 max |x|) and its FFN part within 1e-4 of max |x - e| as well."""
+    name, rows, d, d_a, d_ff, n_act = case
+    inp = W.make_action_inputs(rows, d, d_a, d_ff, n_act, seed=rows + 1)
+    acts = inp["actions"].copy()
+    acts[::13] = n_act + 5  # clamped to the last type
+    with ActionFusion(_dev(inp["table"], torch.float32) if d_a else None, _dev(inp["W_gate"], torch.float32),
+                      _dev(inp["W_up"], torch.float32), _dev(inp["W_down"], torch.float32), n_act) as af:
+        got = af.fuse(_dev(inp["E"], torch.float32), _dev(acts, torch.int32)).cpu().numpy().astype(np.float64)
+        torch.cuda.synchronize()
+    want = AO.action_fuse(inp["E"], np.clip(acts, 0, n_act - 1), inp["table"], inp["W_gate"], inp["W_up"],
+                          inp["W_down"])
+    f_want = want - inp["E"]
+    err_x = float(np.abs(got - want).max()) / float(np.abs(want).max())
+    err_f = float(np.abs((got - inp["E"]) - f_want).max()) / float(np.abs(f_want).max())
+    print(f"[action] {name} x err={err_x:.3e} ffn err={err_f:.3e}", flush=True)
+    assert err_x <= TOL["f32"] and err_f <= TOL["f32"], (err_x, err_f)
