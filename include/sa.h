@@ -344,10 +344,15 @@ sa_status sa_stack_read_kernel_timing(sa_stack h, double* fused_ms, double* redu
  * with the weight gradients summed over the users of the batch.
  *
  * sa_grad_check_config -- what sa_grad_create returns for these scalars:
- * SA_BF16 only, d in {64, 128}, 1 <= k <= 1024 (else SA_ERR_UNSUPPORTED or
- * SA_ERR_INVALID_ARG as for sa_check_config).  Beyond 256 prototypes the
- * row statistics are gathered over blocks of 256 in a first pass, merged,
- * and the gradient of the folded matrix formed in a second pass per block.
+ * d in {64, 128}, 1 <= k <= 1024, SA_BF16 or SA_F32 (else
+ * SA_ERR_UNSUPPORTED or SA_ERR_INVALID_ARG as for sa_check_config).  SA_BF16
+ * runs two streamed passes; beyond 256 prototypes the row statistics are
+ * gathered over blocks of 256 in a first pass, merged, and the gradient of
+ * the folded matrix formed in a second pass per block.  SA_F32 works per
+ * user on passes of at most 65536 rows with the n x k score, weight and
+ * upstream matrices of a pass in the handle's workspace (float32
+ * matrix-core products; about 12 (65536 + d) k bytes at most), for callers
+ * that need float32 gradients rather than speed.
  *
  * sa_grad_create -- prepare the weights once (device pointers in the dtype,
  * as for sa_create; they are not used after the call returns).  The work is
@@ -361,10 +366,10 @@ sa_status sa_grad_create(sa_grad* out, int32_t d, int32_t k, float tau, sa_dtype
 /*
  * sa_grad_compute -- gradients of L for one ragged batch.
  *
- *   X            device, bf16 [offsets[num_users]][d], as for sa_compress_batch
+ *   X            device, [offsets[num_users]][d] in the dtype, as for sa_compress_batch
  *   offsets      host, int64 [num_users + 1], as for sa_compress_batch
  *   grad_sketch  device, float32 [num_users][k][d], dL/dX~ per user
- *   grad_X       device, bf16 [offsets[num_users]][d], fully overwritten
+ *   grad_X       device, [offsets[num_users]][d] in the dtype, fully overwritten
  *   grad_P       device, float32 [k][d]; grad_W_Q, grad_W_K float32 [d][d];
  *                fully overwritten (zero for a batch without rows)
  * All device buffers 16-byte aligned; X and grad_X may be NULL when the

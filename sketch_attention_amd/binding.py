@@ -528,7 +528,7 @@ def sa_grad_check_config(d: int, k: int, tau: float, dtype: Union[str, torch.dty
 
 def sa_grad_create(P: torch.Tensor, W_Q: torch.Tensor, W_K: torch.Tensor, tau: float,
                    stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
-    """Prepare the weights of the backward pass (bfloat16 only; see include/sa.h)."""
+    """Prepare the weights of the backward pass (bfloat16 or float32; see include/sa.h)."""
     for t, n in ((P, "P"), (W_Q, "W_Q"), (W_K, "W_K")):
         _device_tensor(t, n)
     if P.dtype not in _DTYPES or W_Q.dtype != P.dtype or W_K.dtype != P.dtype or P.dim() != 2:

@@ -32,6 +32,7 @@ SOURCES = [
     "sa_stream_d128.hip",
     "sa_refine.hip",
     "sa_grad.hip",
+    "sa_grad_f32.hip",
     "sa_grad_api.cpp",
     "sa_action.hip",
     "sa_action_sa.hip",

@@ -34,9 +34,8 @@ hipError_t launch_action_pack(int d, int kp, const void* Wg, const void* Wu, con
 hipError_t launch_action_fuse(int d, int kp, const ActionArgs& a, int groups, hipStream_t stream,
                               hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 hipError_t action_occupancy(int d, int kp, int* groups_per_cu);
-// float32 path: dst = src^T with the src rows padded by zeros to rows_pad ([cols][rows_pad]), and the
-// gathered rows Z [rows][k_pad] = [E; table[clamp(action)]; 0].
-hipError_t launch_transpose_pad(const float* src, int rows_in, int cols, int rows_pad, float* dst, hipStream_t stream);
+// float32 path (with launch_transpose_pad of sa_internal.h): the gathered rows
+// Z [rows][k_pad] = [E; table[clamp(action)]; 0].
 hipError_t launch_action_gather_f32(const float* E, const int32_t* actions, const float* table, int64_t rows, int d,
                                     int d_a, int k_pad, int n_actions, float* Z, hipStream_t stream);
 

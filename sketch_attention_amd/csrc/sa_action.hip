@@ -261,12 +261,12 @@ hipError_t action_occupancy(int d, int kp, int* groups_per_cu) {
 namespace {
 
 // dst[c][r] = r < rows_in ? src[r][c] : 0 for c < cols, r < rows_pad
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const float* __restrict__ src, int rows_in, int cols,
-                                                            int rows_pad, float* __restrict__ dst) {
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const float* __restrict__ src, int64_t rows_in, int cols,
+                                                            int64_t rows_pad, float* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)cols * rows_pad) return;
-  const int c = (int)(i / rows_pad), r = (int)(i % rows_pad);
-  dst[i] = r < rows_in ? src[(int64_t)r * cols + c] : 0.f;
+  const int64_t c = i / rows_pad, r = i % rows_pad;
+  dst[i] = r < rows_in ? src[r * cols + c] : 0.f;
 }
 
 // Z[r] = [E[r]; table[clamp(actions[r])]; 0 ...] (k_pad floats), one float4 per thread
@@ -291,8 +291,10 @@ __global__ __launch_bounds__(256) void gather_f32_kernel(const float* __restrict
 
 }  // namespace
 
-hipError_t launch_transpose_pad(const float* src, int rows_in, int cols, int rows_pad, float* dst, hipStream_t s) {
+hipError_t launch_transpose_pad(const float* src, int64_t rows_in, int cols, int64_t rows_pad, float* dst,
+                                hipStream_t s) {
   const int64_t n = (int64_t)cols * rows_pad;
+  if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(transpose_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, rows_in, cols,
                      rows_pad, dst);
   return hipGetLastError();

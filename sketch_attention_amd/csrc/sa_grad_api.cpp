@@ -19,6 +19,7 @@
 namespace {
 
 constexpr double kLog2e = 1.4426950408889634073599246810019;
+constexpr int64_t kF32ChunkRows = 65536;  // float32 path: rows per pass of one user
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -63,6 +64,15 @@ struct sa_grad_s {
   size_t partial_floats = 0;
   void* packed = nullptr;
   size_t packed_bytes = 0;
+  // float32 path: prototypes padded to k32 (a multiple of 32); Qp32 [k32][d] = tau P W_Q W_K^T with zero
+  // rows past k, QpT = Qp32^T [d][k32]; per call GT [d][k32], G32 [k32][d] (one user's upstream gradient,
+  // zero-padded); per pass of at most kF32ChunkRows rows S, DA [rows][k32], DST [k32][rows16], XT [d][rows16]
+  sa_dtype dtype = SA_BF16;
+  int k32 = 0;
+  float* Qp32 = nullptr;
+  float* QpT = nullptr;
+  float* f32ws = nullptr;  // GT, G32, D1 [k32][d], S, DA, DST, XT
+  size_t f32ws_floats = 0;
   bool timing = false;
   std::vector<EventPair> pending, spare;
 };
@@ -82,7 +92,8 @@ bool grow(T*& p, size_t& have, size_t need, size_t elem) {
 
 void free_handle(sa_grad_s* h) {
   for (void* p : {(void*)h->M, (void*)h->Qp, (void*)h->Q, (void*)h->P32, (void*)h->WQ32, (void*)h->WK32,
-                  (void*)h->dq, (void*)h->stats, (void*)h->bstats, (void*)h->partial, h->packed})
+                  (void*)h->dq, (void*)h->stats, (void*)h->bstats, (void*)h->partial, h->packed, (void*)h->Qp32,
+                  (void*)h->QpT, (void*)h->f32ws})
     if (p) (void)hipFree(p);
   for (auto* v : {&h->pending, &h->spare})
     for (auto& e : *v)
@@ -96,7 +107,8 @@ void free_handle(sa_grad_s* h) {
 SA_API sa_status sa_grad_check_config(int32_t d, int32_t k, float tau, sa_dtype dtype) {
   sa_status st = sa_check_config(d, k, tau, dtype);
   if (st != SA_OK) return st;
-  if (dtype != SA_BF16 || sa::grad_stats_waves(k) == 0) return SA_ERR_UNSUPPORTED;
+  if (dtype == SA_F32) return SA_OK;  // any k of sa_check_config
+  if (sa::grad_stats_waves(k) == 0) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
 
@@ -114,6 +126,30 @@ SA_API sa_status sa_grad_create(sa_grad* out, int32_t d, int32_t k, float tau, s
   h->d = d;
   h->k = k;
   h->tau = tau;
+  h->dtype = dtype;
+  if (dtype == SA_F32) {
+    h->k32 = 32 * ((k + 31) / 32);
+    const size_t kd = (size_t)k * d, k32d = (size_t)h->k32 * d, dd = (size_t)d * d;
+    if (hipGetDevice(&h->device) != hipSuccess || hipMalloc(&h->Q, kd * 4) != hipSuccess ||
+        hipMalloc(&h->P32, kd * 4) != hipSuccess || hipMalloc(&h->WQ32, dd * 4) != hipSuccess ||
+        hipMalloc(&h->WK32, dd * 4) != hipSuccess || hipMalloc(&h->dq, 3 * kd * 4) != hipSuccess ||
+        hipMalloc(&h->Qp32, k32d * 4) != hipSuccess || hipMalloc(&h->QpT, k32d * 4) != hipSuccess) {
+      free_handle(h);
+      return SA_ERR_OUT_OF_MEMORY;
+    }
+    hipError_t e = sa::launch_fold(0, P, W_Q, W_K, tau, k, h->k32, d, h->Q, h->Qp32, s);
+    if (e == hipSuccess) e = sa::launch_transpose_pad(h->Qp32, h->k32, d, h->k32, h->QpT, s);
+    if (e == hipSuccess) e = sa::launch_unfold(0, P, k, d, h->P32, s);
+    if (e == hipSuccess) e = sa::launch_unfold(0, W_Q, d, d, h->WQ32, s);
+    if (e == hipSuccess) e = sa::launch_unfold(0, W_K, d, d, h->WK32, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      free_handle(h);
+      return SA_ERR_DEVICE;
+    }
+    *out = h;
+    return SA_OK;
+  }
   h->waves = sa::grad_stats_waves(k);
   h->blocks = sa::grad_stats_blocks(k);
   h->k_pad = sa::kGradKW * h->waves * h->blocks;
@@ -153,6 +189,70 @@ SA_API void sa_grad_destroy(sa_grad h) {
   free_handle(h);
 }
 
+namespace {
+
+// float32 backward, per user and per pass of at most kF32ChunkRows rows (additive over rows), with
+// float32 matrix-core products (chain rule of section 2.1, as in include/sa.h):
+//   S = X Qp^T, DA = X G^T                [rows][k32]
+//   A = softmax_j(S), DS = A (DA - c)      (launch_softmax_grad_rows, in place)
+//   dX = A G + DS Qp                       [rows][d]
+//   D1 += DS^T X                           [k32][d], summed over every user and pass
+// then dQ = tau D1 W_K, dW_K = tau D1^T (P W_Q), dP = dQ W_Q^T, dW_Q = P^T dQ.
+sa_status compute_f32(sa_grad_s* h, const float* X, const int64_t* offsets, int32_t num_users, const float* G,
+                      float* dX, float* grad_P, float* grad_W_Q, float* grad_W_K, hipStream_t s) {
+  const int d = h->d, k = h->k, k32 = h->k32;
+  const size_t kd = (size_t)k * d, k32d = (size_t)k32 * d;
+  int64_t max_rows = 0;
+  for (int32_t u = 0; u < num_users; ++u) {
+    const int64_t n = offsets[u + 1] - offsets[u];
+    max_rows = n > max_rows ? n : max_rows;
+  }
+  const int64_t rc = max_rows < kF32ChunkRows ? max_rows : kF32ChunkRows;  // rows per pass
+  const int64_t rc16 = 16 * ((rc + 15) / 16);
+  const size_t need = 3 * k32d + 3 * (size_t)rc16 * k32 + (size_t)d * rc16;
+  if (!grow(h->f32ws, h->f32ws_floats, need, sizeof(float))) return SA_ERR_OUT_OF_MEMORY;
+  float* const GT = h->f32ws;
+  float* const G32 = GT + k32d;
+  float* const D1 = G32 + k32d;
+  float* const Sb = D1 + k32d;
+  float* const DA = Sb + (size_t)rc16 * k32;
+  float* const DST = DA + (size_t)rc16 * k32;
+  float* const XT = DST + (size_t)rc16 * k32;
+  hipError_t e = sa::launch_zero(D1, (int64_t)k32d, s);
+  for (int32_t u = 0; e == hipSuccess && u < num_users; ++u) {
+    const int64_t r0 = offsets[u], r1 = offsets[u + 1];
+    if (r1 == r0) continue;
+    // the user's upstream gradient, zero-padded to k32 rows: G^T [d][k32], then G [k32][d]
+    e = sa::launch_transpose_pad(G + (size_t)u * kd, k, d, k32, GT, s);
+    if (e == hipSuccess) e = sa::launch_transpose_pad(GT, d, k32, d, G32, s);
+    for (int64_t a = r0; e == hipSuccess && a < r1; a += rc) {
+      const int64_t n = r1 - a < rc ? r1 - a : rc;
+      const int64_t n16 = 16 * ((n + 15) / 16);
+      const float* Xa = X + a * d;
+      float* dXa = dX + a * d;
+      e = sa::launch_f32_gemm(Xa, n, d, h->Qp32, k32, Sb, nullptr, false, s);
+      if (e == hipSuccess) e = sa::launch_f32_gemm(Xa, n, d, G32, k32, DA, nullptr, false, s);
+      if (e == hipSuccess) e = sa::launch_softmax_grad_rows(Sb, DA, n, k, k32, s);
+      if (e == hipSuccess) e = sa::launch_f32_gemm(Sb, n, k32, GT, d, dXa, nullptr, false, s);
+      if (e == hipSuccess) e = sa::launch_f32_gemm(DA, n, k32, h->QpT, d, dXa, dXa, false, s);
+      if (e == hipSuccess) e = sa::launch_transpose_pad(DA, n, k32, n16, DST, s);
+      if (e == hipSuccess) e = sa::launch_transpose_pad(Xa, n, d, n16, XT, s);
+      if (e == hipSuccess) e = sa::launch_f32_gemm(DST, k32, (int)n16, XT, d, D1, D1, true, s);
+    }
+  }
+  float* const dQ = h->dq + 2 * kd;
+  // dQ = tau D1 W_K, dW_K = tau D1^T Q, dP = dQ W_Q^T, dW_Q = P^T dQ (D1's first k rows)
+  if (e == hipSuccess)
+    e = sa::launch_small_matmuls({D1, d, 1, h->WK32, d, 1, k, d, d, h->tau, dQ},
+                                 {D1, 1, d, h->Q, d, 1, d, d, k, h->tau, grad_W_K}, s);
+  if (e == hipSuccess)
+    e = sa::launch_small_matmuls({dQ, d, 1, h->WQ32, 1, d, k, d, d, 1.f, grad_P},
+                                 {h->P32, 1, d, dQ, d, 1, d, d, k, 1.f, grad_W_Q}, s);
+  return e == hipSuccess ? SA_OK : SA_ERR_DEVICE;
+}
+
+}  // namespace
+
 SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offsets, int32_t num_users,
                                  const float* grad_sketch, void* grad_X, float* grad_P, float* grad_W_Q,
                                  float* grad_W_K, void* stream) {
@@ -167,6 +267,8 @@ SA_API sa_status sa_grad_compute(sa_grad h, const void* X, const int64_t* offset
 
   DeviceGuard guard(h->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h->dtype == SA_F32) return compute_f32(h, static_cast<const float*>(X), offsets, num_users, grad_sketch,
+                                             static_cast<float*>(grad_X), grad_P, grad_W_Q, grad_W_K, s);
   const int d = h->d, k = h->k, k_pad = h->k_pad, chunks = k_pad / sa::kGradKW;
   const int nb = h->blocks, kb = sa::kGradKW * h->waves;  // blocks of pass 1 and prototypes per block
   const size_t kd = (size_t)k * d;

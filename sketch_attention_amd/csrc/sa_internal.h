@@ -127,6 +127,18 @@ hipError_t launch_ffn(const LnPrologue* ln, const float* Z, int64_t rows, int d,
 // H = silu(Z W_gate) * (Z W_up) [rows][d_ff], X = resid + H W_down [rows][d_out] (float32), with the
 // weights given transposed (gate_t, up_t: [d_ff][k_in]; down_t: [d_out][d_ff]); k_in a multiple of 16,
 // d_out and d_ff multiples of 32.
+// C = A Bt^T ([M][N] float32; A [M][K], Bt [N][K] row-major), plus resid[M][N] when resid is not null
+// (resid may be C itself); K a multiple of 16, N a multiple of 32.  long_k splits the reduction over
+// eight waves (for K in the thousands), else two.
+hipError_t launch_f32_gemm(const float* A, int64_t M, int K, const float* Bt, int N, float* C, const float* resid,
+                           bool long_k, hipStream_t stream);
+// dst = src^T with the rows of src (rows_in of them, cols wide) padded by zeros to rows_pad: [cols][rows_pad].
+hipError_t launch_transpose_pad(const float* src, int64_t rows_in, int cols, int64_t rows_pad, float* dst,
+                                hipStream_t stream);
+// Backward of the prototype-axis softmax, one row per wave (float32): for each of `rows` rows of S and DA
+// ([rows][ld], the first k columns real), A = softmax(S_i) over j < k, c_i = sum_j A_ij DA_ij, and
+// DS_ij = A_ij (DA_ij - c_i); A overwrites S and DS overwrites DA (columns k..ld-1 become 0).
+hipError_t launch_softmax_grad_rows(float* S, float* DA, int64_t rows, int k, int ld, hipStream_t stream);
 hipError_t launch_plain_ffn(const float* Z, int64_t rows, int k_in, int d_out, int d_ff, const float* gate_t,
                             const float* up_t, const float* down_t, float* H, const float* resid, float* X,
                             hipStream_t stream);

@@ -395,6 +395,23 @@ hipError_t launch_ffn(const LnPrologue* ln, const float* Z, int64_t rows, int d,
   return launch_gemm<EPI_STORE, float, 2, 8, false>(dn, 0, s);
 }
 
+hipError_t launch_f32_gemm(const float* A, int64_t M, int K, const float* Bt, int N, float* C, const float* resid,
+                           bool long_k, hipStream_t s) {
+  if (K % 16 != 0 || N % 32 != 0 || M < 0) return hipErrorInvalidValue;
+  if (M == 0) return hipSuccess;
+  GemmArgs g{};
+  g.A = A;
+  g.M = M;
+  g.K = K;
+  g.Bt0 = Bt;
+  g.N = N;
+  g.C = C;
+  g.A2 = resid;
+  if (resid != nullptr)
+    return long_k ? launch_gemm<EPI_RESID, float, 2, 8, false>(g, 0, s) : launch_gemm<EPI_RESID, float, 2, 2, false>(g, 0, s);
+  return long_k ? launch_gemm<EPI_STORE, float, 2, 8, false>(g, 0, s) : launch_gemm<EPI_STORE, float, 2, 2, false>(g, 0, s);
+}
+
 hipError_t launch_plain_ffn(const float* Z, int64_t rows, int k_in, int d_out, int d_ff, const float* gate_t,
                             const float* up_t, const float* down_t, float* H, const float* resid, float* X,
                             hipStream_t s) {

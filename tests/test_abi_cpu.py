@@ -172,7 +172,9 @@ def test_grad_entry_points_validate_before_device_work():
     assert lib.sa_grad_check_config(128, 1024, 0.1, B.SA_BF16) == B.SA_OK
     assert lib.sa_grad_check_config(64, 1000, 0.1, B.SA_BF16) == B.SA_OK
     assert lib.sa_grad_check_config(128, 1025, 0.1, B.SA_BF16) == B.SA_ERR_UNSUPPORTED
-    assert lib.sa_grad_check_config(128, 64, 0.1, B.SA_F32) == B.SA_ERR_UNSUPPORTED
+    assert lib.sa_grad_check_config(128, 64, 0.1, B.SA_F32) == B.SA_OK
+    assert lib.sa_grad_check_config(64, 1024, 0.1, B.SA_F32) == B.SA_OK
+    assert lib.sa_grad_check_config(128, 1025, 0.1, B.SA_F32) == B.SA_ERR_UNSUPPORTED
     assert lib.sa_grad_check_config(96, 64, 0.1, B.SA_BF16) == B.SA_ERR_UNSUPPORTED
     assert lib.sa_grad_check_config(128, 0, 0.1, B.SA_BF16) == B.SA_ERR_INVALID_ARG
     assert lib.sa_grad_check_config(128, 64, float("nan"), B.SA_BF16) == B.SA_ERR_INVALID_ARG

@@ -216,3 +216,38 @@ def test_grad_is_bitwise_deterministic():
         torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+F32_CASES = [
+    # name, d, k, lengths: float32 inputs and gradients, per-user passes of at most 65536 rows
+    ("f32_k16_d64", 64, 16, [1000, 0, 3]),
+    ("f32_k1_d128", 128, 1, [129, 5]),
+    ("f32_k100_d128_pad", 128, 100, [700, 0, 1, 1500]),
+    ("f32_k256_d64", 64, 256, [300, 64]),
+    ("f32_k1024_d128", 128, 1024, [600, 33]),
+    ("f32_k300_two_passes", 128, 300, [70000, 10]),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_grad_f32_parity(case):
+    """All four gradients within 1e-4 normwise (dX per user) of the fp64 oracle."""
+    name, d, k, lengths = case
+    wl = W.make_workload(lengths=lengths, d=d, k=k, dtype="f32", seed=41, name=name)
+    G = W.make_upstream_grad(len(lengths), k, d, seed=9)
+    _check(wl, G, _run(wl, G), tol=TOL["f32"])
+
+
+def test_grad_f32_empty_batch_and_repeat():
+    wl = W.make_workload(lengths=[0, 0], d=64, k=32, dtype="f32", seed=2, name="f32_empty")
+    G = W.make_upstream_grad(2, 32, 64, seed=1)
+    got = _run(wl, G)
+    for t in got[1:]:
+        assert not np.any(t)
+    wl2 = W.make_workload(lengths=[400, 90], d=64, k=32, dtype="f32", seed=3, name="f32_after_empty")
+    X, P, WQ, WK = to_device(wl2)
+    with SketchAttentionGrad(P, WQ, WK, wl2.tau) as h:
+        for _ in range(2):  # the same handle twice: the workspace is reused
+            out = [t.float().cpu().numpy() for t in h.backward(X, wl2.offsets, torch.from_numpy(G).cuda())]
+            torch.cuda.synchronize()
+            _check(wl2, G, out, tol=TOL["f32"])
