@@ -206,12 +206,87 @@ void full() {
   }
 }
 
+// float32 paths: the comparator (each sketch row a convex combination of the user's rows, so bounded by
+// their largest magnitude), the backward (finite weight gradients) and the action fusion (finite rows)
+void full_f32() {
+  Lcg g{777};
+  const int d = 64, k = 300, d_a = 8, d_ff = 64, n_actions = 5;
+  const std::vector<int64_t> lengths = {900, 0, 1, 70000};
+  std::vector<int64_t> off(1, 0);
+  for (int64_t len : lengths) off.push_back(off.back() + len);
+  const int users = (int)lengths.size();
+  const int64_t rows = off.back();
+  auto vals = [&](size_t n, float scale) {
+    std::vector<float> v(n);
+    for (auto& x : v) x = scale * g.next();
+    return v;
+  };
+  auto P = vals((size_t)k * d, 1.0f), WQ = vals((size_t)d * d, 0.2f), WK = vals((size_t)d * d, 0.2f),
+       X = vals((size_t)rows * d, 1.0f), G = vals((size_t)users * k * d, 1.0f);
+  float *dP = dev_copy(P), *dWQ = dev_copy(WQ), *dWK = dev_copy(WK), *dX = dev_copy(X), *dG = dev_copy(G);
+  float *dout = nullptr, *dgX = nullptr, *dgP = nullptr, *dgQ = nullptr, *dgK = nullptr;
+  EXPECT(dP && dWQ && dWK && dX && dG && hipMalloc((void**)&dout, (size_t)users * k * d * 4) == hipSuccess &&
+         hipMalloc((void**)&dgX, (size_t)rows * d * 4 + 16) == hipSuccess &&
+         hipMalloc((void**)&dgP, (size_t)k * d * 4) == hipSuccess &&
+         hipMalloc((void**)&dgQ, (size_t)d * d * 4) == hipSuccess && hipMalloc((void**)&dgK, (size_t)d * d * 4) == hipSuccess);
+  const float tau = 0.125f;
+  sa_handle h = nullptr;
+  EXPECT(sa_create_ex(&h, d, k, tau, SA_F32, dP, dWQ, dWK, SA_NORM_HISTORY, nullptr) == SA_OK);
+  if (h) {
+    EXPECT(sa_compress_batch(h, dX, off.data(), users, dout, nullptr) == SA_OK);
+    EXPECT(hipDeviceSynchronize() == hipSuccess);
+    std::vector<float> out((size_t)users * k * d);
+    EXPECT(hipMemcpy(out.data(), dout, out.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
+    for (int u = 0; u < users; ++u) {
+      float bound = 0.f;
+      for (int64_t i = off[u] * d; i < off[u + 1] * d; ++i) bound = std::fmax(bound, std::fabs(X[i]));
+      for (size_t i = (size_t)u * k * d; i < (size_t)(u + 1) * k * d; ++i) EXPECT(std::fabs(out[i]) <= bound * 1.0001f);
+    }
+    sa_destroy(h);
+  }
+  sa_grad gh = nullptr;
+  EXPECT(sa_grad_create(&gh, d, k, tau, SA_F32, dP, dWQ, dWK, nullptr) == SA_OK);
+  if (gh) {
+    for (int rep = 0; rep < 2; ++rep) {
+      EXPECT(sa_grad_compute(gh, dX, off.data(), users, dG, dgX, dgP, dgQ, dgK, nullptr) == SA_OK);
+      EXPECT(hipDeviceSynchronize() == hipSuccess);
+    }
+    std::vector<float> gk((size_t)d * d);
+    EXPECT(hipMemcpy(gk.data(), dgK, gk.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
+    for (float v : gk) EXPECT(std::isfinite(v));
+    sa_grad_destroy(gh);
+  }
+  auto table = vals((size_t)n_actions * d_a, 1.0f), Wg = vals((size_t)(d + d_a) * d_ff, 0.1f),
+       Wu = vals((size_t)(d + d_a) * d_ff, 0.1f), Wd = vals((size_t)d_ff * d, 0.1f);
+  std::vector<int32_t> acts((size_t)rows);
+  for (int64_t i = 0; i < rows; ++i) acts[i] = (int32_t)(i % (n_actions + 2)) - 1;  // some out of range: clamped
+  float *dT = dev_copy(table), *dWg = dev_copy(Wg), *dWu = dev_copy(Wu), *dWd = dev_copy(Wd);
+  int32_t* dA = dev_copy(acts);
+  sa_action ah = nullptr;
+  EXPECT(dT && dWg && dWu && dWd && dA &&
+         sa_action_create(&ah, d, d_a, d_ff, n_actions, SA_F32, dT, dWg, dWu, dWd, nullptr) == SA_OK);
+  if (ah) {
+    EXPECT(sa_action_fuse(ah, dX, dA, rows, dgX, nullptr) == SA_OK);
+    EXPECT(hipDeviceSynchronize() == hipSuccess);
+    std::vector<float> xr((size_t)rows * d);
+    EXPECT(hipMemcpy(xr.data(), dgX, xr.size() * 4, hipMemcpyDeviceToHost) == hipSuccess);
+    for (float v : xr) EXPECT(std::isfinite(v));
+    sa_action_destroy(ah);
+  }
+  for (void* p : {(void*)dP, (void*)dWQ, (void*)dWK, (void*)dX, (void*)dG, (void*)dout, (void*)dgX, (void*)dgP,
+                  (void*)dgQ, (void*)dgK, (void*)dT, (void*)dWg, (void*)dWu, (void*)dWd, (void*)dA})
+    (void)hipFree(p);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
   const bool run_full = argc > 1 && std::strcmp(argv[1], "full") == 0;
   validate();
-  if (run_full) full();
+  if (run_full) {
+    full();
+    full_f32();
+  }
   std::printf("sa_host_check %s: %d failure(s)\n", run_full ? "full" : "validate", failures);
   std::fflush(stdout);
   std::fflush(stderr);
