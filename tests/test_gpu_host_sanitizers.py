@@ -2,8 +2,9 @@
 on a GPU (tests/sanitize/sa_host_check.cpp in `full` mode): create, compute and
 destroy through the compression (both entry points, ragged batches with empty
 users, more users than one launch, the two-phase prototype counts) and the
-backward, checking statuses and the mass identity; the device code is the
-library's own.  A sanitizer report aborts the program."""
+backward, checking statuses and the mass identity, then the float32
+comparator, backward and action fusion; the device code is the library's
+own.  A sanitizer report aborts the program."""
 import os
 import subprocess
 
