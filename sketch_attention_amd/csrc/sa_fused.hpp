@@ -119,6 +119,23 @@ __device__ __forceinline__ float rows4_sum_scatter(const float (&p)[4], int l16)
   return z;
 }
 
+// ------------------------------------------------- work group -> block
+// Passes split over prototype blocks launch nblk work groups per row range.
+// Work groups are dealt to the 8 XCDs in turn (XCD = index mod 8), so when
+// the row ranges come in multiples of 8 the nblk blocks of one range take
+// indices 8 apart: one XCD, dispatched together, and the range's X tiles,
+// read once per block, meet in that XCD's L2.  Otherwise block = index mod
+// nblk, range = index / nblk.
+struct GroupBlock {
+  int64_t grp;  // row range
+  int blk;      // prototype block
+};
+__device__ __forceinline__ GroupBlock group_block(unsigned bi, unsigned grid, int nblk) {
+  const unsigned nb = (unsigned)nblk;
+  if (nb > 1 && (grid / nb) % 8u == 0) return {(int64_t)(8u * (bi / 8u / nb) + bi % 8u), (int)((bi / 8u) % nb)};
+  return {(int64_t)(bi / nb), (int)(bi % nb)};
+}
+
 // ------------------------------------------------------ static geometry
 // NW waves per work group: WJ split the prototypes (KW each), WI = NW / WJ
 // split the rows of a tile (32 rows each).  The transposed tile copy Xt is
@@ -269,8 +286,9 @@ __device__ __forceinline__ float frag_c_t(const float* xt, int xts, int row, int
 // LM (two-phase modes, FusedArgs::lse_mode): 0 one pass; 1 each row's log2
 // sum over this block's prototypes into stats[block][row], no aggregation;
 // 2 weights 2^(s' - L) with L the row's log2 sum over every block from
-// stats[row] (no row sums, no exact path).  Work group g takes prototype
-// block g % blocks in modes 1, 2 and 3.
+// stats[row] (no row sums, no exact path).  In modes 1, 2 and 3 the work
+// groups split over the row ranges and the prototype blocks as group_block
+// deals them.
 // LM 3 is the comparator (FusedArgs::history_softmax; the SequenceO1 page's
 // section 3.1 baseline): the softmax runs over the user's rows, per
 // prototype, so no row statistics are exchanged between waves.  Per piece
@@ -310,7 +328,8 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
   const int rw = wi * kRowsPerWave;  // first tile row of this wave
   const int jbase = wj * KW;         // first prototype of this wave (within the block)
   const int nblk = LM ? args.blocks : 1;
-  const int blk = LM ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  const GroupBlock gb = group_block(blockIdx.x, gridDim.x, nblk);
+  const int blk = LM ? gb.blk : 0;
   const T* const X = static_cast<const T*>(args.X);
   const T* const Mg = static_cast<const T*>(args.M) + (int64_t)blk * G::KPAD * D;
   const int k = args.k - blk * G::KPAD;  // real prototypes of this block (may exceed KPAD)
@@ -318,7 +337,7 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_fused_kernel(FusedArgs args) 
 
   const int64_t rows = args.rows;
   const int64_t ngroups = gridDim.x / nblk;
-  const int64_t grp = blockIdx.x / nblk;
+  const int64_t grp = gb.grp;
   const int64_t r_begin = grp * rows / ngroups;
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;

@@ -64,14 +64,15 @@ __global__ __launch_bounds__(64 * WJ) void grad_stats_kernel(GradStatsArgs args)
   // prototype block (phases 1 and 2): prototypes KPAD blk .. of M and G
   constexpr int phase = PHASE;  // args.phase, as a template parameter: one block compiles as before
   const int nblk = phase ? args.blocks : 1;
-  const int blk = phase ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  const GroupBlock gb = group_block(blockIdx.x, gridDim.x, nblk);  // the blocks of a row range on one XCD
+  const int blk = phase ? gb.blk : 0;
   const int jbase = wj * KW;                // within the block
   const int jg = blk * KPAD + jbase;        // first global prototype of this wave
   const int k = args.k;
   const bf16* const X = static_cast<const bf16*>(args.X);
   const bf16* const M = static_cast<const bf16*>(args.M) + (int64_t)blk * KPAD * D;
 
-  const int64_t rows = args.rows, ngroups = gridDim.x / nblk, grp = blockIdx.x / nblk;
+  const int64_t rows = args.rows, ngroups = gridDim.x / nblk, grp = gb.grp;
   const int64_t r_begin = grp * rows / ngroups, r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;  // the host launches at most one group per row
 

@@ -49,7 +49,8 @@ struct FusedArgs {
   // rows of M): lse_mode 1 writes each row's log2 sum_j 2^s'_ji over every
   // block into stats [blocks][rows]; lse_mode 2 reads the row's log2 sum over
   // all prototypes from stats [rows] and aggregates 2^(s' - that); 0: the
-  // one-pass kernel.  Work group g handles block g % blocks.
+  // one-pass kernel.  The grid is row ranges x blocks (the blocks of one row
+  // range on one XCD when the ranges come in multiples of 8).
   int32_t lse_mode;
   int32_t blocks;
   float* stats;

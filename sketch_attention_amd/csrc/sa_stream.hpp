@@ -278,18 +278,18 @@ __global__ __launch_bounds__(64 * WJ * WI) void sa_stream_kernel(FusedArgs args)
   const int rw = wi * RW;     // first tile row of this wave
   const int jbase = wj * KW;  // first prototype of this wave
   // the comparator beyond one block of prototypes (its softmax is per
-  // prototype, so blocks need no merge): work group g handles prototype block
-  // g % blocks (consecutive groups read the same rows at about the same time)
-  // for row range g / blocks
+  // prototype, so blocks need no merge): the blocks of a row range run on one
+  // XCD (group_block)
   const int nblk = HS ? args.blocks : 1;
-  const int blk = HS ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  const GroupBlock gb = group_block(blockIdx.x, gridDim.x, nblk);
+  const int blk = HS ? gb.blk : 0;
   const bf16* const X = static_cast<const bf16*>(args.X);
   const bf16* const Mg = static_cast<const bf16*>(args.M) + (int64_t)blk * G::KPAD * D;
   const int k = args.k - blk * G::KPAD;  // real prototypes of this block (may exceed KPAD)
 
   const int64_t rows = args.rows;
   const int64_t ngroups = gridDim.x / nblk;
-  const int64_t grp = blockIdx.x / nblk;
+  const int64_t grp = gb.grp;
   const int64_t r_begin = grp * rows / ngroups;
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;

@@ -147,14 +147,15 @@ __global__ __launch_bounds__(512) void sa_stream32_kernel(FusedArgs args) {
   const int jbase = wj * KW;
 
   const int nblk = LM ? args.blocks : 1;
-  const int blk = LM ? (int)(blockIdx.x % (unsigned)nblk) : 0;
+  const int64_t ngroups = gridDim.x / nblk;
+  const GroupBlock gb = group_block(blockIdx.x, gridDim.x, nblk);  // the nblk blocks of a row range on one XCD
+  const int blk = LM ? gb.blk : 0;
+  const int64_t grp = gb.grp;
   const bf16* const X = static_cast<const bf16*>(args.X);
   const bf16* const Mg = static_cast<const bf16*>(args.M) + (int64_t)blk * KPAD * D;
   const int k = args.k - blk * KPAD;  // real prototypes of this block (may exceed KPAD)
 
   const int64_t rows = args.rows;
-  const int64_t ngroups = gridDim.x / nblk;
-  const int64_t grp = blockIdx.x / nblk;
   const int64_t r_begin = grp * rows / ngroups;
   const int64_t r_end = (grp + 1) * rows / ngroups;
   if (r_begin >= r_end) return;
